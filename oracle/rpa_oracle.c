@@ -1,0 +1,243 @@
+/*
+ * CPU oracle for ragged paged GQA attention — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load or call this library. It shares no code, header or constant with
+ * the HIP library; it reads the same raw input bits and computes the plain
+ * definition in f64, one (token, q head) row at a time, keys in increasing
+ * order, so its results are reproducible bit for bit.
+ *
+ * What it computes follows the ragged paged attention kernel page
+ * (zml platforms/tpu/ragged_paged.zig):
+ *   - `Cfg`: head counts, page geometry, sm_scale, soft_cap, k_scale/v_scale,
+ *     is_causal, sliding_window;
+ *   - `run`, operand list: q [T, Hq, D], kv_pages [P, page, 2*Hkv, D],
+ *     kv_lens, page_indices, cu_q_lens, num_seqs;
+ *   - `createKvAsyncCopyDescriptors`: key j of a sequence lives in physical
+ *     page page_indices[seq, j / page_size], slot j % page_size;
+ *   - `stridedLoadKv`: combined head 2h holds K of kv head h, 2h+1 holds V;
+ *   - `run`, per-kv-head step: dequant x * k_scale (v_scale), q head n reads
+ *     kv head n / (Hq/Hkv);
+ *   - `flashAttention`: scores q.k * sm_scale, then soft-cap
+ *     c*tanh(x/c), then the causal mask (query i of a sequence sits at
+ *     position kv_len - q_len + i and sees keys at positions <= its own),
+ *     then the sliding-window mask (key j hidden when pos - window >= j),
+ *     then softmax over the visible keys and the product with V.
+ * The kernel page reaches that result blockwise with an online softmax; the
+ * oracle writes the plain definition out instead: max, exp, sum, weighted
+ * sum of V, all over the full visible key set at once.
+ *
+ * Readings where the page is silent (listed with the design notes):
+ *   - the log-sum-exp output, natural log of sum exp(score) over visible keys;
+ *   - a row with no visible key gets out = 0 and lse = -inf;
+ *   - e4m3fn decode is the OCP FP8 definition (bias 7, subnormals at
+ *     exponent 0, S.1111.111 is NaN, no infinities); the page only names the
+ *     dtype;
+ *   - dequantised values are code*scale exactly (f64), not re-rounded to the
+ *     q dtype.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_KV_BF16 0
+#define ORACLE_KV_E4M3FN 1
+
+typedef struct {
+  int32_t num_q_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t total_num_pages;
+  int32_t page_size;
+  int32_t max_num_seqs;
+  int32_t pages_per_seq;
+  int32_t kv_dtype;       /* ORACLE_KV_BF16 or ORACLE_KV_E4M3FN */
+  int32_t is_causal;      /* 0 or 1 */
+  int32_t sliding_window; /* <= 0: no window */
+  int32_t has_soft_cap;   /* 0 or 1 */
+  double sm_scale;
+  double soft_cap;
+  double k_scale; /* 1.0 when absent */
+  double v_scale; /* 1.0 when absent */
+} oracle_cfg;
+
+/* bf16 bits are the upper half of an IEEE binary32 value. */
+double oracle_bf16_to_f64(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* OCP FP8 E4M3 ("fn": finite, one NaN pattern per sign): 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits. Exponent 0 encodes subnormals
+ * m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; everything else is
+ * (1 + m/8) * 2^(e-7). */
+double oracle_e4m3fn_to_f64(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* Soft-cap of the kernel page's `Cfg`/`flashAttention`: c * tanh(x / c). */
+double oracle_soft_cap(double x, double c) { return c * tanh(x / c); }
+
+static double kv_elem(const oracle_cfg* c, const void* kv_pages, int64_t idx) {
+  if (c->kv_dtype == ORACLE_KV_E4M3FN) return oracle_e4m3fn_to_f64(((const uint8_t*)kv_pages)[idx]);
+  return oracle_bf16_to_f64(((const uint16_t*)kv_pages)[idx]);
+}
+
+/* Flat index of element d of combined head `comb` for key j of sequence s,
+ * or -1 when the page table does not give a valid physical page. */
+static int64_t kv_index(const oracle_cfg* c, const int32_t* page_indices, int s, int64_t j, int comb, int d) {
+  int64_t logical = j / c->page_size;
+  if (logical >= c->pages_per_seq) return -1;
+  int32_t phys = page_indices[(int64_t)s * c->pages_per_seq + logical];
+  if (phys < 0 || phys >= c->total_num_pages) return -1;
+  int64_t slot = j % c->page_size;
+  return (((int64_t)phys * c->page_size + slot) * (2 * c->num_kv_heads) + comb) * c->head_dim + d;
+}
+
+/* Masks of the kernel page's `flashAttention`: with is_causal a key at
+ * position j is hidden from the query at position `pos` when pos < j; with a
+ * window w it is also hidden when pos - w >= j. Keys at j >= kv_len are never
+ * iterated. */
+static int key_visible(const oracle_cfg* c, int64_t j, int64_t pos) {
+  if (c->is_causal && j > pos) return 0;
+  if (c->sliding_window > 0 && pos - c->sliding_window >= j) return 0;
+  return 1;
+}
+
+/* One output row (token, q head n). Returns 1 if the token is a padding
+ * token (no sequence owns it), 0 on success, -1 on invalid metadata (the row
+ * is then filled with NaN). `scores` is caller scratch of >= kv_len doubles. */
+static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+                      const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, int64_t token, int n,
+                      double* out_row, double* lse, double** scores, int64_t* scores_cap) {
+  const int D = c->head_dim;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  int s = -1;
+  for (int i = 0; i < num_seqs; ++i) {
+    if (token >= cu_q_lens[i] && token < cu_q_lens[i + 1]) {
+      s = i;
+      break;
+    }
+  }
+  if (s < 0) return 1;
+  const int64_t q_len = cu_q_lens[s + 1] - cu_q_lens[s];
+  const int64_t i_tok = token - cu_q_lens[s];
+  const int64_t kv_len = kv_lens[s];
+  const int h = n / G;
+  const int64_t pos = kv_len - q_len + i_tok; /* position of this query among the keys */
+
+  if (kv_len > *scores_cap) {
+    free(*scores);
+    *scores = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
+    *scores_cap = kv_len;
+  }
+  double* sc = *scores;
+  const uint16_t* qrow = q + (token * c->num_q_heads + n) * (int64_t)D;
+
+  /* scores of the visible keys */
+  int64_t n_vis = 0;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < kv_len; ++j) {
+    if (!key_visible(c, j, pos)) continue;
+    int64_t base = kv_index(c, page_indices, s, j, 2 * h, 0);
+    if (base < 0) goto invalid;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += oracle_bf16_to_f64(qrow[d]) * (kv_elem(c, kv_pages, base + d) * c->k_scale);
+    double x = dot * c->sm_scale;
+    if (c->has_soft_cap) x = oracle_soft_cap(x, c->soft_cap);
+    sc[j] = x;
+    /* NaN-propagating maximum, as the kernel page's row max */
+    if (n_vis == 0 || isnan(x) || x > m) m = x;
+    ++n_vis;
+  }
+  for (int d = 0; d < D; ++d) out_row[d] = 0.0;
+  if (n_vis == 0) {
+    *lse = -INFINITY;
+    return 0;
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < kv_len; ++j) {
+    if (!key_visible(c, j, pos)) continue;
+    double p = exp(sc[j] - m);
+    l += p;
+    int64_t base = kv_index(c, page_indices, s, j, 2 * h + 1, 0);
+    for (int d = 0; d < D; ++d) out_row[d] += p * (kv_elem(c, kv_pages, base + d) * c->v_scale);
+  }
+  for (int d = 0; d < D; ++d) out_row[d] /= l;
+  *lse = m + log(l);
+  return 0;
+
+invalid:
+  for (int d = 0; d < D; ++d) out_row[d] = NAN;
+  *lse = NAN;
+  return -1;
+}
+
+/* Rows listed by (tokens[r], heads[r]); out is [n_rows, D], lse [n_rows].
+ * status[r] receives the per-row code of oracle_row. */
+int oracle_rows(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+                const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, const int64_t* tokens,
+                const int32_t* heads, int64_t n_rows, double* out, double* lse, int32_t* status, int nthreads) {
+  if (c->num_kv_heads <= 0 || c->num_q_heads % c->num_kv_heads != 0) return -1;
+  if (num_seqs < 0 || num_seqs > c->max_num_seqs) return -1;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1) reduction(+ : bad)
+  {
+    double* scores = NULL;
+    int64_t cap = 0;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int st = oracle_row(c, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, tokens[r], heads[r],
+                          out + r * (int64_t)c->head_dim, lse + r, &scores, &cap);
+      status[r] = st;
+      if (st < 0) bad += 1;
+    }
+    free(scores);
+  }
+  return bad ? -2 : 0;
+}
+
+/* Every row of [num_q_tokens, Hq]; rows of padding tokens are left as they
+ * were in out/lse. */
+int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+                   const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, double* out, double* lse,
+                   int nthreads) {
+  if (c->num_kv_heads <= 0 || c->num_q_heads % c->num_kv_heads != 0) return -1;
+  if (num_seqs < 0 || num_seqs > c->max_num_seqs) return -1;
+  const int64_t n_rows = (int64_t)c->num_q_tokens * c->num_q_heads;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1) reduction(+ : bad)
+  {
+    double* scores = NULL;
+    int64_t cap = 0;
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)c->head_dim);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t token = r / c->num_q_heads;
+      int n = (int)(r % c->num_q_heads);
+      double l;
+      int st = oracle_row(c, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, token, n, tmp, &l, &scores,
+                          &cap);
+      if (st == 1) continue;
+      if (st < 0) bad += 1;
+      memcpy(out + r * (int64_t)c->head_dim, tmp, sizeof(double) * (size_t)c->head_dim);
+      lse[r] = l;
+    }
+    free(tmp);
+    free(scores);
+  }
+  return bad ? -2 : 0;
+}
