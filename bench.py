@@ -1,0 +1,249 @@
+"""Benchmark of ragged paged GQA attention on one MI355X.
+
+One step = one rpa_forward call (plan, prefill tiles, decode tiles, split
+merge) over one batch of seeded synthetic inputs already resident in HBM.
+The default workload is the decode batch (256 sequences x 1 query token,
+kv_len U[512, 8192], 32 q / 8 kv heads, head_dim 128, page 16, bf16).
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value      query tokens/s of the whole call
+  roofline   the dominant kernel's algorithmic bytes (or flops) per launch
+             over its mean launch time, measured with HIP events recorded
+             around each kernel on the launch stream during the timed steps
+  cpu_baseline  the f64 CPU oracle timed on a bounded sample of the same
+             workload on the host cores (a reported baseline, not a target)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "ragged paged attn: query tokens/s, KV HBM GB/s + TFLOP/s, % of roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "ragged_paged_gqa_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w):
+    """Flops and bytes the method must compute and move (masked work and
+    block over-fetch excluded), from the realized metadata, split by the
+    kernel class that handles each sequence (<= 16 packed rows: decode)."""
+    c = w.cfg
+    G = c.num_q_heads // c.num_kv_heads
+    b_kv = 1 if c.kv_dtype == "fp8_e4m3fn" else 2
+    sw = c.sliding_window or 0
+    res = {"decode": [0.0, 0.0, 0], "prefill": [0.0, 0.0, 0]}  # flops, bytes, tokens
+    for s in range(w.n_seqs):
+        q0, q1 = int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1])
+        ql, kvl = q1 - q0, int(w.kv_lens[s])
+        if ql <= 0:
+            continue
+        i = np.arange(ql, dtype=np.int64)
+        p = kvl - ql + i
+        hi = np.minimum(p + 1, kvl) if c.is_causal else np.full(ql, kvl)
+        lo = np.maximum(0, p - sw + 1) if sw > 0 else np.zeros(ql, np.int64)
+        n_vis = np.maximum(hi - lo, 0)
+        flops = float(c.num_q_heads * 4 * c.head_dim * n_vis.sum())
+        r_s = max(0, int(hi.max()) - int(lo.min()))
+        byts = float(c.num_kv_heads * 2 * c.head_dim * b_kv * r_s + ql * c.num_q_heads * (4 * c.head_dim + 4))
+        cls = "decode" if ql * G <= 16 else "prefill"
+        res[cls][0] += flops
+        res[cls][1] += byts
+        res[cls][2] += ql
+    return res
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The oracle on the first n query tokens (all q heads), n sized for ~target_s."""
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.default_threads()
+    T = w.valid_tokens()
+    Hq = w.cfg.num_q_heads
+
+    def run(n):
+        toks = np.repeat(np.arange(n), Hq)
+        heads = np.tile(np.arange(Hq), n)
+        t0 = time.perf_counter()
+        oracle.rows(w, toks, heads, nthreads=threads)
+        return time.perf_counter() - t0
+
+    n = min(T, 2)
+    dt = run(n)
+    while dt < target_s / 8 and n < T:
+        n = min(T, max(n + 1, int(n * min(8.0, target_s / max(dt, 1e-3)))))
+        dt = run(n)
+    return {"value": n / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} query tokens, all {Hq} q heads, f64 oracle, {dt:.1f} s"}
+
+
+def load_traffic(kernel: str, workload: int):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel}:cfg{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}))
+        return
+
+    import ragged_paged_gqa_amd as rpa
+    import workloads as wl
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import Device
+
+    log(f"[bench] generating workload {args.workload}: {wl.WORKLOADS[args.workload]}")
+    t0 = time.perf_counter()
+    w = wl.named(args.workload)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
+    dev = Device(w)
+    work = algorithmic_work(w)
+    T = w.valid_tokens()
+    F = work["decode"][0] + work["prefill"][0]
+    B = work["decode"][1] + work["prefill"][1]
+
+    for _ in range(args.warmup):
+        dev.run()
+    torch.cuda.synchronize()
+    rpa.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rpa.forward(dev.q, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs, dev.cfg,
+                    workspace=dev.workspace, out=dev_out(dev), lse=dev_lse(dev))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms, ncalls = rpa.profile_end()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kmean = {k: v / max(ncalls, 1) for k, v in kms.items()}
+    log(f"[bench] {ms:.4f} ms/step; kernels (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in kmean.items()))
+
+    dom = "decode" if kmean["decode"] >= kmean["prefill"] else "prefill"
+    f_dom, b_dom = work[dom][0], work[dom][1]
+    t_dom = kmean[dom] * 1e-3
+    ai = f_dom / max(b_dom, 1.0)
+    if dom == "decode" or ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = b_dom / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = f_dom / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = f"{dom}_kernel"
+    roof["kernel_ms"] = round(kmean[dom], 4)
+    roof["algorithmic_bytes"] = b_dom
+    roof["algorithmic_flops"] = f_dom
+    roof["traffic"] = load_traffic(f"{dom}_kernel", args.workload)
+
+    step_s = ms * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(T / step_s, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.cfg.kv_dtype == wl.KV_BF16 else "bf16 q / fp8 e4m3fn kv",
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page table)",
+        "config": {"workload": wl.WORKLOADS[args.workload], "num_seqs": w.n_seqs, "query_tokens": T,
+                   "num_q_heads": w.cfg.num_q_heads, "num_kv_heads": w.cfg.num_kv_heads,
+                   "head_dim": w.cfg.head_dim, "page_size": w.cfg.page_size},
+        "kv_hbm_gbs": round(B / step_s / 1e9, 1),
+        "tflops": round(F / step_s / 1e12, 2),
+        "roofline_frac_step": round(max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / step_s, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in kmean.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+_outs = {}
+
+
+def dev_out(dev):
+    import torch
+    key = id(dev)
+    if key not in _outs:
+        c = dev.cfg
+        _outs[key] = (torch.empty((c.num_q_tokens, c.num_q_heads, c.head_dim), dtype=torch.bfloat16,
+                                  device="cuda"),
+                      torch.empty((c.num_q_tokens, c.num_q_heads), dtype=torch.float32, device="cuda"))
+    return _outs[key][0]
+
+
+def dev_lse(dev):
+    dev_out(dev)
+    return _outs[id(dev)][1]
+
+
+if __name__ == "__main__":
+    main()

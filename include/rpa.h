@@ -1,0 +1,182 @@
+/*
+ * rpa.h — C ABI of the MI355X (gfx950) ragged paged GQA attention library.
+ *
+ * The operation is the one defined by the ragged paged attention kernel page
+ * (zml platforms/tpu/ragged_paged.zig): for every sequence s < num_seqs, its
+ * q_len = cu_q_lens[s+1] - cu_q_lens[s] query tokens attend, head by head,
+ * to the kv_lens[s] keys and values that the page table gathers from a
+ * paged cache. In detail (`Cfg`, `run` and `flashAttention` on that page):
+ *
+ *   - key j of sequence s is slot j % page_size of physical page
+ *     page_indices[s, j / page_size]; combined head 2h of that slot holds
+ *     K of kv head h and combined head 2h+1 holds V (`stridedLoadKv`);
+ *   - q head n reads kv head n / (num_q_heads / num_kv_heads);
+ *   - query token i of sequence s sits at key position kv_len - q_len + i;
+ *   - score = (q . K * k_scale) * sm_scale; if soft_cap > 0 the score becomes
+ *     soft_cap * tanh(score / soft_cap);
+ *   - with is_causal a key at position j is hidden when j > the query's
+ *     position p; with sliding_window w > 0 it is also hidden when
+ *     p - w >= j;
+ *   - out = softmax over the visible keys of the scores, times V * v_scale;
+ *   - lse (not on the page; an output of this library) = natural log of the
+ *     sum over visible keys of exp(score).
+ *
+ * All data pointers are DEVICE pointers, owned by the caller, and must stay
+ * valid until the work enqueued on `stream` has finished. Nothing in this
+ * library allocates device memory on the call path, synchronises, or keeps
+ * state between calls beyond cached device properties. `stream` is a
+ * hipStream_t passed as void* (NULL = the null stream).
+ */
+#ifndef RPA_H
+#define RPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (the page's `Cfg` q_dtype / kv_dtype). */
+typedef enum {
+  RPA_DTYPE_BF16 = 0,       /* bfloat16 */
+  RPA_DTYPE_FP8_E4M3FN = 1, /* OCP FP8 E4M3 (finite, NaN = S.1111.111) */
+} rpa_dtype;
+
+typedef enum {
+  RPA_OK = 0,
+  RPA_ERR_INVALID_ARGUMENT = 1,   /* bad shape, scale, window or null pointer */
+  RPA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, page_size, dtype */
+  RPA_ERR_WORKSPACE_TOO_SMALL = 3,
+  RPA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+  RPA_ERR_METADATA = 5,           /* rpa_check_metadata found a broken precondition */
+} rpa_status;
+
+/*
+ * Shapes and numeric knobs: the page's `Cfg` (shape fields, dtypes, sm_scale,
+ * soft_cap, k_scale, v_scale, is_causal, sliding_window). Block-size tuning
+ * knobs of the page are not part of this ABI; tiling is internal.
+ */
+typedef struct rpa_config {
+  int32_t num_q_tokens;    /* rows of q, out and lse (>= cu_q_lens[num_seqs]) */
+  int32_t num_q_heads;     /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;    /* Hkv; kv_pages holds 2*Hkv combined heads */
+  int32_t head_dim;        /* D: 64, 128 or 256 */
+  int32_t total_num_pages; /* P: first dimension of kv_pages */
+  int32_t page_size;       /* keys per page: a multiple of 16, at most 1024 */
+  int32_t max_num_seqs;    /* rows of page_indices and kv_lens */
+  int32_t pages_per_seq;   /* columns of page_indices */
+  int32_t q_dtype;         /* rpa_dtype; RPA_DTYPE_BF16 (q and out) */
+  int32_t kv_dtype;        /* rpa_dtype; RPA_DTYPE_BF16 or RPA_DTYPE_FP8_E4M3FN */
+  float sm_scale;          /* score scale, finite */
+  float soft_cap;          /* > 0: cap on; 0: off */
+  float k_scale;           /* dequant factor of K; 1.0f for none */
+  float v_scale;           /* dequant factor of V; 1.0f for none */
+  int32_t is_causal;       /* 0 or 1 */
+  int32_t sliding_window;  /* > 0: window in keys; 0: off */
+} rpa_config;
+
+/*
+ * Bytes of device workspace rpa_forward needs for `cfg` on the current HIP
+ * device (the tile plan, work counters and split-KV partial results). The
+ * size depends only on cfg and the device's compute-unit count.
+ * Errors: RPA_ERR_INVALID_ARGUMENT / RPA_ERR_UNSUPPORTED as rpa_forward.
+ */
+rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes);
+
+/*
+ * Ragged paged attention forward pass (the page's `run` operands):
+ *   q            [num_q_tokens, num_q_heads, head_dim]                 q_dtype
+ *   kv_pages     [total_num_pages, page_size, 2*num_kv_heads, head_dim] kv_dtype
+ *   kv_lens      [max_num_seqs] int32
+ *   page_indices [max_num_seqs, pages_per_seq] int32
+ *   cu_q_lens    [max_num_seqs + 1] int32, non-decreasing
+ *   num_seqs     [1] int32, device-resident
+ *   out          [num_q_tokens, num_q_heads, head_dim]                 q_dtype
+ *   lse          [num_q_tokens, num_q_heads] float32, or NULL
+ *   workspace    >= rpa_workspace_bytes(cfg) bytes, 256-byte aligned
+ * All arrays are dense, row-major, in device memory; out and lse must not
+ * alias any input. Rows of tokens >= cu_q_lens[num_seqs] are left untouched.
+ *
+ * Data preconditions (not checked here; rpa_check_metadata checks host copies):
+ * 0 <= q_len <= kv_len <= pages_per_seq * page_size, page ids in
+ * [0, total_num_pages), num_seqs <= max_num_seqs, cu_q_lens[num_seqs] <=
+ * num_q_tokens. Broken preconditions give unspecified values in the affected
+ * rows but no out-of-bounds access: page ids are clamped, the page count is
+ * clamped to pages_per_seq and token ranges to num_q_tokens. A row with no
+ * visible key gets out = 0 and lse = -inf.
+ *
+ * The call validates cfg and pointers on the host, then enqueues four kernels
+ * (plan, prefill tiles, decode tiles, split merge) on `stream` and returns.
+ * Errors: RPA_ERR_INVALID_ARGUMENT, RPA_ERR_UNSUPPORTED,
+ * RPA_ERR_WORKSPACE_TOO_SMALL (nothing enqueued), RPA_ERR_HIP (launch failed).
+ */
+rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                       const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* rpa_status_string(rpa_status status);
+
+/*
+ * Host-side check of the data preconditions listed for rpa_forward, on HOST
+ * copies of the metadata (kv_lens [max_num_seqs], page_indices
+ * [max_num_seqs, pages_per_seq], cu_q_lens [max_num_seqs + 1]).
+ * Returns RPA_OK or RPA_ERR_METADATA (or RPA_ERR_INVALID_ARGUMENT for a bad
+ * cfg / null pointer). Touches no device.
+ */
+rpa_status rpa_check_metadata(const rpa_config* cfg, const int32_t* kv_lens, const int32_t* page_indices,
+                              const int32_t* cu_q_lens, int32_t num_seqs);
+
+/*
+ * Plan inspection, for tests: runs only the planning kernel on `stream` into
+ * `workspace`, then describes where the plan lives in it. The plan is a list
+ * of units (one sequence, one kv head, a run of packed query rows
+ * row = token_in_seq * (Hq/Hkv) + g, and the key range those rows can see)
+ * and a list of items (a unit and one key chunk of it); see
+ * rpa_plan_layout. Same errors as rpa_forward.
+ */
+rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t* cu_q_lens,
+                    const int32_t* num_seqs, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Byte offsets inside the workspace (host-only, no device access):
+ *   offsets[0] header: int32[16] = {n_dec_units, n_pf_units, n_dec_items,
+ *              n_pf_items, dec_chunk, pf_chunk, n_split_units, ...}
+ *   offsets[1] decode units   int32[max_dec_units][8]
+ *   offsets[2] prefill units  int32[max_pf_units][8]
+ *   offsets[3] decode items   int32[max_dec_items][2]
+ *   offsets[4] prefill items  int32[max_pf_items][2]
+ * A unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}; an item is
+ * {unit, chunk}, covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo + (chunk+1)*C))
+ * with C the class's chunk size. limits = {max_dec_units, max_pf_units,
+ * max_dec_items, max_pf_items, dec_rows_max, pf_rows_max}.
+ */
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t limits[6]);
+
+/*
+ * Debug helper for tests: decode n fp8 e4m3fn codes (device array) to
+ * float32 (device array) with the same conversion the attention kernels use.
+ */
+rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, void* stream);
+
+/*
+ * Event timing for benchmarks. rpa_profile_begin(max_calls) makes the next
+ * max_calls rpa_forward calls (process-wide) record HIP events on their
+ * stream before and after each of their four kernels (plan, prefill tiles,
+ * decode tiles, split merge). rpa_profile_end waits for the last recorded
+ * event and returns, per kernel, the elapsed milliseconds summed over the
+ * recorded calls, and how many calls were recorded; it then releases the
+ * events. Events are created in rpa_profile_begin, never on the forward path.
+ * Not meant for concurrent forward calls from several threads.
+ * Errors: RPA_ERR_INVALID_ARGUMENT (bad count, nested begin, end without
+ * begin), RPA_ERR_HIP.
+ */
+rpa_status rpa_profile_begin(int32_t max_calls);
+rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H */

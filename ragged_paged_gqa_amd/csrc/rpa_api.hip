@@ -1,0 +1,403 @@
+// C ABI of the ragged paged GQA attention library: host-side validation,
+// workspace carving and the launch sequence (plan -> prefill tiles -> decode
+// tiles -> split merge), all on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "rpa.h"
+#include "rpa_combine.h"
+#include "rpa_common.h"
+#include "rpa_decode.h"
+#include "rpa_plan.h"
+#include "rpa_prefill.h"
+
+namespace {
+
+using namespace rpa;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached per device ordinal).
+bool device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (dev >= 0 && dev < kMaxDevices) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return true;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return false;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return true;
+}
+
+rpa_status validate(const rpa_config* c) {
+  if (!c) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->num_q_tokens < 0 || c->num_q_heads < 1 || c->num_kv_heads < 1) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->num_q_heads % c->num_kv_heads != 0) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->total_num_pages < 1 || c->max_num_seqs < 1 || c->pages_per_seq < 1) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->page_size < 1 || c->head_dim < 1) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->is_causal != 0 && c->is_causal != 1) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->sliding_window < 0) return RPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(c->sm_scale) || !std::isfinite(c->k_scale) || !std::isfinite(c->v_scale))
+    return RPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(c->soft_cap) || c->soft_cap < 0.f) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->max_num_seqs >= (1 << 28)) return RPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)c->pages_per_seq * c->page_size > INT32_MAX) return RPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)c->max_num_seqs * c->pages_per_seq > INT32_MAX) return RPA_ERR_INVALID_ARGUMENT;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return RPA_ERR_UNSUPPORTED;
+  if (c->page_size % 16 != 0 || c->page_size > 1024) return RPA_ERR_UNSUPPORTED;
+  if (c->q_dtype != RPA_DTYPE_BF16) return RPA_ERR_UNSUPPORTED;
+  if (c->kv_dtype != RPA_DTYPE_BF16 && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN) return RPA_ERR_UNSUPPORTED;
+  return RPA_OK;
+}
+
+struct Layout {
+  size_t hdr, du, pu, di, pi, split, dpart, dplse, ppart, pplse, total;
+  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Sizes follow from cfg alone (see the item bound in the planning kernel:
+// items <= units + target because every chunk size is >= total / target).
+bool make_layout(const rpa_config* c, int cus, Layout* L) {
+  const int64_t G = c->num_q_heads / c->num_kv_heads;
+  const int64_t Hkv = c->num_kv_heads;
+  const int64_t D = c->head_dim;
+  const int64_t max_du = Hkv * c->max_num_seqs;
+  const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + kPfRows - 1) / kPfRows + c->max_num_seqs);
+  const int64_t tgt_d = (int64_t)cus * 32;
+  const int64_t tgt_p = (int64_t)cus * 8;
+  const int64_t max_di = max_du + tgt_d;
+  const int64_t max_pi = max_pu + tgt_p;
+  if (max_du >= (1 << 30) || max_pu >= (1 << 30) || max_di >= INT32_MAX || max_pi >= INT32_MAX) return false;
+  size_t off = 0;
+  L->hdr = off;   off = align256(off + sizeof(Header));
+  L->du = off;    off = align256(off + sizeof(Unit) * (size_t)max_du);
+  L->pu = off;    off = align256(off + sizeof(Unit) * (size_t)max_pu);
+  L->di = off;    off = align256(off + sizeof(Item) * (size_t)max_di);
+  L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
+  L->split = off; off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
+  L->dpart = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows * D);
+  L->dplse = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows);
+  L->ppart = off; off = align256(off + sizeof(float) * (size_t)max_pi * kPfRows * D);
+  L->pplse = off; off = align256(off + sizeof(float) * (size_t)max_pi * kPfRows);
+  L->total = off;
+  L->max_du = (int32_t)max_du;
+  L->max_pu = (int32_t)max_pu;
+  L->max_di = (int32_t)max_di;
+  L->max_pi = (int32_t)max_pi;
+  L->tgt_d = (int32_t)tgt_d;
+  L->tgt_p = (int32_t)tgt_p;
+  return true;
+}
+
+Params make_params(const rpa_config* c, const Layout& L, void* ws) {
+  Params p;
+  std::memset(&p, 0, sizeof p);
+  char* w = static_cast<char*>(ws);
+  p.hdr = reinterpret_cast<Header*>(w + L.hdr);
+  p.dec_units = reinterpret_cast<Unit*>(w + L.du);
+  p.pf_units = reinterpret_cast<Unit*>(w + L.pu);
+  p.dec_items = reinterpret_cast<Item*>(w + L.di);
+  p.pf_items = reinterpret_cast<Item*>(w + L.pi);
+  p.split_units = reinterpret_cast<int32_t*>(w + L.split);
+  p.dec_part = reinterpret_cast<float*>(w + L.dpart);
+  p.dec_plse = reinterpret_cast<float*>(w + L.dplse);
+  p.pf_part = reinterpret_cast<float*>(w + L.ppart);
+  p.pf_plse = reinterpret_cast<float*>(w + L.pplse);
+  p.T = c->num_q_tokens;
+  p.Hq = c->num_q_heads;
+  p.Hkv = c->num_kv_heads;
+  p.G = c->num_q_heads / c->num_kv_heads;
+  p.D = c->head_dim;
+  p.page = c->page_size;
+  p.P = c->total_num_pages;
+  p.S_max = c->max_num_seqs;
+  p.pps = c->pages_per_seq;
+  p.max_dec_units = L.max_du;
+  p.max_pf_units = L.max_pu;
+  p.max_dec_items = L.max_di;
+  p.max_pf_items = L.max_pi;
+  p.target_dec_items = L.tgt_d;
+  p.target_pf_items = L.tgt_p;
+  p.sm_scale = c->sm_scale * c->k_scale;
+  p.soft_cap = c->soft_cap;
+  p.v_scale = c->v_scale;
+  p.is_causal = c->is_causal;
+  p.window = c->sliding_window;
+  return p;
+}
+
+rpa_status check_launch() { return hipGetLastError() == hipSuccess ? RPA_OK : RPA_ERR_HIP; }
+
+// Optional event timing of the four launches of each call (for benchmarks).
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  int max_calls = 0;
+  int n_calls = 0;
+  std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
+};
+constexpr int kProfEvents = 5;
+Profiler g_prof;
+
+void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
+  if (ev) (void)hipEventRecord(ev[k], st);
+}
+
+template <int D, bool FP8>
+rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
+  {
+    // LDS bounds the number of resident workgroups; more would only idle.
+    const int per_cu = PrefillLds<D>::kBytes > 80 * 1024 ? 1 : 2;
+    int grid = cus * per_cu;
+    if (grid > p.max_pf_items) grid = p.max_pf_items;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    prof_record(ev, 2, st);
+  }
+  {
+    int per_cu = (int)((160 * 1024) / DecodeLds<D>::kBytes);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    int grid = cus * per_cu;
+    const int need = (p.max_dec_items + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
+    if (grid > need) grid = need;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((decode_kernel<D, FP8>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    prof_record(ev, 3, st);
+  }
+  {
+    int grid = cus * 2;
+    const int need = p.max_dec_units + p.max_pf_units;
+    if (grid > need) grid = need;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(grid), dim3(kCombineWaves * 64), 0, st, p);
+    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    prof_record(ev, 4, st);
+  }
+  return RPA_OK;
+}
+
+rpa_status launch_plan(const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
+  return check_launch();
+}
+
+__global__ void decode_fp8_kernel(const uint8_t* codes, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (4 * i >= n) return;
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k)
+    if (4 * i + k < n) w |= (uint32_t)codes[4 * i + k] << (8 * k);
+  u32x2 ww = {w, 0u};
+  bf16x8 b = fp8x8_to_bf16(ww);
+  for (int k = 0; k < 4; ++k)
+    if (4 * i + k < n) out[4 * i + k] = (float)b[k];
+}
+
+}  // namespace
+
+extern "C" {
+
+rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes) {
+  if (!bytes) return RPA_ERR_INVALID_ARGUMENT;
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  int cus = 0;
+  if (!device_cus(&cus)) return RPA_ERR_HIP;
+  Layout L;
+  if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
+  *bytes = L.total;
+  return RPA_OK;
+}
+
+static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspace_bytes, Params* p, int* cus_out) {
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RPA_ERR_INVALID_ARGUMENT;
+  int cus = 0;
+  if (!device_cus(&cus)) return RPA_ERR_HIP;
+  Layout L;
+  if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < L.total) return RPA_ERR_WORKSPACE_TOO_SMALL;
+  *p = make_params(cfg, L, workspace);
+  *cus_out = cus;
+  return RPA_OK;
+}
+
+rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                       const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs || !out)
+    return RPA_ERR_INVALID_ARGUMENT;
+  Params p;
+  int cus = 0;
+  rpa_status st = prepare(cfg, workspace, workspace_bytes, &p, &cus);
+  if (st != RPA_OK) return st;
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_pages);
+  p.kv_lens = kv_lens;
+  p.page_indices = page_indices;
+  p.cu_q_lens = cu_q_lens;
+  p.num_seqs = num_seqs;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (g_prof.on && g_prof.n_calls < g_prof.max_calls) ev = &g_prof.ev[kProfEvents * g_prof.n_calls++];
+  }
+  prof_record(ev, 0, s);
+  st = launch_plan(p, s);
+  if (st != RPA_OK) return st;
+  prof_record(ev, 1, s);
+  const bool fp8 = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN;
+  switch (cfg->head_dim) {
+    case 64: return fp8 ? launch_attention<64, true>(p, cus, s, ev) : launch_attention<64, false>(p, cus, s, ev);
+    case 128: return fp8 ? launch_attention<128, true>(p, cus, s, ev) : launch_attention<128, false>(p, cus, s, ev);
+    case 256: return fp8 ? launch_attention<256, true>(p, cus, s, ev) : launch_attention<256, false>(p, cus, s, ev);
+    default: return RPA_ERR_UNSUPPORTED;
+  }
+}
+
+rpa_status rpa_profile_begin(int32_t max_calls) {
+  if (max_calls < 1 || max_calls > (1 << 20)) return RPA_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (g_prof.on) return RPA_ERR_INVALID_ARGUMENT;
+  g_prof.ev.assign((size_t)kProfEvents * max_calls, nullptr);
+  for (auto& e : g_prof.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto& f : g_prof.ev)
+        if (f) (void)hipEventDestroy(f);
+      g_prof.ev.clear();
+      return RPA_ERR_HIP;
+    }
+  }
+  g_prof.max_calls = max_calls;
+  g_prof.n_calls = 0;
+  g_prof.on = true;
+  return RPA_OK;
+}
+
+rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
+  if (!kernel_ms || !n_calls) return RPA_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on) return RPA_ERR_INVALID_ARGUMENT;
+  rpa_status st = RPA_OK;
+  for (int k = 0; k < 4; ++k) kernel_ms[k] = 0.f;
+  if (g_prof.n_calls > 0 && hipEventSynchronize(g_prof.ev[kProfEvents * g_prof.n_calls - 1]) != hipSuccess)
+    st = RPA_ERR_HIP;
+  for (int c = 0; c < g_prof.n_calls && st == RPA_OK; ++c) {
+    for (int k = 0; k < 4; ++k) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_prof.ev[kProfEvents * c + k], g_prof.ev[kProfEvents * c + k + 1]) !=
+          hipSuccess) {
+        st = RPA_ERR_HIP;
+        break;
+      }
+      kernel_ms[k] += ms;
+    }
+  }
+  *n_calls = g_prof.n_calls;
+  for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  g_prof.n_calls = 0;
+  return st;
+}
+
+rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv_lens || !cu_q_lens || !num_seqs) return RPA_ERR_INVALID_ARGUMENT;
+  Params p;
+  int cus = 0;
+  rpa_status st = prepare(cfg, workspace, workspace_bytes, &p, &cus);
+  if (st != RPA_OK) return st;
+  p.kv_lens = kv_lens;
+  p.cu_q_lens = cu_q_lens;
+  p.num_seqs = num_seqs;
+  return launch_plan(p, static_cast<hipStream_t>(stream));
+}
+
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t limits[6]) {
+  if (!offsets || !limits) return RPA_ERR_INVALID_ARGUMENT;
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  int cus = 0;
+  if (!device_cus(&cus)) return RPA_ERR_HIP;
+  Layout L;
+  if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
+  offsets[0] = L.hdr;
+  offsets[1] = L.du;
+  offsets[2] = L.pu;
+  offsets[3] = L.di;
+  offsets[4] = L.pi;
+  limits[0] = L.max_du;
+  limits[1] = L.max_pu;
+  limits[2] = L.max_di;
+  limits[3] = L.max_pi;
+  limits[4] = kDecRows;
+  limits[5] = kPfRows;
+  return RPA_OK;
+}
+
+const char* rpa_status_string(rpa_status s) {
+  switch (s) {
+    case RPA_OK: return "ok";
+    case RPA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RPA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RPA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RPA_ERR_HIP: return "HIP runtime error";
+    case RPA_ERR_METADATA: return "metadata violates a precondition";
+  }
+  return "unknown status";
+}
+
+rpa_status rpa_check_metadata(const rpa_config* cfg, const int32_t* kv_lens, const int32_t* page_indices,
+                              const int32_t* cu_q_lens, int32_t num_seqs) {
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  if (!kv_lens || !page_indices || !cu_q_lens) return RPA_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 0 || num_seqs > cfg->max_num_seqs) return RPA_ERR_METADATA;
+  if (cu_q_lens[0] < 0) return RPA_ERR_METADATA;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t ql = (int64_t)cu_q_lens[s + 1] - cu_q_lens[s];
+    const int64_t kvl = kv_lens[s];
+    if (ql < 0 || kvl < ql) return RPA_ERR_METADATA;
+    if (kvl > (int64_t)cfg->pages_per_seq * cfg->page_size) return RPA_ERR_METADATA;
+    const int64_t pages = (kvl + cfg->page_size - 1) / cfg->page_size;
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t ph = page_indices[(int64_t)s * cfg->pages_per_seq + j];
+      if (ph < 0 || ph >= cfg->total_num_pages) return RPA_ERR_METADATA;
+    }
+  }
+  if (cu_q_lens[num_seqs] > cfg->num_q_tokens) return RPA_ERR_METADATA;
+  return RPA_OK;
+}
+
+rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, void* stream) {
+  if (!codes || !values || n < 0) return RPA_ERR_INVALID_ARGUMENT;
+  if (n == 0) return RPA_OK;
+  const int threads = (n + 3) / 4;
+  hipLaunchKernelGGL(decode_fp8_kernel, dim3((threads + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), codes, values, n);
+  return check_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Shared device-side definitions of the ragged paged attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Rows of a decode-class unit: one 16-wide MFMA column block.
+constexpr int kDecRows = 16;
+// Rows of a prefill-class tile: 4 waves x 32 rows.
+constexpr int kPfWaves = 4;
+constexpr int kPfRows = kPfWaves * 32;
+// Keys per pipeline step in both attention kernels.
+constexpr int kStepKeys = 32;
+
+// ----------------------------------------------------------------------------
+// Plan records written by the planning kernel, read by the attention and
+// merge kernels. A unit is one sequence, one kv head and a run of packed query
+// rows (row = token_in_seq * G + g, the GQA row packing of the kernel page's
+// per-kv-head step). An item is one key chunk of a unit.
+struct Unit {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t row0;   // first packed row of the unit, relative to the sequence
+  int32_t nrows;  // number of packed rows
+  int32_t kv_lo;  // start of the unit's chunk grid (16-aligned)
+  int32_t kv_hi;  // one past the last key any of the rows can see
+  int32_t nch;    // chunks (>= 1)
+  int32_t item0;  // index of the unit's first item
+};
+static_assert(sizeof(Unit) == 32, "unit record is int32[8]");
+
+struct Item {
+  int32_t unit;
+  int32_t chunk;
+};
+
+struct Header {
+  int32_t n_dec_units;
+  int32_t n_pf_units;
+  int32_t n_dec_items;
+  int32_t n_pf_items;
+  int32_t dec_chunk;
+  int32_t pf_chunk;
+  int32_t n_split_units;
+  int32_t dec_counter;  // work queues, zeroed by the planning kernel
+  int32_t pf_counter;
+  int32_t pad[7];
+};
+static_assert(sizeof(Header) == 64, "header is int32[16]");
+
+// Everything a kernel needs, passed by value.
+struct Params {
+  // inputs
+  const uint16_t* q;         // [T, Hq, D] bf16 bits
+  const uint8_t* kv;         // [P, page, 2Hkv, D] bf16 or fp8 bytes
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* cu_q_lens;
+  const int32_t* num_seqs;
+  // outputs
+  uint16_t* out;             // [T, Hq, D] bf16 bits
+  float* lse;                // [T, Hq] or null
+  // workspace views
+  Header* hdr;
+  Unit* dec_units;
+  Unit* pf_units;
+  Item* dec_items;
+  Item* pf_items;
+  int32_t* split_units;      // (class << 30) | unit index
+  float* dec_part;           // [max_dec_items][kDecRows][D]
+  float* dec_plse;           // [max_dec_items][kDecRows]
+  float* pf_part;            // [max_pf_items][kPfRows][D]
+  float* pf_plse;            // [max_pf_items][kPfRows]
+  // shapes
+  int32_t T, Hq, Hkv, G, D, page, P, S_max, pps;
+  int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
+  int32_t target_dec_items, target_pf_items;
+  // numerics
+  float sm_scale;      // sm_scale * k_scale
+  float soft_cap;      // > 0: on
+  float v_scale;
+  int32_t is_causal;
+  int32_t window;      // > 0: on
+};
+
+// ----------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// c * tanh(x / c) as c - 2c / (1 + e^(2x/c)): one exp2 and one reciprocal, the
+// logistic form of the spatial-compiler page's `capped` soft-cap. Saturates to
+// +-c for large |x| (e^.. -> inf gives c, -> 0 gives -c).
+__device__ __forceinline__ float soft_cap_f(float x, float c, float two_log2e_over_c) {
+  float e = fast_exp2(x * two_log2e_over_c);
+  return c - 2.0f * c * fast_rcp(1.0f + e);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight fp8 e4m3fn codes (two dwords) -> eight bf16 (exact: every e4m3fn value
+// is a bf16 value).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, true);
+  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read: within each 16-lane group, lane 4q+r receives element r
+// of the 8-byte rows loaded by lanes q, q+4, q+8, q+12 (measured on gfx950).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// Physical page of key `key` of sequence s, clamped into [0, P).
+__device__ __forceinline__ int32_t page_of(const Params& p, int32_t s, int32_t key) {
+  int32_t logical = key / p.page;
+  logical = logical < p.pps ? logical : p.pps - 1;
+  int32_t phys = p.page_indices[(int64_t)s * p.pps + logical];
+  phys = phys < 0 ? 0 : phys;
+  phys = phys < p.P ? phys : p.P - 1;
+  return phys;
+}
+
+// Token range of sequence s, clamped into [0, T].
+__device__ __forceinline__ void seq_tokens(const Params& p, int32_t s, int32_t& q0, int32_t& ql) {
+  int32_t a = p.cu_q_lens[s], b = p.cu_q_lens[s + 1];
+  a = a < 0 ? 0 : (a > p.T ? p.T : a);
+  b = b < a ? a : (b > p.T ? p.T : b);
+  q0 = a;
+  ql = b - a;
+}
+
+}  // namespace rpa

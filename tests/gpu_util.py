@@ -1,0 +1,82 @@
+"""Shared helpers of the GPU parity tests: upload a seeded workload, run the
+HIP path through the C ABI, compare with the oracle at the stated bar."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import ragged_paged_gqa_amd as rpa
+import workloads as wl
+
+# Parity bar: bf16 outputs within |d| <= ATOL + RTOL*|ref| of the f64 oracle,
+# per-row LSE within LSE_TOL (natural log units).
+ATOL = 2e-2
+RTOL = 2e-2
+LSE_TOL = 1e-3
+# Additional, stricter check on the whole compared set: relative RMS error.
+REL_RMS_TOL = 2e-2
+
+
+def lib_config(w: wl.Workload) -> rpa.Config:
+    c = w.cfg
+    return rpa.Config(
+        num_q_tokens=c.num_q_tokens, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
+        head_dim=c.head_dim, total_num_pages=c.total_num_pages, page_size=c.page_size,
+        max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq,
+        kv_dtype=rpa.DTYPE_FP8_E4M3FN if c.kv_dtype == wl.KV_FP8 else rpa.DTYPE_BF16,
+        sm_scale=c.sm_scale, soft_cap=c.soft_cap or 0.0,
+        k_scale=1.0 if c.k_scale is None else c.k_scale,
+        v_scale=1.0 if c.v_scale is None else c.v_scale,
+        is_causal=c.is_causal, sliding_window=c.sliding_window or 0)
+
+
+class Device:
+    """A workload's inputs resident on the GPU."""
+
+    def __init__(self, w: wl.Workload, device="cuda"):
+        self.w = w
+        self.cfg = lib_config(w)
+        self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
+        if w.cfg.kv_dtype == wl.KV_FP8:
+            self.kv = torch.from_numpy(w.kv_pages).to(device)
+        else:
+            self.kv = torch.from_numpy(w.kv_pages.view(np.int16)).to(device).view(torch.bfloat16)
+        self.kv_lens = torch.from_numpy(w.kv_lens).to(device)
+        self.page_indices = torch.from_numpy(w.page_indices).to(device)
+        self.cu_q_lens = torch.from_numpy(w.cu_q_lens).to(device)
+        self.num_seqs = torch.from_numpy(w.num_seqs).to(device)
+        self.workspace = rpa.alloc_workspace(self.cfg)
+
+    def run(self, out=None, lse=None, want_lse=True):
+        out, lse = rpa.forward(self.q, self.kv, self.kv_lens, self.page_indices, self.cu_q_lens,
+                               self.num_seqs, self.cfg, out=out, lse=lse, workspace=self.workspace,
+                               want_lse=want_lse)
+        torch.cuda.synchronize()
+        return out, lse
+
+
+def run_numpy(w: wl.Workload):
+    d = Device(w)
+    out, lse = d.run()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, what=""):
+    """out/ref_out [..., D]; lse/ref_lse [...]; only rows given are compared."""
+    out = np.asarray(out, np.float64)
+    ref_out = np.asarray(ref_out, np.float64)
+    assert np.isfinite(ref_out).all(), f"{what}: oracle produced non-finite values"
+    diff = np.abs(out - ref_out)
+    bound = ATOL + RTOL * np.abs(ref_out)
+    bad = ~(diff <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outputs outside the bar; "
+                           f"max |d| {np.nanmax(diff):.3e}")
+    rms_ref = float(np.sqrt(np.mean(ref_out ** 2)))
+    rel_rms = float(np.sqrt(np.mean((out - ref_out) ** 2))) / max(rms_ref, 1e-30)
+    assert rel_rms <= REL_RMS_TOL, f"{what}: relative RMS error {rel_rms:.3e}"
+    if lse is not None:
+        dl = np.abs(np.asarray(lse, np.float64) - np.asarray(ref_lse, np.float64))
+        badl = ~(dl <= LSE_TOL)
+        assert not badl.any(), f"{what}: {int(badl.sum())} lse values off; max |d| {np.nanmax(dl):.3e}"
+    return dict(max_abs=float(np.max(diff)) if diff.size else 0.0, rel_rms=rel_rms)

@@ -1,0 +1,102 @@
+"""Exact checks of the planning kernel's tile list (needs an MI355X).
+
+The plan is copied back from the workspace and checked against the metadata,
+with no second implementation of the planner: every packed query row of every
+sequence is owned by exactly one unit of the right class, each unit's key range
+covers exactly the keys its rows can see (rounded down to 16 at the start),
+and the items of each unit tile that range in chunks with no gap or overlap.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import ragged_paged_gqa_amd as rpa
+import workloads as wl
+from gpu_util import lib_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(w):
+    cfg = lib_config(w)
+    ws = rpa.plan(torch.from_numpy(w.kv_lens).cuda(), torch.from_numpy(w.cu_q_lens).cuda(),
+                  torch.from_numpy(w.num_seqs).cuda(), cfg)
+    torch.cuda.synchronize()
+    offs, lim = rpa.plan_layout(cfg)
+    host = ws.cpu().numpy()
+    hdr = host[offs[0]:offs[0] + 64].view(np.int32)
+    n_du, n_pu, n_di, n_pi, dch, pch = (int(x) for x in hdr[:6])
+    du = host[offs[1]:offs[1] + 32 * n_du].view(np.int32).reshape(n_du, 8)
+    pu = host[offs[2]:offs[2] + 32 * n_pu].view(np.int32).reshape(n_pu, 8)
+    di = host[offs[3]:offs[3] + 8 * n_di].view(np.int32).reshape(n_di, 2)
+    pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
+    return dict(du=du, pu=pu, di=di, pi=pi, dch=dch, pch=pch, lim=lim)
+
+
+def _check(w):
+    P = _plan(w)
+    c = w.cfg
+    G = c.num_q_heads // c.num_kv_heads
+    dec_rows, pf_rows = P["lim"][4], P["lim"][5]
+    owner = {}
+    for cls, units, items, ch in (("dec", P["du"], P["di"], P["dch"]), ("pf", P["pu"], P["pi"], P["pch"])):
+        seen_items = np.zeros(len(items), dtype=int)
+        for ui, (s, h, r0, nr, lo, hi, nch, it0) in enumerate(units):
+            q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = int(w.kv_lens[s])
+            rows = ql * G
+            assert (rows <= dec_rows) == (cls == "dec")
+            assert 1 <= nr <= (dec_rows if cls == "dec" else pf_rows)
+            for r in range(r0, r0 + nr):
+                assert (s, h, r) not in owner
+                owner[(s, h, r)] = cls
+            # visible key range of the unit's rows
+            firsts, lasts = [], []
+            for r in range(r0, r0 + nr):
+                p = kvl - ql + r // G
+                last = p if c.is_causal else kvl - 1
+                first = max(0, p - c.sliding_window + 1) if c.sliding_window else 0
+                firsts.append(first); lasts.append(min(last, kvl - 1))
+            assert lo == (min(firsts) // 16) * 16
+            assert hi == max(lasts) + 1
+            # chunks tile [lo, hi) exactly
+            assert nch == max(1, -(-(hi - lo) // ch))
+            for k in range(nch):
+                assert tuple(items[it0 + k]) == (ui, k)
+                seen_items[it0 + k] += 1
+                a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
+                assert a < b or (nch == 1 and hi <= lo)
+        assert np.all(seen_items == 1), cls
+    for s in range(w.n_seqs):
+        ql = int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])
+        for h in range(c.num_kv_heads):
+            for r in range(ql * G):
+                assert (s, h, r) in owner
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_plan_small(seed):
+    _check(wl.random_small(seed, max_seqs=6, max_q=50, max_extra_kv=3000, window=None if seed != 2 else 300))
+
+
+def test_plan_named_tiny():
+    _check(wl.named(1))
+
+
+@pytest.mark.parametrize("number", [2, 3, 5])
+def test_plan_named_lengths(number):
+    # lengths of the large workloads, with a 1-page cache: the plan reads metadata only
+    rng = np.random.Generator(np.random.PCG64(number))
+    q_lens, kv_lens = wl.lengths(number, rng)
+    kw = dict(wl.cfg_kw(number))
+    page = kw["page_size"]
+    S = len(q_lens)
+    pps = kw["pages_per_seq"]
+    cfg = wl.Config(total_num_pages=1, max_num_seqs=S, num_q_tokens=int(np.sum(q_lens)),
+                    **{k: v for k, v in kw.items() if k != "pages_per_seq"}, pages_per_seq=pps)
+    cu = np.zeros(S + 1, np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    w = wl.Workload("lens", cfg, np.zeros((1, 1, 1), np.uint16), np.zeros((1,), np.uint16),
+                    np.asarray(kv_lens, np.int32), np.zeros((S, pps), np.int32), cu, np.array([S], np.int32))
+    _check(w)
+    _ = page
