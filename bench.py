@@ -1,7 +1,8 @@
 """Benchmark of ragged paged GQA attention on one MI355X.
 
-One step = one rpa_forward call (plan, prefill tiles, decode tiles, split
-merge) over one batch of seeded synthetic inputs already resident in HBM.
+One step = one rpa_forward call (plan, prefill-class tiles, decode-class
+tiles, split-KV merge inside them) over one batch of seeded synthetic inputs
+already resident in HBM.
 The default workload is the decode batch (256 sequences x 1 query token,
 kv_len U[512, 8192], 32 q / 8 kv heads, head_dim 128, page 16, bf16).
 

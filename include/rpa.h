@@ -106,8 +106,10 @@ rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes);
  * clamped to pages_per_seq and token ranges to num_q_tokens. A row with no
  * visible key gets out = 0 and lse = -inf.
  *
- * The call validates cfg and pointers on the host, then enqueues four kernels
- * (plan, prefill tiles, decode tiles, split merge) on `stream` and returns.
+ * The call validates cfg and pointers on the host, then enqueues three kernels
+ * (plan, prefill-class tiles, decode-class tiles; a unit split into several
+ * key chunks is merged by whichever tile finishes its last chunk) on
+ * `stream` and returns.
  * Errors: RPA_ERR_INVALID_ARGUMENT, RPA_ERR_UNSUPPORTED,
  * RPA_ERR_WORKSPACE_TOO_SMALL (nothing enqueued), RPA_ERR_HIP (launch failed).
  */
@@ -143,6 +145,7 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
  * Byte offsets inside the workspace (host-only, no device access):
  *   offsets[0] header: int32[16] = {n_dec_units, n_pf_units, n_dec_items,
  *              n_pf_items, dec_chunk, pf_chunk, n_split_units, ...}
+ *              (n_split_units counts units with more than one chunk)
  *   offsets[1] decode units   int32[max_dec_units][8]
  *   offsets[2] prefill units  int32[max_pf_units][8]
  *   offsets[3] decode items   int32[max_dec_items][2]
@@ -163,8 +166,8 @@ rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, 
 /*
  * Event timing for benchmarks. rpa_profile_begin(max_calls) makes the next
  * max_calls rpa_forward calls (process-wide) record HIP events on their
- * stream before and after each of their four kernels (plan, prefill tiles,
- * decode tiles, split merge). rpa_profile_end waits for the last recorded
+ * stream before and after each of their three kernels (plan, prefill-class
+ * tiles, decode-class tiles). rpa_profile_end waits for the last recorded
  * event and returns, per kernel, the elapsed milliseconds summed over the
  * recorded calls, and how many calls were recorded; it then releases the
  * events. Events are created in rpa_profile_begin, never on the forward path.
@@ -173,7 +176,7 @@ rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, 
  * begin), RPA_ERR_HIP.
  */
 rpa_status rpa_profile_begin(int32_t max_calls);
-rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls);
+rpa_status rpa_profile_end(float kernel_ms[3], int32_t* n_calls);
 
 #ifdef __cplusplus
 }

@@ -118,7 +118,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_status_string", "rpa_check_metadata", "rpa_plan",
            "rpa_plan_layout", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
-KERNELS = ("plan", "prefill", "decode", "merge")
+KERNELS = ("plan", "prefill", "decode")
 
 
 def _check(status: int, what: str) -> None:
@@ -249,7 +249,7 @@ def profile_begin(max_calls: int) -> None:
 
 def profile_end():
     """Wait for the recorded events; returns ({kernel: summed ms}, n_calls)."""
-    ms = (ctypes.c_float * 4)()
+    ms = (ctypes.c_float * len(KERNELS))()
     n = ctypes.c_int32(0)
     _check(lib().rpa_profile_end(ms, ctypes.byref(n)), "rpa_profile_end")
     return dict(zip(KERNELS, (float(x) for x in ms))), int(n.value)

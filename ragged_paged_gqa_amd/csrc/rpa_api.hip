@@ -1,6 +1,7 @@
 // C ABI of the ragged paged GQA attention library: host-side validation,
 // workspace carving and the launch sequence (plan -> prefill tiles -> decode
-// tiles -> split merge), all on the caller's stream.
+// tiles; split units are merged inside the tile kernels), all on the caller's
+// stream.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -11,7 +12,6 @@
 #include <vector>
 
 #include "rpa.h"
-#include "rpa_combine.h"
 #include "rpa_common.h"
 #include "rpa_decode.h"
 #include "rpa_plan.h"
@@ -56,6 +56,8 @@ rpa_status validate(const rpa_config* c) {
   if (c->max_num_seqs >= (1 << 28)) return RPA_ERR_INVALID_ARGUMENT;
   if ((int64_t)c->pages_per_seq * c->page_size > INT32_MAX) return RPA_ERR_INVALID_ARGUMENT;
   if ((int64_t)c->max_num_seqs * c->pages_per_seq > INT32_MAX) return RPA_ERR_INVALID_ARGUMENT;
+  // 16 key slots of K|V rows must be addressable with 32-bit offsets
+  if ((int64_t)c->num_kv_heads * c->head_dim > (1 << 24)) return RPA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return RPA_ERR_UNSUPPORTED;
   if (c->page_size % 16 != 0 || c->page_size > 1024) return RPA_ERR_UNSUPPORTED;
   if (c->q_dtype != RPA_DTYPE_BF16) return RPA_ERR_UNSUPPORTED;
@@ -64,8 +66,8 @@ rpa_status validate(const rpa_config* c) {
 }
 
 struct Layout {
-  size_t hdr, du, pu, di, pi, split, dpart, dplse, ppart, pplse, total;
-  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p;
+  size_t hdr, du, pu, di, pi, qlist, done, dpart, dplse, ppart, pplse, total;
+  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p, pf_rows;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -76,12 +78,15 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t G = c->num_q_heads / c->num_kv_heads;
   const int64_t Hkv = c->num_kv_heads;
   const int64_t D = c->head_dim;
+  const int64_t pf_rows = 32 * pf_waves_for(c->head_dim);
   const int64_t max_du = Hkv * c->max_num_seqs;
-  const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + kPfRows - 1) / kPfRows + c->max_num_seqs);
+  const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
   const int64_t tgt_d = (int64_t)cus * 32;
-  const int64_t tgt_p = (int64_t)cus * 8;
+  const int64_t tgt_p = (int64_t)cus * 4;
   const int64_t max_di = max_du + tgt_d;
-  const int64_t max_pi = max_pu + tgt_p;
+  // prefill chunks are also capped at kPfMaxChunk keys
+  const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
+  const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);
   if (max_du >= (1 << 30) || max_pu >= (1 << 30) || max_di >= INT32_MAX || max_pi >= INT32_MAX) return false;
   size_t off = 0;
   L->hdr = off;   off = align256(off + sizeof(Header));
@@ -89,11 +94,12 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->pu = off;    off = align256(off + sizeof(Unit) * (size_t)max_pu);
   L->di = off;    off = align256(off + sizeof(Item) * (size_t)max_di);
   L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
-  L->split = off; off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
+  L->qlist = off; off = align256(off + sizeof(int32_t) * (size_t)max_pi);
+  L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
   L->dpart = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows * D);
   L->dplse = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows);
-  L->ppart = off; off = align256(off + sizeof(float) * (size_t)max_pi * kPfRows * D);
-  L->pplse = off; off = align256(off + sizeof(float) * (size_t)max_pi * kPfRows);
+  L->ppart = off; off = align256(off + sizeof(float) * (size_t)max_pi * pf_rows * D);
+  L->pplse = off; off = align256(off + sizeof(float) * (size_t)max_pi * pf_rows);
   L->total = off;
   L->max_du = (int32_t)max_du;
   L->max_pu = (int32_t)max_pu;
@@ -101,6 +107,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->max_pi = (int32_t)max_pi;
   L->tgt_d = (int32_t)tgt_d;
   L->tgt_p = (int32_t)tgt_p;
+  L->pf_rows = (int32_t)pf_rows;
   return true;
 }
 
@@ -113,7 +120,8 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.pf_units = reinterpret_cast<Unit*>(w + L.pu);
   p.dec_items = reinterpret_cast<Item*>(w + L.di);
   p.pf_items = reinterpret_cast<Item*>(w + L.pi);
-  p.split_units = reinterpret_cast<int32_t*>(w + L.split);
+  p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
+  p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
   p.dec_part = reinterpret_cast<float*>(w + L.dpart);
   p.dec_plse = reinterpret_cast<float*>(w + L.dplse);
   p.pf_part = reinterpret_cast<float*>(w + L.ppart);
@@ -127,6 +135,7 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.P = c->total_num_pages;
   p.S_max = c->max_num_seqs;
   p.pps = c->pages_per_seq;
+  p.pf_rows = L.pf_rows;
   p.max_dec_units = L.max_du;
   p.max_pf_units = L.max_pu;
   p.max_dec_items = L.max_di;
@@ -151,7 +160,7 @@ struct Profiler {
   int n_calls = 0;
   std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
 };
-constexpr int kProfEvents = 5;
+constexpr int kProfEvents = 4;
 Profiler g_prof;
 
 void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
@@ -161,12 +170,16 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
 template <int D, bool FP8>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   {
-    // LDS bounds the number of resident workgroups; more would only idle.
-    const int per_cu = PrefillLds<D>::kBytes > 80 * 1024 ? 1 : 2;
-    int grid = cus * per_cu;
+    constexpr int NW = pf_waves_for(D);
+    // registers allow 8 waves per CU; LDS (double-buffered K|V tiles) bounds
+    // the workgroups per CU further for wide heads
+    constexpr int by_regs = 8 / NW;
+    constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfPageCache + 64));
+    constexpr int per_cu = by_regs < by_lds ? by_regs : by_lds;
+    int grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid > p.max_pf_items) grid = p.max_pf_items;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW>), dim3(grid), dim3(NW * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
   }
@@ -180,15 +193,6 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     hipLaunchKernelGGL((decode_kernel<D, FP8>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
-  }
-  {
-    int grid = cus * 2;
-    const int need = p.max_dec_units + p.max_pf_units;
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(grid), dim3(kCombineWaves * 64), 0, st, p);
-    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 4, st);
   }
   return RPA_OK;
 }
@@ -236,6 +240,11 @@ static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspa
   if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.total) return RPA_ERR_WORKSPACE_TOO_SMALL;
   *p = make_params(cfg, L, workspace);
+  // every workspace view the kernels dereference must be assigned
+  const void* views[] = {p->hdr,       p->dec_units, p->pf_units, p->dec_items, p->pf_items, p->pf_qlist,
+                         p->unit_done, p->dec_part,  p->dec_plse, p->pf_part,   p->pf_plse};
+  for (const void* v : views)
+    if (!v) return RPA_ERR_INVALID_ARGUMENT;
   *cus_out = cus;
   return RPA_OK;
 }
@@ -295,16 +304,16 @@ rpa_status rpa_profile_begin(int32_t max_calls) {
   return RPA_OK;
 }
 
-rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
+rpa_status rpa_profile_end(float kernel_ms[3], int32_t* n_calls) {
   if (!kernel_ms || !n_calls) return RPA_ERR_INVALID_ARGUMENT;
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on) return RPA_ERR_INVALID_ARGUMENT;
   rpa_status st = RPA_OK;
-  for (int k = 0; k < 4; ++k) kernel_ms[k] = 0.f;
+  for (int k = 0; k < kProfEvents - 1; ++k) kernel_ms[k] = 0.f;
   if (g_prof.n_calls > 0 && hipEventSynchronize(g_prof.ev[kProfEvents * g_prof.n_calls - 1]) != hipSuccess)
     st = RPA_ERR_HIP;
   for (int c = 0; c < g_prof.n_calls && st == RPA_OK; ++c) {
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kProfEvents - 1; ++k) {
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, g_prof.ev[kProfEvents * c + k], g_prof.ev[kProfEvents * c + k + 1]) !=
           hipSuccess) {
@@ -353,7 +362,7 @@ rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t lim
   limits[2] = L.max_di;
   limits[3] = L.max_pi;
   limits[4] = kDecRows;
-  limits[5] = kPfRows;
+  limits[5] = L.pf_rows;
   return RPA_OK;
 }
 

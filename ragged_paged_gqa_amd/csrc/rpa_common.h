@@ -20,11 +20,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Rows of a decode-class unit: one 16-wide MFMA column block.
 constexpr int kDecRows = 16;
-// Rows of a prefill-class tile: 4 waves x 32 rows.
-constexpr int kPfWaves = 4;
-constexpr int kPfRows = kPfWaves * 32;
+// Waves (of 32 rows each) of a prefill-class tile: 8 for head_dim <= 128;
+// 4 for head_dim 256, whose accumulators need a whole SIMD's registers.
+constexpr int pf_waves_for(int D) { return D >= 256 ? 4 : 8; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;
+// Largest key chunk of a prefill-class item (bounds the per-item page cache).
+constexpr int kPfMaxChunk = 32768;
 
 // ----------------------------------------------------------------------------
 // Plan records written by the planning kernel, read by the attention and
@@ -48,6 +50,12 @@ struct Item {
   int32_t chunk;
 };
 
+// Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
+// L2). All row blocks of one (sequence, kv head) go to the same queue, in
+// chunk-major order, so the workgroups of one XCD that run at the same time
+// stream the same K/V chunk and share it through that XCD's L2.
+constexpr int kQueues = 8;
+
 struct Header {
   int32_t n_dec_units;
   int32_t n_pf_units;
@@ -56,11 +64,14 @@ struct Header {
   int32_t dec_chunk;
   int32_t pf_chunk;
   int32_t n_split_units;
-  int32_t dec_counter;  // work queues, zeroed by the planning kernel
-  int32_t pf_counter;
-  int32_t pad[7];
+  int32_t dec_counter;  // work queue of decode items, zeroed by the planning kernel
+  int32_t pad0[8];
+  int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist
+  int32_t pf_q_count[kQueues];  // its length
+  int32_t pf_q_next[kQueues];   // its head, zeroed by the planning kernel
+  int32_t pad1[24];
 };
-static_assert(sizeof(Header) == 64, "header is int32[16]");
+static_assert(sizeof(Header) == 256, "header is int32[64]");
 
 // Everything a kernel needs, passed by value.
 struct Params {
@@ -80,13 +91,15 @@ struct Params {
   Unit* pf_units;
   Item* dec_items;
   Item* pf_items;
-  int32_t* split_units;      // (class << 30) | unit index
+  int32_t* pf_qlist;         // prefill item indices in queue order [max_pf_items]
+  int32_t* unit_done;        // finished chunks per unit: [max_dec_units] then [max_pf_units]
   float* dec_part;           // [max_dec_items][kDecRows][D]
   float* dec_plse;           // [max_dec_items][kDecRows]
-  float* pf_part;            // [max_pf_items][kPfRows][D]
-  float* pf_plse;            // [max_pf_items][kPfRows]
+  float* pf_part;            // [max_pf_items][pf_rows][D]
+  float* pf_plse;            // [max_pf_items][pf_rows]
   // shapes
   int32_t T, Hq, Hkv, G, D, page, P, S_max, pps;
+  int32_t pf_rows;           // packed rows of a prefill-class unit
   int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
   int32_t target_dec_items, target_pf_items;
   // numerics
@@ -129,6 +142,39 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v;
+}
+
+// Split-KV partials cross workgroups (and XCDs, whose L2 caches are not
+// coherent with each other). They are written and read with device-coherent
+// (agent-scope) accesses, which bypass the per-XCD L2 state, so the handoff
+// needs no L2 write-back or invalidate: the writer waits for its stores to
+// complete, then bumps the unit's counter; the merger reads after the counter.
+__device__ __forceinline__ void store_coherent(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent4(float* dst, f32x4 v) {  // dst 16-byte aligned
+  unsigned long long* d = reinterpret_cast<unsigned long long*>(dst);
+  __hip_atomic_store(d, __builtin_bit_cast(unsigned long long, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, __builtin_bit_cast(unsigned long long, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* src) {
+  return __hip_atomic_load(const_cast<float*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_coherent2(const float* src) {  // src 8-byte aligned
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(const_cast<float*>(src));
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Wait until this wave's stores have completed (and are therefore visible to
+// device-coherent reads); also a compiler barrier.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float wave_max_xor16_32(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));

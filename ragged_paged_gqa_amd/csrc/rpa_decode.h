@@ -25,10 +25,12 @@
 // k_scale is folded into the score scale and v_scale into the final
 // normalisation.
 // An item that is its unit's only chunk writes bf16 out and f32 lse; otherwise
-// it writes a normalised f32 partial and its lse for the merge kernel.
+// it writes a normalised f32 partial and its lse, and the wave that finishes
+// the unit's last chunk merges them (rpa_merge.h).
 #pragma once
 
 #include "rpa_common.h"
+#include "rpa_merge.h"
 
 namespace rpa {
 
@@ -61,12 +63,10 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void decode_kernel(Params p
   const bool capped = p.soft_cap > 0.f;
   const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
 
-  for (;;) {
-    int item = 0;
-    if (lane == 0) item = atomicAdd(&p.hdr->dec_counter, 1);
-    item = __builtin_amdgcn_readfirstlane(__shfl(item, 0));
-    if (item >= n_items) break;
-
+  // first item of each wave is static; later ones come from the queue
+  int item = blockIdx.x * kDecWavesPerBlock + wave;
+  const int first_dynamic = gridDim.x * kDecWavesPerBlock;
+  while (item < n_items) {
     const Item it = p.dec_items[item];
     const Unit u = p.dec_units[it.unit];
     const int s = u.seq;
@@ -102,15 +102,21 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void decode_kernel(Params p
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // page position of the step start, advanced without division
+    const int32_t* ptab = p.page_indices + (int64_t)s * p.pps;
+    int lp = c_lo / p.page;
+    int sl = c_lo - lp * p.page;
     for (int k0 = c_lo; k0 < c_hi; k0 += kStepKeys) {
       bf16x8 ka[2][NI];
       bf16x8 va[2][NI];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int kb = k0 + 16 * b;
+        const int lpb = (b == 0 || sl + 16 < p.page) ? lp : lp + 1;
+        const int slb = b == 0 ? sl : (sl + 16 < p.page ? sl + 16 : 0);
         if (kb < c_hi) {
-          const int phys = page_of(p, s, kb);
-          const int slot = kb % p.page + col;
+          const int phys = min(max(ptab[min(lpb, p.pps - 1)], 0), p.P - 1);
+          const int slot = slb + col;
           const uint8_t* base = p.kv + ((int64_t)phys * p.page + slot) * key_stride + (int64_t)2 * h * D * EB;
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
@@ -129,6 +135,16 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void decode_kernel(Params p
             va[b][i] = bf16x8{};
           }
         }
+      }
+
+      sl += kStepKeys;
+      if (sl >= p.page) {
+        sl -= p.page;
+        ++lp;
+      }
+      if (sl >= p.page) {
+        sl -= p.page;
+        ++lp;
       }
 
       // S^T: lane (col, g) gets keys k0 + 16b + 4g + j of row `col`.
@@ -210,22 +226,43 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void decode_kernel(Params p
     const float l_row = wave_sum_xor16_32(lsum);
     const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
     const float lse_v = l_row > 0.f ? (m + fast_log2(l_row)) * kLn2 : -INFINITY;
-    if (!rvalid) {
-      // rows past the unit: nothing to store
-    } else if (u.nch == 1) {
-      uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
+    if (u.nch == 1) {
+      if (rvalid) {
+        uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        u32x2 w = {bf16x2_bits(o[d][0] * inv, o[d][1] * inv), bf16x2_bits(o[d][2] * inv, o[d][3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = w;
+        for (int d = 0; d < ND; ++d) {
+          u32x2 w = {bf16x2_bits(o[d][0] * inv, o[d][1] * inv), bf16x2_bits(o[d][2] * inv, o[d][3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = w;
+        }
+        if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
       }
-      if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
     } else {
-      float* pp = p.dec_part + ((int64_t)item * kDecRows + col) * D;
+      if (rvalid) {
+        float* pp = p.dec_part + ((int64_t)item * kDecRows + col) * D;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) *reinterpret_cast<f32x4*>(pp + 16 * d + 4 * g) = o[d] * inv;
-      if (g == 0) p.dec_plse[(int64_t)item * kDecRows + col] = lse_v;
+        for (int d = 0; d < ND; ++d) store_coherent4(pp + 16 * d + 4 * g, o[d] * inv);
+        if (g == 0) store_coherent(p.dec_plse + (int64_t)item * kDecRows + col, lse_v);
+      }
+      // publish the partial, count the chunk; the last one merges the unit
+      wait_stores();
+      int done = 0;
+      if (lane == 0) done = atomicAdd(&p.unit_done[it.unit], 1);
+      done = __builtin_amdgcn_readfirstlane(__shfl(done, 0));
+      if (done == u.nch - 1) {
+        // the wave's V staging tile is free here; it holds the per-row stats
+        auto wave_sync = [] {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        merge_unit<D>(p, u, p.dec_part, p.dec_plse, kDecRows, lane, 64, reinterpret_cast<float*>(vs), wave_sync);
+        wave_sync();
+      }
     }
+
+    int nx = 0;
+    if (lane == 0) nx = atomicAdd(&p.hdr->dec_counter, 1);
+    item = first_dynamic + __builtin_amdgcn_readfirstlane(__shfl(nx, 0));
   }
 }
 

@@ -1,0 +1,81 @@
+// Split-KV merge, run by whichever wave/workgroup finishes a split unit's
+// last chunk (each chunk bumps the unit's counter after its partial is
+// written with device-coherent stores).
+//
+// Every chunk c of a row left a normalised partial O_c (f32) and its
+// log-sum-exp L_c. The row's result is the same merge of softmax blocks the
+// kernel page performs block to block inside `flashAttention` (new max, then
+// each side rescaled by exp(old max - new max)), applied once over all chunks:
+//   L = max_c L_c + log sum_c exp(L_c - max_c L_c),
+//   O = sum_c exp(L_c - L) * O_c,
+// summed in chunk order, so the result does not depend on which workgroup
+// merges or on timing. A row whose chunks all saw no key (every L_c = -inf)
+// gets O = 0 and L = -inf.
+//
+// Two phases, both fully parallel over the cooperating threads: (A) per row,
+// the max and the normalising sum of the chunk LSEs (kept in LDS, the row's
+// LSE written out); (B) per (row, 4-element piece of head_dim), the weighted
+// sum over chunks with all loads independent.
+#pragma once
+
+#include "rpa_common.h"
+
+namespace rpa {
+
+// Threads tid in [0, nt) cooperate; `sync` is called between the phases and
+// must synchronise exactly those threads. `stat` is LDS scratch of
+// 2 * u.nrows floats.
+template <int D, typename Sync>
+__device__ void merge_unit(const Params& p, const Unit& u, const float* part, const float* plse, int slot_rows,
+                           int tid, int nt, float* stat, Sync sync) {
+  int q0, ql;
+  seq_tokens(p, u.seq, q0, ql);
+  const float* lse_base = plse + (int64_t)u.item0 * slot_rows;
+  // phase A: per-row max and 1 / sum of exp(L_c - max)
+  for (int r = tid; r < u.nrows; r += nt) {
+    float mx = -INFINITY;
+    for (int c = 0; c < u.nch; ++c) mx = fmaxf(mx, load_coherent(lse_base + (int64_t)c * slot_rows + r));
+    float wsum = 0.f;
+    if (mx != -INFINITY)
+      for (int c = 0; c < u.nch; ++c) wsum += expf(load_coherent(lse_base + (int64_t)c * slot_rows + r) - mx);
+    stat[2 * r] = mx;
+    stat[2 * r + 1] = wsum > 0.f ? 1.0f / wsum : 0.f;
+    if (p.lse) {
+      const int prow = u.row0 + r;
+      const int t = prow / p.G;
+      const int qh = u.kv_head * p.G + (prow - t * p.G);
+      p.lse[(int64_t)(q0 + t) * p.Hq + qh] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
+    }
+  }
+  sync();
+  // phase B: out[row, 4 elements] = sum_c exp(L_c - max) / sum * O_c[row, 4 elements]
+  constexpr int PIECES = D / 4;
+  const float* part_base = part + (int64_t)u.item0 * slot_rows * D;
+  for (int idx = tid; idx < u.nrows * PIECES; idx += nt) {
+    const int r = idx / PIECES;
+    const int e0 = 4 * (idx % PIECES);
+    const float mx = stat[2 * r];
+    const float inv = stat[2 * r + 1];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (mx != -INFINITY) {
+#pragma unroll 4
+      for (int c = 0; c < u.nch; ++c) {
+        const float w = expf(load_coherent(lse_base + (int64_t)c * slot_rows + r) - mx);
+        const float* src = part_base + ((int64_t)c * slot_rows + r) * D + e0;
+        const f32x2 a = load_coherent2(src), b = load_coherent2(src + 2);
+        acc[0] += w * a[0];
+        acc[1] += w * a[1];
+        acc[2] += w * b[0];
+        acc[3] += w * b[1];
+      }
+    }
+    const int prow = u.row0 + r;
+    const int t = prow / p.G;
+    const int qh = u.kv_head * p.G + (prow - t * p.G);
+    uint16_t* op = p.out + ((int64_t)(q0 + t) * p.Hq + qh) * D + e0;
+    const u32x2 w2 = {bf16x2_bits(acc[0] * inv, acc[1] * inv), bf16x2_bits(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(op) = w2;
+  }
+}
+
+}  // namespace rpa

@@ -9,14 +9,14 @@
 //   * every sequence with q_len tokens gives q_len * G packed rows per kv head
 //     (row = token * G + g, G = Hq / Hkv: the page's GQA row packing);
 //   * sequences with <= kDecRows rows become one decode-class unit per kv
-//     head, longer ones become prefill-class units of kPfRows rows;
+//     head, longer ones become prefill-class units of pf_rows rows;
 //   * a unit's key range is only the keys some of its rows can see: up to the
 //     last row's causal position and, with a sliding window, from the first
 //     row's window start (rounded down to 16), so masked-out blocks are never
 //     read;
 //   * each unit is cut into chunks of a per-class key count chosen so that
-//     the whole batch yields about `target_*_items` items; units with more
-//     than one chunk are listed for the split merge.
+//     the whole batch yields about `target_*_items` items; the unit's
+//     finished-chunk counter is cleared for the split merge.
 #pragma once
 
 #include "rpa_common.h"
@@ -53,11 +53,12 @@ __device__ __forceinline__ int32_t n_chunks(int32_t lo16, int32_t hi, int32_t ch
   return n > 0 ? n : 1;
 }
 
-__device__ __forceinline__ int32_t pick_chunk(int64_t total_keys, int32_t target, int32_t min_chunk) {
+__device__ __forceinline__ int32_t pick_chunk(int64_t total_keys, int32_t target, int32_t min_chunk,
+                                              int32_t max_chunk) {
   int64_t c = (total_keys + target - 1) / (target > 0 ? target : 1);
   c = (c + 63) & ~(int64_t)63;
   if (c < min_chunk) c = min_chunk;
-  if (c > (1 << 28)) c = 1 << 28;
+  if (c > max_chunk) c = max_chunk;
   return (int32_t)c;
 }
 
@@ -115,8 +116,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       UnitRange r = unit_range(p, ql, kvl, 0, rows);
       dec_keys += (int64_t)p.Hkv * max(0, r.hi - r.lo16);
     } else {
-      for (int32_t r0 = 0; r0 < rows; r0 += kPfRows) {
-        UnitRange r = unit_range(p, ql, kvl, r0, min(kPfRows, rows - r0));
+      for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
+        UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
         pf_keys += (int64_t)p.Hkv * max(0, r.hi - r.lo16);
       }
     }
@@ -136,11 +137,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     tot_dec += red[0][w];
     tot_pf += red[1][w];
   }
-  const int32_t dec_chunk = pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk);
-  const int32_t pf_chunk = pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk);
+  const int32_t dec_chunk = pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, 1 << 28);
+  const int32_t pf_chunk = pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk);
+
+  // pass 1b: prefill items per queue (queue of (seq, kv head) = (seq*Hkv + h) % kQueues)
+  __shared__ int32_t q_tot[kQueues];
+  if (tid < kQueues) q_tot[tid] = 0;
+  __syncthreads();
+  for (int32_t s = tid; s < n; s += kPlanThreads) {
+    int32_t q0, ql, kvl;
+    seq_meta(p, s, q0, ql, kvl);
+    const int32_t rows = ql * p.G;
+    if (ql <= 0 || rows <= kDecRows) continue;
+    int32_t per_head = 0;
+    for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
+      UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
+      per_head += n_chunks(r.lo16, r.hi, pf_chunk);
+    }
+    for (int32_t h = 0; h < p.Hkv; ++h) atomicAdd(&q_tot[(s * p.Hkv + h) % kQueues], per_head);
+  }
+  __syncthreads();
+  int32_t q_base[kQueues];
+  {
+    int32_t run = 0;
+    for (int x = 0; x < kQueues; ++x) {
+      q_base[x] = run;
+      run += q_tot[x];
+    }
+  }
 
   // pass 2: per-sequence counts -> scans -> records
   int32_t base_du = 0, base_pu = 0, base_di = 0, base_pi = 0, base_sp = 0;
+  int32_t q_run[kQueues];
+  for (int x = 0; x < kQueues; ++x) q_run[x] = 0;
   for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
     const int32_t s = s0 + tid;
     int32_t q0 = 0, ql = 0, kvl = 0;
@@ -159,8 +188,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
           c_sp = nch > 1 ? p.Hkv : 0;
         } else {
           int32_t per_head_items = 0, per_head_split = 0, nrb = 0;
-          for (int32_t r0 = 0; r0 < rows; r0 += kPfRows) {
-            UnitRange r = unit_range(p, ql, kvl, r0, min(kPfRows, rows - r0));
+          for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
+            UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
             const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
             per_head_items += nch;
             per_head_split += nch > 1 ? 1 : 0;
@@ -177,7 +206,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     int32_t o_pu = base_pu + block_exclusive_scan(c_pu, sh, &t_pu);
     int32_t o_di = base_di + block_exclusive_scan(c_di, sh, &t_di);
     int32_t o_pi = base_pi + block_exclusive_scan(c_pi, sh, &t_pi);
-    int32_t o_sp = base_sp + block_exclusive_scan(c_sp, sh, &t_sp);
+    (void)block_exclusive_scan(c_sp, sh, &t_sp);
+    // this sequence's position in each prefill queue
+    int32_t o_q[kQueues];
+    for (int x = 0; x < kQueues; ++x) {
+      int32_t cnt = 0;
+      if (!is_dec && s < n && ql > 0)
+        for (int32_t h = 0; h < p.Hkv; ++h) cnt += ((s * p.Hkv + h) % kQueues == x) ? c_pi / p.Hkv : 0;
+      int32_t t_q;
+      o_q[x] = q_base[x] + q_run[x] + block_exclusive_scan(cnt, sh, &t_q);
+      q_run[x] += t_q;
+    }
 
     if (s < n && ql > 0) {
       const int32_t rows = ql * p.G;
@@ -191,17 +230,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
           u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = rows;
           u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = o_di + h * nch;
           p.dec_units[ui] = u;
+          p.unit_done[ui] = 0;
           for (int32_t c = 0; c < nch; ++c) {
             const int32_t ii = u.item0 + c;
             if (ii < p.max_dec_items) p.dec_items[ii] = Item{ui, c};
           }
-          if (nch > 1) p.split_units[o_sp++] = (0 << 30) | ui;
         }
       } else {
         int32_t ui = o_pu, ii = o_pi;
         for (int32_t h = 0; h < p.Hkv; ++h) {
-          for (int32_t r0 = 0; r0 < rows; r0 += kPfRows) {
-            const int32_t nr = min(kPfRows, rows - r0);
+          for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
+            const int32_t nr = min(p.pf_rows, rows - r0);
             UnitRange r = unit_range(p, ql, kvl, r0, nr);
             const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
             if (ui < p.max_pf_units) {
@@ -209,13 +248,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
               u.seq = s; u.kv_head = h; u.row0 = r0; u.nrows = nr;
               u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = ii;
               p.pf_units[ui] = u;
+              p.unit_done[p.max_dec_units + ui] = 0;
               for (int32_t c = 0; c < nch; ++c)
                 if (ii + c < p.max_pf_items) p.pf_items[ii + c] = Item{ui, c};
-              if (nch > 1) p.split_units[o_sp++] = (1 << 30) | ui;
             }
             ++ui;
             ii += nch;
           }
+        }
+        // queue entries of each head: chunk-major, then row block
+        int32_t ii_h = o_pi;
+        for (int32_t h = 0; h < p.Hkv; ++h) {
+          const int x = (s * p.Hkv + h) % kQueues;
+          int32_t k = o_q[x];
+          const int32_t per_head = c_pi / p.Hkv;
+          for (int32_t c = 0;; ++c) {
+            bool any = false;
+            int32_t ii_rb = ii_h;
+            for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
+              UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
+              const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
+              if (c < nch) {
+                any = true;
+                if (k < p.max_pf_items && ii_rb + c < p.max_pf_items) p.pf_qlist[k] = ii_rb + c;
+                ++k;
+              }
+              ii_rb += nch;
+            }
+            if (!any) break;
+          }
+          o_q[x] = k;
+          ii_h += per_head;
         }
       }
     }
@@ -231,7 +294,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     h.pf_chunk = pf_chunk;
     h.n_split_units = base_sp;
     h.dec_counter = 0;
-    h.pf_counter = 0;
+    for (int x = 0; x < kQueues; ++x) {
+      h.pf_q_base[x] = min(q_base[x], p.max_pf_items);
+      h.pf_q_count[x] = max(0, min(q_tot[x], p.max_pf_items - h.pf_q_base[x]));
+      h.pf_q_next[x] = 0;
+    }
     *p.hdr = h;
   }
 }

@@ -1,263 +1,469 @@
-// Prefill/mixed-class attention kernel: units of up to 128 packed query rows
-// (row = token * G + g) of one sequence and one kv head, i.e. the kernel
-// page's q block of `num_queries_per_block` tokens times G grouped q heads
-// stacked into one MFMA M dimension (`run`, per-kv-head step).
+// Prefill/mixed-class attention kernel: units of up to kPfRows packed query
+// rows (row = token * G + g) of one sequence and one kv head — the kernel
+// page's q block of `num_queries_per_block` tokens times the G q heads of one
+// kv head, stacked into one MFMA dimension (`run`, per-kv-head step).
 //
-// A workgroup of 4 waves owns one item at a time (pulled from a device-wide
-// queue); wave w owns rows [32w, 32w + 32) as two 16-wide column blocks.
-// Per 32-key step the workgroup
-//   1. gathers the step's K and V rows of kv head h (combined heads 2h, 2h+1,
-//      adjacent in memory, `stridedLoadKv`) through the page table into
-//      registers with 16-byte loads — issued one step ahead so the HBM latency
-//      overlaps the MFMA work of the current step — and writes them to a
-//      double-buffered LDS tile (V zeroed past kv_len);
-//   2. per wave: S^T = K Q^T (v_mfma_f32_16x16x32_bf16, K from LDS, Q^T held in
-//      registers), sm_scale (k_scale folded in), soft-cap, masks by selection,
-//      base-2 online softmax (`flashAttention`), then O^T += V^T P^T with V^T
-//      read by ds_read_b64_tr_b16 and P^T taken straight from the S^T layout.
-// One barrier per step protects the double buffer.
+// A workgroup of NW waves owns one item (a key chunk of a unit) at a time,
+// pulled from a device-wide queue; wave w owns rows [32w, 32w + 32). Split
+// units leave partials; the workgroup finishing a unit's last chunk merges
+// them (rpa_merge.h).
+// Per 32-key step:
+//   * loader: the step's K and V rows of kv head h (combined heads 2h and
+//     2h+1, adjacent in memory — `stridedLoadKv`) are gathered through the
+//     page table into a ring of LDS tiles whose rows are padded so that the
+//     MFMA operand reads below are bank-conflict free. bf16 rows go straight
+//     from HBM to LDS (global_load_lds_dwordx4, one padded row per
+//     instruction) kStagesBf16 - 1 steps ahead of the compute; fp8 rows are
+//     staged through registers one step ahead and widened to bf16 on the way.
+//     Page position is tracked incrementally (no integer division in the
+//     loop);
+//   * S^T [32 keys x 32 rows] = K Q^T with v_mfma_f32_32x32x16_bf16, Q^T kept
+//     in registers; lane (row, half h) holds 16 keys of its row, so a row
+//     maximum needs one cross-lane exchange;
+//   * masks (`flashAttention`: causal, sliding window, kv length) are applied
+//     only on steps that can contain a hidden key; other steps take an
+//     unmasked path;
+//   * base-2 online softmax with a lazily moved reference maximum: the
+//     accumulator is rescaled only when some row's maximum grows by more than
+//     kRescaleSlack (2^8), which keeps every exponentiated score <= 2^8;
+//   * O^T [D x 32 rows] += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T
+//     taken straight from the S^T accumulator layout.
 #pragma once
 
 #include "rpa_common.h"
+#include "rpa_merge.h"
 
 namespace rpa {
 
-template <int D>
-struct PrefillLds {
-  static constexpr int kKStride = D + 8;   // +16 B per K row
-  static constexpr int kVStride = D + 16;  // +32 B per V row
-  static constexpr int kKElems = kStepKeys * kKStride;
-  static constexpr int kVElems = kStepKeys * kVStride;
-  static constexpr size_t kBytes = (size_t)2 * (kKElems + kVElems) * 2;
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kStagesBf16 = 4;
+// Cached page-table entries per item: the largest chunk over the smallest page
+// (16 keys), plus the partial pages at both ends.
+constexpr int kPfPageCache = kPfMaxChunk / 16 + 4;
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_kernel(Params p) {
-  constexpr int NI = D / 32;
-  constexpr int ND = D / 16;
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KST = PrefillLds<D>::kKStride;
-  constexpr int VST = PrefillLds<D>::kVStride;
-  constexpr int NT = kPfWaves * 64;
-  // 16-byte global chunks per key (K and V together) and per thread per step
-  constexpr int CPK = 2 * D * EB / 16;
-  constexpr int CPT = kStepKeys * CPK / NT;
-  static_assert(kStepKeys * CPK % NT == 0, "chunks must divide evenly");
+struct PrefillLds {
+  // K row (2D bytes) then V row (2D bytes), padded to 16*(16n+3) bytes so that
+  // 16 consecutive keys start in distinct 16-byte bank groups.
+  static constexpr int kRowBytes = 4 * D + 48;
+  static constexpr int kBufBytes = kStepKeys * kRowBytes;
+  static constexpr int kStages = FP8 ? 2 : kStagesBf16;
+  static constexpr size_t kBytes = (size_t)kStages * kBufBytes;
+};
 
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][PrefillLds<D>::kKElems];
-  __shared__ __attribute__((aligned(16))) __bf16 vsm[2][PrefillLds<D>::kVElems];
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
+// lane (global_load_lds_dwordx4; lds_addr is the wave-uniform LDS byte
+// address, passed through M0, which is restored afterwards). Written as inline
+// assembly so that the compiler does not add its own conservative wait for the
+// LDS write before every later LDS read: completion is tracked explicitly with
+// wait_vmcnt before the barrier that publishes a stage. An SALU write of M0
+// needs one wait state before an instruction that reads M0 (the compiler puts
+// the same s_nop between its own M0 write and LDS DMA); one more keeps the
+// restore clear of the DMA.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// Scheduling hints: the next `n` LDS reads, then the next `n` MFMAs.
+#define RPA_SCHED_DS_READS(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
+#define RPA_SCHED_MFMAS(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
+
+template <int D, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
+  constexpr int NS = D / 16;                  // k-steps of the QK product
+  constexpr int NDB = D / 32;                 // 32-row blocks of O^T
+  constexpr int EB = FP8 ? 1 : 2;             // bytes per K/V element in HBM
+  constexpr int NT = NW * 64;
+  constexpr int RB = PrefillLds<D, FP8>::kRowBytes;
+  constexpr int BUF = PrefillLds<D, FP8>::kBufBytes;
+  constexpr int NST = PrefillLds<D, FP8>::kStages;
+  constexpr int GCH = 2 * D * EB / 16;        // 16-byte global chunks per key (K and V)
+  constexpr int CPT = (kStepKeys * GCH + NT - 1) / NT;  // fp8 path: chunks per thread per step
+  constexpr int RPW = kStepKeys / NW;         // bf16 path: rows each wave moves per step
+  constexpr int LPR = 4 * D / 16;             // bf16 path: lanes per row (16 bytes each)
+  static_assert(NDB >= 2, "head_dim >= 64");
+  static_assert(LPR <= 64, "one row per DMA instruction");
+
+  __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
+  __shared__ int sh_pages[kPfPageCache];  // physical pages of the current item
   __shared__ int sh_item[2];
+  __shared__ int sh_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;
-  const int g = lane >> 4;
+  const int r32 = lane & 31;  // S^T column = row within the wave
+  const int h = lane >> 5;    // which half of the row's keys this lane holds
 
-  const int n_items = p.hdr->n_pf_items;
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
   const bool capped = p.soft_cap > 0.f;
   const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
+  // scores in base-2 units: s2 = S * c2 (no cap) ; negative scales flip Q's sign
+  const bool neg = p.sm_scale < 0.f;
+  const float sm = neg ? -p.sm_scale : p.sm_scale;
+  const float c2 = sm * kLog2e;
+
+  // LDS read bases (byte offsets inside a buffer)
+  const int k_rd = r32 * RB + 16 * h;  // K[key = r32][8h ...] ; + 32*s per k-step
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int v_rd = (4 * (g16 >> 1) + (l16 >> 2)) * RB + 2 * D + 2 * (16 * (g16 & 1) + 4 * (l16 & 3));
+
+  // queues: start with this XCD's, then steal from the others in turn
+  const int home = xcc_id() % kQueues;
+  int qsel = 0;  // used by thread 0 only
+  auto next_item = [&]() -> int {
+    while (qsel < kQueues) {
+      const int x = (home + qsel) % kQueues;
+      const int k = atomicAdd(&p.hdr->pf_q_next[x], 1);
+      if (k < p.hdr->pf_q_count[x]) return p.pf_qlist[p.hdr->pf_q_base[x] + k];
+      ++qsel;
+    }
+    return -1;
+  };
 
   int parity = 0;
-  int buf = 0;
+  int ring = 0;  // LDS ring slot of the next step to compute
   for (;;) {
-    if (tid == 0) sh_item[parity] = atomicAdd(&p.hdr->pf_counter, 1);
+    if (tid == 0) sh_item[parity] = next_item();
     __syncthreads();
     const int item = sh_item[parity];
     parity ^= 1;
-    if (item >= n_items) break;
+    if (item < 0) break;
 
     const Item it = p.pf_items[item];
     const Unit u = p.pf_units[it.unit];
     const int s = u.seq;
-    const int h = u.kv_head;
+    const int kvh = u.kv_head;
     int q0, ql;
     seq_tokens(p, s, q0, ql);
     int kvl = p.kv_lens[s];
     kvl = max(0, min(kvl, p.pps * p.page));
     const int c_lo = u.kv_lo + it.chunk * chunk;
     const int c_hi = min(u.kv_hi, c_lo + chunk);
-    const uint8_t* kv_h = p.kv + (int64_t)2 * h * D * EB;
+    const int n_steps = c_hi > c_lo ? (c_hi - c_lo + kStepKeys - 1) / kStepKeys : 0;
+    const uint8_t* kv_h = p.kv + (int64_t)2 * kvh * D * EB;
+    const int32_t* ptab = p.page_indices + (int64_t)s * p.pps;
+    // physical pages of the item's key range, clamped, cached in LDS
+    const int lp0 = c_lo / p.page;
+    const int n_pg = min(n_steps > 0 ? (c_lo + n_steps * kStepKeys - 1) / p.page - lp0 + 1 : 0, kPfPageCache);
+    for (int i = tid; i < n_pg; i += NT) sh_pages[i] = min(max(ptab[min(lp0 + i, p.pps - 1)], 0), p.P - 1);
+    __syncthreads();
 
-    // this lane's two query rows (one per column block)
-    bool rvalid[2];
-    int tok[2], qh[2], pos[2];
-    bf16x8 qb[2][NI];
+    // this lane's query row
+    const int r = 32 * wave + r32;
+    const bool rvalid = r < u.nrows;
+    const int prow = u.row0 + r;
+    const int t = prow / p.G;
+    const int qh = kvh * p.G + (prow - t * p.G);
+    const int tok = q0 + t;
+    const int pos = kvl - ql + t;
+    bf16x8 qb[NS];
+    if (rvalid) {
+      const uint16_t* qp = p.q + ((int64_t)tok * p.Hq + qh) * D;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int r = 32 * wave + 16 * cb + col;
-      rvalid[cb] = r < u.nrows;
-      const int prow = u.row0 + r;
-      const int t = prow / p.G;
-      qh[cb] = h * p.G + (prow - t * p.G);
-      tok[cb] = q0 + t;
-      pos[cb] = kvl - ql + t;
-      if (rvalid[cb]) {
-        const uint16_t* qp = p.q + ((int64_t)tok[cb] * p.Hq + qh[cb]) * D;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) qb[cb][i] = *reinterpret_cast<const bf16x8*>(qp + 32 * i + 8 * g);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) qb[cb][i] = bf16x8{};
+      for (int i = 0; i < NS; ++i) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * i + 8 * h);
+        if (neg) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        qb[i] = __builtin_bit_cast(bf16x8, v);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) qb[i] = bf16x8{};
     }
+    // the wave's row span, for the masked-step test
+    const int wr_last = min(32 * wave + 31, u.nrows - 1);
+    const int pos_lo = kvl - ql + (u.row0 + 32 * wave) / p.G;
+    const int pos_hi = kvl - ql + (u.row0 + max(wr_last, 32 * wave)) / p.G;
 
-    float m[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};
-    f32x4 o[2][ND];
+    float m_ref = -INFINITY;  // reference max (base-2 units) of this lane's row
+    float lsum = 0.f;
+    f32x16 o[NDB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int d = 0; d < ND; ++d) o[cb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
 
-    // global -> register staging of one step
+    // page position of the next step to load, advanced without division
+    int lp = c_lo / p.page;
+    int sl = c_lo - lp * p.page;
+    auto advance = [&]() {
+      sl += kStepKeys;
+      if (sl >= p.page) {
+        sl -= p.page;
+        ++lp;
+      }
+      if (sl >= p.page) {
+        sl -= p.page;
+        ++lp;
+      }
+    };
+    // base addresses of the two 16-key blocks of the step at (lp, sl)
+    auto block_bases = [&](int k0, const uint8_t*& b0, const uint8_t*& b1, bool& on1) {
+      int lp1 = lp, sl1 = sl + 16;
+      if (sl1 >= p.page) {
+        sl1 = 0;
+        lp1 = lp + 1;
+      }
+      const int ph0 = sh_pages[min(lp - lp0, kPfPageCache - 1)];
+      on1 = k0 + 16 < c_hi;
+      const int ph1 = on1 ? sh_pages[min(lp1 - lp0, kPfPageCache - 1)] : ph0;
+      b0 = kv_h + ((int64_t)ph0 * p.page + sl) * key_stride;
+      b1 = on1 ? kv_h + ((int64_t)ph1 * p.page + sl1) * key_stride : b0;
+    };
+
+    // ---- loader, bf16: rows straight into the LDS ring ----
+    auto issue_dma = [&](int k0, char* dst) {
+      const uint8_t *b0, *b1;
+      bool on1;
+      block_bases(k0, b0, b1, on1);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int key = wave * RPW + i;
+        // an out-of-range block re-reads block 0 (harmless: masked, V zeroed)
+        const uint8_t* src = (key >= 16 ? b1 : b0) + (int64_t)(key & 15) * key_stride;
+        if (lane < LPR) dma16(src + 16 * lane, lds_addr_of(dst + key * RB));
+      }
+    };
+    // ---- loader, fp8: registers one step ahead, widened to bf16 ----
     u32x4 stage[CPT];
-    auto load_step = [&](int k0) {
+    auto load_regs = [&](int k0) {
+      const uint8_t *b0, *b1;
+      bool on1;
+      block_bases(k0, b0, b1, on1);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + NT * c;
-        const int key = idx / CPK;
-        const int w16 = idx % CPK;
-        const int kb = k0 + (key & ~15);
-        if (kb < c_hi) {
-          const int phys = page_of(p, s, k0 + key);
-          const int slot = (k0 + key) % p.page;
-          const uint8_t* src = kv_h + ((int64_t)phys * p.page + slot) * key_stride + 16 * w16;
-          stage[c] = *reinterpret_cast<const u32x4*>(src);
+        const int key = idx / GCH;
+        if (idx < kStepKeys * GCH && (key < 16 || on1)) {
+          const int off = (key & 15) * (int)key_stride + 16 * (idx % GCH);
+          stage[c] = *reinterpret_cast<const u32x4*>((key >= 16 ? b1 : b0) + off);
         } else {
           stage[c] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     };
-    auto store_step = [&](int k0, int b) {
+    auto store_regs = [&](int k0, char* dst) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + NT * c;
-        const int key = idx / CPK;
-        const int w16 = idx % CPK;
-        const bool valid_v = k0 + key < kvl;
-        if constexpr (FP8) {
-          // 16 codes -> 16 bf16; K codes occupy the first D bytes of the key
-          const int e0 = 16 * w16;
-          const bool is_v = e0 >= D;
-          const int d0 = is_v ? e0 - D : e0;
-          u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
-          bf16x8 a = fp8x8_to_bf16(lo2), bb = fp8x8_to_bf16(hi2);
-          if (is_v && !valid_v) {
-            a = bf16x8{};
-            bb = bf16x8{};
-          }
-          __bf16* dst = is_v ? &vsm[b][key * VST + d0] : &ks[b][key * KST + d0];
-          *reinterpret_cast<bf16x8*>(dst) = a;
-          *reinterpret_cast<bf16x8*>(dst + 8) = bb;
-        } else {
-          const int e0 = 8 * w16;
-          const bool is_v = e0 >= D;
-          const int d0 = is_v ? e0 - D : e0;
-          u32x4 v = stage[c];
-          if (is_v && !valid_v) v = u32x4{0u, 0u, 0u, 0u};
-          __bf16* dst = is_v ? &vsm[b][key * VST + d0] : &ks[b][key * KST + d0];
-          *reinterpret_cast<u32x4*>(dst) = v;
+        if (idx >= kStepKeys * GCH) continue;
+        const int key = idx / GCH;
+        const int dst_off = key * RB + 32 * (idx % GCH);  // 16 codes -> 32 bytes
+        u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
+        bf16x8 a = fp8x8_to_bf16(lo2), b = fp8x8_to_bf16(hi2);
+        if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
+          a = bf16x8{};
+          b = bf16x8{};
         }
+        *reinterpret_cast<bf16x8*>(dst + dst_off) = a;
+        *reinterpret_cast<bf16x8*>(dst + dst_off + 16) = b;
       }
     };
+    auto slot_ptr = [&](int k) { return lds + ((ring + k) % NST) * BUF; };
 
-    if (c_lo < c_hi) load_step(c_lo);
-    for (int k0 = c_lo; k0 < c_hi; k0 += kStepKeys) {
-      store_step(k0, buf);
-      __syncthreads();
-      if (k0 + kStepKeys < c_hi) load_step(k0 + kStepKeys);
+    // prologue: NST - 1 steps in flight
+    int issued = 0;
+    if constexpr (FP8) {
+      if (n_steps > 0) {
+        load_regs(c_lo);
+        advance();
+        issued = 1;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NST - 1; ++k) {
+        if (k < n_steps) {
+          issue_dma(c_lo + k * kStepKeys, slot_ptr(k));
+          advance();
+          issued = k + 1;
+        }
+      }
+    }
 
-      const __bf16* kt = ks[buf];
-      const __bf16* vt = vsm[buf];
-      f32x4 sc[2][2];  // [key block][column block]
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sc[b][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + (16 * b + col) * KST + 32 * i + 8 * g);
-          sc[b][0] = mfma16x16x32(ka, qb[0][i], sc[b][0]);
-          sc[b][1] = mfma16x16x32(ka, qb[1][i], sc[b][1]);
+    for (int n = 0; n < n_steps; ++n) {
+      const int k0 = c_lo + n * kStepKeys;
+      char* cur = slot_ptr(0);
+      if constexpr (FP8) {
+        store_regs(k0, cur);
+        __syncthreads();
+        if (issued < n_steps) {
+          load_regs(c_lo + issued * kStepKeys);
+          advance();
+          ++issued;
+        }
+      } else {
+        // wait for this step's rows: later steps may stay in flight
+        const int ahead = issued - n - 1;
+        if (ahead >= 2) {
+          wait_vmcnt<2 * RPW>();
+        } else if (ahead == 1) {
+          wait_vmcnt<RPW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (k0 + kStepKeys > kvl || k0 + kStepKeys > c_hi) {
+          // zero V of rows past kv_len or past the loaded blocks
+          for (int i = tid; i < kStepKeys * (2 * D / 16); i += NT) {
+            const int key = i / (2 * D / 16);
+            const bool loaded = key < 16 || k0 + 16 < c_hi;
+            if (k0 + key >= kvl || !loaded)
+              *reinterpret_cast<u32x4*>(cur + key * RB + 2 * D + 16 * (i % (2 * D / 16))) = u32x4{0u, 0u, 0u, 0u};
+          }
+          __syncthreads();
+        }
+        // refill the slot freed by the previous step (every wave is past it)
+        if (issued < n_steps) {
+          issue_dma(c_lo + issued * kStepKeys, slot_ptr(NST - 1));
+          advance();
+          ++issued;
         }
       }
 
+      // S^T = K Q^T
+      f32x16 st = f32x16{};
+      {
+        const char* kr = cur + k_rd;
+        bf16x8 ka[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + 32 * i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st = mfma32x32x16(ka[i], qb[i], st);
+        RPA_SCHED_DS_READS(NS);
+        RPA_SCHED_MFMAS(NS);
+      }
+
+      // scores -> base-2 units, masked where needed
+      const bool need_mask = k0 + kStepKeys > min(kvl, c_hi) || (p.is_causal && k0 + kStepKeys - 1 > pos_lo) ||
+                             (p.window > 0 && k0 <= pos_hi - p.window);
+      if (capped) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st[j] = soft_cap_f(st[j] * sm, p.soft_cap, cap_k) * kLog2e;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st[j] *= c2;
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 8 * (j >> 2) + 4 * h + (j & 3);
+          bool vis = rvalid && key < kvl && key < c_hi;
+          if (p.is_causal) vis = vis && key <= pos;
+          if (p.window > 0) vis = vis && key > pos - p.window;
+          st[j] = vis ? st[j] : -INFINITY;
+        }
+      }
+      float mx = st[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // move the reference max only when some row outgrew it by the slack
+      if (__any(mx > m_ref + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = fast_exp2(m_ref - (m_new == -INFINITY ? 0.f : m_new));
+        m_ref = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       bf16x8 pb[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 16 * b + 4 * g + j;
-            float x = sc[b][cb][j] * p.sm_scale;
-            if (capped) x = soft_cap_f(x, p.soft_cap, cap_k);
-            bool vis = rvalid[cb] && key < kvl && key < c_hi;
-            if (p.is_causal) vis = vis && key <= pos[cb];
-            if (p.window > 0) vis = vis && key > pos[cb] - p.window;
-            const float s2 = vis ? x * kLog2e : -INFINITY;
-            sc[b][cb][j] = s2;
-            mx = fmaxf(mx, s2);
-          }
-        }
-        mx = wave_max_xor16_32(mx);
-        const float m_new = fmaxf(m[cb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m[cb] - m_use);
-        m[cb] = m_new;
-        lsum[cb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) o[cb][d] *= alpha;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float pv = fast_exp2(sc[b][cb][j] - m_use);
-            lsum[cb] += pv;
-            pb[cb][4 * b + j] = (__bf16)pv;
-          }
+      for (int j = 0; j < 16; ++j) {
+        const float pv = fast_exp2(st[j] - m_use);
+        lsum += pv;
+        pb[j >> 3][j & 7] = (__bf16)pv;
       }
 
-      const __bf16* vrow = vt + (4 * g + (col >> 2)) * VST + 4 * (col & 3);
+      // O^T += V^T P^T (two 16-key k-steps)
+      const char* vr = cur + v_rd;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const bf16x4 lo = lds_read_tr16(vrow + 16 * d);
-        const bf16x4 hi = lds_read_tr16(vrow + 16 * VST + 16 * d);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[0][d] = mfma16x16x32(a, pb[0], o[0][d]);
-        o[1][d] = mfma16x16x32(a, pb[1], o[1][d]);
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 va[NDB];
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + 64 * d));
+          const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + 64 * d));
+          va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[d] = mfma32x32x16(va[d], pb[ks], o[d]);
+        RPA_SCHED_DS_READS(2 * NDB);
+        RPA_SCHED_MFMAS(NDB);
       }
-      buf ^= 1;
+      ring = (ring + 1) % NST;
     }
 
+    const float l_row = lsum + __shfl_xor(lsum, 32);
+    const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
+    const float lse_v = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
+    // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
+    if (u.nch == 1) {
+      if (rvalid) {
+        uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D + 4 * h;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float l_row = wave_sum_xor16_32(lsum[cb]);
-      const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
-      const float lse_v = l_row > 0.f ? (m[cb] + fast_log2(l_row)) * kLn2 : -INFINITY;
-      const int r = 32 * wave + 16 * cb + col;
-      if (!rvalid[cb]) {
-        // rows past the unit: nothing to store
-      } else if (u.nch == 1) {
-        uint16_t* op = p.out + ((int64_t)tok[cb] * p.Hq + qh[cb]) * D;
+        for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          u32x2 w = {bf16x2_bits(o[cb][d][0] * inv, o[cb][d][1] * inv),
-                     bf16x2_bits(o[cb][d][2] * inv, o[cb][d][3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = w;
-        }
-        if (g == 0 && p.lse) p.lse[(int64_t)tok[cb] * p.Hq + qh[cb]] = lse_v;
-      } else {
-        float* pp = p.pf_part + ((int64_t)item * kPfRows + r) * D;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x2 w = {bf16x2_bits(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv),
+                       bf16x2_bits(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(op + 32 * d + 8 * q4) = w;
+          }
+        if (h == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
+      }
+    } else {
+      if (rvalid) {
+        float* pp = p.pf_part + ((int64_t)item * p.pf_rows + r) * D + 4 * h;
 #pragma unroll
-        for (int d = 0; d < ND; ++d) *reinterpret_cast<f32x4*>(pp + 16 * d + 4 * g) = o[cb][d] * inv;
-        if (g == 0) p.pf_plse[(int64_t)item * kPfRows + r] = lse_v;
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 w = {o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv, o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
+            store_coherent4(pp + 32 * d + 8 * q4, w);
+          }
+        if (h == 0) store_coherent(p.pf_plse + (int64_t)item * p.pf_rows + r, lse_v);
+      }
+      // publish the partial, count the chunk; the last one merges the unit
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) sh_last = atomicAdd(&p.unit_done[p.max_dec_units + it.unit], 1) == u.nch - 1;
+      __syncthreads();
+      if (sh_last) {
+        // the LDS ring is idle here (every wave is past its last step); it
+        // holds the per-row stats of the merge
+        auto wg_sync = [] { __syncthreads(); };
+        merge_unit<D>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
       }
     }
+    // every wave must be done with the ring before the next item refills it
+    __syncthreads();
   }
 }
 
