@@ -28,10 +28,12 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *compile_flags(), "-o", tmp, SRC]
+def build(verbose: bool = False, out: str | None = None, defines: tuple[str, ...] = ()) -> str:
+    """Compile librpa.so (or `out`); `defines` are NAME=VALUE tuning overrides."""
+    lib = out or LIB
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *compile_flags(), *(f"-D{d}" for d in defines), "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,9 +44,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    print(build(verbose=True, out=a.out, defines=tuple(a.defines)))

@@ -22,7 +22,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDecRows = 16;
 // Waves (of 32 rows each) of a prefill-class tile: 8 for head_dim <= 128;
 // 4 for head_dim 256, whose accumulators need a whole SIMD's registers.
-constexpr int pf_waves_for(int D) { return D >= 256 ? 4 : 8; }
+#ifndef RPA_PF_WAVES_NARROW
+#define RPA_PF_WAVES_NARROW 8
+#endif
+constexpr int pf_waves_for(int D) { return D >= 256 ? 4 : RPA_PF_WAVES_NARROW; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;
 // Largest key chunk of a prefill-class item (bounds the per-item page cache).

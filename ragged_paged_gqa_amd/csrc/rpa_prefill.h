@@ -43,7 +43,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kStagesBf16 = 4;
+#ifndef RPA_PF_STAGES
+#define RPA_PF_STAGES 4
+#endif
+constexpr int kStagesBf16 = RPA_PF_STAGES;
 // Cached page-table entries per item: the largest chunk over the smallest page
 // (16 keys), plus the partial pages at both ends.
 constexpr int kPfPageCache = kPfMaxChunk / 16 + 4;
@@ -123,6 +126,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int r32 = lane & 31;  // S^T column = row within the wave
   const int h = lane >> 5;    // which half of the row's keys this lane holds
 
+  if (p.hdr->n_pf_items == 0) return;  // nothing of this class in the batch
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
   const bool capped = p.soft_cap > 0.f;
