@@ -143,19 +143,24 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
 
 /*
  * Byte offsets inside the workspace (host-only, no device access):
- *   offsets[0] header: int32[16] = {n_dec_units, n_pf_units, n_dec_items,
- *              n_pf_items, dec_chunk, pf_chunk, n_split_units, ...}
- *              (n_split_units counts units with more than one chunk)
+ *   offsets[0] header: int32[64] = {n_dec_units, n_pf_units, n_dec_items,
+ *              n_pf_items, dec_chunk, pf_chunk, n_split_units, dec_counter,
+ *              pad[8], queue_base[8], queue_count[8], queue_next[8], pad[24]}
+ *              (n_split_units counts units with more than one chunk; the
+ *              prefill items are dealt into 8 queues, one per XCD, and queue
+ *              x is queue_count[x] entries of the queue list from
+ *              queue_base[x] = x * max_pf_items on)
  *   offsets[1] decode units   int32[max_dec_units][8]
  *   offsets[2] prefill units  int32[max_pf_units][8]
  *   offsets[3] decode items   int32[max_dec_items][2]
  *   offsets[4] prefill items  int32[max_pf_items][2]
+ *   offsets[5] queue list     int32[8][max_pf_items] (prefill item indices)
  * A unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}; an item is
  * {unit, chunk}, covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo + (chunk+1)*C))
  * with C the class's chunk size. limits = {max_dec_units, max_pf_units,
  * max_dec_items, max_pf_items, dec_rows_max, pf_rows_max}.
  */
-rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t limits[6]);
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[6], int32_t limits[6]);
 
 /*
  * Debug helper for tests: decode n fp8 e4m3fn codes (device array) to

@@ -139,7 +139,7 @@ def workspace_bytes(cfg: Config) -> int:
 
 def plan_layout(cfg: Config):
     c = cfg.to_c()
-    offs = (ctypes.c_size_t * 5)()
+    offs = (ctypes.c_size_t * 6)()
     lim = (ctypes.c_int32 * 6)()
     _check(lib().rpa_plan_layout(ctypes.byref(c), offs, lim), "rpa_plan_layout")
     return list(offs), list(lim)

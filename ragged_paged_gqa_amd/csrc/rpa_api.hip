@@ -87,14 +87,14 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   // prefill chunks are also capped at kPfMaxChunk keys
   const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
   const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);
-  if (max_du >= (1 << 30) || max_pu >= (1 << 30) || max_di >= INT32_MAX || max_pi >= INT32_MAX) return false;
+  if (max_du >= (1 << 30) || max_pu >= (1 << 30) || max_di >= INT32_MAX || max_pi >= INT32_MAX / kQueues) return false;
   size_t off = 0;
   L->hdr = off;   off = align256(off + sizeof(Header));
   L->du = off;    off = align256(off + sizeof(Unit) * (size_t)max_du);
   L->pu = off;    off = align256(off + sizeof(Unit) * (size_t)max_pu);
   L->di = off;    off = align256(off + sizeof(Item) * (size_t)max_di);
   L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
-  L->qlist = off; off = align256(off + sizeof(int32_t) * (size_t)max_pi);
+  L->qlist = off; off = align256(off + sizeof(int32_t) * kQueues * (size_t)max_pi);
   L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
   L->dpart = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows * D);
   L->dplse = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows);
@@ -344,7 +344,7 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
   return launch_plan(p, static_cast<hipStream_t>(stream));
 }
 
-rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t limits[6]) {
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[6], int32_t limits[6]) {
   if (!offsets || !limits) return RPA_ERR_INVALID_ARGUMENT;
   rpa_status st = validate(cfg);
   if (st != RPA_OK) return st;
@@ -357,6 +357,7 @@ rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[5], int32_t lim
   offsets[2] = L.pu;
   offsets[3] = L.di;
   offsets[4] = L.pi;
+  offsets[5] = L.qlist;
   limits[0] = L.max_du;
   limits[1] = L.max_pu;
   limits[2] = L.max_di;

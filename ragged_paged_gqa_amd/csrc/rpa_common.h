@@ -54,9 +54,9 @@ struct Item {
 };
 
 // Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
-// L2). All row blocks of one (sequence, kv head) go to the same queue, in
-// chunk-major order, so the workgroups of one XCD that run at the same time
-// stream the same K/V chunk and share it through that XCD's L2.
+// L2). All row blocks of one (sequence, kv head) go to the same queue, one
+// after the other, so the workgroups of one XCD that run at the same time
+// stream the same K/V pages and share them through that XCD's L2.
 constexpr int kQueues = 8;
 
 struct Header {
@@ -69,7 +69,7 @@ struct Header {
   int32_t n_split_units;
   int32_t dec_counter;  // work queue of decode items, zeroed by the planning kernel
   int32_t pad0[8];
-  int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist
+  int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist (x * max_pf_items)
   int32_t pf_q_count[kQueues];  // its length
   int32_t pf_q_next[kQueues];   // its head, zeroed by the planning kernel
   int32_t pad1[24];
@@ -94,7 +94,7 @@ struct Params {
   Unit* pf_units;
   Item* dec_items;
   Item* pf_items;
-  int32_t* pf_qlist;         // prefill item indices in queue order [max_pf_items]
+  int32_t* pf_qlist;         // prefill item indices in queue order [kQueues][max_pf_items]
   int32_t* unit_done;        // finished chunks per unit: [max_dec_units] then [max_pf_units]
   float* dec_part;           // [max_dec_items][kDecRows][D]
   float* dec_plse;           // [max_dec_items][kDecRows]

@@ -16,40 +16,66 @@
 //     read;
 //   * each unit is cut into chunks of a per-class key count chosen so that
 //     the whole batch yields about `target_*_items` items; the unit's
-//     finished-chunk counter is cleared for the split merge.
+//     finished-chunk counter is cleared for the split merge;
+//   * prefill items are dealt into one queue per XCD: all items of a
+//     (sequence, kv head) go to queue (seq * Hkv + h) % kQueues, chunk-major,
+//     so an XCD's concurrently running workgroups stream the same K/V chunk
+//     and share it in that XCD's L2. Queue x lives at
+//     pf_qlist[x * max_pf_items].
+//
+// Work split inside the workgroup: sequences are taken in tiles of
+// kPlanThreads, one thread per sequence for the per-sequence counts and for
+// the one block scan that turns them into record offsets; a prefill
+// sequence's row blocks are handled by one wave, a row block per lane.
+// Divisions by G and by the chunk size use an exact double-precision
+// reciprocal.
 #pragma once
 
 #include "rpa_common.h"
 
 namespace rpa {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 512;  // 1024 would cap a wave at 128 VGPRs and spill
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kDecMinChunk = 256;
 constexpr int kPfMinChunk = 512;
+
+// a / d for 0 <= a < 2^31, d > 0: the double product is within 1e-6 of the
+// quotient, so truncation is off by at most one, which the remainder fixes.
+struct FastDiv {
+  int32_t d;
+  double inv;
+};
+__device__ __forceinline__ FastDiv make_div(int32_t d) { return FastDiv{d, 1.0 / (double)d}; }
+__device__ __forceinline__ int32_t fdiv(int32_t a, const FastDiv& f) {
+  int32_t q = (int32_t)((double)a * f.inv);
+  const int32_t r = a - q * f.d;
+  if (r < 0) --q;
+  else if (r >= f.d) ++q;
+  return q;
+}
 
 struct UnitRange {
   int32_t lo16, hi;
 };
 
 // Keys that rows [row0, row0 + nrows) of a sequence (q_len, kv_len) can see.
-__device__ __forceinline__ UnitRange unit_range(const Params& p, int32_t ql, int32_t kvl, int32_t row0,
-                                                int32_t nrows) {
-  const int32_t t_first = row0 / p.G;
-  const int32_t t_last = (row0 + nrows - 1) / p.G;
-  const int32_t p_first = kvl - ql + t_first;
-  const int32_t p_last = kvl - ql + t_last;
+__device__ __forceinline__ UnitRange unit_range(const Params& p, const FastDiv& G, int32_t ql, int32_t kvl,
+                                                int32_t row0, int32_t nrows) {
+  const int32_t p_first = kvl - ql + fdiv(row0, G);
+  const int32_t p_last = kvl - ql + fdiv(row0 + nrows - 1, G);
   int32_t hi = p.is_causal ? min(kvl, p_last + 1) : kvl;
   hi = max(hi, 0);
-  int32_t lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
-  UnitRange r;
-  r.lo16 = lo & ~15;
-  r.hi = hi;
-  return r;
+  const int32_t lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
+  return UnitRange{lo & ~15, hi};
 }
 
-__device__ __forceinline__ int32_t n_chunks(int32_t lo16, int32_t hi, int32_t chunk) {
-  int32_t keys = hi > lo16 ? hi - lo16 : 0;
-  int32_t n = (keys + chunk - 1) / chunk;
+__device__ __forceinline__ int32_t range_keys(const UnitRange& r) { return r.hi > r.lo16 ? r.hi - r.lo16 : 0; }
+
+__device__ __forceinline__ int32_t n_chunks(const UnitRange& r, const FastDiv& chunk) {
+  const int32_t keys = range_keys(r);
+  int32_t n = fdiv(keys, chunk);
+  n += n * chunk.d < keys;
   return n > 0 ? n : 1;
 }
 
@@ -63,240 +89,328 @@ __device__ __forceinline__ int32_t pick_chunk(int64_t total_keys, int32_t target
 }
 
 // Clamped metadata of sequence s.
-__device__ __forceinline__ void seq_meta(const Params& p, int32_t s, int32_t& q0, int32_t& ql, int32_t& kvl) {
+__device__ __forceinline__ void seq_meta(const Params& p, int32_t s, int32_t& ql, int32_t& kvl) {
+  int32_t q0;
   seq_tokens(p, s, q0, ql);
   kvl = p.kv_lens[s];
   const int32_t cap = p.pps * p.page;
   kvl = kvl < 0 ? 0 : (kvl > cap ? cap : kvl);
 }
 
-// Block-wide exclusive scan of one int per thread; returns the prefix and
-// writes the block total to *total. Uses `sh` (kPlanThreads/64 + 1 ints).
-__device__ int32_t block_exclusive_scan(int32_t v, int32_t* sh, int32_t* total) {
+// Block-wide exclusive scan of NV ints per thread at once: excl[k] gets the
+// sum of v[k] over lower threads, tot[k] the block total. `sh` holds
+// kPlanWaves * NV ints.
+template <int NV>
+__device__ void block_scan(const int32_t (&v)[NV], int32_t (&excl)[NV], int32_t (&tot)[NV], int32_t* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
+  int32_t x[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) x[k] = v[k];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      int32_t t = sh[w];
-      sh[w] = run;
-      run += t;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int32_t y = __shfl_up(x[k], o);
+      if (lane >= o) x[k] += y;
     }
-    sh[kPlanThreads / 64] = run;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) sh[wave * NV + k] = x[k];
   }
   __syncthreads();
-  int32_t r = sh[wave] + x - v;
-  *total = sh[kPlanThreads / 64];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    int32_t before = 0, all = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int32_t t = sh[w * NV + k];
+      before += w < wave ? t : 0;
+      all += t;
+    }
+    excl[k] = before + x[k] - v[k];
+    tot[k] = all;
+  }
   __syncthreads();
-  return r;
 }
 
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Per-sequence counts (scan slots): 0 decode units, 1 prefill units,
+// 2 decode items, 3 prefill items, 4 split units, 5.. prefill items per queue
+constexpr int kScanN = 5 + kQueues;
+
+// Per prefill sequence of a tile, filled by its wave.
+struct PfInfo {
+  int32_t s;         // sequence
+  int32_t per_head;  // items of one kv head
+  int32_t nsplit;    // row blocks with more than one chunk
+  int32_t max_nch;   // most chunks of one row block
+};
+
+// Offsets of a prefill sequence's records, from the block scan.
+struct PfOffs {
+  int32_t unit, item;
+  int32_t queue[kQueues];
+};
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
-  __shared__ int64_t red[2][kPlanThreads / 64];
-  __shared__ int32_t sh[kPlanThreads / 64 + 1];
-  const int tid = threadIdx.x;
+  __shared__ int64_t red[2][kPlanWaves];
+  __shared__ int32_t sh[kPlanWaves * kScanN];
+  __shared__ int32_t n_pf_tile;
+  __shared__ PfInfo pf_info[kPlanThreads];
+  __shared__ PfOffs pf_offs[kPlanThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t n = *p.num_seqs;
   n = n < 0 ? 0 : (n > p.S_max ? p.S_max : n);
+  const FastDiv G = make_div(p.G);
+  const int32_t R = p.pf_rows;
+
+  // Collects this tile's prefill sequences into pf_info[0, n_pf_tile); the
+  // thread's sequence gets its slot in `slot` (-1: not prefill).
+  auto collect = [&](int32_t s, int32_t ql, int32_t& slot) {
+    slot = -1;
+    if (s < n && ql * p.G > kDecRows) {
+      slot = atomicAdd(&n_pf_tile, 1);
+      pf_info[slot].s = s;
+    }
+  };
 
   // pass 1: total visible keys of each class, to size the chunks
   int64_t dec_keys = 0, pf_keys = 0;
-  for (int32_t s = tid; s < n; s += kPlanThreads) {
-    int32_t q0, ql, kvl;
-    seq_meta(p, s, q0, ql, kvl);
-    if (ql <= 0) continue;
-    const int32_t rows = ql * p.G;
-    if (rows <= kDecRows) {
-      UnitRange r = unit_range(p, ql, kvl, 0, rows);
-      dec_keys += (int64_t)p.Hkv * max(0, r.hi - r.lo16);
-    } else {
-      for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
-        UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
-        pf_keys += (int64_t)p.Hkv * max(0, r.hi - r.lo16);
-      }
+  for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
+    if (tid == 0) n_pf_tile = 0;
+    __syncthreads();
+    const int32_t s = s0 + tid;
+    int32_t ql = 0, kvl = 0, slot;
+    if (s < n) seq_meta(p, s, ql, kvl);
+    if (s < n && ql > 0 && ql * p.G <= kDecRows)
+      dec_keys += (int64_t)p.Hkv * range_keys(unit_range(p, G, ql, kvl, 0, ql * p.G));
+    collect(s, ql, slot);
+    __syncthreads();
+    for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
+      const int32_t ps = pf_info[i].s;
+      int32_t pql, pkvl;
+      seq_meta(p, ps, pql, pkvl);
+      const int32_t rows = pql * p.G;
+      for (int32_t r0 = lane * R; r0 < rows; r0 += 64 * R)
+        pf_keys += (int64_t)p.Hkv * range_keys(unit_range(p, G, pql, pkvl, r0, min(R, rows - r0)));
     }
+    __syncthreads();
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     dec_keys += __shfl_xor(dec_keys, o);
     pf_keys += __shfl_xor(pf_keys, o);
   }
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = dec_keys;
-    red[1][tid >> 6] = pf_keys;
+  if (lane == 0) {
+    red[0][wave] = dec_keys;
+    red[1][wave] = pf_keys;
   }
   __syncthreads();
   int64_t tot_dec = 0, tot_pf = 0;
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  for (int w = 0; w < kPlanWaves; ++w) {
     tot_dec += red[0][w];
     tot_pf += red[1][w];
   }
-  const int32_t dec_chunk = pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, 1 << 28);
-  const int32_t pf_chunk = pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk);
+  const FastDiv dec_chunk = make_div(pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, 1 << 28));
+  const FastDiv pf_chunk = make_div(pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk));
 
-  // pass 1b: prefill items per queue (queue of (seq, kv head) = (seq*Hkv + h) % kQueues)
-  __shared__ int32_t q_tot[kQueues];
-  if (tid < kQueues) q_tot[tid] = 0;
-  __syncthreads();
-  for (int32_t s = tid; s < n; s += kPlanThreads) {
-    int32_t q0, ql, kvl;
-    seq_meta(p, s, q0, ql, kvl);
-    const int32_t rows = ql * p.G;
-    if (ql <= 0 || rows <= kDecRows) continue;
-    int32_t per_head = 0;
-    for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
-      UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
-      per_head += n_chunks(r.lo16, r.hi, pf_chunk);
-    }
-    for (int32_t h = 0; h < p.Hkv; ++h) atomicAdd(&q_tot[(s * p.Hkv + h) % kQueues], per_head);
-  }
-  __syncthreads();
-  int32_t q_base[kQueues];
-  {
-    int32_t run = 0;
-    for (int x = 0; x < kQueues; ++x) {
-      q_base[x] = run;
-      run += q_tot[x];
-    }
-  }
-
-  // pass 2: per-sequence counts -> scans -> records
-  int32_t base_du = 0, base_pu = 0, base_di = 0, base_pi = 0, base_sp = 0;
-  int32_t q_run[kQueues];
-  for (int x = 0; x < kQueues; ++x) q_run[x] = 0;
+  // pass 2: per-sequence counts -> one scan per tile -> records
+  int32_t base[kScanN];
+#pragma unroll
+  for (int k = 0; k < kScanN; ++k) base[k] = 0;
   for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
+    if (tid == 0) n_pf_tile = 0;
+    __syncthreads();
     const int32_t s = s0 + tid;
-    int32_t q0 = 0, ql = 0, kvl = 0;
-    int32_t c_du = 0, c_pu = 0, c_di = 0, c_pi = 0, c_sp = 0;
-    bool is_dec = false;
-    if (s < n) {
-      seq_meta(p, s, q0, ql, kvl);
-      if (ql > 0) {
-        const int32_t rows = ql * p.G;
-        if (rows <= kDecRows) {
-          is_dec = true;
-          UnitRange r = unit_range(p, ql, kvl, 0, rows);
-          const int32_t nch = n_chunks(r.lo16, r.hi, dec_chunk);
-          c_du = p.Hkv;
-          c_di = p.Hkv * nch;
-          c_sp = nch > 1 ? p.Hkv : 0;
-        } else {
-          int32_t per_head_items = 0, per_head_split = 0, nrb = 0;
-          for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
-            UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
-            const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
-            per_head_items += nch;
-            per_head_split += nch > 1 ? 1 : 0;
-            ++nrb;
-          }
-          c_pu = p.Hkv * nrb;
-          c_pi = p.Hkv * per_head_items;
-          c_sp = p.Hkv * per_head_split;
-        }
+    int32_t ql = 0, kvl = 0, slot;
+    if (s < n) seq_meta(p, s, ql, kvl);
+    collect(s, ql, slot);
+    __syncthreads();
+    // (a) a wave per prefill sequence: chunk counts of its row blocks
+    for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
+      const int32_t ps = pf_info[i].s;
+      int32_t pql, pkvl;
+      seq_meta(p, ps, pql, pkvl);
+      const int32_t rows = pql * p.G;
+      int32_t items = 0, nsplit = 0, max_nch = 0;
+      for (int32_t r0 = lane * R; r0 < rows; r0 += 64 * R) {
+        const int32_t nch = n_chunks(unit_range(p, G, pql, pkvl, r0, min(R, rows - r0)), pf_chunk);
+        items += nch;
+        nsplit += nch > 1;
+        max_nch = max(max_nch, nch);
+      }
+      items = wave_sum(items);
+      nsplit = wave_sum(nsplit);
+      max_nch = wave_max(max_nch);
+      if (lane == 0) {
+        pf_info[i].per_head = items;
+        pf_info[i].nsplit = nsplit;
+        pf_info[i].max_nch = max_nch;
       }
     }
-    int32_t t_du, t_pu, t_di, t_pi, t_sp;
-    int32_t o_du = base_du + block_exclusive_scan(c_du, sh, &t_du);
-    int32_t o_pu = base_pu + block_exclusive_scan(c_pu, sh, &t_pu);
-    int32_t o_di = base_di + block_exclusive_scan(c_di, sh, &t_di);
-    int32_t o_pi = base_pi + block_exclusive_scan(c_pi, sh, &t_pi);
-    (void)block_exclusive_scan(c_sp, sh, &t_sp);
-    // this sequence's position in each prefill queue
-    int32_t o_q[kQueues];
-    for (int x = 0; x < kQueues; ++x) {
-      int32_t cnt = 0;
-      if (!is_dec && s < n && ql > 0)
-        for (int32_t h = 0; h < p.Hkv; ++h) cnt += ((s * p.Hkv + h) % kQueues == x) ? c_pi / p.Hkv : 0;
-      int32_t t_q;
-      o_q[x] = q_base[x] + q_run[x] + block_exclusive_scan(cnt, sh, &t_q);
-      q_run[x] += t_q;
+    __syncthreads();
+    // (b) a thread per sequence: counts, scan
+    int32_t cnt[kScanN];
+#pragma unroll
+    for (int k = 0; k < kScanN; ++k) cnt[k] = 0;
+    int32_t nch_dec = 0;
+    const bool is_dec = s < n && ql > 0 && ql * p.G <= kDecRows;
+    if (is_dec) {
+      nch_dec = n_chunks(unit_range(p, G, ql, kvl, 0, ql * p.G), dec_chunk);
+      cnt[0] = p.Hkv;
+      cnt[2] = p.Hkv * nch_dec;
+      cnt[4] = nch_dec > 1 ? p.Hkv : 0;
+    } else if (slot >= 0) {
+      const PfInfo& f = pf_info[slot];
+      const int32_t nrb = (ql * p.G + R - 1) / R;
+      cnt[1] = p.Hkv * nrb;
+      cnt[3] = p.Hkv * f.per_head;
+      cnt[4] = p.Hkv * f.nsplit;
+      for (int32_t h = 0; h < p.Hkv; ++h) {
+        const int x = (s * p.Hkv + h) % kQueues;
+#pragma unroll
+        for (int k = 0; k < kQueues; ++k) cnt[5 + k] += x == k ? f.per_head : 0;
+      }
     }
+    int32_t off[kScanN], tot[kScanN];
+    block_scan<kScanN>(cnt, off, tot, sh);
+#pragma unroll
+    for (int k = 0; k < kScanN; ++k) off[k] += base[k];
+#pragma unroll
+    for (int k = 0; k < kScanN; ++k) base[k] += tot[k];
 
-    if (s < n && ql > 0) {
+    if (is_dec) {  // decode records, by the sequence's thread
       const int32_t rows = ql * p.G;
-      if (is_dec) {
-        UnitRange r = unit_range(p, ql, kvl, 0, rows);
-        const int32_t nch = n_chunks(r.lo16, r.hi, dec_chunk);
-        for (int32_t h = 0; h < p.Hkv; ++h) {
-          const int32_t ui = o_du + h;
-          if (ui >= p.max_dec_units) break;
-          Unit u;
-          u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = rows;
-          u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = o_di + h * nch;
-          p.dec_units[ui] = u;
-          p.unit_done[ui] = 0;
-          for (int32_t c = 0; c < nch; ++c) {
-            const int32_t ii = u.item0 + c;
-            if (ii < p.max_dec_items) p.dec_items[ii] = Item{ui, c};
+      const UnitRange r = unit_range(p, G, ql, kvl, 0, rows);
+      for (int32_t h = 0; h < p.Hkv; ++h) {
+        const int32_t ui = off[0] + h;
+        if (ui >= p.max_dec_units) break;
+        Unit u;
+        u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = rows;
+        u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch_dec; u.item0 = off[2] + h * nch_dec;
+        p.dec_units[ui] = u;
+        p.unit_done[ui] = 0;
+        for (int32_t c = 0; c < nch_dec; ++c) {
+          const int32_t ii = u.item0 + c;
+          if (ii < p.max_dec_items) p.dec_items[ii] = Item{ui, c};
+        }
+      }
+    } else if (slot >= 0) {
+      pf_offs[slot].unit = off[1];
+      pf_offs[slot].item = off[3];
+#pragma unroll
+      for (int x = 0; x < kQueues; ++x) pf_offs[slot].queue[x] = off[5 + x];
+    }
+    __syncthreads();
+
+    // (c) a wave per prefill sequence: its units, items and queue entries
+    for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
+      const PfInfo f = pf_info[i];
+      const int32_t ps = f.s;
+      int32_t pql, pkvl;
+      seq_meta(p, ps, pql, pkvl);
+      const int32_t rows = pql * p.G;
+      const int32_t nrb = (rows + R - 1) / R;
+      const int32_t unit0 = pf_offs[i].unit, item0 = pf_offs[i].item;
+      // units and items: unit of (h, rb) is unit0 + h * nrb + rb, its items
+      // start at item0 + h * per_head + (chunks of the earlier row blocks)
+      int32_t carry = 0;
+      for (int32_t rb0 = 0; rb0 < nrb; rb0 += 64) {
+        const int32_t rb = rb0 + lane;
+        int32_t nch = 0;
+        UnitRange r{0, 0};
+        int32_t r0 = 0, nr = 0;
+        if (rb < nrb) {
+          r0 = rb * R;
+          nr = min(R, rows - r0);
+          r = unit_range(p, G, pql, pkvl, r0, nr);
+          nch = n_chunks(r, pf_chunk);
+        }
+        const int32_t incl = wave_incl_scan(nch);
+        const int32_t item_off = carry + incl - nch;
+        carry += __shfl(incl, 63);
+        if (rb < nrb) {
+          for (int32_t h = 0; h < p.Hkv; ++h) {
+            const int32_t ui = unit0 + h * nrb + rb;
+            const int32_t ii = item0 + h * f.per_head + item_off;
+            if (ui >= p.max_pf_units) break;
+            Unit u;
+            u.seq = ps; u.kv_head = h; u.row0 = r0; u.nrows = nr;
+            u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = ii;
+            p.pf_units[ui] = u;
+            p.unit_done[p.max_dec_units + ui] = 0;
+            for (int32_t c = 0; c < nch; ++c)
+              if (ii + c < p.max_pf_items) p.pf_items[ii + c] = Item{ui, c};
           }
         }
-      } else {
-        int32_t ui = o_pu, ii = o_pi;
-        for (int32_t h = 0; h < p.Hkv; ++h) {
-          for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
-            const int32_t nr = min(p.pf_rows, rows - r0);
-            UnitRange r = unit_range(p, ql, kvl, r0, nr);
-            const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
-            if (ui < p.max_pf_units) {
-              Unit u;
-              u.seq = s; u.kv_head = h; u.row0 = r0; u.nrows = nr;
-              u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = ii;
-              p.pf_units[ui] = u;
-              p.unit_done[p.max_dec_units + ui] = 0;
-              for (int32_t c = 0; c < nch; ++c)
-                if (ii + c < p.max_pf_items) p.pf_items[ii + c] = Item{ui, c};
-            }
-            ++ui;
-            ii += nch;
+      }
+      // queue entries, chunk-major: chunk 0 of every row block, then chunk 1
+      // of those that have one, ...; a head's entries are contiguous, after
+      // those of this sequence's earlier heads in the same queue
+      int32_t pos = 0;  // entries of this sequence's head so far
+      for (int32_t c = 0; c < f.max_nch; ++c) {
+        int32_t carry_items = 0;
+        for (int32_t rb0 = 0; rb0 < nrb; rb0 += 64) {
+          const int32_t rb = rb0 + lane;
+          int32_t nch = 0;
+          if (rb < nrb) {
+            const int32_t r0 = rb * R;
+            nch = n_chunks(unit_range(p, G, pql, pkvl, r0, min(R, rows - r0)), pf_chunk);
           }
-        }
-        // queue entries of each head: chunk-major, then row block
-        int32_t ii_h = o_pi;
-        for (int32_t h = 0; h < p.Hkv; ++h) {
-          const int x = (s * p.Hkv + h) % kQueues;
-          int32_t k = o_q[x];
-          const int32_t per_head = c_pi / p.Hkv;
-          for (int32_t c = 0;; ++c) {
-            bool any = false;
-            int32_t ii_rb = ii_h;
-            for (int32_t r0 = 0; r0 < rows; r0 += p.pf_rows) {
-              UnitRange r = unit_range(p, ql, kvl, r0, min(p.pf_rows, rows - r0));
-              const int32_t nch = n_chunks(r.lo16, r.hi, pf_chunk);
-              if (c < nch) {
-                any = true;
-                if (k < p.max_pf_items && ii_rb + c < p.max_pf_items) p.pf_qlist[k] = ii_rb + c;
-                ++k;
-              }
-              ii_rb += nch;
+          const int32_t incl = wave_incl_scan(nch);
+          const int32_t item_off = carry_items + incl - nch;
+          carry_items += __shfl(incl, 63);
+          const bool has = c < nch;
+          const uint64_t m = __ballot(has);
+          const int32_t before = __popcll(m & ((1ull << lane) - 1ull));
+          if (has) {
+            for (int32_t h = 0; h < p.Hkv; ++h) {
+              const int x = (ps * p.Hkv + h) % kQueues;
+              const int32_t j = h / kQueues;  // earlier heads of this sequence in queue x
+              const int32_t k = pf_offs[i].queue[x] + j * f.per_head + pos + before;
+              const int32_t item = item0 + h * f.per_head + item_off + c;
+              if (k < p.max_pf_items && item < p.max_pf_items)
+                p.pf_qlist[(int64_t)x * p.max_pf_items + k] = item;
             }
-            if (!any) break;
           }
-          o_q[x] = k;
-          ii_h += per_head;
+          pos += __popcll(m);
         }
       }
     }
-    base_du += t_du; base_pu += t_pu; base_di += t_di; base_pi += t_pi; base_sp += t_sp;
+    __syncthreads();
   }
   if (tid == 0) {
     Header h = {};
-    h.n_dec_units = min(base_du, p.max_dec_units);
-    h.n_pf_units = min(base_pu, p.max_pf_units);
-    h.n_dec_items = min(base_di, p.max_dec_items);
-    h.n_pf_items = min(base_pi, p.max_pf_items);
-    h.dec_chunk = dec_chunk;
-    h.pf_chunk = pf_chunk;
-    h.n_split_units = base_sp;
+    h.n_dec_units = min(base[0], p.max_dec_units);
+    h.n_pf_units = min(base[1], p.max_pf_units);
+    h.n_dec_items = min(base[2], p.max_dec_items);
+    h.n_pf_items = min(base[3], p.max_pf_items);
+    h.dec_chunk = dec_chunk.d;
+    h.pf_chunk = pf_chunk.d;
+    h.n_split_units = base[4];
     h.dec_counter = 0;
     for (int x = 0; x < kQueues; ++x) {
-      h.pf_q_base[x] = min(q_base[x], p.max_pf_items);
-      h.pf_q_count[x] = max(0, min(q_tot[x], p.max_pf_items - h.pf_q_base[x]));
+      h.pf_q_base[x] = x * p.max_pf_items;
+      h.pf_q_count[x] = max(0, min(base[5 + x], p.max_pf_items));
       h.pf_q_next[x] = 0;
     }
     *p.hdr = h;

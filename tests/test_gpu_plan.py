@@ -25,13 +25,42 @@ def _plan(w):
     torch.cuda.synchronize()
     offs, lim = rpa.plan_layout(cfg)
     host = ws.cpu().numpy()
-    hdr = host[offs[0]:offs[0] + 64].view(np.int32)
+    hdr = host[offs[0]:offs[0] + 256].view(np.int32)
     n_du, n_pu, n_di, n_pi, dch, pch = (int(x) for x in hdr[:6])
     du = host[offs[1]:offs[1] + 32 * n_du].view(np.int32).reshape(n_du, 8)
     pu = host[offs[2]:offs[2] + 32 * n_pu].view(np.int32).reshape(n_pu, 8)
     di = host[offs[3]:offs[3] + 8 * n_di].view(np.int32).reshape(n_di, 2)
     pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
-    return dict(du=du, pu=pu, di=di, pi=pi, dch=dch, pch=pch, lim=lim)
+    qbase, qcount, qnext = hdr[16:24].copy(), hdr[24:32].copy(), hdr[32:40].copy()
+    ql = host[offs[5]:offs[5] + 4 * 8 * int(lim[3])].view(np.int32)
+    return dict(du=du, pu=pu, di=di, pi=pi, dch=dch, pch=pch, lim=lim, qbase=qbase, qcount=qcount,
+                qnext=qnext, qlist=ql)
+
+
+def _check_queues(P, n_kv_heads):
+    """Each prefill item sits in exactly one of the 8 queues, the one of its
+    (sequence, kv head); queue x starts at x * max_pf_items and starts empty;
+    within a queue, one (sequence, kv head)'s items come chunk-major."""
+    n_pi = len(P["pi"])
+    max_pi = P["lim"][3]
+    assert np.all(P["qnext"] == 0)
+    assert int(P["qcount"].sum()) == n_pi
+    assert np.all(P["qbase"] == np.arange(8) * max_pi)
+    entries = []
+    for x in range(8):
+        q = P["qlist"][x * max_pi:x * max_pi + int(P["qcount"][x])]
+        entries.append(q)
+        last = {}
+        for it in q:
+            ui, c = P["pi"][it]
+            s, h, r0 = P["pu"][ui][:3]
+            assert (s * n_kv_heads + h) % 8 == x
+            key = (c, r0)
+            if (s, h) in last:
+                assert key > last[(s, h)]
+            last[(s, h)] = key
+    allq = np.concatenate(entries) if entries else np.zeros(0, np.int32)
+    assert np.array_equal(np.sort(allq), np.arange(n_pi))
 
 
 def _check(w):
@@ -67,6 +96,7 @@ def _check(w):
                 a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
                 assert a < b or (nch == 1 and hi <= lo)
         assert np.all(seen_items == 1), cls
+    _check_queues(P, c.num_kv_heads)
     for s in range(w.n_seqs):
         ql = int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])
         for h in range(c.num_kv_heads):
