@@ -117,6 +117,58 @@ def load_traffic(kernel: str, workload: int):
     return e.get("bytes_per_launch")
 
 
+def _counter_per_kernel(path: str, counter: str) -> dict:
+    """Mean value (KiB per dispatch) of one rocprofv3 counter, per kernel name."""
+    import csv
+    import collections
+
+    agg = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def ingest_counters(pmc_dir: str, workload: int) -> dict:
+    """Turns two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
+    WRITE_SIZE) plus the same two runs of `--copy-calibration` into HBM bytes
+    per launch of each attention kernel, scaled by what each counter reads
+    per true byte of the plain 1 GiB copy; stores them in the traffic file."""
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        copies = [v for k, v in _counter_per_kernel(
+            os.path.join(pmc_dir, f"copy_{c}", "run_counter_collection.csv"), c).items() if "copyBuffer" in k]
+        if not copies:
+            raise SystemExit(f"no copy kernel in the {c} calibration run")
+        scale[c] = copies[0] * 1024.0 / float(1 << 30)  # counter bytes per true byte
+    per = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for k, v in _counter_per_kernel(
+                os.path.join(pmc_dir, f"w{workload}_{c}", "run_counter_collection.csv"), c).items():
+            for name in ("decode_kernel", "prefill_kernel", "plan_kernel"):
+                if f"rpa::{name}" in k:
+                    per.setdefault(name, {})[c] = v * 1024.0 / scale[c]
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    h = kernel_source_hash()
+    for name, d in per.items():
+        if "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+            t[f"{name}:cfg{workload}"] = {
+                "bytes_per_launch": round(d["FETCH_SIZE"] + d["WRITE_SIZE"]),
+                "read_bytes": round(d["FETCH_SIZE"]), "write_bytes": round(d["WRITE_SIZE"]),
+                "fetch_counter_per_byte": round(scale["FETCH_SIZE"], 4),
+                "write_counter_per_byte": round(scale["WRITE_SIZE"], 4),
+                "source_hash": h}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return {k: v for k, v in t.items() if k.endswith(f":cfg{workload}")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,7 +178,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
+                         "(copy_<C>/ and w<workload>_<C>/) into the traffic file")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(args.ingest_counters, args.workload), sort_keys=True))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
