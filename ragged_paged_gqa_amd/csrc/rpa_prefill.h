@@ -7,7 +7,7 @@
 // pulled from a device-wide queue; wave w owns rows [32w, 32w + 32). Split
 // units leave partials; the workgroup finishing a unit's last chunk merges
 // them (rpa_merge.h).
-// Per 32-key step:
+// Per load step (64 keys for bf16 with head_dim <= 128, else 32):
 //   * loader: the step's K and V rows of kv head h (combined heads 2h and
 //     2h+1, adjacent in memory — `stridedLoadKv`) are gathered through the
 //     page table into a ring of LDS tiles whose rows are padded so that the
@@ -16,19 +16,24 @@
 //     instruction) kStagesBf16 - 1 steps ahead of the compute; fp8 rows are
 //     staged through registers one step ahead and widened to bf16 on the way.
 //     Page position is tracked incrementally (no integer division in the
-//     loop);
+//     loop). One barrier per step publishes the tile.
+// Per 32-key block of the step:
 //   * S^T [32 keys x 32 rows] = K Q^T with v_mfma_f32_32x32x16_bf16, Q^T kept
 //     in registers; lane (row, half h) holds 16 keys of its row, so a row
-//     maximum needs one cross-lane exchange;
+//     maximum needs one cross-lane exchange (v_permlane32_swap);
 //   * masks (`flashAttention`: causal, sliding window, kv length) are applied
-//     only on steps that can contain a hidden key; other steps take an
-//     unmasked path;
+//     only on blocks that can contain a hidden key;
 //   * base-2 online softmax with a lazily moved reference maximum: the
 //     accumulator is rescaled only when some row's maximum grows by more than
-//     kRescaleSlack (2^8), which keeps every exponentiated score <= 2^8;
+//     kRescaleSlack, and that rescale runs outside the block loop, so inside
+//     it the accumulator is only ever an MFMA operand; P = 2^(s*c - m) is one
+//     FMA and one exp2 per score;
 //   * O^T [D x 32 rows] += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T
 //     taken straight from the S^T accumulator layout.
 #pragma once
+
+#include <climits>
+#include <type_traits>
 
 #include "rpa_common.h"
 #include "rpa_merge.h"
@@ -37,11 +42,19 @@ namespace rpa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr float kRescaleSlack = 8.0f;
+// The reference maximum of a row moves only when the row's maximum outgrows
+// it by more than this (base-2 units): exponentiated scores stay <= 2^16,
+// far inside f32 and bf16 range, and the accumulator rescale (which leaves
+// the step loop, see below) is rare.
+constexpr float kRescaleSlack = 16.0f;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// Keys per load step (one LDS ring slot, one barrier): 64 for bf16 with
+// head_dim <= 128, else 32. Scores are always computed 32 keys at a time.
+constexpr int pf_step_keys(int D, bool fp8) { return (!fp8 && D <= 128) ? 64 : 32; }
 
 #ifndef RPA_PF_STAGES
 #define RPA_PF_STAGES 4
@@ -56,6 +69,7 @@ struct PrefillLds {
   // K row (2D bytes) then V row (2D bytes), padded to 16*(16n+3) bytes so that
   // 16 consecutive keys start in distinct 16-byte bank groups.
   static constexpr int kRowBytes = 4 * D + 48;
+  static constexpr int kStepKeys = pf_step_keys(D, FP8);
   static constexpr int kBufBytes = kStepKeys * kRowBytes;
   static constexpr int kStages = FP8 ? 2 : kStagesBf16;
   static constexpr size_t kBytes = (size_t)kStages * kBufBytes;
@@ -91,8 +105,39 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
       : "memory");
 }
 
+// Same, with the global address split into a wave-uniform 64-bit base (SGPR
+// pair) and a per-lane 32-bit byte offset: no per-lane 64-bit address math.
+__device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
+// A pointer known to be equal on every lane, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// Value of lane l ^ 32 (v_permlane32_swap; no LDS round trip).
+__device__ __forceinline__ float other_half(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (uint32_t)(lane_id() < 32 ? r[1] : r[0]));
 }
 
 // Scheduling hints: the next `n` LDS reads, then the next `n` MFMAs.
@@ -105,15 +150,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   constexpr int NDB = D / 32;                 // 32-row blocks of O^T
   constexpr int EB = FP8 ? 1 : 2;             // bytes per K/V element in HBM
   constexpr int NT = NW * 64;
+  constexpr int KS = PrefillLds<D, FP8>::kStepKeys;
+  constexpr int NB = KS / 32;                 // 32-key score blocks per load step
+  constexpr int NB16 = KS / 16;               // 16-key page blocks per load step
   constexpr int RB = PrefillLds<D, FP8>::kRowBytes;
   constexpr int BUF = PrefillLds<D, FP8>::kBufBytes;
   constexpr int NST = PrefillLds<D, FP8>::kStages;
   constexpr int GCH = 2 * D * EB / 16;        // 16-byte global chunks per key (K and V)
-  constexpr int CPT = (kStepKeys * GCH + NT - 1) / NT;  // fp8 path: chunks per thread per step
-  constexpr int RPW = kStepKeys / NW;         // bf16 path: rows each wave moves per step
+  constexpr int CPT = (KS * GCH + NT - 1) / NT;  // fp8 path: chunks per thread per step
+  constexpr int RPW = KS / NW;                // bf16 path: rows each wave moves per step
   constexpr int LPR = 4 * D / 16;             // bf16 path: lanes per row (16 bytes each)
   static_assert(NDB >= 2, "head_dim >= 64");
   static_assert(LPR <= 64, "one row per DMA instruction");
+  static_assert(KS % NW == 0 && (NB == 1 || NB == 2), "step shape");
+  static_assert(!FP8 || NST == 2, "fp8 path stages through registers one step ahead");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
   __shared__ int sh_pages[kPfPageCache];  // physical pages of the current item
@@ -122,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31;  // S^T column = row within the wave
   const int h = lane >> 5;    // which half of the row's keys this lane holds
 
@@ -131,10 +181,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
   const bool capped = p.soft_cap > 0.f;
   const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
-  // scores in base-2 units: s2 = S * c2 (no cap) ; negative scales flip Q's sign
+  // scores in base-2 units are st * cmul (capped: the cap is applied to st
+  // first and cmul = 1); negative scales flip Q's sign instead
   const bool neg = p.sm_scale < 0.f;
   const float sm = neg ? -p.sm_scale : p.sm_scale;
-  const float c2 = sm * kLog2e;
+  const float cmul = capped ? 1.0f : sm * kLog2e;
 
   // LDS read bases (byte offsets inside a buffer)
   const int k_rd = r32 * RB + 16 * h;  // K[key = r32][8h ...] ; + 32*s per k-step
@@ -159,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   for (;;) {
     if (tid == 0) sh_item[parity] = next_item();
     __syncthreads();
-    const int item = sh_item[parity];
+    const int item = __builtin_amdgcn_readfirstlane(sh_item[parity]);  // same on every lane
     parity ^= 1;
     if (item < 0) break;
 
@@ -173,12 +224,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     kvl = max(0, min(kvl, p.pps * p.page));
     const int c_lo = u.kv_lo + it.chunk * chunk;
     const int c_hi = min(u.kv_hi, c_lo + chunk);
-    const int n_steps = c_hi > c_lo ? (c_hi - c_lo + kStepKeys - 1) / kStepKeys : 0;
+    const int n_sub = c_hi > c_lo ? (c_hi - c_lo + 31) / 32 : 0;  // 32-key score blocks
+    const int n_steps = (n_sub + NB - 1) / NB;                     // load steps
     const uint8_t* kv_h = p.kv + (int64_t)2 * kvh * D * EB;
     const int32_t* ptab = p.page_indices + (int64_t)s * p.pps;
     // physical pages of the item's key range, clamped, cached in LDS
     const int lp0 = c_lo / p.page;
-    const int n_pg = min(n_steps > 0 ? (c_lo + n_steps * kStepKeys - 1) / p.page - lp0 + 1 : 0, kPfPageCache);
+    const int n_pg = min(n_steps > 0 ? (c_lo + n_steps * KS - 1) / p.page - lp0 + 1 : 0, kPfPageCache);
     for (int i = tid; i < n_pg; i += NT) sh_pages[i] = min(max(ptab[min(lp0 + i, p.pps - 1)], 0), p.P - 1);
     __syncthreads();
 
@@ -203,10 +255,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) qb[i] = bf16x8{};
     }
-    // the wave's row span, for the masked-step test
+    // the wave's row span, for the masked-block test
     const int wr_last = min(32 * wave + 31, u.nrows - 1);
     const int pos_lo = kvl - ql + (u.row0 + 32 * wave) / p.G;
     const int pos_hi = kvl - ql + (u.row0 + max(wr_last, 32 * wave)) / p.G;
+    const int vis_hi = min(kvl, c_hi);
+    // can this lane's row see key `key` (`flashAttention` masks, kv length,
+    // chunk end)?
+    const int win_lo = p.window > 0 ? pos - p.window : INT_MIN;  // keys <= win_lo are hidden
+    const int vis_end = p.is_causal ? min(vis_hi, pos + 1) : vis_hi;
+    auto visible = [&](int key) { return rvalid && key < vis_end && key > win_lo; };
 
     float m_ref = -INFINITY;  // reference max (base-2 units) of this lane's row
     float lsum = 0.f;
@@ -218,56 +276,74 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     int lp = c_lo / p.page;
     int sl = c_lo - lp * p.page;
     auto advance = [&]() {
-      sl += kStepKeys;
-      if (sl >= p.page) {
-        sl -= p.page;
-        ++lp;
-      }
-      if (sl >= p.page) {
-        sl -= p.page;
-        ++lp;
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) {
+        sl += 16;
+        if (sl >= p.page) {
+          sl -= p.page;
+          ++lp;
+        }
       }
     };
-    // base addresses of the two 16-key blocks of the step at (lp, sl)
-    auto block_bases = [&](int k0, const uint8_t*& b0, const uint8_t*& b1, bool& on1) {
-      int lp1 = lp, sl1 = sl + 16;
-      if (sl1 >= p.page) {
-        sl1 = 0;
-        lp1 = lp + 1;
+    // base addresses of the 16-key blocks of the step at (lp, sl); a block
+    // past the chunk re-reads block 0 (harmless: its keys are masked and
+    // their V rows zeroed)
+    auto block_bases = [&](int k0, const uint8_t* (&bb)[NB16]) {
+      int lpb = lp, slb = sl;
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) {
+        const int ph = sh_pages[min(lpb - lp0, kPfPageCache - 1)];
+        const uint8_t* base = kv_h + ((int64_t)ph * p.page + slb) * key_stride;
+        bb[b] = (b == 0 || k0 + 16 * b < c_hi) ? base : bb[0];
+        slb += 16;
+        if (slb >= p.page) {
+          slb = 0;
+          ++lpb;
+        }
       }
-      const int ph0 = sh_pages[min(lp - lp0, kPfPageCache - 1)];
-      on1 = k0 + 16 < c_hi;
-      const int ph1 = on1 ? sh_pages[min(lp1 - lp0, kPfPageCache - 1)] : ph0;
-      b0 = kv_h + ((int64_t)ph0 * p.page + sl) * key_stride;
-      b1 = on1 ? kv_h + ((int64_t)ph1 * p.page + sl1) * key_stride : b0;
     };
 
     // ---- loader, bf16: rows straight into the LDS ring ----
-    auto issue_dma = [&](int k0, char* dst) {
-      const uint8_t *b0, *b1;
-      bool on1;
-      block_bases(k0, b0, b1, on1);
+    // Wave w moves keys [w * RPW, (w + 1) * RPW) of each step, all inside one
+    // 16-key page block; per lane only a fixed byte offset inside the block
+    // is needed, the block base is wave-uniform.
+    constexpr int kWaveBlk = (RPW <= 16) ? 0 : -1;
+    static_assert(kWaveBlk == 0 && 16 % RPW == 0, "a wave's rows stay inside one 16-key block");
+    const int my_blk = (wave * RPW) >> 4;
+    uint32_t row_off[RPW];
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int key = wave * RPW + i;
-        // an out-of-range block re-reads block 0 (harmless: masked, V zeroed)
-        const uint8_t* src = (key >= 16 ? b1 : b0) + (int64_t)(key & 15) * key_stride;
-        if (lane < LPR) dma16(src + 16 * lane, lds_addr_of(dst + key * RB));
+    for (int i = 0; i < RPW; ++i) row_off[i] = (uint32_t)(((wave * RPW + i) & 15) * key_stride) + 16u * lane;
+    auto issue_dma = [&](int k0, char* dst) {
+      // page block my_blk of the step at (lp, sl), or block 0 past the chunk
+      int lpb = lp, slb = sl;
+      if (k0 + 16 * my_blk < c_hi) {
+        for (int b = 0; b < my_blk; ++b) {
+          slb += 16;
+          if (slb >= p.page) {
+            slb = 0;
+            ++lpb;
+          }
+        }
       }
+      const int ph = __builtin_amdgcn_readfirstlane(sh_pages[min(lpb - lp0, kPfPageCache - 1)]);
+      const uint8_t* base = uniform_ptr(kv_h + ((int64_t)ph * p.page + slb) * key_stride);
+      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst + wave * RPW * RB));
+#pragma unroll
+      for (int i = 0; i < RPW; ++i)
+        if (lane < LPR) dma16_sbase(base, row_off[i], dst0 + i * RB);
     };
     // ---- loader, fp8: registers one step ahead, widened to bf16 ----
     u32x4 stage[CPT];
     auto load_regs = [&](int k0) {
-      const uint8_t *b0, *b1;
-      bool on1;
-      block_bases(k0, b0, b1, on1);
+      const uint8_t* bb[NB16];
+      block_bases(k0, bb);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + NT * c;
         const int key = idx / GCH;
-        if (idx < kStepKeys * GCH && (key < 16 || on1)) {
+        if (idx < KS * GCH && (key < 16 || k0 + 16 * (key >> 4) < c_hi)) {
           const int off = (key & 15) * (int)key_stride + 16 * (idx % GCH);
-          stage[c] = *reinterpret_cast<const u32x4*>((key >= 16 ? b1 : b0) + off);
+          stage[c] = *reinterpret_cast<const u32x4*>(bb[key >> 4] + off);
         } else {
           stage[c] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -277,7 +353,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + NT * c;
-        if (idx >= kStepKeys * GCH) continue;
+        if (idx >= KS * GCH) continue;
         const int key = idx / GCH;
         const int dst_off = key * RB + 32 * (idx % GCH);  // 16 codes -> 32 bytes
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
@@ -304,128 +380,165 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
       for (int k = 0; k < NST - 1; ++k) {
         if (k < n_steps) {
-          issue_dma(c_lo + k * kStepKeys, slot_ptr(k));
+          issue_dma(c_lo + k * KS, slot_ptr(k));
           advance();
           issued = k + 1;
         }
       }
     }
 
-    for (int n = 0; n < n_steps; ++n) {
-      const int k0 = c_lo + n * kStepKeys;
-      char* cur = slot_ptr(0);
-      if constexpr (FP8) {
-        store_regs(k0, cur);
-        __syncthreads();
-        if (issued < n_steps) {
-          load_regs(c_lo + issued * kStepKeys);
-          advance();
-          ++issued;
-        }
-      } else {
-        // wait for this step's rows: later steps may stay in flight
-        const int ahead = issued - n - 1;
-        if (ahead >= 2) {
-          wait_vmcnt<2 * RPW>();
-        } else if (ahead == 1) {
-          wait_vmcnt<RPW>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        __syncthreads();
-        if (k0 + kStepKeys > kvl || k0 + kStepKeys > c_hi) {
-          // zero V of rows past kv_len or past the loaded blocks
-          for (int i = tid; i < kStepKeys * (2 * D / 16); i += NT) {
-            const int key = i / (2 * D / 16);
-            const bool loaded = key < 16 || k0 + 16 < c_hi;
-            if (k0 + key >= kvl || !loaded)
-              *reinterpret_cast<u32x4*>(cur + key * RB + 2 * D + 16 * (i % (2 * D / 16))) = u32x4{0u, 0u, 0u, 0u};
+    // Score blocks of 32 keys; block u belongs to load step u / NB. The
+    // accumulator is touched only by MFMAs inside the loop: when a row's
+    // maximum outgrows the reference, the loop is left, the accumulator
+    // rescaled, and the same block resumed (its scores kept in st).
+    f32x16 st = f32x16{};
+    int ub = 0;
+    bool resume = false;
+    for (;;) {
+      bool pending = false;
+      float m_blk = -INFINITY;
+      for (; ub < n_sub; ++ub) {
+        const int n = ub / NB;
+        const int b = ub % NB;
+        const int k0 = c_lo + n * KS;
+        const int kb = k0 + 32 * b;
+        char* cur = slot_ptr(0);
+        // does this block hold a key that some row of the wave cannot see?
+        const bool need_mask = kb + 32 > vis_hi || (p.is_causal && kb + 31 > pos_lo) ||
+                               (p.window > 0 && kb <= pos_hi - p.window);
+        if (!resume) {
+          if (b == 0) {
+            if constexpr (FP8) {
+              store_regs(k0, cur);
+              __syncthreads();
+              if (issued < n_steps) {
+                load_regs(c_lo + issued * KS);
+                advance();
+                ++issued;
+              }
+            } else {
+              // wait for this step's rows: later steps may stay in flight
+              const int ahead = issued - n - 1;
+              if (ahead >= 2) {
+                wait_vmcnt<2 * RPW>();
+              } else if (ahead == 1) {
+                wait_vmcnt<RPW>();
+              } else {
+                wait_vmcnt<0>();
+              }
+              __syncthreads();
+              if (k0 + KS > kvl || k0 + KS > c_hi) {
+                // zero V of rows past kv_len or in blocks past the chunk
+                for (int i = tid; i < KS * (2 * D / 16); i += NT) {
+                  const int key = i / (2 * D / 16);
+                  const bool loaded = key < 16 || k0 + 16 * (key >> 4) < c_hi;
+                  if (k0 + key >= kvl || !loaded)
+                    *reinterpret_cast<u32x4*>(cur + key * RB + 2 * D + 16 * (i % (2 * D / 16))) =
+                        u32x4{0u, 0u, 0u, 0u};
+                }
+                __syncthreads();
+              }
+              // refill the slot freed by the previous step (every wave is past it)
+              if (issued < n_steps) {
+                issue_dma(c_lo + issued * KS, slot_ptr(NST - 1));
+                advance();
+                ++issued;
+              }
+            }
           }
-          __syncthreads();
-        }
-        // refill the slot freed by the previous step (every wave is past it)
-        if (issued < n_steps) {
-          issue_dma(c_lo + issued * kStepKeys, slot_ptr(NST - 1));
-          advance();
-          ++issued;
-        }
-      }
 
-      // S^T = K Q^T
-      f32x16 st = f32x16{};
-      {
-        const char* kr = cur + k_rd;
-        bf16x8 ka[NS];
+          // S^T = K Q^T for keys [kb, kb + 32)
+          st = f32x16{};
+          {
+            const char* kr = cur + 32 * b * RB + k_rd;
+            bf16x8 ka[NS];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + 32 * i);
+            for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + 32 * i);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) st = mfma32x32x16(ka[i], qb[i], st);
-        RPA_SCHED_DS_READS(NS);
-        RPA_SCHED_MFMAS(NS);
-      }
-
-      // scores -> base-2 units, masked where needed
-      const bool need_mask = k0 + kStepKeys > min(kvl, c_hi) || (p.is_causal && k0 + kStepKeys - 1 > pos_lo) ||
-                             (p.window > 0 && k0 <= pos_hi - p.window);
-      if (capped) {
+            for (int i = 0; i < NS; ++i) st = mfma32x32x16(ka[i], qb[i], st);
+            RPA_SCHED_DS_READS(NS);
+            RPA_SCHED_MFMAS(NS);
+          }
+          if (capped) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) st[j] = soft_cap_f(st[j] * sm, p.soft_cap, cap_k) * kLog2e;
-      } else {
+            for (int j = 0; j < 16; ++j) st[j] = soft_cap_f(st[j] * sm, p.soft_cap, cap_k) * kLog2e;
+          }
+          // row maximum over the visible keys, in base-2 units
+          float mx;
+          if (need_mask) {
+            mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) st[j] *= c2;
-      }
-      if (need_mask) {
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, visible(kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? st[j] : -INFINITY);
+          } else {
+            mx = st[0];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + 8 * (j >> 2) + 4 * h + (j & 3);
-          bool vis = rvalid && key < kvl && key < c_hi;
-          if (p.is_causal) vis = vis && key <= pos;
-          if (p.window > 0) vis = vis && key > pos - p.window;
-          st[j] = vis ? st[j] : -INFINITY;
+            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[j]);
+          }
+          mx = fmaxf(mx, other_half(mx));
+          m_blk = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
+          if (__any(m_blk > m_ref + kRescaleSlack)) {
+            pending = true;
+            break;
+          }
         }
-      }
-      float mx = st[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // move the reference max only when some row outgrew it by the slack
-      if (__any(mx > m_ref + kRescaleSlack)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = fast_exp2(m_ref - (m_new == -INFINITY ? 0.f : m_new));
-        m_ref = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[d] *= alpha;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pv = fast_exp2(st[j] - m_use);
-        lsum += pv;
-        pb[j >> 3][j & 7] = (__bf16)pv;
-      }
+        resume = false;
 
-      // O^T += V^T P^T (two 16-key k-steps)
-      const char* vr = cur + v_rd;
+        // P = 2^(score - reference), packed to bf16 for the PV product; the
+        // row sum is taken in f32 over the unrounded values (the LSE needs
+        // them: one dominant key rounded to bf16 moves it by up to 2^-8)
+        const float negm = m_ref == -INFINITY ? 0.f : -m_ref;
+        bf16x8 pb[2];
+        auto make_p = [&](auto masked) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 va[NDB];
+          for (int jp = 0; jp < 8; ++jp) {
+            float p0 = fast_exp2(__builtin_fmaf(st[2 * jp], cmul, negm));
+            float p1 = fast_exp2(__builtin_fmaf(st[2 * jp + 1], cmul, negm));
+            if constexpr (decltype(masked)::value) {
+              const int key0 = kb + 8 * (jp >> 1) + 4 * h + 2 * (jp & 1);
+              p0 = visible(key0) ? p0 : 0.f;
+              p1 = visible(key0 + 1) ? p1 : 0.f;
+            }
+            lsum += p0 + p1;
+            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
+            pb[jp >> 2][2 * (jp & 3)] = pair[0];
+            pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
+          }
+        };
+        if (need_mask)
+          make_p(std::true_type{});
+        else
+          make_p(std::false_type{});
+
+        // O^T += V^T P^T (two 16-key k-steps)
+        const char* vr = cur + 32 * b * RB + v_rd;
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + 64 * d));
-          const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + 64 * d));
-          va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 va[NDB];
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) {
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + 64 * d));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + 64 * d));
+            va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) o[d] = mfma32x32x16(va[d], pb[ks], o[d]);
+          RPA_SCHED_DS_READS(2 * NDB);
+          RPA_SCHED_MFMAS(NDB);
         }
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[d] = mfma32x32x16(va[d], pb[ks], o[d]);
-        RPA_SCHED_DS_READS(2 * NDB);
-        RPA_SCHED_MFMAS(NDB);
+        if (b == NB - 1 || ub == n_sub - 1) ring = (ring + 1) % NST;
       }
-      ring = (ring + 1) % NST;
+      if (!pending) break;
+      // move the reference max (every row of the wave at once; alpha <= 1)
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+      resume = true;
     }
 
-    const float l_row = lsum + __shfl_xor(lsum, 32);
+    const float l_row = lsum + other_half(lsum);
     const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
     const float lse_v = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
     // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
