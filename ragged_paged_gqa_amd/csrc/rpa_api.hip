@@ -78,7 +78,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t G = c->num_q_heads / c->num_kv_heads;
   const int64_t Hkv = c->num_kv_heads;
   const int64_t D = c->head_dim;
-  const int64_t pf_rows = 32 * pf_waves_for(c->head_dim);
+  const int64_t pf_rows = pf_rows_for(c->head_dim);
   const int64_t max_du = Hkv * c->max_num_seqs;
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
   const int64_t tgt_d = (int64_t)cus * 32;
@@ -170,16 +170,12 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
 template <int D, bool FP8>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   {
-    constexpr int NW = pf_waves_for(D);
-    // registers allow 8 waves per CU; LDS (double-buffered K|V tiles) bounds
-    // the workgroups per CU further for wide heads
-    constexpr int by_regs = 8 / NW;
     constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfPageCache + 64));
-    constexpr int per_cu = by_regs < by_lds ? by_regs : by_lds;
+    constexpr int per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
     int grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid > p.max_pf_items) grid = p.max_pf_items;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW>), dim3(grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
   }

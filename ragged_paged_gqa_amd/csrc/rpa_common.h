@@ -20,12 +20,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Rows of a decode-class unit: one 16-wide MFMA column block.
 constexpr int kDecRows = 16;
-// Waves (of 32 rows each) of a prefill-class tile: 8 for head_dim <= 128;
-// 4 for head_dim 256, whose accumulators need a whole SIMD's registers.
-#ifndef RPA_PF_WAVES_NARROW
-#define RPA_PF_WAVES_NARROW 8
-#endif
-constexpr int pf_waves_for(int D) { return D >= 256 ? 4 : RPA_PF_WAVES_NARROW; }
+// A prefill-class tile is worked by 4 waves of 32 packed rows each. For
+// head_dim <= 128 two such workgroups share a CU (two waves per SIMD, with
+// barriers that couple only their own 4 waves); head_dim 256 needs a whole
+// SIMD's registers per wave.
+constexpr int kPfWaves = 4;
+constexpr int pf_halves_for(int D) { return D > 0 ? 1 : 1; }  // 32-row halves per wave
+constexpr int pf_rows_for(int D) { return 32 * pf_halves_for(D) * kPfWaves; }
+constexpr int pf_wgs_per_cu(int D) { return D >= 256 ? 1 : 2; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;
 // Largest key chunk of a prefill-class item (bounds the per-item page cache).

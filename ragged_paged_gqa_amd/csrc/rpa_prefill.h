@@ -52,9 +52,9 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Keys per load step (one LDS ring slot, one barrier): 64 for bf16 with
-// head_dim <= 128, else 32. Scores are always computed 32 keys at a time.
-constexpr int pf_step_keys(int D, bool fp8) { return (!fp8 && D <= 128) ? 64 : 32; }
+// Keys per load step (one LDS ring slot, one barrier). Scores are computed
+// 32 keys at a time.
+constexpr int pf_step_keys(int D, bool fp8) { return (D > 0 && !fp8) ? 32 : 32; }
 
 #ifndef RPA_PF_STAGES
 #define RPA_PF_STAGES 4
@@ -144,8 +144,11 @@ __device__ __forceinline__ float other_half(float v) {
 #define RPA_SCHED_DS_READS(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
 #define RPA_SCHED_MFMAS(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
 
-template <int D, bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
+  constexpr int NW = kPfWaves;
+  constexpr int NH = pf_halves_for(D);        // 32-row halves per wave
+  constexpr int WR = 32 * NH;                 // rows per wave
   constexpr int NS = D / 16;                  // k-steps of the QK product
   constexpr int NDB = D / 32;                 // 32-row blocks of O^T
   constexpr int EB = FP8 ? 1 : 2;             // bytes per K/V element in HBM
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   static_assert(LPR <= 64, "one row per DMA instruction");
   static_assert(KS % NW == 0 && (NB == 1 || NB == 2), "step shape");
   static_assert(!FP8 || NST == 2, "fp8 path stages through registers one step ahead");
+  static_assert(16 % RPW == 0 || RPW == 16, "a wave's rows stay inside one 16-key block");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
   __shared__ int sh_pages[kPfPageCache];  // physical pages of the current item
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int r32 = lane & 31;  // S^T column = row within the wave
+  const int r32 = lane & 31;  // S^T column = row within a 32-row half
   const int h = lane >> 5;    // which half of the row's keys this lane holds
 
   if (p.hdr->n_pf_items == 0) return;  // nothing of this class in the batch
@@ -191,6 +195,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int k_rd = r32 * RB + 16 * h;  // K[key = r32][8h ...] ; + 32*s per k-step
   const int g16 = lane >> 4, l16 = lane & 15;
   const int v_rd = (4 * (g16 >> 1) + (l16 >> 2)) * RB + 2 * D + 2 * (16 * (g16 & 1) + 4 * (l16 & 3));
+  // bf16 loader: this wave moves keys [wave * RPW, (wave + 1) * RPW) of every
+  // step, all inside 16-key page block my_blk; per lane only a fixed byte
+  // offset inside that block is needed
+  const int my_blk = (wave * RPW) >> 4;
+  uint32_t row_off[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) row_off[i] = (uint32_t)(((wave * RPW + i) & 15) * key_stride) + 16u * lane;
 
   // queues: start with this XCD's, then steal from the others in turn
   const int home = xcc_id() % kQueues;
@@ -234,43 +245,51 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     for (int i = tid; i < n_pg; i += NT) sh_pages[i] = min(max(ptab[min(lp0 + i, p.pps - 1)], 0), p.P - 1);
     __syncthreads();
 
-    // this lane's query row
-    const int r = 32 * wave + r32;
-    const bool rvalid = r < u.nrows;
-    const int prow = u.row0 + r;
-    const int t = prow / p.G;
-    const int qh = kvh * p.G + (prow - t * p.G);
-    const int tok = q0 + t;
-    const int pos = kvl - ql + t;
-    bf16x8 qb[NS];
-    if (rvalid) {
-      const uint16_t* qp = p.q + ((int64_t)tok * p.Hq + qh) * D;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * i + 8 * h);
-        if (neg) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-        qb[i] = __builtin_bit_cast(bf16x8, v);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) qb[i] = bf16x8{};
-    }
-    // the wave's row span, for the masked-block test
-    const int wr_last = min(32 * wave + 31, u.nrows - 1);
-    const int pos_lo = kvl - ql + (u.row0 + 32 * wave) / p.G;
-    const int pos_hi = kvl - ql + (u.row0 + max(wr_last, 32 * wave)) / p.G;
+    // this lane's query rows, one per half
     const int vis_hi = min(kvl, c_hi);
-    // can this lane's row see key `key` (`flashAttention` masks, kv length,
-    // chunk end)?
-    const int win_lo = p.window > 0 ? pos - p.window : INT_MIN;  // keys <= win_lo are hidden
-    const int vis_end = p.is_causal ? min(vis_hi, pos + 1) : vis_hi;
-    auto visible = [&](int key) { return rvalid && key < vis_end && key > win_lo; };
-
-    float m_ref = -INFINITY;  // reference max (base-2 units) of this lane's row
-    float lsum = 0.f;
-    f32x16 o[NDB];
+    int row[NH], tok[NH], qh[NH], vis_end[NH], win_lo[NH];
+    bool rvalid[NH];
+    bf16x8 qb[NH][NS];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
+    for (int hf = 0; hf < NH; ++hf) {
+      row[hf] = WR * wave + 32 * hf + r32;
+      rvalid[hf] = row[hf] < u.nrows;
+      const int prow = u.row0 + row[hf];
+      const int t = prow / p.G;
+      qh[hf] = kvh * p.G + (prow - t * p.G);
+      tok[hf] = q0 + t;
+      const int pos = kvl - ql + t;
+      // key visibility (`flashAttention` masks, kv length, chunk end)
+      win_lo[hf] = p.window > 0 ? pos - p.window : INT_MIN;  // keys <= win_lo are hidden
+      vis_end[hf] = p.is_causal ? min(vis_hi, pos + 1) : vis_hi;
+      if (rvalid[hf]) {
+        const uint16_t* qp = p.q + ((int64_t)tok[hf] * p.Hq + qh[hf]) * D;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * i + 8 * h);
+          if (neg) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+          qb[hf][i] = __builtin_bit_cast(bf16x8, v);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) qb[hf][i] = bf16x8{};
+      }
+    }
+    auto visible = [&](int hf, int key) { return rvalid[hf] && key < vis_end[hf] && key > win_lo[hf]; };
+    // the wave's row span, for the masked-block test
+    const int wr_last = min(WR * wave + WR - 1, u.nrows - 1);
+    const int pos_lo = kvl - ql + (u.row0 + WR * wave) / p.G;
+    const int pos_hi = kvl - ql + (u.row0 + max(wr_last, WR * wave)) / p.G;
+
+    float m_ref[NH], lsum[NH];  // reference max (base-2 units) and running sum of this lane's rows
+    f32x16 o[NH][NDB];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      m_ref[hf] = -INFINITY;
+      lsum[hf] = 0.f;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[hf][d] = f32x16{};
+    }
 
     // page position of the next step to load, advanced without division
     int lp = c_lo / p.page;
@@ -285,36 +304,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
         }
       }
     };
-    // base addresses of the 16-key blocks of the step at (lp, sl); a block
-    // past the chunk re-reads block 0 (harmless: its keys are masked and
-    // their V rows zeroed)
-    auto block_bases = [&](int k0, const uint8_t* (&bb)[NB16]) {
-      int lpb = lp, slb = sl;
-#pragma unroll
-      for (int b = 0; b < NB16; ++b) {
-        const int ph = sh_pages[min(lpb - lp0, kPfPageCache - 1)];
-        const uint8_t* base = kv_h + ((int64_t)ph * p.page + slb) * key_stride;
-        bb[b] = (b == 0 || k0 + 16 * b < c_hi) ? base : bb[0];
-        slb += 16;
-        if (slb >= p.page) {
-          slb = 0;
-          ++lpb;
-        }
-      }
-    };
 
     // ---- loader, bf16: rows straight into the LDS ring ----
-    // Wave w moves keys [w * RPW, (w + 1) * RPW) of each step, all inside one
-    // 16-key page block; per lane only a fixed byte offset inside the block
-    // is needed, the block base is wave-uniform.
-    constexpr int kWaveBlk = (RPW <= 16) ? 0 : -1;
-    static_assert(kWaveBlk == 0 && 16 % RPW == 0, "a wave's rows stay inside one 16-key block");
-    const int my_blk = (wave * RPW) >> 4;
-    uint32_t row_off[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) row_off[i] = (uint32_t)(((wave * RPW + i) & 15) * key_stride) + 16u * lane;
     auto issue_dma = [&](int k0, char* dst) {
       // page block my_blk of the step at (lp, sl), or block 0 past the chunk
+      // (a harmless re-read: its keys are masked and their V rows zeroed)
       int lpb = lp, slb = sl;
       if (k0 + 16 * my_blk < c_hi) {
         for (int b = 0; b < my_blk; ++b) {
@@ -333,6 +327,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
         if (lane < LPR) dma16_sbase(base, row_off[i], dst0 + i * RB);
     };
     // ---- loader, fp8: registers one step ahead, widened to bf16 ----
+    // base addresses of the 16-key blocks of the step at (lp, sl)
+    auto block_bases = [&](int k0, const uint8_t* (&bb)[NB16]) {
+      int lpb = lp, slb = sl;
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) {
+        const int ph = sh_pages[min(lpb - lp0, kPfPageCache - 1)];
+        const uint8_t* base = kv_h + ((int64_t)ph * p.page + slb) * key_stride;
+        bb[b] = (b == 0 || k0 + 16 * b < c_hi) ? base : bb[0];
+        slb += 16;
+        if (slb >= p.page) {
+          slb = 0;
+          ++lpb;
+        }
+      }
+    };
     u32x4 stage[CPT];
     auto load_regs = [&](int k0) {
       const uint8_t* bb[NB16];
@@ -387,16 +396,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
       }
     }
 
-    // Score blocks of 32 keys; block u belongs to load step u / NB. The
-    // accumulator is touched only by MFMAs inside the loop: when a row's
-    // maximum outgrows the reference, the loop is left, the accumulator
+    // Score blocks of 32 keys; block ub belongs to load step ub / NB. The
+    // accumulators are touched only by MFMAs inside the loop: when a row's
+    // maximum outgrows its reference, the loop is left, the accumulators
     // rescaled, and the same block resumed (its scores kept in st).
-    f32x16 st = f32x16{};
+    f32x16 st[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) st[hf] = f32x16{};
+    float m_blk[NH];
     int ub = 0;
     bool resume = false;
     for (;;) {
       bool pending = false;
-      float m_blk = -INFINITY;
       for (; ub < n_sub; ++ub) {
         const int n = ub / NB;
         const int b = ub % NB;
@@ -447,36 +458,45 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
             }
           }
 
-          // S^T = K Q^T for keys [kb, kb + 32)
-          st = f32x16{};
+          // S^T = K Q^T for keys [kb, kb + 32): one K operand feeds every half
           {
             const char* kr = cur + 32 * b * RB + k_rd;
             bf16x8 ka[NS];
 #pragma unroll
             for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + 32 * i);
 #pragma unroll
-            for (int i = 0; i < NS; ++i) st = mfma32x32x16(ka[i], qb[i], st);
+            for (int hf = 0; hf < NH; ++hf) st[hf] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+#pragma unroll
+              for (int hf = 0; hf < NH; ++hf) st[hf] = mfma32x32x16(ka[i], qb[hf][i], st[hf]);
             RPA_SCHED_DS_READS(NS);
-            RPA_SCHED_MFMAS(NS);
+            RPA_SCHED_MFMAS(NS * NH);
           }
-          if (capped) {
+          // row maxima over the visible keys, in base-2 units
+          bool grow = false;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) st[j] = soft_cap_f(st[j] * sm, p.soft_cap, cap_k) * kLog2e;
+          for (int hf = 0; hf < NH; ++hf) {
+            if (capped) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) st[hf][j] = soft_cap_f(st[hf][j] * sm, p.soft_cap, cap_k) * kLog2e;
+            }
+            float mx;
+            if (need_mask) {
+              mx = -INFINITY;
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                mx = fmaxf(mx, visible(hf, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? st[hf][j] : -INFINITY);
+            } else {
+              mx = st[hf][0];
+#pragma unroll
+              for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[hf][j]);
+            }
+            mx = fmaxf(mx, other_half(mx));
+            m_blk[hf] = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
+            grow = grow || m_blk[hf] > m_ref[hf] + kRescaleSlack;
           }
-          // row maximum over the visible keys, in base-2 units
-          float mx;
-          if (need_mask) {
-            mx = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, visible(kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? st[j] : -INFINITY);
-          } else {
-            mx = st[0];
-#pragma unroll
-            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[j]);
-          }
-          mx = fmaxf(mx, other_half(mx));
-          m_blk = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
-          if (__any(m_blk > m_ref + kRescaleSlack)) {
+          if (__any(grow)) {
             pending = true;
             break;
           }
@@ -486,87 +506,117 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
         // P = 2^(score - reference), packed to bf16 for the PV product; the
         // row sum is taken in f32 over the unrounded values (the LSE needs
         // them: one dominant key rounded to bf16 moves it by up to 2^-8)
-        const float negm = m_ref == -INFINITY ? 0.f : -m_ref;
-        bf16x8 pb[2];
-        auto make_p = [&](auto masked) {
+        bf16x8 pb[NH][2];
+        auto make_p = [&](auto hfc, auto masked) {
+          constexpr int hf = decltype(hfc)::value;
+          const float negm = m_ref[hf] == -INFINITY ? 0.f : -m_ref[hf];
 #pragma unroll
           for (int jp = 0; jp < 8; ++jp) {
-            float p0 = fast_exp2(__builtin_fmaf(st[2 * jp], cmul, negm));
-            float p1 = fast_exp2(__builtin_fmaf(st[2 * jp + 1], cmul, negm));
+            float p0 = fast_exp2(__builtin_fmaf(st[hf][2 * jp], cmul, negm));
+            float p1 = fast_exp2(__builtin_fmaf(st[hf][2 * jp + 1], cmul, negm));
             if constexpr (decltype(masked)::value) {
               const int key0 = kb + 8 * (jp >> 1) + 4 * h + 2 * (jp & 1);
-              p0 = visible(key0) ? p0 : 0.f;
-              p1 = visible(key0 + 1) ? p1 : 0.f;
+              p0 = visible(hf, key0) ? p0 : 0.f;
+              p1 = visible(hf, key0 + 1) ? p1 : 0.f;
             }
-            lsum += p0 + p1;
+            lsum[hf] += p0 + p1;
             const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
-            pb[jp >> 2][2 * (jp & 3)] = pair[0];
-            pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
+            pb[hf][jp >> 2][2 * (jp & 3)] = pair[0];
+            pb[hf][jp >> 2][2 * (jp & 3) + 1] = pair[1];
           }
         };
-        if (need_mask)
-          make_p(std::true_type{});
-        else
-          make_p(std::false_type{});
+        auto p_of_half = [&](auto hfc) {
+          if (need_mask)
+            make_p(hfc, std::true_type{});
+          else
+            make_p(hfc, std::false_type{});
+        };
 
-        // O^T += V^T P^T (two 16-key k-steps)
+        // O^T += V^T P^T (two 16-key k-steps); one V^T operand feeds every half
         const char* vr = cur + 32 * b * RB + v_rd;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 va[NDB];
+        auto read_va = [&](int ks, bf16x8 (&va)[NDB]) {
 #pragma unroll
           for (int d = 0; d < NDB; ++d) {
             const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + 64 * d));
             const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + 64 * d));
             va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
+        };
+        if constexpr (NH == 1) {
+          p_of_half(std::integral_constant<int, 0>{});
 #pragma unroll
-          for (int d = 0; d < NDB; ++d) o[d] = mfma32x32x16(va[d], pb[ks], o[d]);
-          RPA_SCHED_DS_READS(2 * NDB);
-          RPA_SCHED_MFMAS(NDB);
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 va1[NDB];
+            read_va(ks, va1);
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) o[0][d] = mfma32x32x16(va1[d], pb[0][ks], o[0][d]);
+            RPA_SCHED_DS_READS(2 * NDB);
+            RPA_SCHED_MFMAS(NDB);
+          }
+        } else {
+          bf16x8 va[2][NDB];
+          read_va(0, va[0]);
+          read_va(1, va[1]);
+          p_of_half(std::integral_constant<int, 0>{});
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) o[0][d] = mfma32x32x16(va[ks][d], pb[0][ks], o[0][d]);
+          // the second half's softmax runs while the first half's PV MFMAs execute
+          p_of_half(std::integral_constant<int, NH - 1>{});
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) o[NH - 1][d] = mfma32x32x16(va[ks][d], pb[NH - 1][ks], o[NH - 1][d]);
         }
         if (b == NB - 1 || ub == n_sub - 1) ring = (ring + 1) % NST;
       }
       if (!pending) break;
       // move the reference max (every row of the wave at once; alpha <= 1)
-      const float m_new = fmaxf(m_ref, m_blk);
-      const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      lsum *= alpha;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+      for (int hf = 0; hf < NH; ++hf) {
+        const float m_new = fmaxf(m_ref[hf], m_blk[hf]);
+        const float alpha = m_ref[hf] == -INFINITY ? 0.f : fast_exp2(m_ref[hf] - m_new);
+        m_ref[hf] = m_new;
+        lsum[hf] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[hf][d] *= alpha;
+      }
       resume = true;
     }
 
-    const float l_row = lsum + other_half(lsum);
-    const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
-    const float lse_v = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
     // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
-    if (u.nch == 1) {
-      if (rvalid) {
-        uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D + 4 * h;
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const float l_row = lsum[hf] + other_half(lsum[hf]);
+      const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
+      const float lse_v = l_row > 0.f ? (m_ref[hf] + fast_log2(l_row)) * kLn2 : -INFINITY;
+      if (!rvalid[hf]) continue;
+      if (u.nch == 1) {
+        uint16_t* op = p.out + ((int64_t)tok[hf] * p.Hq + qh[hf]) * D + 4 * h;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            u32x2 w = {bf16x2_bits(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv),
-                       bf16x2_bits(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv)};
+            u32x2 w = {bf16x2_bits(o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv),
+                       bf16x2_bits(o[hf][d][4 * q4 + 2] * inv, o[hf][d][4 * q4 + 3] * inv)};
             *reinterpret_cast<u32x2*>(op + 32 * d + 8 * q4) = w;
           }
-        if (h == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
-      }
-    } else {
-      if (rvalid) {
-        float* pp = p.pf_part + ((int64_t)item * p.pf_rows + r) * D + 4 * h;
+        if (h == 0 && p.lse) p.lse[(int64_t)tok[hf] * p.Hq + qh[hf]] = lse_v;
+      } else {
+        float* pp = p.pf_part + ((int64_t)item * p.pf_rows + row[hf]) * D + 4 * h;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 w = {o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv, o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
+            f32x4 w = {o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv, o[hf][d][4 * q4 + 2] * inv,
+                       o[hf][d][4 * q4 + 3] * inv};
             store_coherent4(pp + 32 * d + 8 * q4, w);
           }
-        if (h == 0) store_coherent(p.pf_plse + (int64_t)item * p.pf_rows + r, lse_v);
+        if (h == 0) store_coherent(p.pf_plse + (int64_t)item * p.pf_rows + row[hf], lse_v);
       }
+    }
+    if (u.nch > 1) {
       // publish the partial, count the chunk; the last one merges the unit
       wait_stores();
       __syncthreads();
