@@ -19,7 +19,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "librpa.so")
+# RPA_LIB_PATH may name another build of the same sources (e.g. a tuning variant).
+LIB_PATH = os.environ.get("RPA_LIB_PATH") or os.path.join(_HERE, "_build", "librpa.so")
 
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3FN = 1

@@ -64,16 +64,41 @@ constexpr int kStagesBf16 = RPA_PF_STAGES;
 // (16 keys), plus the partial pages at both ends.
 constexpr int kPfPageCache = kPfMaxChunk / 16 + 4;
 
+// Two LDS layouts of a ring slot, both bank-conflict free for the MFMA
+// operand reads below:
+//   * swizzled (a key's K and V rows together are under 1 KB): the step's K
+//     rows (region 0) and V rows (region 1), each kStepKeys unpadded rows of
+//     2D bytes whose 16-byte chunks are XOR-swizzled by the key (swz_k /
+//     swz_v), so that one DMA instruction writes 1 KB of whole rows;
+//   * padded (head_dim 256: K row then V row of a key is exactly 1 KB, one
+//     DMA instruction): rows of K|V padded to 16 * (16n + 3) bytes, so 16
+//     consecutive keys start in distinct 16-byte bank groups.
 template <int D, bool FP8>
 struct PrefillLds {
-  // K row (2D bytes) then V row (2D bytes), padded to 16*(16n+3) bytes so that
-  // 16 consecutive keys start in distinct 16-byte bank groups.
-  static constexpr int kRowBytes = 4 * D + 48;
+  static constexpr bool kSwizzled = 4 * D < 1024;
+  static constexpr int kRowBytes = kSwizzled ? 2 * D : 4 * D + 48;  // row stride
+  static constexpr int kChunks = 2 * D / 16;   // 16-byte chunks per K or V row
   static constexpr int kStepKeys = pf_step_keys(D, FP8);
-  static constexpr int kBufBytes = kStepKeys * kRowBytes;
+  static constexpr int kRegionBytes = kSwizzled ? kStepKeys * kRowBytes : 2 * D;  // V offset
+  static constexpr int kBufBytes = kSwizzled ? 2 * kStepKeys * kRowBytes : kStepKeys * kRowBytes;
   static constexpr int kStages = FP8 ? 2 : kStagesBf16;
   static constexpr size_t kBytes = (size_t)kStages * kBufBytes;
 };
+
+// Chunk swizzles. K is read by MFMA operand loads in which 16 lanes hold 16
+// consecutive keys at the same chunk: XOR with the key's low bits spreads
+// them over the banks. V is read transposed (ds_read_b64_tr_b16) by 4 keys
+// x 4 chunks per 16 lanes: XOR of the chunk's block-of-4 index with key % 4.
+template <int D>
+__device__ __forceinline__ int swz_k(int key) {
+  constexpr int C = 2 * D / 16;
+  return key & ((C < 16 ? C : 16) - 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int key) {
+  constexpr int C = 2 * D / 16;
+  return (4 * (key & 3)) & (C - 1);
+}
 
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
 template <int N>
@@ -157,17 +182,24 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   constexpr int NB = KS / 32;                 // 32-key score blocks per load step
   constexpr int NB16 = KS / 16;               // 16-key page blocks per load step
   constexpr int RB = PrefillLds<D, FP8>::kRowBytes;
+  constexpr int CPR = PrefillLds<D, FP8>::kChunks;
+  constexpr int REG = PrefillLds<D, FP8>::kRegionBytes;  // byte offset of a key's V row from its K row
+  constexpr bool SWZ = PrefillLds<D, FP8>::kSwizzled;
   constexpr int BUF = PrefillLds<D, FP8>::kBufBytes;
   constexpr int NST = PrefillLds<D, FP8>::kStages;
   constexpr int GCH = 2 * D * EB / 16;        // 16-byte global chunks per key (K and V)
   constexpr int CPT = (KS * GCH + NT - 1) / NT;  // fp8 path: chunks per thread per step
-  constexpr int RPW = KS / NW;                // bf16 path: rows each wave moves per step
-  constexpr int LPR = 4 * D / 16;             // bf16 path: lanes per row (16 bytes each)
+  // bf16 path: full-width DMA instructions of 1 KB. Swizzled: RPI rows of one
+  // region each, wave w moving region w / 2, keys [16 (w % 2), + 16).
+  // Padded: one key's K|V row each, wave w moving keys [8 w, 8 w + 8). Either
+  // way a wave's keys lie in one 16-key page block.
+  constexpr int RPI = SWZ ? 1024 / RB : 1;    // rows per DMA instruction
+  constexpr int NIW = SWZ ? (2 * KS / RPI) / NW : KS / NW;  // DMA instructions per wave per step
   static_assert(NDB >= 2, "head_dim >= 64");
-  static_assert(LPR <= 64, "one row per DMA instruction");
+  static_assert(SWZ ? RPI * CPR == 64 : 2 * CPR == 64, "whole rows per full-width DMA instruction");
   static_assert(KS % NW == 0 && (NB == 1 || NB == 2), "step shape");
   static_assert(!FP8 || NST == 2, "fp8 path stages through registers one step ahead");
-  static_assert(16 % RPW == 0 || RPW == 16, "a wave's rows stay inside one 16-key block");
+  static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == (SWZ ? 16 : 8)), "a wave's rows stay in one 16-key block");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
   __shared__ int sh_pages[kPfPageCache];  // physical pages of the current item
@@ -191,17 +223,40 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   const float sm = neg ? -p.sm_scale : p.sm_scale;
   const float cmul = capped ? 1.0f : sm * kLog2e;
 
-  // LDS read bases (byte offsets inside a buffer)
-  const int k_rd = r32 * RB + 16 * h;  // K[key = r32][8h ...] ; + 32*s per k-step
-  const int g16 = lane >> 4, l16 = lane & 15;
-  const int v_rd = (4 * (g16 >> 1) + (l16 >> 2)) * RB + 2 * D + 2 * (16 * (g16 & 1) + 4 * (l16 & 3));
-  // bf16 loader: this wave moves keys [wave * RPW, (wave + 1) * RPW) of every
-  // step, all inside 16-key page block my_blk; per lane only a fixed byte
-  // offset inside that block is needed
-  const int my_blk = (wave * RPW) >> 4;
-  uint32_t row_off[RPW];
+  // LDS read offsets inside a slot (loop-invariant per lane):
+  //   K operand of k-step i: key r32, chunk 2i + h
+  //   V^T operand of d-block d: key 4 (g16 / 2) + l16 / 4 (+ 8, + 16 ks),
+  //   bytes 32 (g16 % 2) + 8 (l16 % 4) + 64 d of the row
+  // (swizzled: per-lane tables; padded: one base plus immediate offsets)
+  int k_off[SWZ ? NS : 1];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) row_off[i] = (uint32_t)(((wave * RPW + i) & 15) * key_stride) + 16u * lane;
+  for (int i = 0; i < (SWZ ? NS : 1); ++i) k_off[i] = r32 * RB + 16 * (SWZ ? ((2 * i + h) ^ swz_k<D>(r32)) : h);
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int v_key = 4 * (g16 >> 1) + (l16 >> 2);
+  int v_off[SWZ ? NDB : 1];
+#pragma unroll
+  for (int d = 0; d < (SWZ ? NDB : 1); ++d) {
+    const int byte = 32 * (g16 & 1) + 8 * (l16 & 3) + 64 * d;
+    v_off[d] = REG + v_key * RB + (SWZ ? 16 * ((byte >> 4) ^ swz_v<D>(v_key)) + (byte & 15) : byte);
+  }
+  auto k_at = [&](int i) { return SWZ ? k_off[SWZ ? i : 0] : k_off[0] + 32 * i; };
+  auto v_at = [&](int d) { return SWZ ? v_off[SWZ ? d : 0] : v_off[0] + 64 * d; };
+  // bf16 loader: this wave's DMA instructions and its lanes' fixed source
+  // offsets inside the page block
+  const int my_blk = SWZ ? (wave & 1) : (wave >> 1);
+  const int my_region = SWZ ? (wave >> 1) : 0;
+  uint32_t dma_off[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    if constexpr (SWZ) {
+      const int krow = RPI * j + lane / CPR;  // key within the 16-key block
+      const int c_lds = lane % CPR;
+      const int c_g = c_lds ^ (my_region ? swz_v<D>(krow) : swz_k<D>(krow));
+      dma_off[j] = (uint32_t)(krow * key_stride) + (uint32_t)(my_region * 2 * D) + 16u * c_g;
+    } else {
+      dma_off[j] = (uint32_t)(((wave * NIW + j) & 15) * key_stride) + 16u * lane;
+    }
+  }
 
   // queues: start with this XCD's, then steal from the others in turn
   const int home = xcc_id() % kQueues;
@@ -321,10 +376,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
       const int ph = __builtin_amdgcn_readfirstlane(sh_pages[min(lpb - lp0, kPfPageCache - 1)]);
       const uint8_t* base = uniform_ptr(kv_h + ((int64_t)ph * p.page + slb) * key_stride);
-      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst + wave * RPW * RB));
+      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
+          lds_addr_of(dst + (SWZ ? my_region * REG + 16 * my_blk * RB : wave * NIW * RB)));
 #pragma unroll
-      for (int i = 0; i < RPW; ++i)
-        if (lane < LPR) dma16_sbase(base, row_off[i], dst0 + i * RB);
+      for (int j = 0; j < NIW; ++j) dma16_sbase(base, dma_off[j], dst0 + (SWZ ? 1024 : RB) * j);
     };
     // ---- loader, fp8: registers one step ahead, widened to bf16 ----
     // base addresses of the 16-key blocks of the step at (lp, sl)
@@ -364,15 +419,19 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         const int idx = tid + NT * c;
         if (idx >= KS * GCH) continue;
         const int key = idx / GCH;
-        const int dst_off = key * RB + 32 * (idx % GCH);  // 16 codes -> 32 bytes
+        const int gc = idx % GCH;              // 16 codes: K chunks first, then V
+        const int region = gc / (GCH / 2);
+        const int c0 = 2 * (gc % (GCH / 2));   // first of the two bf16 chunks they become
+        const int sw = !SWZ ? 0 : (region ? swz_v<D>(key) : swz_k<D>(key));
+        char* row_p = dst + region * REG + key * RB;
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
         bf16x8 a = fp8x8_to_bf16(lo2), b = fp8x8_to_bf16(hi2);
         if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
           a = bf16x8{};
           b = bf16x8{};
         }
-        *reinterpret_cast<bf16x8*>(dst + dst_off) = a;
-        *reinterpret_cast<bf16x8*>(dst + dst_off + 16) = b;
+        *reinterpret_cast<bf16x8*>(row_p + 16 * (c0 ^ sw)) = a;
+        *reinterpret_cast<bf16x8*>(row_p + 16 * ((c0 + 1) ^ sw)) = b;
       }
     };
     auto slot_ptr = [&](int k) { return lds + ((ring + k) % NST) * BUF; };
@@ -431,21 +490,20 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
               // wait for this step's rows: later steps may stay in flight
               const int ahead = issued - n - 1;
               if (ahead >= 2) {
-                wait_vmcnt<2 * RPW>();
+                wait_vmcnt<2 * NIW>();
               } else if (ahead == 1) {
-                wait_vmcnt<RPW>();
+                wait_vmcnt<NIW>();
               } else {
                 wait_vmcnt<0>();
               }
               __syncthreads();
               if (k0 + KS > kvl || k0 + KS > c_hi) {
                 // zero V of rows past kv_len or in blocks past the chunk
-                for (int i = tid; i < KS * (2 * D / 16); i += NT) {
-                  const int key = i / (2 * D / 16);
+                for (int i = tid; i < KS * CPR; i += NT) {
+                  const int key = i / CPR;
                   const bool loaded = key < 16 || k0 + 16 * (key >> 4) < c_hi;
                   if (k0 + key >= kvl || !loaded)
-                    *reinterpret_cast<u32x4*>(cur + key * RB + 2 * D + 16 * (i % (2 * D / 16))) =
-                        u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4*>(cur + REG + key * RB + 16 * (i % CPR)) = u32x4{0u, 0u, 0u, 0u};
                 }
                 __syncthreads();
               }
@@ -460,10 +518,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 
           // S^T = K Q^T for keys [kb, kb + 32): one K operand feeds every half
           {
-            const char* kr = cur + 32 * b * RB + k_rd;
+            const char* kr = cur + 32 * b * RB;
             bf16x8 ka[NS];
 #pragma unroll
-            for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + 32 * i);
+            for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + k_at(i));
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf) st[hf] = f32x16{};
 #pragma unroll
@@ -533,12 +591,12 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         };
 
         // O^T += V^T P^T (two 16-key k-steps); one V^T operand feeds every half
-        const char* vr = cur + 32 * b * RB + v_rd;
+        const char* vr = cur + 32 * b * RB;
         auto read_va = [&](int ks, bf16x8 (&va)[NDB]) {
 #pragma unroll
           for (int d = 0; d < NDB; ++d) {
-            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + 64 * d));
-            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + 64 * d));
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + v_at(d)));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + v_at(d)));
             va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
         };
