@@ -17,6 +17,14 @@
 #include "rpa_plan.h"
 #include "rpa_prefill.h"
 
+// Work items the planner aims for per compute unit, per kernel class.
+#ifndef RPA_DEC_ITEMS_PER_CU
+#define RPA_DEC_ITEMS_PER_CU 32
+#endif
+#ifndef RPA_PF_ITEMS_PER_CU
+#define RPA_PF_ITEMS_PER_CU 4
+#endif
+
 namespace {
 
 using namespace rpa;
@@ -81,9 +89,13 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t pf_rows = pf_rows_for(c->head_dim);
   const int64_t max_du = Hkv * c->max_num_seqs;
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
-  const int64_t tgt_d = (int64_t)cus * 32;
-  const int64_t tgt_p = (int64_t)cus * 4;
-  const int64_t max_di = max_du + tgt_d;
+  const int64_t tgt_d = (int64_t)cus * RPA_DEC_ITEMS_PER_CU;
+  const int64_t tgt_p = (int64_t)cus * RPA_PF_ITEMS_PER_CU;
+  // decode chunks are also capped at dec_max_chunk(page) keys
+  const int64_t dec_cap = dec_max_chunk(c->page_size);
+  const int64_t max_kv = (int64_t)c->pages_per_seq * c->page_size;
+  const int64_t dec_per_unit = (max_kv + dec_cap - 1) / dec_cap;
+  const int64_t max_di = max_du + (tgt_d > max_du * dec_per_unit ? tgt_d : max_du * dec_per_unit);
   // prefill chunks are also capped at kPfMaxChunk keys
   const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
   const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);
@@ -92,7 +104,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->hdr = off;   off = align256(off + sizeof(Header));
   L->du = off;    off = align256(off + sizeof(Unit) * (size_t)max_du);
   L->pu = off;    off = align256(off + sizeof(Unit) * (size_t)max_pu);
-  L->di = off;    off = align256(off + sizeof(Item) * (size_t)max_di);
+  L->di = off;    off = align256(off + sizeof(DecItem) * (size_t)max_di);
   L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
   L->qlist = off; off = align256(off + sizeof(int32_t) * kQueues * (size_t)max_pi);
   L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
@@ -118,7 +130,7 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.hdr = reinterpret_cast<Header*>(w + L.hdr);
   p.dec_units = reinterpret_cast<Unit*>(w + L.du);
   p.pf_units = reinterpret_cast<Unit*>(w + L.pu);
-  p.dec_items = reinterpret_cast<Item*>(w + L.di);
+  p.dec_items = reinterpret_cast<DecItem*>(w + L.di);
   p.pf_items = reinterpret_cast<Item*>(w + L.pi);
   p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
@@ -180,13 +192,26 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     prof_record(ev, 2, st);
   }
   {
+    // resident workgroups per CU: LDS and the register budget (waves per SIMD
+    // x 4 SIMDs / waves per workgroup) both limit it
     int per_cu = (int)((160 * 1024) / DecodeLds<D>::kBytes);
-    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    const int by_regs = dec_waves_per_simd(D) * 4 / kDecWavesPerBlock;
+    per_cu = per_cu < by_regs ? per_cu : by_regs;
+    per_cu = per_cu < 1 ? 1 : per_cu;
     int grid = cus * per_cu;
     const int need = (p.max_dec_items + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((decode_kernel<D, FP8>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    if (p.soft_cap > 0.f)
+      hipLaunchKernelGGL((decode_kernel<D, FP8, true>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, FP8, false>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    // merge of the split decode units (a wave per unit, grid-stride)
+    int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
+    if (cgrid > cus * 4) cgrid = cus * 4;
+    if (cgrid < 1) cgrid = 1;
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
   }

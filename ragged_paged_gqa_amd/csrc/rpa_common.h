@@ -30,6 +30,10 @@ constexpr int pf_rows_for(int D) { return 32 * pf_halves_for(D) * kPfWaves; }
 constexpr int pf_wgs_per_cu(int D) { return D >= 256 ? 1 : 2; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;
+// Physical pages a decode-class wave holds in registers for its item (one per
+// lane, two registers); a decode item's chunk is capped so its pages fit.
+constexpr int kDecPageWindow = 128;
+__host__ __device__ constexpr int dec_max_chunk(int page) { return ((kDecPageWindow - 1) * page) & ~63; }
 // Largest key chunk of a prefill-class item (bounds the per-item page cache).
 constexpr int kPfMaxChunk = 32768;
 
@@ -54,6 +58,26 @@ struct Item {
   int32_t unit;
   int32_t chunk;
 };
+
+// A decode-class item carries everything its wave needs, so that starting it
+// costs one load: the sequence's metadata and the chunk's key range. The
+// chunks of a unit split its key range evenly (16-aligned boundaries).
+struct DecItem {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t c_lo;   // first key of the chunk (16-aligned)
+  int32_t c_hi;   // one past its last key
+  int32_t kvl;    // kv_len, clamped to the page table's reach
+  int32_t q0;     // first token of the sequence
+  int32_t ql;     // its query tokens
+  int32_t row0;   // first packed row of the unit
+  int32_t nrows;  // packed rows of the unit
+  int32_t nch;    // chunks of the unit (1: the item writes the output itself)
+  int32_t unit;   // unit index
+  int32_t chunk;  // chunk index within the unit
+  int32_t pad[4];
+};
+static_assert(sizeof(DecItem) == 64, "decode item record is int32[16]");
 
 // Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
 // L2). All row blocks of one (sequence, kv head) go to the same queue, one
@@ -94,7 +118,7 @@ struct Params {
   Header* hdr;
   Unit* dec_units;
   Unit* pf_units;
-  Item* dec_items;
+  DecItem* dec_items;
   Item* pf_items;
   int32_t* pf_qlist;         // prefill item indices in queue order [kQueues][max_pf_items]
   int32_t* unit_done;        // finished chunks per unit: [max_dec_units] then [max_pf_units]
@@ -147,6 +171,23 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Values known to be equal on every lane, moved to scalar registers (so the
+// compiler treats them, and what is computed from them, as wave-uniform).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A pointer known to be equal on every lane, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
 
 // Index of the XCD (accelerator complex die) this wave runs on.
 __device__ __forceinline__ int xcc_id() {
@@ -201,6 +242,40 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
+// lane (global_load_lds_dwordx4; lds_addr is the wave-uniform LDS byte
+// address, passed through M0, which is restored afterwards). Written as inline
+// assembly so that the compiler does not add its own conservative wait for the
+// LDS write before every later LDS read: completion is tracked explicitly with
+// wait_vmcnt before the barrier that publishes a stage. An SALU write of M0
+// needs one wait state before an instruction that reads M0 (the compiler puts
+// the same s_nop between its own M0 write and LDS DMA); one more keeps the
+// restore clear of the DMA.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
 }
 
 // Physical page of key `key` of sequence s, clamped into [0, P).

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     tot_dec += red[0][w];
     tot_pf += red[1][w];
   }
-  const FastDiv dec_chunk = make_div(pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, 1 << 28));
+  const FastDiv dec_chunk = make_div(pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, dec_max_chunk(p.page)));
   const FastDiv pf_chunk = make_div(pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk));
 
   // pass 2: per-sequence counts -> one scan per tile -> records
@@ -301,6 +301,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     if (is_dec) {  // decode records, by the sequence's thread
       const int32_t rows = ql * p.G;
       const UnitRange r = unit_range(p, G, ql, kvl, 0, rows);
+      int32_t q0, qlx;
+      seq_tokens(p, s, q0, qlx);
+      const int64_t keys = range_keys(r);
       for (int32_t h = 0; h < p.Hkv; ++h) {
         const int32_t ui = off[0] + h;
         if (ui >= p.max_dec_units) break;
@@ -309,9 +312,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
         u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch_dec; u.item0 = off[2] + h * nch_dec;
         p.dec_units[ui] = u;
         p.unit_done[ui] = 0;
+        // chunk c covers [b(c), b(c + 1)): b(c) = lo + c * keys / nch rounded
+        // down to 16, b(nch) = hi; every chunk is at most dec_chunk keys and,
+        // when the unit splits, at least half of that
         for (int32_t c = 0; c < nch_dec; ++c) {
           const int32_t ii = u.item0 + c;
-          if (ii < p.max_dec_items) p.dec_items[ii] = Item{ui, c};
+          if (ii >= p.max_dec_items) break;
+          DecItem d;
+          d.seq = s; d.kv_head = h;
+          d.c_lo = r.lo16 + (int32_t)(((int64_t)c * keys / nch_dec) & ~(int64_t)15);
+          d.c_hi = c + 1 == nch_dec ? max(r.hi, r.lo16) : r.lo16 + (int32_t)(((int64_t)(c + 1) * keys / nch_dec) & ~(int64_t)15);
+          d.kvl = kvl; d.q0 = q0; d.ql = ql; d.row0 = 0; d.nrows = rows;
+          d.nch = nch_dec; d.unit = ui; d.chunk = c;
+          d.pad[0] = d.pad[1] = d.pad[2] = d.pad[3] = 0;
+          p.dec_items[ii] = d;
         }
       }
     } else if (slot >= 0) {

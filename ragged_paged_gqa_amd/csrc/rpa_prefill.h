@@ -100,36 +100,6 @@ __device__ __forceinline__ int swz_v(int key) {
   return (4 * (key & 3)) & (C - 1);
 }
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
-// lane (global_load_lds_dwordx4; lds_addr is the wave-uniform LDS byte
-// address, passed through M0, which is restored afterwards). Written as inline
-// assembly so that the compiler does not add its own conservative wait for the
-// LDS write before every later LDS read: completion is tracked explicitly with
-// wait_vmcnt before the barrier that publishes a stage. An SALU write of M0
-// needs one wait state before an instruction that reads M0 (the compiler puts
-// the same s_nop between its own M0 write and LDS DMA); one more keeps the
-// restore clear of the DMA.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-      : "memory");
-}
-
 // Same, with the global address split into a wave-uniform 64-bit base (SGPR
 // pair) and a per-lane 32-bit byte offset: no per-lane 64-bit address math.
 __device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
@@ -144,18 +114,6 @@ __device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff,
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds_addr)
       : "memory");
-}
-
-// A pointer known to be equal on every lane, moved to scalar registers.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
-  const uint64_t v = (uint64_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
 }
 
 // Value of lane l ^ 32 (v_permlane32_swap; no LDS round trip).

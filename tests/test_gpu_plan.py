@@ -29,7 +29,9 @@ def _plan(w):
     n_du, n_pu, n_di, n_pi, dch, pch = (int(x) for x in hdr[:6])
     du = host[offs[1]:offs[1] + 32 * n_du].view(np.int32).reshape(n_du, 8)
     pu = host[offs[2]:offs[2] + 32 * n_pu].view(np.int32).reshape(n_pu, 8)
-    di = host[offs[3]:offs[3] + 8 * n_di].view(np.int32).reshape(n_di, 2)
+    # decode items are full descriptors: seq, kv_head, c_lo, c_hi, kvl, q0, ql,
+    # row0, nrows, nch, unit, chunk, 4 x pad
+    di = host[offs[3]:offs[3] + 64 * n_di].view(np.int32).reshape(n_di, 16)
     pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
     qbase, qcount, qnext = hdr[16:24].copy(), hdr[24:32].copy(), hdr[32:40].copy()
     ql = host[offs[5]:offs[5] + 4 * 8 * int(lim[3])].view(np.int32)
@@ -91,10 +93,24 @@ def _check(w):
             # chunks tile [lo, hi) exactly
             assert nch == max(1, -(-(hi - lo) // ch))
             for k in range(nch):
-                assert tuple(items[it0 + k]) == (ui, k)
                 seen_items[it0 + k] += 1
-                a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
+                if cls == "pf":
+                    assert tuple(items[it0 + k]) == (ui, k)
+                    a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
+                    assert a < b or (nch == 1 and hi <= lo)
+                    continue
+                d = items[it0 + k]
+                assert (d[10], d[11]) == (ui, k)
+                assert (d[0], d[1], d[7], d[8], d[9]) == (s, h, r0, nr, nch)
+                assert (d[4], d[5], d[6]) == (kvl, q0, ql)
+                # even split: consecutive, 16-aligned starts, at most ch + 15 keys
+                a, b = int(d[2]), int(d[3])
+                assert a == (lo if k == 0 else int(items[it0 + k - 1][3]))
+                assert a % 16 == 0 and (b == hi if k == nch - 1 else b % 16 == 0)
                 assert a < b or (nch == 1 and hi <= lo)
+                assert b - a <= ch + 15
+                # its pages fit the 128-entry page window of the wave
+                assert (max(b - 1, a)) // c.page_size - a // c.page_size + 1 <= 128
         assert np.all(seen_items == 1), cls
     _check_queues(P, c.num_kv_heads)
     for s in range(w.n_seqs):
