@@ -144,23 +144,34 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
 /*
  * Byte offsets inside the workspace (host-only, no device access):
  *   offsets[0] header: int32[64] = {n_dec_units, n_pf_units, n_dec_items,
- *              n_pf_items, dec_chunk, pf_chunk, n_split_units, dec_counter,
- *              pad[8], queue_base[8], queue_count[8], queue_next[8], pad[24]}
- *              (n_split_units counts units with more than one chunk; the
- *              prefill items are dealt into 8 queues, one per XCD, and queue
- *              x is queue_count[x] entries of the queue list from
+ *              n_pf_items, 0, pf_chunk, n_split_units, dec_blocks,
+ *              dec_waves_used, pad[7], queue_base[8], queue_count[8],
+ *              queue_next[8], pad[24]}
+ *              (n_split_units counts units with more than one item;
+ *              dec_blocks is the number of 16-key blocks of all decode
+ *              units, split over the first dec_waves_used = min(dec_waves,
+ *              dec_blocks) decode waves (at least 1); the prefill items are dealt into 8 queues, one per XCD,
+ *              and queue x is queue_count[x] entries of the queue list from
  *              queue_base[x] = x * max_pf_items on)
  *   offsets[1] decode units   int32[max_dec_units][8]
  *   offsets[2] prefill units  int32[max_pf_units][8]
- *   offsets[3] decode items   int32[max_dec_items][2]
+ *   offsets[3] decode items   int32[max_dec_items][16]
  *   offsets[4] prefill items  int32[max_pf_items][2]
  *   offsets[5] queue list     int32[8][max_pf_items] (prefill item indices)
- * A unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}; an item is
- * {unit, chunk}, covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo + (chunk+1)*C))
- * with C the class's chunk size. limits = {max_dec_units, max_pf_units,
- * max_dec_items, max_pf_items, dec_rows_max, pf_rows_max}.
+ *   offsets[6] first decode item of each decode wave, int32[dec_waves]
+ *              (INT32_MAX for a wave with no item)
+ *   offsets[7] 0 (reserved)
+ * A unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}. A prefill
+ * item is {unit, chunk}, covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo +
+ * (chunk+1)*C)) with C = pf_chunk. A decode item is {seq, kv_head, c_lo, c_hi,
+ * kv_len, q0, q_len, row0, nrows, nch, unit, chunk, wave, 0, 0, 0}: keys
+ * [c_lo, c_hi) of its unit, run by decode wave `wave`; the decode units' key
+ * blocks, laid end to end, are split into dec_waves_used equal contiguous
+ * ranges and each wave's items are consecutive. limits = {max_dec_units,
+ * max_pf_units, max_dec_items, max_pf_items, dec_rows_max, pf_rows_max,
+ * dec_waves, 0}.
  */
-rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[6], int32_t limits[6]);
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[8], int32_t limits[8]);
 
 /*
  * Debug helper for tests: decode n fp8 e4m3fn codes (device array) to

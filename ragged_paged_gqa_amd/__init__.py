@@ -140,8 +140,8 @@ def workspace_bytes(cfg: Config) -> int:
 
 def plan_layout(cfg: Config):
     c = cfg.to_c()
-    offs = (ctypes.c_size_t * 6)()
-    lim = (ctypes.c_int32 * 6)()
+    offs = (ctypes.c_size_t * 8)()
+    lim = (ctypes.c_int32 * 8)()
     _check(lib().rpa_plan_layout(ctypes.byref(c), offs, lim), "rpa_plan_layout")
     return list(offs), list(lim)
 

@@ -74,9 +74,25 @@ rpa_status validate(const rpa_config* c) {
 }
 
 struct Layout {
-  size_t hdr, du, pu, di, pi, qlist, done, dpart, dplse, ppart, pplse, total;
-  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p, pf_rows;
+  size_t hdr, du, pu, di, pi, qlist, done, wfirst, dpart, dplse, ppart, pplse, total;
+  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p, pf_rows, dec_waves;
 };
+
+// Workgroups of the decode launch: one resident set (the stream-K split is
+// made over exactly these waves).
+template <int D, bool FP8>
+int dec_grid(int cus) {
+  const int per_cu = dec_wgs_per_cu<D, FP8>();
+  return cus * (per_cu > 0 ? per_cu : 1);
+}
+int dec_grid_for(const rpa_config* c, int cus) {
+  const bool fp8 = c->kv_dtype == RPA_DTYPE_FP8_E4M3FN;
+  switch (c->head_dim) {
+    case 64: return fp8 ? dec_grid<64, true>(cus) : dec_grid<64, false>(cus);
+    case 128: return fp8 ? dec_grid<128, true>(cus) : dec_grid<128, false>(cus);
+    default: return fp8 ? dec_grid<256, true>(cus) : dec_grid<256, false>(cus);
+  }
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -91,11 +107,9 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
   const int64_t tgt_d = (int64_t)cus * RPA_DEC_ITEMS_PER_CU;
   const int64_t tgt_p = (int64_t)cus * RPA_PF_ITEMS_PER_CU;
-  // decode chunks are also capped at dec_max_chunk(page) keys
-  const int64_t dec_cap = dec_max_chunk(c->page_size);
-  const int64_t max_kv = (int64_t)c->pages_per_seq * c->page_size;
-  const int64_t dec_per_unit = (max_kv + dec_cap - 1) / dec_cap;
-  const int64_t max_di = max_du + (tgt_d > max_du * dec_per_unit ? tgt_d : max_du * dec_per_unit);
+  // stream-K: every decode wave boundary inside a unit adds one item
+  const int64_t dec_waves = (int64_t)dec_grid_for(c, cus) * kDecWavesPerBlock;
+  const int64_t max_di = max_du + dec_waves + 1;
   // prefill chunks are also capped at kPfMaxChunk keys
   const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
   const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);
@@ -108,6 +122,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
   L->qlist = off; off = align256(off + sizeof(int32_t) * kQueues * (size_t)max_pi);
   L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
+  L->wfirst = off; off = align256(off + sizeof(int32_t) * (size_t)dec_waves);
   L->dpart = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows * D);
   L->dplse = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows);
   L->ppart = off; off = align256(off + sizeof(float) * (size_t)max_pi * pf_rows * D);
@@ -120,6 +135,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->tgt_d = (int32_t)tgt_d;
   L->tgt_p = (int32_t)tgt_p;
   L->pf_rows = (int32_t)pf_rows;
+  L->dec_waves = (int32_t)dec_waves;
   return true;
 }
 
@@ -134,6 +150,8 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.pf_items = reinterpret_cast<Item*>(w + L.pi);
   p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
+  p.dec_wave_first = reinterpret_cast<int32_t*>(w + L.wfirst);
+  p.dec_waves = L.dec_waves;
   p.dec_part = reinterpret_cast<float*>(w + L.dpart);
   p.dec_plse = reinterpret_cast<float*>(w + L.dplse);
   p.pf_part = reinterpret_cast<float*>(w + L.ppart);
@@ -192,16 +210,8 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     prof_record(ev, 2, st);
   }
   {
-    // resident workgroups per CU: LDS and the register budget (waves per SIMD
-    // x 4 SIMDs / waves per workgroup) both limit it
-    int per_cu = (int)((160 * 1024) / DecodeLds<D>::kBytes);
-    const int by_regs = dec_waves_per_simd(D) * 4 / kDecWavesPerBlock;
-    per_cu = per_cu < by_regs ? per_cu : by_regs;
-    per_cu = per_cu < 1 ? 1 : per_cu;
-    int grid = cus * per_cu;
-    const int need = (p.max_dec_items + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
+    // exactly the waves the planner split the decode work over
+    const int grid = p.dec_waves / kDecWavesPerBlock;
     if (p.soft_cap > 0.f)
       hipLaunchKernelGGL((decode_kernel<D, FP8, true>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     else
@@ -262,8 +272,8 @@ static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspa
   if (workspace_bytes < L.total) return RPA_ERR_WORKSPACE_TOO_SMALL;
   *p = make_params(cfg, L, workspace);
   // every workspace view the kernels dereference must be assigned
-  const void* views[] = {p->hdr,       p->dec_units, p->pf_units, p->dec_items, p->pf_items, p->pf_qlist,
-                         p->unit_done, p->dec_part,  p->dec_plse, p->pf_part,   p->pf_plse};
+  const void* views[] = {p->hdr,       p->dec_units,      p->pf_units, p->dec_items, p->pf_items, p->pf_qlist,
+                         p->unit_done, p->dec_wave_first, p->dec_part, p->dec_plse,  p->pf_part,  p->pf_plse};
   for (const void* v : views)
     if (!v) return RPA_ERR_INVALID_ARGUMENT;
   *cus_out = cus;
@@ -365,7 +375,7 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
   return launch_plan(p, static_cast<hipStream_t>(stream));
 }
 
-rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[6], int32_t limits[6]) {
+rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[8], int32_t limits[8]) {
   if (!offsets || !limits) return RPA_ERR_INVALID_ARGUMENT;
   rpa_status st = validate(cfg);
   if (st != RPA_OK) return st;
@@ -379,12 +389,16 @@ rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[6], int32_t lim
   offsets[3] = L.di;
   offsets[4] = L.pi;
   offsets[5] = L.qlist;
+  offsets[6] = L.wfirst;
+  offsets[7] = 0;
   limits[0] = L.max_du;
   limits[1] = L.max_pu;
   limits[2] = L.max_di;
   limits[3] = L.max_pi;
   limits[4] = kDecRows;
   limits[5] = L.pf_rows;
+  limits[6] = L.dec_waves;
+  limits[7] = 0;
   return RPA_OK;
 }
 

@@ -30,10 +30,6 @@ constexpr int pf_rows_for(int D) { return 32 * pf_halves_for(D) * kPfWaves; }
 constexpr int pf_wgs_per_cu(int D) { return D >= 256 ? 1 : 2; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;
-// Physical pages a decode-class wave holds in registers for its item (one per
-// lane, two registers); a decode item's chunk is capped so its pages fit.
-constexpr int kDecPageWindow = 128;
-__host__ __device__ constexpr int dec_max_chunk(int page) { return ((kDecPageWindow - 1) * page) & ~63; }
 // Largest key chunk of a prefill-class item (bounds the per-item page cache).
 constexpr int kPfMaxChunk = 32768;
 
@@ -60,8 +56,11 @@ struct Item {
 };
 
 // A decode-class item carries everything its wave needs, so that starting it
-// costs one load: the sequence's metadata and the chunk's key range. The
-// chunks of a unit split its key range evenly (16-aligned boundaries).
+// costs one (scalar) load: the sequence's metadata, the chunk's key range and
+// the decode wave that runs it. Decode work is scheduled stream-K style: the
+// key blocks of all decode units, laid end to end, are cut into equal
+// contiguous ranges, one per decode wave, and an item is the part of one unit
+// that falls into one wave's range.
 struct DecItem {
   int32_t seq;
   int32_t kv_head;
@@ -75,7 +74,8 @@ struct DecItem {
   int32_t nch;    // chunks of the unit (1: the item writes the output itself)
   int32_t unit;   // unit index
   int32_t chunk;  // chunk index within the unit
-  int32_t pad[4];
+  int32_t wave;   // the decode wave that runs it
+  int32_t pad[3];
 };
 static_assert(sizeof(DecItem) == 64, "decode item record is int32[16]");
 
@@ -93,8 +93,8 @@ struct Header {
   int32_t dec_chunk;
   int32_t pf_chunk;
   int32_t n_split_units;
-  int32_t dec_counter;  // work queue of decode items, zeroed by the planning kernel
-  int32_t pad0[8];
+  int32_t dec_blocks;   // 16-key blocks of all decode units (the stream-K total)
+  int32_t pad0[8];      // pad0[0]: decode waves given work (min(dec_waves, dec_blocks), >= 1)
   int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist (x * max_pf_items)
   int32_t pf_q_count[kQueues];  // its length
   int32_t pf_q_next[kQueues];   // its head, zeroed by the planning kernel
@@ -122,6 +122,7 @@ struct Params {
   Item* pf_items;
   int32_t* pf_qlist;         // prefill item indices in queue order [kQueues][max_pf_items]
   int32_t* unit_done;        // finished chunks per unit: [max_dec_units] then [max_pf_units]
+  int32_t* dec_wave_first;   // first decode item of each decode wave [dec_waves] (INT32_MAX: none)
   float* dec_part;           // [max_dec_items][kDecRows][D]
   float* dec_plse;           // [max_dec_items][kDecRows]
   float* pf_part;            // [max_pf_items][pf_rows][D]
@@ -131,6 +132,7 @@ struct Params {
   int32_t pf_rows;           // packed rows of a prefill-class unit
   int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
   int32_t target_dec_items, target_pf_items;
+  int32_t dec_waves;         // waves of the decode launch (the stream-K split)
   // numerics
   float sm_scale;      // sm_scale * k_scale
   float soft_cap;      // > 0: on
@@ -271,6 +273,22 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+// Same, with the global address split into a wave-uniform 64-bit base (SGPR
+// pair) and a per-lane 32-bit byte offset: no per-lane 64-bit address math.
+__device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
       : "memory");
 }
 

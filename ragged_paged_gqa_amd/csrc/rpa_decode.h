@@ -1,44 +1,46 @@
 // Decode-class attention kernel: units of at most 16 packed query rows
 // (q_len * G <= 16, e.g. one decode token of 4..16 grouped q heads).
 //
-// The kernel streams K/V from HBM and is bound by it. A wave works through a
-// sequence of items (key chunks of one sequence and one kv head), the first
-// one fixed by its position in the grid and the rest claimed from a
-// device-wide queue, as one continuous pipeline of 32-key steps:
-//   * loads: K and V rows go straight from HBM into registers, one step ahead
-//     of the compute. Lane (key = lane % 16, k-group g = lane / 16) reads
-//     16-byte pieces of its key row; K of kv head h is combined head 2h and V
-//     is combined head 2h+1 right after it (`stridedLoadKv` on the kernel
-//     page). The load side moves on to the next item as soon as the current
-//     one has no step left, so the pipeline never drains between items;
-//   * pages: each 16-key block takes its physical page (the kernel page's
-//     `createKvAsyncCopyDescriptors`: page_indices[seq, key / page]) from a
-//     128-entry window of the page table that the wave holds in registers, one
-//     entry per lane (v_readlane); a chunk never spans more than 128 pages;
-//   * next item: its queue slot is claimed when the current item starts, and
-//     its descriptor, page window and Q rows are loaded one dependent step at
-//     a time behind the current item's loads, so no load on the critical
-//     path ever waits for another.
-// Per 32-key block:
-//   1. S^T [keys x rows] = K Q^T with v_mfma_f32_16x16x32_bf16 against the
-//      register-resident Q^T, times sm_scale (k_scale folded in), the optional
-//      soft-cap, then the causal / window / length masks of `flashAttention`
-//      by selection (masked scores become -inf, so NaN in unread tail slots
-//      cannot leak in); blocks that every row sees whole skip the mask;
-//   2. the online-softmax update of `flashAttention` in base 2 (running max,
-//      rescale factor alpha = 2^(m_old - m_new), running sum), with the
-//      accumulator kept un-normalised until the end;
-//   3. V (zeroed past kv_len: 0 * NaN would otherwise poison the sum) is
-//      staged through a per-wave LDS tile and read back transposed with
-//      ds_read_b64_tr_b16 as the A operand of O^T += V^T P^T, whose B operand
-//      P^T is exactly the S^T result layout — no shuffle of P.
+// The kernel streams K/V from HBM and is bound by it. Work is split
+// stream-K style by the planner: the 16-key blocks of all decode units, laid
+// end to end, are cut into one equal contiguous range per wave, so every wave
+// moves the same number of bytes and no queue is needed. A wave runs its items
+// (the parts of units inside its range) as one continuous pipeline of 16-key
+// steps:
+//   * loads: each step's K rows and V rows of kv head h (combined heads 2h and
+//     2h+1, adjacent in memory: `stridedLoadKv` on the kernel page) go
+//     straight from HBM into a per-wave ring of LDS slots with
+//     global_load_lds_dwordx4, 1 KB of whole rows per instruction, kept
+//     NST - 1 steps ahead of the compute across item boundaries. The 16-byte
+//     chunks of a row are XOR-swizzled by the key, so that the MFMA operand
+//     reads below hit distinct LDS banks. Completion is tracked by counting
+//     vector-memory instructions (s_waitcnt vmcnt), so nothing else waits on
+//     the stream;
+//   * pages and metadata: the physical page of each 16-key block (the kernel
+//     page's `createKvAsyncCopyDescriptors`: page_indices[seq, key / page])
+//     and the item descriptors are read with scalar loads one step ahead, and
+//     the next item's Q rows are fetched into an LDS slot by the same DMA
+//     while the current item runs.
+// Per 16-key step:
+//   1. S^T [16 keys x 16 rows] = K Q^T with v_mfma_f32_16x16x32_bf16 against
+//      the register-resident Q^T, times sm_scale (k_scale folded in), the
+//      optional soft-cap, then the causal / window / length masks of
+//      `flashAttention` by selection (masked scores become -inf, so NaN in
+//      unread tail slots cannot leak in); steps that every row sees whole skip
+//      the mask;
+//   2. the online-softmax update of `flashAttention` in base 2, with a lazily
+//      moved reference maximum (the accumulator is rescaled only when a row's
+//      maximum outgrows it by more than kDecSlack);
+//   3. O^T [D x 16 rows] += V^T P^T with v_mfma_f32_16x16x16_bf16: V^T read
+//      with ds_read_b64_tr_b16, P^T exactly the S^T result layout. V rows past
+//      kv_len are zeroed first (0 * NaN would otherwise poison the sum).
 // fp8 e4m3fn K/V are widened to bf16 exactly with v_cvt_scalef32_pk_bf16_fp8
-// at compute time (the in-flight registers hold raw bytes); k_scale is folded
-// into the score scale and v_scale into the final normalisation.
-// The contraction over head_dim may visit d in any order as long as K and Q
-// use the same one: for fp8 a lane's 16-byte piece covers 16 consecutive d,
-// which become two 8-wide k-slots of the MFMA, and Q is loaded to match.
-// An item that is its unit's only chunk writes bf16 out and f32 lse; otherwise
+// after the LDS read (V through a small bf16 staging tile); k_scale is folded
+// into the score scale and v_scale into the final normalisation. The
+// contraction over head_dim may visit d in any order as long as K and Q use
+// the same one: a lane's 16-byte K piece covers 16 consecutive d for fp8,
+// which become two 8-wide k-slots of the MFMA, and Q is read to match.
+// An item that is its unit's only one writes bf16 out and f32 lse; otherwise
 // it writes a normalised f32 partial and its lse, which the combine kernel
 // merges once every item is done (combine_kernel below).
 #pragma once
@@ -49,54 +51,125 @@
 namespace rpa {
 
 constexpr int kDecWavesPerBlock = 4;
-
-template <int D>
-struct DecodeLds {
-  static constexpr int kVStride = D + 16;  // bf16 elements per staged V row (+32 B)
-  static constexpr int kWaveElems = kStepKeys * kVStride;
-  static constexpr size_t kBytes = (size_t)kDecWavesPerBlock * kWaveElems * 2;
-};
+constexpr int kDecStepKeys = 16;
+// The reference maximum of a row moves only when the row's maximum outgrows it
+// by more than this (base-2 units): exponentiated scores stay <= 2^12.
+constexpr float kDecSlack = 12.0f;
+// LDS budget of one decode wave (4 waves per workgroup; 40 KB: one
+// workgroup per CU)
+#ifndef RPA_DEC_WAVE_LDS
+#define RPA_DEC_WAVE_LDS (20 * 1024)
+#endif
+constexpr int kDecWaveLds = RPA_DEC_WAVE_LDS;
 
 template <int D, bool FP8>
-struct DecShape {
-  static constexpr int NI = D / 32;        // 8-wide k-slots per lane over head_dim (MFMA k-steps)
-  static constexpr int ND = D / 16;        // 16-row blocks of O^T
-  static constexpr int EB = FP8 ? 1 : 2;   // bytes per K/V element
-  static constexpr int NLD = D * EB / 64;  // 16-byte loads per lane per 16-key block, K or V
+struct DecCfg {
+  static constexpr int EB = FP8 ? 1 : 2;         // bytes per K/V element
+  static constexpr int RB = D * EB;              // bytes of one K (or V) row of a head
+  static constexpr int REGION = 16 * RB;         // the step's 16 K (or V) rows
+  static constexpr int STAGE = 2 * REGION;       // K region, then V region
+  static constexpr int NDR = REGION / 1024;      // DMA instructions per region
+  static constexpr int NDMA = 2 * NDR;           // DMA instructions per step
+  static constexpr int CPR = RB / 16;            // 16-byte chunks per row
+  static constexpr int RP = RB >= 256 ? 1 : 256 / RB;  // rows per 256 bytes (one LDS bank sweep)
+  static constexpr int NI = D / 32;              // 8-wide k-slots of Q^T per lane (16x16x32 k-steps)
+  static constexpr int ND = D / 16;              // 16-row blocks of O^T
+  static constexpr int NLD = RB / 64;            // 16-byte K pieces per lane
+  static constexpr int VST = D + 16;             // fp8: row stride (elements) of the bf16 V staging tile
+  static constexpr int STG = FP8 ? 16 * VST * 2 : 0;
+  static constexpr int QSLOT = 16 * D * 2;       // the next item's 16 Q rows (bf16)
+  static constexpr int NST_FIT = (kDecWaveLds - STG - QSLOT) / STAGE;
+  static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 8 ? 8 : NST_FIT);  // ring slots
+  static constexpr int WAVE_LDS = NST * STAGE + STG + QSLOT;
+  static_assert(REGION % 1024 == 0, "whole 1 KB DMA instructions per region");
+  static_assert(WAVE_LDS * kDecWavesPerBlock <= 160 * 1024, "LDS of a workgroup");
+  static_assert((NST - 2) * NDMA < 64, "vmcnt range");
 };
-// waves per SIMD the register budget is sized for
-constexpr int dec_waves_per_simd(int D) { return D >= 256 ? 1 : 2; }
+template <int D, bool FP8>
+constexpr int dec_wgs_per_cu() {
+  return (160 * 1024) / (DecCfg<D, FP8>::WAVE_LDS * kDecWavesPerBlock);
+}
+// resident decode waves per SIMD (sizes the register budget)
+constexpr int dec_waves_per_simd(int D, bool fp8) {
+  return fp8 ? dec_wgs_per_cu<64, true>() * 0 + (D == 64 ? dec_wgs_per_cu<64, true>()
+                                                  : D == 128 ? dec_wgs_per_cu<128, true>() : dec_wgs_per_cu<256, true>())
+             : (D == 64 ? dec_wgs_per_cu<64, false>()
+                        : D == 128 ? dec_wgs_per_cu<128, false>() : dec_wgs_per_cu<256, false>());
+}
 
-// First d of k-slot i for lane group g (K rows, Q rows and staged V rows use
-// the same map). bf16: the 16-byte piece i of lane g is d = 32 i + 8 g; fp8:
-// piece j = i / 2 of lane g covers d = 64 j + 16 g .. + 15, split in two
-// 8-wide slots.
+// Chunk swizzles of a region's rows (key = row 0..15): K pieces are read by
+// 16 lanes holding 16 keys at the same chunk; V is read transposed by 4 keys
+// x 2 chunks per 16 lanes. Both spread a read over all 64 banks.
+template <int D, bool FP8>
+__device__ __forceinline__ int dswz_k(int key) {
+  using C = DecCfg<D, FP8>;
+  return (key / C::RP) & ((C::CPR < 16 ? C::CPR : 16) - 1);
+}
+template <int D, bool FP8>
+__device__ __forceinline__ int dswz_v(int key) {
+  using C = DecCfg<D, FP8>;
+  return 2 * ((key / C::RP) & ((C::CPR < 16 ? C::CPR : 16) / 2 - 1));
+}
+
+// First d of k-slot i for lane group g (K pieces and Q use the same map).
+// bf16: the 16-byte piece i of lane g is d = 32 i + 8 g; fp8: piece j = i / 2
+// of lane g covers d = 64 j + 16 g .. + 15, split in two 8-wide slots.
 template <bool FP8>
 __device__ __forceinline__ int slot_d(int i, int g) {
   return FP8 ? 64 * (i >> 1) + 16 * g + 8 * (i & 1) : 32 * i + 8 * g;
 }
 
+// Scalar (SMEM) loads of metadata the kernel never writes: page-table entries
+// and item descriptors go to scalar registers through the scalar cache and
+// never wait on (or make anything wait on) the K/V stream.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ int sload(const int32_t* ptr) { return *(cint32*)(ptr); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                   0, 0);
+}
+
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel
 // carries no cap arithmetic at all).
 template <int D, bool FP8, bool CAP>
-__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D)) void decode_kernel(Params p) {
-  using S = DecShape<D, FP8>;
-  constexpr int NI = S::NI, ND = S::ND, EB = S::EB, NLD = S::NLD;
-  constexpr int VST = DecodeLds<D>::kVStride;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[kDecWavesPerBlock * DecodeLds<D>::kWaveElems];
+__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8)) void decode_kernel(Params p) {
+  using Cf = DecCfg<D, FP8>;
+  constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
+                NDMA = Cf::NDMA, CPR = Cf::CPR, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, VST = Cf::VST,
+                NST = Cf::NST;
+  __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * Cf::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int g = lane >> 4;
-  __bf16* vs = lds + wave * DecodeLds<D>::kWaveElems;
+  char* wl = lds + wave * Cf::WAVE_LDS;       // this wave's LDS: ring slots, then staging, then Q slot
+  char* ring = wl;
+  __bf16* stg = reinterpret_cast<__bf16*>(wl + NST * STAGE);
+  __bf16* qs = reinterpret_cast<__bf16*>(wl + NST * STAGE + Cf::STG);
+  const uint32_t ring_lds = lds_addr_of(ring);
+  const uint32_t qs_lds = lds_addr_of(qs);
 
   const int n_items = uni(p.hdr->n_dec_items);
-  const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;  // bytes between consecutive slots
+  const int key_stride = 2 * p.Hkv * D * EB;  // bytes between consecutive slots (< 2^26)
   const float cap_k = CAP ? 2.0f * kLog2e / p.soft_cap : 0.f;
   const float sc_mul = CAP ? p.sm_scale : p.sm_scale * kLog2e;  // uncapped: straight to base 2
-  // this lane's byte offset inside a 16-key block (piece 0 of K)
-  const uint32_t lane_off = (uint32_t)(col * key_stride) + 16u * g;
+
+  // per-lane DMA source offsets inside a 16-key block (loop-invariant): LDS
+  // chunk c of row `key` holds global chunk c ^ swizzle(key)
+  uint32_t voff[2][NDR];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int j = 0; j < NDR; ++j) {
+      const int o = 1024 * j + 16 * lane;
+      const int key = o / RB;
+      const int cl = (o % RB) / 16;
+      const int sw = (r == 1 && !FP8) ? dswz_v<D, FP8>(key) : dswz_k<D, FP8>(key);
+      voff[r][j] = (uint32_t)(key * key_stride + r * RB + 16 * (cl ^ sw));
+    }
 
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -104,113 +177,116 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D)) void
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- item descriptors: one load of 16 words, one word per lane ----
+  // ---- items ----
+  const int w = blockIdx.x * kDecWavesPerBlock + wave;  // stream-K rank
   struct Info {
-    int idx, s, h, c_lo, c_hi, kvl, q0, ql, row0, nrows, nch;
+    int idx, s, h, c_lo, c_hi, kvl, q0, ql, row0, nrows, nch, wave;
   };
-  auto load_desc = [&](int idx) -> int {
-    return lane < 16 ? reinterpret_cast<const int32_t*>(p.dec_items + idx)[lane] : 0;
-  };
-  auto unpack = [&](int idx, int dv) {
+  auto load_info = [&](int idx) {
     Info I;
     I.idx = idx;
-    I.s = __builtin_amdgcn_readlane(dv, 0);
-    I.h = __builtin_amdgcn_readlane(dv, 1);
-    I.c_lo = __builtin_amdgcn_readlane(dv, 2);
-    I.c_hi = max(__builtin_amdgcn_readlane(dv, 3), I.c_lo);
-    I.kvl = __builtin_amdgcn_readlane(dv, 4);
-    I.q0 = __builtin_amdgcn_readlane(dv, 5);
-    I.ql = __builtin_amdgcn_readlane(dv, 6);
-    I.row0 = __builtin_amdgcn_readlane(dv, 7);
-    I.nrows = __builtin_amdgcn_readlane(dv, 8);
-    I.nch = __builtin_amdgcn_readlane(dv, 9);
+    if (idx >= n_items) {
+      I.wave = -1;
+      return I;
+    }
+    const int32_t* d = reinterpret_cast<const int32_t*>(p.dec_items + idx);
+    I.s = sload(d + 0);
+    I.h = sload(d + 1);
+    I.c_lo = sload(d + 2);
+    I.c_hi = max(sload(d + 3), I.c_lo);
+    I.kvl = sload(d + 4);
+    I.q0 = sload(d + 5);
+    I.ql = sload(d + 6);
+    I.row0 = sload(d + 7);
+    I.nrows = sload(d + 8);
+    I.nch = sload(d + 9);
+    I.wave = sload(d + 12);
     return I;
   };
-  // the item's physical pages: lane l of window w holds logical page
-  // c_lo / page + 64 w + l, clamped to the item's last page (entries past it
-  // are never read)
-  auto load_window = [&](const Info& I, int (&win)[2]) {
-    const int lp0 = I.c_lo / p.page;
-    const int lp_last = max(I.c_hi - 1, I.c_lo) / p.page;
-    const int32_t* ptab = p.page_indices + (int64_t)I.s * p.pps;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) win[w] = ptab[min(min(lp0 + 64 * w + lane, lp_last), p.pps - 1)];
-  };
-  auto load_q = [&](const Info& I, bf16x8 (&qb)[NI]) {
-    const int prow = I.row0 + col;
-    const int t = prow / p.G;
-    const int qh = I.h * p.G + (prow - t * p.G);
-    if (col < I.nrows) {
-      const uint16_t* qp = p.q + ((int64_t)(I.q0 + t) * p.Hq + qh) * D;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) qb[i] = *reinterpret_cast<const bf16x8*>(qp + slot_d<FP8>(i, g));
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) qb[i] = bf16x8{};
-    }
-  };
-
-  // 32-key steps of an item; an empty key range (only outside the data
+  auto mine = [&](const Info& I) { return I.wave == w; };
+  // 16-key steps of an item; an empty key range (only outside the data
   // preconditions) still takes one fully masked step, so that the load and
   // compute sides always agree on the step count
-  auto item_steps = [](const Info& I) { return max(1, (I.c_hi - I.c_lo + kStepKeys - 1) / kStepKeys); };
+  auto item_steps = [](const Info& I) { return max(1, (I.c_hi - I.c_lo + kDecStepKeys - 1) / kDecStepKeys); };
+
+  // Q rows of an item, 16 x D bf16, straight into the wave's Q slot (row r =
+  // packed row row0 + r; rows past nrows re-read row 0 and are ignored).
+  auto dma_q = [&](const Info& I) {
+    constexpr int QROW = 2 * D, QRPI = 1024 / QROW, QNI = 16 / QRPI;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
+#pragma unroll
+    for (int j = 0; j < QNI; ++j) {
+      const int r = QRPI * j + (lane * 16) / QROW;
+      const int prow = I.row0 + (r < I.nrows ? r : 0);
+      const int t = prow / p.G;
+      const int qh = I.h * p.G + (prow - t * p.G);
+      const uint8_t* src =
+          reinterpret_cast<const uint8_t*>(p.q + ((int64_t)(I.q0 + t) * p.Hq + qh) * D) + (lane * 16) % QROW;
+      dma16(src, qs_lds + 1024u * j);
+    }
+  };
+  // Q^T operand from the Q slot: lane (row col, group g) takes k-slot i
+  auto read_q = [&](const Info& I, bf16x8 (&qb)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qs + col * D + slot_d<FP8>(i, g));
+      qb[i] = col < I.nrows ? v : bf16x8{};
+    }
+  };
 
   // ---- loader: the item whose steps are being loaded ----
   struct Loader {
-    int h, c_hi, lp0, lp, sl, key, left;  // left: steps not yet loaded
+    Info I;
+    int hoff;   // byte offset of combined head 2h in a slot
+    int lp, sl, key;  // next block: logical page, slot in the page, first key
+    int left;   // steps not yet loaded
+    int pg;     // physical page of the next block (scalar-loaded ahead)
+  };
+  auto page_id = [&](const Info& I, int lp) {
+    return sload(p.page_indices + (int64_t)I.s * p.pps + min(lp, p.pps - 1));
   };
   auto loader_for = [&](const Info& I) {
     Loader L;
-    L.h = I.h;
-    L.c_hi = I.c_hi;
-    L.lp0 = I.c_lo / p.page;
-    L.lp = L.lp0;
-    L.sl = I.c_lo - L.lp0 * p.page;
+    L.I = I;
+    L.hoff = 2 * I.h * D * EB;
+    L.lp = I.c_lo / p.page;
+    L.sl = I.c_lo - L.lp * p.page;
     L.key = I.c_lo;
     L.left = item_steps(I);
+    L.pg = page_id(I, L.lp);
     return L;
   };
-  struct Stage {
-    u32x4 k[2][NLD];
-    u32x4 v[2][NLD];
-  };
-  // Loads the next step of L (or, with nothing left, re-reads its last block:
-  // harmless, never computed).
-  auto load_step = [&](Loader& L, const int (&win)[2], Stage& st) {
-    const bool real = L.left > 0;
+  // Issues the DMA of L's next step into ring slot `slot`, then moves L on.
+  auto issue_step = [&](Loader& L, int slot) {
+    const int phys = min(max(L.pg, 0), p.P - 1);
+    const uint8_t* base = uniform_ptr(p.kv + ((int64_t)phys * p.page + L.sl) * key_stride + L.hoff);
+    const uint32_t dst = (uint32_t)uni((int)(ring_lds + (uint32_t)(slot * STAGE)));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int rel = min(L.lp - L.lp0, kDecPageWindow - 1);
-      int phys = rel < 64 ? __builtin_amdgcn_readlane(win[0], rel) : __builtin_amdgcn_readlane(win[1], rel - 64);
-      phys = min(max(phys, 0), p.P - 1);
-      const uint8_t* base = p.kv + uni64(((int64_t)phys * p.page + L.sl) * key_stride + (int64_t)2 * L.h * D * EB);
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        st.k[b][j] = *reinterpret_cast<const u32x4*>(base + lane_off + 64 * j);
-        st.v[b][j] = *reinterpret_cast<const u32x4*>(base + lane_off + D * EB + 64 * j);
-      }
-      // advance to the next 16-key block if it is still inside the item
-      if (real && L.key + 16 < L.c_hi) {
-        L.key += 16;
-        L.sl += 16;
-        if (L.sl >= p.page) {
-          L.sl = 0;
-          ++L.lp;
-        }
+      for (int j = 0; j < NDR; ++j) dma16_sbase(base, voff[r][j], dst + r * REGION + 1024 * j);
+    --L.left;
+    if (L.left > 0) {
+      L.key += kDecStepKeys;
+      L.sl += kDecStepKeys;
+      if (L.sl >= p.page) {
+        L.sl = 0;
+        ++L.lp;
+        L.pg = page_id(L.I, L.lp);
       }
     }
-    if (real) --L.left;
   };
+
   // ---- compute state of the current item ----
   Info C;
   bf16x8 qb[NI];
-  float m, lsum;
+  float m_ref, lsum;
   f32x4 o[ND];
   int steps_done, n_steps;
   bool rvalid;
   int tok, qh, pos, pos_lo, pos_hi, vis_hi;
   auto begin_item = [&]() {
-    m = -INFINITY;
+    m_ref = -INFINITY;
     lsum = 0.f;
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,120 +304,122 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D)) void
     vis_hi = min(C.c_hi, C.kvl);
   };
 
-  // One 32-key block: keys [kb, kb + 32).
-  auto compute_block = [&](const Stage& st, int kb) {
-    bf16x8 ka[2][NI];
+  // One 16-key step: keys [kb, kb + 16) in ring slot `slot`.
+  auto compute_step = [&](int slot, int kb) {
+    const char* kr = ring + slot * STAGE;
+    const char* vr = kr + REGION;
+    // K operand: lane (key col, group g) reads its pieces (swizzled chunks)
+    bf16x8 ka[NI];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        if constexpr (FP8) {
-          ka[b][2 * j] = fp8x8_to_bf16(u32x2{st.k[b][j][0], st.k[b][j][1]});
-          ka[b][2 * j + 1] = fp8x8_to_bf16(u32x2{st.k[b][j][2], st.k[b][j][3]});
-        } else {
-          ka[b][j] = __builtin_bit_cast(bf16x8, st.k[b][j]);
-        }
+    for (int j = 0; j < NLD; ++j) {
+      const int chunk = 4 * j + g;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * (chunk ^ dswz_k<D, FP8>(col)));
+      if constexpr (FP8) {
+        ka[2 * j] = fp8x8_to_bf16(u32x2{v[0], v[1]});
+        ka[2 * j + 1] = fp8x8_to_bf16(u32x2{v[2], v[3]});
+      } else {
+        ka[j] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    // S^T: lane (col, g) gets keys kb + 16b + 4g + j of row `col`.
-    f32x4 sc[2];
+    // S^T: lane (col, g) gets keys kb + 4g + j of row `col`
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sc[b] = mfma16x16x32(ka[b][i], qb[i], sc[b]);
-    }
-    // does the block hold a key that some row of the unit cannot see?
-    const bool need_mask = kb + 32 > vis_hi || (p.is_causal && kb + 31 > pos_lo) ||
+    for (int i = 0; i < NI; ++i) sc = mfma16x16x32(ka[i], qb[i], sc);
+    // does the step hold a key that some row of the unit cannot see?
+    const bool need_mask = kb + 16 > vis_hi || (p.is_causal && kb + 15 > pos_lo) ||
                            (p.window > 0 && kb <= pos_hi - p.window);
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = sc[b][j] * sc_mul;
-        if constexpr (CAP) x = soft_cap_f(x, p.soft_cap, cap_k) * kLog2e;
-        if (need_mask) {
-          const int key = kb + 16 * b + 4 * g + j;
-          bool vis = key < vis_hi;
-          if (p.is_causal) vis = vis && key <= pos;
-          if (p.window > 0) vis = vis && key > pos - p.window;
-          x = vis ? x : -INFINITY;
-        }
-        sc[b][j] = x;
-        mx = fmaxf(mx, x);
+    for (int j = 0; j < 4; ++j) {
+      float x = sc[j] * sc_mul;
+      if constexpr (CAP) x = soft_cap_f(x, p.soft_cap, cap_k) * kLog2e;
+      if (need_mask) {
+        const int key = kb + 4 * g + j;
+        bool vis = key < vis_hi;
+        if (p.is_causal) vis = vis && key <= pos;
+        if (p.window > 0) vis = vis && key > pos - p.window;
+        x = vis ? x : -INFINITY;
       }
+      sc[j] = x;
+      mx = fmaxf(mx, x);
     }
     mx = wave_max_xor16_32(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-    lsum *= alpha;
+    // lazily moved reference maximum
+    if (__any(mx > m_ref + kDecSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      lsum *= alpha;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
-    float pv[2][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[b][j] = fast_exp2(sc[b][j] - m_use);
-        lsum += pv[b][j];
-      }
-
-    // Stage V rows [kb, kb + 32) in LDS as bf16, zero past kv_len / the chunk.
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const bool vok = kb + 16 * b + col < vis_hi;
-      __bf16* vrow_w = vs + (16 * b + col) * VST;
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        if constexpr (FP8) {
-          bf16x8 lo = fp8x8_to_bf16(u32x2{st.v[b][j][0], st.v[b][j][1]});
-          bf16x8 hi = fp8x8_to_bf16(u32x2{st.v[b][j][2], st.v[b][j][3]});
-          if (!vok) {
-            lo = bf16x8{};
-            hi = bf16x8{};
-          }
-          *reinterpret_cast<bf16x8*>(vrow_w + slot_d<FP8>(2 * j, g)) = lo;
-          *reinterpret_cast<bf16x8*>(vrow_w + slot_d<FP8>(2 * j + 1, g)) = hi;
-        } else {
-          const u32x4 v = vok ? st.v[b][j] : u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(vrow_w + slot_d<FP8>(j, g)) = v;
-        }
-      }
+      for (int d = 0; d < ND; ++d) o[d] *= alpha;
     }
-    wave_sync();
-
-    bf16x8 pb;
+    const float negm = m_ref == -INFINITY ? 0.f : -m_ref;
+    bf16x4 pb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pb[j] = (__bf16)pv[0][j];
-      pb[4 + j] = (__bf16)pv[1][j];
+      const float pj = fast_exp2(sc[j] + negm);
+      lsum += pj;
+      pb[j] = (__bf16)pj;
     }
-    const __bf16* vrow = vs + (4 * g + (col >> 2)) * VST + 4 * (col & 3);
+
+    // V^T operand: lane x of group g reads V[4g + x/4][16 d + 4 (x%4) .. + 3]
+    const int vkey = 4 * g + (col >> 2);
+    const int q4 = col & 3;
+    if constexpr (FP8) {
+      // widen V to bf16 through the staging tile; rows past kv_len become 0
+      const bool vok = kb + col < vis_hi;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const bf16x4 lo = lds_read_tr16(vrow + 16 * d);
-      const bf16x4 hi = lds_read_tr16(vrow + 16 * VST + 16 * d);
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[d] = mfma16x16x32(a, pb, o[d]);
+      for (int j = 0; j < NLD; ++j) {
+        const int chunk = 4 * j + g;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(vr + col * RB + 16 * (chunk ^ dswz_k<D, FP8>(col)));
+        bf16x8 lo = fp8x8_to_bf16(u32x2{v[0], v[1]});
+        bf16x8 hi = fp8x8_to_bf16(u32x2{v[2], v[3]});
+        if (!vok) {
+          lo = bf16x8{};
+          hi = bf16x8{};
+        }
+        *reinterpret_cast<bf16x8*>(stg + col * VST + slot_d<FP8>(2 * j, g)) = lo;
+        *reinterpret_cast<bf16x8*>(stg + col * VST + slot_d<FP8>(2 * j + 1, g)) = hi;
+      }
+      wave_sync();
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const bf16x4 a = lds_read_tr16(stg + vkey * VST + 16 * d + 4 * q4);
+        o[d] = mfma16x16x16(a, pb, o[d]);
+      }
+      wave_sync();
+    } else {
+      if (kb + 16 > vis_hi) {
+        // zero the V rows of keys at or past vis_hi (their chunks in any order)
+        char* vw = const_cast<char*>(vr);
+        for (int e = lane; e < 16 * CPR; e += 64) {
+          const int key = e / CPR;
+          if (kb + key >= vis_hi) *reinterpret_cast<u32x4*>(vw + key * RB + 16 * (e % CPR)) = u32x4{0u, 0u, 0u, 0u};
+        }
+        wave_sync();
+      }
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const int chunk = 2 * d + (q4 >> 1);
+        const bf16x4 a = lds_read_tr16(
+            reinterpret_cast<const __bf16*>(vr + vkey * RB + 16 * (chunk ^ dswz_v<D, FP8>(vkey)) + 8 * (q4 & 1)));
+        o[d] = mfma16x16x16(a, pb, o[d]);
+      }
     }
-    wave_sync();
   };
 
   // Result of the current item: bf16 out + lse, or an f32 partial + lse.
   auto finish_item = [&]() {
     const float l_row = wave_sum_xor16_32(lsum);
     const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
-    const float lse_v = l_row > 0.f ? (m + fast_log2(l_row)) * kLn2 : -INFINITY;
+    const float lse_v = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
     if (!rvalid) return;
     if (C.nch == 1) {
       uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        u32x2 w = {bf16x2_bits(o[d][0] * inv, o[d][1] * inv), bf16x2_bits(o[d][2] * inv, o[d][3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = w;
+        u32x2 v = {bf16x2_bits(o[d][0] * inv, o[d][1] * inv), bf16x2_bits(o[d][2] * inv, o[d][3] * inv)};
+        *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = v;
       }
       if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
     } else {
@@ -352,90 +430,84 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D)) void
     }
   };
 
-  // ---- the next item, prepared one dependent load per step ----
-  // nstate: 0 slot claimed (claim_v in flight), 1 descriptor in flight,
-  // 2 window and Q in flight / ready, 3 the queue is empty
-  const int first_dynamic = gridDim.x * kDecWavesPerBlock;
-  int nstate = 3, claim_v = 0, ndv = 0;
-  Info N;
-  N.idx = -1;
-  int nwin[2] = {0, 0};
-  bf16x8 nq[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) nq[i] = bf16x8{};
-  auto claim = [&]() {
-    claim_v = 0;
-    if (lane == 0) claim_v = atomicAdd(&p.hdr->dec_counter, 1);
-    nstate = 0;
-  };
-  auto hop = [&]() {
-    if (nstate == 0) {
-      const int idx = first_dynamic + __builtin_amdgcn_readfirstlane(__shfl(claim_v, 0));
-      if (idx < n_items) {
-        N.idx = idx;
-        ndv = load_desc(idx);
-        nstate = 1;
-      } else {
-        nstate = 3;
-      }
-    } else if (nstate == 1) {
-      N = unpack(N.idx, ndv);
-      load_window(N, nwin);
-      load_q(N, nq);
-      nstate = 2;
+  // ---- the wave's items, one continuous pipeline ----
+  const int first = sload(p.dec_wave_first + min(w, p.dec_waves - 1));
+  if (w >= p.dec_waves || first >= n_items) return;
+  C = load_info(first);
+  if (!mine(C)) return;
+  Info Cn = load_info(first + 1);  // the compute side's next item
+  dma_q(C);
+  wait_vmcnt<0>();
+  wave_sync();
+  read_q(C, qb);
+  if (mine(Cn)) dma_q(Cn);
+  int q_age = 0;  // steps computed since the Q slot's DMA was issued
+  begin_item();
+
+  Loader L = loader_for(C);
+  Info Ln = Cn;          // the load side's next item
+  bool loading = true;   // the load side still has steps to issue
+  // Moves the load side to its next step: the same item, or the next of the wave.
+  auto loader_next = [&]() {
+    if (L.left > 0) return;
+    if (mine(Ln)) {
+      L = loader_for(Ln);
+      Ln = load_info(Ln.idx + 1);
+    } else {
+      loading = false;
     }
   };
 
-  // ---- first item (fixed by grid position) ----
-  {
-    const int first = blockIdx.x * kDecWavesPerBlock + wave;
-    if (first >= n_items) return;
-    C = unpack(first, load_desc(first));
+  // prologue: NST - 1 steps in flight
+  int ahead = 0;  // steps issued beyond the one being computed
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k) {
+    if (loading) {
+      issue_step(L, k);
+      ++ahead;
+      loader_next();
+    }
   }
-  int lwin[2];
-  load_window(C, lwin);
-  load_q(C, qb);
-  Loader L = loader_for(C);
-  bool loader_on_next = false;
-  claim();
-  begin_item();
-
-  Stage st[2];
-  load_step(L, lwin, st[0]);
-  for (;;) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      // load side: the step after the one computed below
-      if (L.left == 0 && !loader_on_next) {
-        while (nstate < 2) hop();  // only for items shorter than the chain
-        if (nstate == 2) {
-          L = loader_for(N);
-          lwin[0] = nwin[0];
-          lwin[1] = nwin[1];
-          loader_on_next = true;
-        }
+  --ahead;  // the first issued step is the one computed first
+  for (int n = 0;; ++n) {
+    // this step's rows are in LDS once at most `ahead` later steps are in flight
+    if (ahead == NST - 2) {
+      wait_vmcnt<(NST - 2) * NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // refill: the slot computed last step is free
+    if (loading) {
+      issue_step(L, (n + NST - 1) % NST);
+      ++ahead;
+      loader_next();
+    }
+    compute_step(n % NST, C.c_lo + steps_done * kDecStepKeys);
+    ++steps_done;
+    ++q_age;
+    --ahead;
+    if (steps_done == n_steps) {
+      finish_item();
+      if (!mine(Cn)) return;  // the wave's range is done
+      C = Cn;
+      Cn = load_info(C.idx + 1);
+      // the Q slot's DMA is complete once a wait above covered a step issued
+      // after it (NST steps later); for short items wait for it here
+      if (q_age < NST) wait_vmcnt<0>();
+      wave_sync();
+      read_q(C, qb);
+      if (mine(Cn)) {
+        dma_q(Cn);
+        q_age = 0;
       }
-      load_step(L, lwin, st[k ^ 1]);
-      // compute side
-      compute_block(st[k], C.c_lo + steps_done * kStepKeys);
-      ++steps_done;
-      hop();
-      if (steps_done == n_steps) {
-        finish_item();
-        if (!loader_on_next) return;  // the queue is empty
-        C = N;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) qb[i] = nq[i];
-        loader_on_next = false;
-        claim();
-        begin_item();
-      }
+      begin_item();
     }
   }
 }
 
 // Merges the split decode-class units once every decode item is done: one
-// wave per unit, the chunks' partials combined by merge_unit.
+// wave per unit, the items' partials combined by merge_unit; a unit with no
+// key to see (and so no item) gets out = 0 and lse = -inf.
 template <int D>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params p) {
   __shared__ float stat[kDecWavesPerBlock][2 * kDecRows];
@@ -457,7 +529,20 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
     U.kv_hi = uni(p.dec_units[u].kv_hi);
     U.nch = uni(p.dec_units[u].nch);
     U.item0 = uni(p.dec_units[u].item0);
-    if (U.nch <= 1) continue;
+    if (U.nch == 1) continue;  // its item wrote the rows
+    if (U.nch == 0) {
+      // no visible key (only outside the data preconditions): out 0, lse -inf
+      int q0, ql;
+      seq_tokens(p, U.seq, q0, ql);
+      for (int e = lane; e < U.nrows * (D / 4); e += 64) {
+        const int prow = U.row0 + e / (D / 4);
+        const int t = prow / p.G;
+        const int qh = U.kv_head * p.G + (prow - t * p.G);
+        *reinterpret_cast<u32x2*>(p.out + ((int64_t)(q0 + t) * p.Hq + qh) * D + 4 * (e % (D / 4))) = u32x2{0u, 0u};
+        if (p.lse && e % (D / 4) == 0) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = -INFINITY;
+      }
+      continue;
+    }
     merge_unit<D>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
     wave_sync();
   }

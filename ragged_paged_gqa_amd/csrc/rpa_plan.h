@@ -37,7 +37,6 @@ namespace rpa {
 
 constexpr int kPlanThreads = 512;  // 1024 would cap a wave at 128 VGPRs and spill
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kDecMinChunk = 256;
 constexpr int kPfMinChunk = 512;
 
 // a / d for 0 <= a < 2^31, d > 0: the double product is within 1e-6 of the
@@ -171,11 +170,59 @@ struct PfOffs {
   int32_t queue[kQueues];
 };
 
+// A decode sequence of a tile and its record offsets, for the wave that
+// writes its units and items.
+struct DecInfo {
+  int32_t s, unit0, item0, blk0, nb, rows, lo16, hi, kvl, q0, ql;
+};
+
+// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31: the double quotient is within
+// one of the true one, which the remainder fixes.
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  const int64_t r = a - q * b;
+  if (r < 0) --q;
+  else if (r >= b) ++q;
+  return q;
+}
+
+// Stream-K split of the decode work: the Tb key blocks of all decode units,
+// laid end to end (unit (s, h) at blocks [blk0_s + h * nb_s, + nb_s)), are cut
+// into W contiguous ranges, W <= Tb so that none is empty; wave w runs blocks
+// [start(w), start(w + 1)). A unit with no key block gets no item (the combine
+// kernel writes its rows).
+// Range starts of up to this many decode waves are tabulated in LDS.
+constexpr int kPlanMaxDecWaves = 4096;
+
+struct StreamK {
+  int64_t Tb;
+  int32_t W;
+  const int32_t* table;  // start(w) for w <= W when W <= kPlanMaxDecWaves, else null
+  __device__ int32_t start_exact(int32_t w) const { return (int32_t)floor_div(Tb * w, W); }
+  __device__ int32_t start(int32_t w) const { return table ? table[w] : start_exact(w); }
+  // the wave whose range holds block x (0 <= x < Tb)
+  __device__ int32_t wave_of(int32_t x) const {
+    const int64_t w = floor_div((int64_t)(x + 1) * W - 1, Tb);
+    return (int32_t)(w < W - 1 ? w : W - 1);
+  }
+  // items of unit blocks [b0, b0 + nb): one per wave from wa to wb
+  __device__ int32_t n_items(int32_t b0, int32_t nb, int32_t& wa) const {
+    if (nb <= 0 || Tb <= 0) {
+      wa = 0;
+      return 0;
+    }
+    wa = wave_of(b0);
+    return wave_of(b0 + nb - 1) - wa + 1;
+  }
+};
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ int64_t red[2][kPlanWaves];
   __shared__ int32_t sh[kPlanWaves * kScanN];
-  __shared__ int32_t n_pf_tile;
+  __shared__ int32_t n_pf_tile, n_dec_tile;
   __shared__ PfInfo pf_info[kPlanThreads];
+  __shared__ DecInfo dec_info[kPlanThreads];
+  __shared__ int32_t sk_start[kPlanMaxDecWaves + 1];
   __shared__ PfOffs pf_offs[kPlanThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t n = *p.num_seqs;
@@ -202,7 +249,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     int32_t ql = 0, kvl = 0, slot;
     if (s < n) seq_meta(p, s, ql, kvl);
     if (s < n && ql > 0 && ql * p.G <= kDecRows)
-      dec_keys += (int64_t)p.Hkv * range_keys(unit_range(p, G, ql, kvl, 0, ql * p.G));
+      dec_keys += (int64_t)p.Hkv * ((range_keys(unit_range(p, G, ql, kvl, 0, ql * p.G)) + 15) / 16);
     collect(s, ql, slot);
     __syncthreads();
     for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
@@ -230,15 +277,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     tot_dec += red[0][w];
     tot_pf += red[1][w];
   }
-  const FastDiv dec_chunk = make_div(pick_chunk(tot_dec, p.target_dec_items, kDecMinChunk, dec_max_chunk(p.page)));
+  // tot_dec counts 16-key blocks of decode units; with fewer blocks than
+  // waves only the first tot_dec waves get work, so every used wave's range
+  // holds at least one block
+  const int32_t n_dec_waves = (int32_t)max((int64_t)1, min((int64_t)max(p.dec_waves, 1), tot_dec));
+  const bool tabulate = n_dec_waves <= kPlanMaxDecWaves;
+  const StreamK sk{tot_dec, n_dec_waves, tabulate ? sk_start : nullptr};
+  if (tabulate)
+    for (int32_t w = tid; w <= n_dec_waves; w += kPlanThreads) sk_start[w] = sk.start_exact(w);
+  for (int32_t w = tid; w < max(p.dec_waves, 1); w += kPlanThreads) p.dec_wave_first[w] = INT32_MAX;
   const FastDiv pf_chunk = make_div(pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk));
 
   // pass 2: per-sequence counts -> one scan per tile -> records
   int32_t base[kScanN];
 #pragma unroll
   for (int k = 0; k < kScanN; ++k) base[k] = 0;
+  int32_t base_blk = 0;  // decode blocks of the earlier tiles
   for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
-    if (tid == 0) n_pf_tile = 0;
+    if (tid == 0) {
+      n_pf_tile = 0;
+      n_dec_tile = 0;
+    }
     __syncthreads();
     const int32_t s = s0 + tid;
     int32_t ql = 0, kvl = 0, slot;
@@ -272,13 +331,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     int32_t cnt[kScanN];
 #pragma unroll
     for (int k = 0; k < kScanN; ++k) cnt[k] = 0;
-    int32_t nch_dec = 0;
     const bool is_dec = s < n && ql > 0 && ql * p.G <= kDecRows;
+    // decode: the sequence's block offset in the stream-K order first
+    int32_t nb = 0;
+    if (is_dec) nb = (range_keys(unit_range(p, G, ql, kvl, 0, ql * p.G)) + 15) / 16;
+    int32_t blk0;
+    {
+      const int32_t v[1] = {p.Hkv * nb};
+      int32_t e[1], t[1];
+      block_scan<1>(v, e, t, sh);
+      blk0 = base_blk + e[0];
+      base_blk += t[0];
+    }
     if (is_dec) {
-      nch_dec = n_chunks(unit_range(p, G, ql, kvl, 0, ql * p.G), dec_chunk);
+      int32_t items = 0, nsplit = 0;
+      for (int32_t h = 0; h < p.Hkv; ++h) {
+        int32_t wa;
+        const int32_t ni = sk.n_items(blk0 + h * nb, nb, wa);
+        items += ni;
+        nsplit += ni > 1;
+      }
       cnt[0] = p.Hkv;
-      cnt[2] = p.Hkv * nch_dec;
-      cnt[4] = nch_dec > 1 ? p.Hkv : 0;
+      cnt[2] = items;
+      cnt[4] = nsplit;
     } else if (slot >= 0) {
       const PfInfo& f = pf_info[slot];
       const int32_t nrb = (ql * p.G + R - 1) / R;
@@ -298,36 +373,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
 #pragma unroll
     for (int k = 0; k < kScanN; ++k) base[k] += tot[k];
 
-    if (is_dec) {  // decode records, by the sequence's thread
-      const int32_t rows = ql * p.G;
-      const UnitRange r = unit_range(p, G, ql, kvl, 0, rows);
+    if (is_dec) {  // listed for the wave that writes its records
+      const UnitRange r = unit_range(p, G, ql, kvl, 0, ql * p.G);
       int32_t q0, qlx;
       seq_tokens(p, s, q0, qlx);
-      const int64_t keys = range_keys(r);
-      for (int32_t h = 0; h < p.Hkv; ++h) {
-        const int32_t ui = off[0] + h;
-        if (ui >= p.max_dec_units) break;
-        Unit u;
-        u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = rows;
-        u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch_dec; u.item0 = off[2] + h * nch_dec;
-        p.dec_units[ui] = u;
-        p.unit_done[ui] = 0;
-        // chunk c covers [b(c), b(c + 1)): b(c) = lo + c * keys / nch rounded
-        // down to 16, b(nch) = hi; every chunk is at most dec_chunk keys and,
-        // when the unit splits, at least half of that
-        for (int32_t c = 0; c < nch_dec; ++c) {
-          const int32_t ii = u.item0 + c;
-          if (ii >= p.max_dec_items) break;
-          DecItem d;
-          d.seq = s; d.kv_head = h;
-          d.c_lo = r.lo16 + (int32_t)(((int64_t)c * keys / nch_dec) & ~(int64_t)15);
-          d.c_hi = c + 1 == nch_dec ? max(r.hi, r.lo16) : r.lo16 + (int32_t)(((int64_t)(c + 1) * keys / nch_dec) & ~(int64_t)15);
-          d.kvl = kvl; d.q0 = q0; d.ql = ql; d.row0 = 0; d.nrows = rows;
-          d.nch = nch_dec; d.unit = ui; d.chunk = c;
-          d.pad[0] = d.pad[1] = d.pad[2] = d.pad[3] = 0;
-          p.dec_items[ii] = d;
-        }
-      }
+      const int32_t i = atomicAdd(&n_dec_tile, 1);
+      dec_info[i] = DecInfo{s, off[0], off[2], blk0, nb, ql * p.G, r.lo16, r.hi, kvl, q0, ql};
     } else if (slot >= 0) {
       pf_offs[slot].unit = off[1];
       pf_offs[slot].item = off[3];
@@ -336,7 +387,50 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     }
     __syncthreads();
 
-    // (c) a wave per prefill sequence: its units, items and queue entries
+    // (c) a wave per decode sequence: a lane per kv head writes the head's
+    // unit and its items (one per wave its blocks fall on)
+    for (int32_t i = wave; i < n_dec_tile; i += kPlanWaves) {
+      const DecInfo f = dec_info[i];
+      int32_t carry = f.item0;
+      for (int32_t h0 = 0; h0 < p.Hkv; h0 += 64) {
+        const int32_t h = h0 + lane;
+        const int32_t b0 = f.blk0 + h * f.nb;
+        int32_t wa = 0, nch = 0;
+        if (h < p.Hkv) nch = sk.n_items(b0, f.nb, wa);
+        const int32_t incl = wave_incl_scan(nch);
+        const int32_t item0 = carry + incl - nch;
+        carry += __shfl(incl, 63);
+        const int32_t ui = f.unit0 + h;
+        if (h >= p.Hkv || ui >= p.max_dec_units) continue;
+        Unit u;
+        u.seq = f.s; u.kv_head = h; u.row0 = 0; u.nrows = f.rows;
+        u.kv_lo = f.lo16; u.kv_hi = f.hi; u.nch = nch; u.item0 = item0;
+        p.dec_units[ui] = u;
+        p.unit_done[ui] = 0;
+        int32_t ws = nch > 0 ? sk.start(wa) : 0;
+        for (int32_t c = 0; c < nch; ++c) {
+          const int32_t ii = item0 + c;
+          const int32_t w = wa + c;
+          if (ii >= p.max_dec_items) break;
+          // the unit's blocks inside wave w's range
+          const int32_t we = w + 1 < sk.W ? sk.start(w + 1) : (int32_t)sk.Tb;
+          const int32_t x0 = max(b0, ws);
+          const int32_t x1 = min(b0 + f.nb, we);
+          DecItem d;
+          d.seq = f.s; d.kv_head = h;
+          d.c_lo = f.lo16 + 16 * (x0 - b0);
+          d.c_hi = min(f.hi, f.lo16 + 16 * (x1 - b0));
+          d.kvl = f.kvl; d.q0 = f.q0; d.ql = f.ql; d.row0 = 0; d.nrows = f.rows;
+          d.nch = nch; d.unit = ui; d.chunk = c; d.wave = w;
+          d.pad[0] = d.pad[1] = d.pad[2] = 0;
+          p.dec_items[ii] = d;
+          // the item holding a wave's first block starts the wave's items
+          if (b0 <= ws) p.dec_wave_first[w] = ii;
+          ws = we;
+        }
+      }
+    }
+    // (d) a wave per prefill sequence: its units, items and queue entries
     for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
       const PfInfo f = pf_info[i];
       const int32_t ps = f.s;
@@ -418,10 +512,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     h.n_pf_units = min(base[1], p.max_pf_units);
     h.n_dec_items = min(base[2], p.max_dec_items);
     h.n_pf_items = min(base[3], p.max_pf_items);
-    h.dec_chunk = dec_chunk.d;
+    h.dec_chunk = 0;
     h.pf_chunk = pf_chunk.d;
     h.n_split_units = base[4];
-    h.dec_counter = 0;
+    h.dec_blocks = (int32_t)min(tot_dec, (int64_t)INT32_MAX);
+    h.pad0[0] = n_dec_waves;
     for (int x = 0; x < kQueues; ++x) {
       h.pf_q_base[x] = x * p.max_pf_items;
       h.pf_q_count[x] = max(0, min(base[5 + x], p.max_pf_items));

@@ -100,22 +100,6 @@ __device__ __forceinline__ int swz_v(int key) {
   return (4 * (key & 3)) & (C - 1);
 }
 
-// Same, with the global address split into a wave-uniform 64-bit base (SGPR
-// pair) and a per-lane 32-bit byte offset: no per-lane 64-bit address math.
-__device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
-      : "memory");
-}
-
 // Value of lane l ^ 32 (v_permlane32_swap; no LDS round trip).
 __device__ __forceinline__ float other_half(float v) {
   const uint32_t b = __builtin_bit_cast(uint32_t, v);

@@ -35,8 +35,33 @@ def _plan(w):
     pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
     qbase, qcount, qnext = hdr[16:24].copy(), hdr[24:32].copy(), hdr[32:40].copy()
     ql = host[offs[5]:offs[5] + 4 * 8 * int(lim[3])].view(np.int32)
+    W = int(lim[6])
+    wfirst = host[offs[6]:offs[6] + 4 * W].view(np.int32)
     return dict(du=du, pu=pu, di=di, pi=pi, dch=dch, pch=pch, lim=lim, qbase=qbase, qcount=qcount,
-                qnext=qnext, qlist=ql)
+                qnext=qnext, qlist=ql, W=W, wfirst=wfirst, dec_blocks=int(hdr[7]), W_used=int(hdr[8]))
+
+
+def _check_stream_k(P):
+    """Decode items run in stream-K order: the units' 16-key blocks laid end
+    to end are split into W equal contiguous ranges; each wave's items are
+    consecutive, cover exactly its range and start at wfirst[wave]."""
+    di, W, Tb, Wu = P["di"], P["W"], P["dec_blocks"], P["W_used"]
+    assert Wu == max(1, min(W, Tb))
+    waves = di[:, 12]
+    assert np.all(np.diff(waves) >= 0)
+    assert np.all((waves >= 0) & (waves < Wu))
+    blocks = np.zeros(Wu, np.int64)
+    for d in di:
+        blocks[d[12]] += -(-(int(d[3]) - int(d[2])) // 16)
+    starts = (Tb * np.arange(Wu + 1, dtype=np.int64)) // Wu
+    assert np.array_equal(blocks, np.diff(starts))
+    for w in range(W):
+        idx = np.nonzero(waves == w)[0]
+        if len(idx) == 0:
+            assert P["wfirst"][w] == np.iinfo(np.int32).max
+        else:
+            assert P["wfirst"][w] == idx[0]
+            assert np.array_equal(idx, np.arange(idx[0], idx[0] + len(idx)))
 
 
 def _check_queues(P, n_kv_heads):
@@ -90,8 +115,11 @@ def _check(w):
                 firsts.append(first); lasts.append(min(last, kvl - 1))
             assert lo == (min(firsts) // 16) * 16
             assert hi == max(lasts) + 1
-            # chunks tile [lo, hi) exactly
-            assert nch == max(1, -(-(hi - lo) // ch))
+            # items tile [lo, hi) exactly (a decode unit with no key has none)
+            if cls == "pf":
+                assert nch == max(1, -(-(hi - lo) // ch))
+            else:
+                assert nch >= (1 if hi > lo else 0) and (nch == 0) == (hi <= lo)
             for k in range(nch):
                 seen_items[it0 + k] += 1
                 if cls == "pf":
@@ -103,16 +131,16 @@ def _check(w):
                 assert (d[10], d[11]) == (ui, k)
                 assert (d[0], d[1], d[7], d[8], d[9]) == (s, h, r0, nr, nch)
                 assert (d[4], d[5], d[6]) == (kvl, q0, ql)
-                # even split: consecutive, 16-aligned starts, at most ch + 15 keys
+                # consecutive, 16-aligned boundaries, on consecutive waves
                 a, b = int(d[2]), int(d[3])
                 assert a == (lo if k == 0 else int(items[it0 + k - 1][3]))
-                assert a % 16 == 0 and (b == hi if k == nch - 1 else b % 16 == 0)
-                assert a < b or (nch == 1 and hi <= lo)
-                assert b - a <= ch + 15
-                # its pages fit the 128-entry page window of the wave
-                assert (max(b - 1, a)) // c.page_size - a // c.page_size + 1 <= 128
+                assert (a - lo) % 16 == 0 and (b == max(hi, lo) if k == nch - 1 else (b - lo) % 16 == 0)
+                assert a < b
+                if k > 0:
+                    assert d[12] == items[it0 + k - 1][12] + 1
         assert np.all(seen_items == 1), cls
     _check_queues(P, c.num_kv_heads)
+    _check_stream_k(P)
     for s in range(w.n_seqs):
         ql = int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])
         for h in range(c.num_kv_heads):
