@@ -83,7 +83,7 @@ struct DecCfg {
   static constexpr int WAVE_LDS = NST * STAGE + STG + QSLOT;
   static_assert(REGION % 1024 == 0, "whole 1 KB DMA instructions per region");
   static_assert(WAVE_LDS * kDecWavesPerBlock <= 160 * 1024, "LDS of a workgroup");
-  static_assert((NST - 2) * NDMA < 64, "vmcnt range");
+  static_assert((NST - 1) * NDMA < 64, "vmcnt range");
 };
 template <int D, bool FP8>
 constexpr int dec_wgs_per_cu() {
@@ -137,7 +137,7 @@ template <int D, bool FP8, bool CAP>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8)) void decode_kernel(Params p) {
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
-                NDMA = Cf::NDMA, CPR = Cf::CPR, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, VST = Cf::VST,
+                NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, VST = Cf::VST,
                 NST = Cf::NST;
   __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * Cf::WAVE_LDS];
 
@@ -304,21 +304,49 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     vis_hi = min(C.c_hi, C.kvl);
   };
 
-  // One 16-key step: keys [kb, kb + 16) in ring slot `slot`.
-  auto compute_step = [&](int slot, int kb) {
+  // Operands of one 16-key step, read out of its ring slot so that the slot
+  // can be refilled while the step is computed.
+  struct Ops {
+    u32x4 k[NLD];                 // K pieces (raw bf16 or fp8)
+    u32x4 v[FP8 ? NLD : 1];       // fp8: V pieces (raw)
+    bf16x4 vt[FP8 ? 1 : ND];      // bf16: V^T operand of each 16-row block of O^T
+  };
+  // V^T operand layout (ds_read_b64_tr_b16): lane x of group g reads
+  // V[4g + x/4][16 d + 4 (x%4) .. + 3] and receives V^T[16 d + x][4g .. 4g + 3]
+  const int vkey = 4 * g + (col >> 2);
+  const int q4 = col & 3;
+  auto read_ops = [&](int slot, Ops& op) {
     const char* kr = ring + slot * STAGE;
     const char* vr = kr + REGION;
-    // K operand: lane (key col, group g) reads its pieces (swizzled chunks)
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      op.k[j] = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        op.v[j] = *reinterpret_cast<const u32x4*>(vr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
+    } else {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const int chunk = 2 * d + (q4 >> 1);
+        op.vt[d] = lds_read_tr16(
+            reinterpret_cast<const __bf16*>(vr + vkey * RB + 16 * (chunk ^ dswz_v<D, FP8>(vkey)) + 8 * (q4 & 1)));
+      }
+    }
+    // every read of the slot has completed: it may be refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // One 16-key step: keys [kb, kb + 16).
+  auto compute_step = [&](const Ops& op, int kb) {
     bf16x8 ka[NI];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const int chunk = 4 * j + g;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * (chunk ^ dswz_k<D, FP8>(col)));
       if constexpr (FP8) {
-        ka[2 * j] = fp8x8_to_bf16(u32x2{v[0], v[1]});
-        ka[2 * j + 1] = fp8x8_to_bf16(u32x2{v[2], v[3]});
+        ka[2 * j] = fp8x8_to_bf16(u32x2{op.k[j][0], op.k[j][1]});
+        ka[2 * j + 1] = fp8x8_to_bf16(u32x2{op.k[j][2], op.k[j][3]});
       } else {
-        ka[j] = __builtin_bit_cast(bf16x8, v);
+        ka[j] = __builtin_bit_cast(bf16x8, op.k[j]);
       }
     }
     // S^T: lane (col, g) gets keys kb + 4g + j of row `col`
@@ -362,18 +390,13 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       pb[j] = (__bf16)pj;
     }
 
-    // V^T operand: lane x of group g reads V[4g + x/4][16 d + 4 (x%4) .. + 3]
-    const int vkey = 4 * g + (col >> 2);
-    const int q4 = col & 3;
     if constexpr (FP8) {
       // widen V to bf16 through the staging tile; rows past kv_len become 0
       const bool vok = kb + col < vis_hi;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int chunk = 4 * j + g;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(vr + col * RB + 16 * (chunk ^ dswz_k<D, FP8>(col)));
-        bf16x8 lo = fp8x8_to_bf16(u32x2{v[0], v[1]});
-        bf16x8 hi = fp8x8_to_bf16(u32x2{v[2], v[3]});
+        bf16x8 lo = fp8x8_to_bf16(u32x2{op.v[j][0], op.v[j][1]});
+        bf16x8 hi = fp8x8_to_bf16(u32x2{op.v[j][2], op.v[j][3]});
         if (!vok) {
           lo = bf16x8{};
           hi = bf16x8{};
@@ -389,20 +412,16 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       }
       wave_sync();
     } else {
-      if (kb + 16 > vis_hi) {
-        // zero the V rows of keys at or past vis_hi (their chunks in any order)
-        char* vw = const_cast<char*>(vr);
-        for (int e = lane; e < 16 * CPR; e += 64) {
-          const int key = e / CPR;
-          if (kb + key >= vis_hi) *reinterpret_cast<u32x4*>(vw + key * RB + 16 * (e % CPR)) = u32x4{0u, 0u, 0u, 0u};
-        }
-        wave_sync();
-      }
+      // V of keys at or past vis_hi reads as 0 (0 * NaN would poison the sum)
+      const bool partial = kb + 16 > vis_hi;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const int chunk = 2 * d + (q4 >> 1);
-        const bf16x4 a = lds_read_tr16(
-            reinterpret_cast<const __bf16*>(vr + vkey * RB + 16 * (chunk ^ dswz_v<D, FP8>(vkey)) + 8 * (q4 & 1)));
+        bf16x4 a = op.vt[d];
+        if (partial) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            if (kb + 4 * g + kk >= vis_hi) a[kk] = (__bf16)0.f;
+        }
         o[d] = mfma16x16x16(a, pb, o[d]);
       }
     }
@@ -458,10 +477,10 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     }
   };
 
-  // prologue: NST - 1 steps in flight
+  // prologue: NST steps in flight
   int ahead = 0;  // steps issued beyond the one being computed
 #pragma unroll
-  for (int k = 0; k < NST - 1; ++k) {
+  for (int k = 0; k < NST; ++k) {
     if (loading) {
       issue_step(L, k);
       ++ahead;
@@ -469,20 +488,22 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     }
   }
   --ahead;  // the first issued step is the one computed first
+  Ops op;
   for (int n = 0;; ++n) {
     // this step's rows are in LDS once at most `ahead` later steps are in flight
-    if (ahead == NST - 2) {
-      wait_vmcnt<(NST - 2) * NDMA>();
+    if (ahead == NST - 1) {
+      wait_vmcnt<(NST - 1) * NDMA>();
     } else {
       wait_vmcnt<0>();
     }
-    // refill: the slot computed last step is free
+    read_ops(n % NST, op);
+    // refill the slot just read
     if (loading) {
-      issue_step(L, (n + NST - 1) % NST);
+      issue_step(L, n % NST);
       ++ahead;
       loader_next();
     }
-    compute_step(n % NST, C.c_lo + steps_done * kDecStepKeys);
+    compute_step(op, C.c_lo + steps_done * kDecStepKeys);
     ++steps_done;
     ++q_age;
     --ahead;
@@ -492,8 +513,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       C = Cn;
       Cn = load_info(C.idx + 1);
       // the Q slot's DMA is complete once a wait above covered a step issued
-      // after it (NST steps later); for short items wait for it here
-      if (q_age < NST) wait_vmcnt<0>();
+      // after it (NST + 1 steps later); for short items wait for it here
+      if (q_age <= NST) wait_vmcnt<0>();
       wave_sync();
       read_q(C, qb);
       if (mine(Cn)) {

@@ -176,10 +176,11 @@ struct DecInfo {
   int32_t s, unit0, item0, blk0, nb, rows, lo16, hi, kvl, q0, ql;
 };
 
-// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31: the double quotient is within
-// one of the true one, which the remainder fixes.
-__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
-  int64_t q = (int64_t)((double)a / (double)b);
+// floor(a / b) for 0 <= a < 2^48, 0 < b < 2^31, given inv = 1.0 / b: the
+// double product is within one of the quotient, which the remainder fixes
+// (a multiply instead of a double-precision division).
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b, double inv) {
+  int64_t q = (int64_t)((double)a * inv);
   const int64_t r = a - q * b;
   if (r < 0) --q;
   else if (r >= b) ++q;
@@ -197,12 +198,15 @@ constexpr int kPlanMaxDecWaves = 4096;
 struct StreamK {
   int64_t Tb;
   int32_t W;
-  const int32_t* table;  // start(w) for w <= W when W <= kPlanMaxDecWaves, else null
-  __device__ int32_t start_exact(int32_t w) const { return (int32_t)floor_div(Tb * w, W); }
+  // start(w) for w <= W when W <= kPlanMaxDecWaves, else null (an LDS pointer:
+  // a generic one would make every lookup wait for the kernel's global stores)
+  const __attribute__((address_space(3))) int32_t* table;
+  double inv_Tb, inv_W;
+  __device__ int32_t start_exact(int32_t w) const { return (int32_t)floor_div(Tb * w, W, inv_W); }
   __device__ int32_t start(int32_t w) const { return table ? table[w] : start_exact(w); }
   // the wave whose range holds block x (0 <= x < Tb)
   __device__ int32_t wave_of(int32_t x) const {
-    const int64_t w = floor_div((int64_t)(x + 1) * W - 1, Tb);
+    const int64_t w = floor_div((int64_t)(x + 1) * W - 1, Tb, inv_Tb);
     return (int32_t)(w < W - 1 ? w : W - 1);
   }
   // items of unit blocks [b0, b0 + nb): one per wave from wa to wb
@@ -282,7 +286,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   // holds at least one block
   const int32_t n_dec_waves = (int32_t)max((int64_t)1, min((int64_t)max(p.dec_waves, 1), tot_dec));
   const bool tabulate = n_dec_waves <= kPlanMaxDecWaves;
-  const StreamK sk{tot_dec, n_dec_waves, tabulate ? sk_start : nullptr};
+  const StreamK sk{tot_dec, n_dec_waves,
+                   tabulate ? (const __attribute__((address_space(3))) int32_t*)sk_start : nullptr,
+                   tot_dec > 0 ? 1.0 / (double)tot_dec : 0.0, 1.0 / (double)n_dec_waves};
   if (tabulate)
     for (int32_t w = tid; w <= n_dec_waves; w += kPlanThreads) sk_start[w] = sk.start_exact(w);
   for (int32_t w = tid; w < max(p.dec_waves, 1); w += kPlanThreads) p.dec_wave_first[w] = INT32_MAX;
