@@ -205,7 +205,10 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     int grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid > p.max_pf_items) grid = p.max_pf_items;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+    if (p.soft_cap > 0.f)
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, true>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, false>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
   }

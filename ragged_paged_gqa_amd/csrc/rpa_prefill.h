@@ -59,6 +59,9 @@ constexpr int pf_step_keys(int D, bool fp8) { return (D > 0 && !fp8) ? 32 : 32; 
 #ifndef RPA_PF_STAGES
 #define RPA_PF_STAGES 4
 #endif
+#ifndef RPA_PF_HINTS
+#define RPA_PF_HINTS 0
+#endif
 constexpr int kStagesBf16 = RPA_PF_STAGES;
 // Cached page-table entries per item: the largest chunk over the smallest page
 // (16 keys), plus the partial pages at both ends.
@@ -81,7 +84,7 @@ struct PrefillLds {
   static constexpr int kStepKeys = pf_step_keys(D, FP8);
   static constexpr int kRegionBytes = kSwizzled ? kStepKeys * kRowBytes : 2 * D;  // V offset
   static constexpr int kBufBytes = kSwizzled ? 2 * kStepKeys * kRowBytes : kStepKeys * kRowBytes;
-  static constexpr int kStages = FP8 ? 2 : kStagesBf16;
+  static constexpr int kStages = FP8 ? 3 : kStagesBf16;
   static constexpr size_t kBytes = (size_t)kStages * kBufBytes;
 };
 
@@ -111,7 +114,9 @@ __device__ __forceinline__ float other_half(float v) {
 #define RPA_SCHED_DS_READS(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
 #define RPA_SCHED_MFMAS(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
 
-template <int D, bool FP8>
+// CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
+// block loop has no branch and no cap arithmetic).
+template <int D, bool FP8, bool CAP>
 __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
   constexpr int NW = kPfWaves;
   constexpr int NH = pf_halves_for(D);        // 32-row halves per wave
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   static_assert(NDB >= 2, "head_dim >= 64");
   static_assert(SWZ ? RPI * CPR == 64 : 2 * CPR == 64, "whole rows per full-width DMA instruction");
   static_assert(KS % NW == 0 && (NB == 1 || NB == 2), "step shape");
-  static_assert(!FP8 || NST == 2, "fp8 path stages through registers one step ahead");
+  static_assert(!FP8 || NST == 3, "fp8 path stages through registers one step ahead");
   static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == (SWZ ? 16 : 8)), "a wave's rows stay in one 16-key block");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   if (p.hdr->n_pf_items == 0) return;  // nothing of this class in the batch
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
-  const bool capped = p.soft_cap > 0.f;
+  constexpr bool capped = CAP;
   const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
   // scores in base-2 units are st * cmul (capped: the cap is applied to st
   // first and cmul = 1); negative scales flip Q's sign instead
@@ -376,10 +381,57 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         *reinterpret_cast<bf16x8*>(row_p + 16 * ((c0 + 1) ^ sw)) = b;
       }
     };
-    auto slot_ptr = [&](int k) { return lds + ((ring + k) % NST) * BUF; };
 
-    // prologue: NST - 1 steps in flight
+    static_assert(NH == 1 && NB == 1, "the pipelined block loop takes 32 rows and 32-key steps per wave");
+    // ring slot of this item's load step n
+    const int ring0 = ring;
+    auto slot_of = [&](int n) { return lds + ((ring0 + n) % NST) * BUF; };
     int issued = 0;
+    // Makes load step n's K/V rows visible to every wave and keeps the ring
+    // full. Called one block ahead of the compute (before the QK product of
+    // block n), so a slot is refilled only when every wave is past the
+    // barrier here, i.e. done with the PV product of the step that used it
+    // (bf16: step n - 2; fp8, whose rows go through registers: step n - 3).
+    auto sync_step = [&](int n) {
+      const int k0 = c_lo + n * KS;
+      char* cur = slot_of(n);
+      if constexpr (FP8) {
+        store_regs(k0, cur);
+        __syncthreads();
+        if (issued < n_steps) {
+          load_regs(c_lo + issued * KS);
+          advance();
+          ++issued;
+        }
+      } else {
+        // wait for this step's rows: later steps may stay in flight
+        const int ahead = issued - n - 1;
+        if (ahead >= 2) {
+          wait_vmcnt<2 * NIW>();
+        } else if (ahead == 1) {
+          wait_vmcnt<NIW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (k0 + KS > kvl || k0 + KS > c_hi) {
+          // zero V of rows past kv_len or in blocks past the chunk
+          for (int i = tid; i < KS * CPR; i += NT) {
+            const int key = i / CPR;
+            const bool loaded = key < 16 || k0 + 16 * (key >> 4) < c_hi;
+            if (k0 + key >= kvl || !loaded)
+              *reinterpret_cast<u32x4*>(cur + REG + key * RB + 16 * (i % CPR)) = u32x4{0u, 0u, 0u, 0u};
+          }
+          __syncthreads();
+        }
+        if (issued < n_steps) {
+          issue_dma(c_lo + issued * KS, slot_of(issued));
+          advance();
+          ++issued;
+        }
+      }
+    };
+    // prologue: the first load steps in flight
     if constexpr (FP8) {
       if (n_steps > 0) {
         load_regs(c_lo);
@@ -388,202 +440,175 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < NST - 1; ++k) {
+      for (int k = 0; k < NST - 2; ++k) {
         if (k < n_steps) {
-          issue_dma(c_lo + k * KS, slot_ptr(k));
+          issue_dma(c_lo + k * KS, slot_of(k));
           advance();
           issued = k + 1;
         }
       }
     }
 
-    // Score blocks of 32 keys; block ub belongs to load step ub / NB. The
-    // accumulators are touched only by MFMAs inside the loop: when a row's
-    // maximum outgrows its reference, the loop is left, the accumulators
-    // rescaled, and the same block resumed (its scores kept in st).
-    f32x16 st[NH];
+    // S^T [32 keys x 32 rows] = K Q^T of the block in `slot`
+    auto qk = [&](const char* slot) {
+      bf16x8 ka[NS];
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf) st[hf] = f32x16{};
-    float m_blk[NH];
-    int ub = 0;
-    bool resume = false;
-    for (;;) {
-      bool pending = false;
-      for (; ub < n_sub; ++ub) {
-        const int n = ub / NB;
-        const int b = ub % NB;
-        const int k0 = c_lo + n * KS;
-        const int kb = k0 + 32 * b;
-        char* cur = slot_ptr(0);
-        // does this block hold a key that some row of the wave cannot see?
-        const bool need_mask = kb + 32 > vis_hi || (p.is_causal && kb + 31 > pos_lo) ||
-                               (p.window > 0 && kb <= pos_hi - p.window);
-        if (!resume) {
-          if (b == 0) {
-            if constexpr (FP8) {
-              store_regs(k0, cur);
-              __syncthreads();
-              if (issued < n_steps) {
-                load_regs(c_lo + issued * KS);
-                advance();
-                ++issued;
-              }
-            } else {
-              // wait for this step's rows: later steps may stay in flight
-              const int ahead = issued - n - 1;
-              if (ahead >= 2) {
-                wait_vmcnt<2 * NIW>();
-              } else if (ahead == 1) {
-                wait_vmcnt<NIW>();
-              } else {
-                wait_vmcnt<0>();
-              }
-              __syncthreads();
-              if (k0 + KS > kvl || k0 + KS > c_hi) {
-                // zero V of rows past kv_len or in blocks past the chunk
-                for (int i = tid; i < KS * CPR; i += NT) {
-                  const int key = i / CPR;
-                  const bool loaded = key < 16 || k0 + 16 * (key >> 4) < c_hi;
-                  if (k0 + key >= kvl || !loaded)
-                    *reinterpret_cast<u32x4*>(cur + REG + key * RB + 16 * (i % CPR)) = u32x4{0u, 0u, 0u, 0u};
-                }
-                __syncthreads();
-              }
-              // refill the slot freed by the previous step (every wave is past it)
-              if (issued < n_steps) {
-                issue_dma(c_lo + issued * KS, slot_ptr(NST - 1));
-                advance();
-                ++issued;
-              }
-            }
-          }
+      for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(slot + k_at(i));
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NS; ++i) sc = mfma32x32x16(ka[i], qb[0][i], sc);
+      return sc;
+    };
+    // Scores of a block: soft-cap (then in base-2 units); returns the row
+    // maximum in base-2 units.
+    auto finish_scores = [&](f32x16& sc) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float x = sc[j];
+        if constexpr (CAP) x = soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
+        sc[j] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, other_half(mx));
+      return mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
+    };
+    // Hidden keys of the block at kb to -inf (masks of `flashAttention`, kv
+    // length, chunk end; by selection, so NaN in unread slots cannot leak);
+    // returns the new row maximum in base-2 units.
+    auto mask_scores = [&](f32x16& sc, int kb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float x = visible(0, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? sc[j] : -INFINITY;
+        sc[j] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, other_half(mx));
+      return mx * cmul;
+    };
+    // Lazily moved reference maximum: the accumulator is rescaled only when a
+    // row's maximum outgrows the reference by more than kRescaleSlack. The
+    // rescale runs outside the block loop (below), so inside it the
+    // accumulator is only ever an MFMA operand and stays in its registers.
+    auto needs_rescale = [&](float mb) { return __any(mb > m_ref[0] + kRescaleSlack); };
+    auto rescale = [&](float mb) {
+      const float m_new = fmaxf(m_ref[0], mb);
+      const float alpha = m_ref[0] == -INFINITY ? 0.f : fast_exp2(m_ref[0] - m_new);
+      m_ref[0] = m_new;
+      lsum[0] *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[0][d] *= alpha;
+    };
+    // does the block at kb hold a key that some row of the wave cannot see?
+    auto need_mask = [&](int kb) {
+      return kb + 32 > vis_hi || (p.is_causal && kb + 31 > pos_lo) || (p.window > 0 && kb <= pos_hi - p.window);
+    };
 
-          // S^T = K Q^T for keys [kb, kb + 32): one K operand feeds every half
-          {
-            const char* kr = cur + 32 * b * RB;
-            bf16x8 ka[NS];
+    // Software-pipelined block loop. Entering iteration ub, block ub's scores
+    // are final (capped, masked) and the reference maximum covers them. The
+    // iteration runs the next block's QK MFMAs beside this block's softmax
+    // VALU work, then this block's PV MFMAs beside the next block's score
+    // epilogue, so the matrix and vector units work at the same time.
+    f32x16 sc_cur = f32x16{};
+    float mb_pending = -INFINITY;
+    bool pending = false;
+    if (n_sub > 0) {
+      sync_step(0);
+      sc_cur = qk(slot_of(0));
+      mb_pending = finish_scores(sc_cur);
+      if (need_mask(c_lo)) mb_pending = mask_scores(sc_cur, c_lo);
+      pending = needs_rescale(mb_pending);
+    }
+    int ub = 0;
+    for (;;) {
+      if (pending) rescale(mb_pending);
+      pending = false;
+      for (; ub < n_sub; ++ub) {
+        const int kb = c_lo + 32 * ub;
+        const bool has_next = ub + 1 < n_sub;
+        if (has_next) sync_step(ub + 1);
+        // (the last block computes a throw-away QK on its own slot, so that
+        // the two units' work stays in one straight-line block)
+        const char* nslot = slot_of(has_next ? ub + 1 : ub);
+        float mb_next;
+        {
+          // The iteration in an explicit order (sched_barrier fences keep the
+          // compiler's scheduler from regrouping it): the next block's K
+          // reads; each of its QK MFMAs followed by a share of this block's
+          // softmax; each PV MFMA of this block followed by a share of the
+          // next block's score epilogue, with V^T reads two MFMAs ahead.
+          const char* ns = nslot;
+          bf16x8 ka[NS];
 #pragma unroll
-            for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kr + k_at(i));
+          for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(ns + k_at(i));
+          __builtin_amdgcn_sched_barrier(0);
+          const float negm = m_ref[0] == -INFINITY ? 0.f : -m_ref[0];
+          f32x16 sc_next = f32x16{};
+          bf16x8 pb[2];
 #pragma unroll
-            for (int hf = 0; hf < NH; ++hf) st[hf] = f32x16{};
+          for (int i = 0; i < NS; ++i) {
+            sc_next = mfma32x32x16(ka[i], qb[0][i], sc_next);
 #pragma unroll
-            for (int i = 0; i < NS; ++i)
-#pragma unroll
-              for (int hf = 0; hf < NH; ++hf) st[hf] = mfma32x32x16(ka[i], qb[hf][i], st[hf]);
-            RPA_SCHED_DS_READS(NS);
-            RPA_SCHED_MFMAS(NS * NH);
-          }
-          // row maxima over the visible keys, in base-2 units
-          bool grow = false;
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf) {
-            if (capped) {
-#pragma unroll
-              for (int j = 0; j < 16; ++j) st[hf][j] = soft_cap_f(st[hf][j] * sm, p.soft_cap, cap_k) * kLog2e;
+            for (int jp = (8 * i) / NS; jp < (8 * (i + 1)) / NS; ++jp) {
+              // P = 2^(score - reference) for scores 2jp, 2jp+1, packed to
+              // bf16; the row sum is taken in f32 over the unrounded values
+              // (the LSE needs them: one dominant key rounded to bf16 moves it
+              // by up to 2^-8)
+              const float p0 = fast_exp2(__builtin_fmaf(sc_cur[2 * jp], cmul, negm));
+              const float p1 = fast_exp2(__builtin_fmaf(sc_cur[2 * jp + 1], cmul, negm));
+              lsum[0] += p0 + p1;
+              const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
+              pb[jp >> 2][2 * (jp & 3)] = pair[0];
+              pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
             }
-            float mx;
-            if (need_mask) {
-              mx = -INFINITY;
-#pragma unroll
-              for (int j = 0; j < 16; ++j)
-                mx = fmaxf(mx, visible(hf, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? st[hf][j] : -INFINITY);
-            } else {
-              mx = st[hf][0];
-#pragma unroll
-              for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[hf][j]);
-            }
-            mx = fmaxf(mx, other_half(mx));
-            m_blk[hf] = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
-            grow = grow || m_blk[hf] > m_ref[hf] + kRescaleSlack;
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (__any(grow)) {
+          // O^T += V^T P^T: MFMA m = ks * NDB + d takes key half ks, 32 rows of d
+          const char* cs = slot_of(ub);
+          constexpr int NM = 2 * NDB;
+          bf16x8 va[NM];
+          auto read_va = [&](int m) {
+            const int ks = m / NDB, d = m % NDB;
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(cs + (16 * ks) * RB + v_at(d)));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(cs + (16 * ks + 8) * RB + v_at(d)));
+            va[m] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          };
+          read_va(0);
+          read_va(1);
+          __builtin_amdgcn_sched_barrier(0);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            if (m + 2 < NM) read_va(m + 2);
+            o[0][m % NDB] = mfma32x32x16(va[m], pb[m / NDB], o[0][m % NDB]);
+#pragma unroll
+            for (int j = (16 * m) / NM; j < (16 * (m + 1)) / NM; ++j) {
+              float x = sc_next[j];
+              if constexpr (CAP) x = soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
+              sc_next[j] = x;
+              mx = fmaxf(mx, x);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          mx = fmaxf(mx, other_half(mx));
+          mb_next = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
+          sc_cur = sc_next;
+        }
+        if (has_next) {
+          if (need_mask(kb + 32)) mb_next = mask_scores(sc_cur, kb + 32);
+          if (needs_rescale(mb_next)) {
+            // leave the loop to rescale, then resume at the next block
+            mb_pending = mb_next;
             pending = true;
+            ++ub;
             break;
           }
         }
-        resume = false;
-
-        // P = 2^(score - reference), packed to bf16 for the PV product; the
-        // row sum is taken in f32 over the unrounded values (the LSE needs
-        // them: one dominant key rounded to bf16 moves it by up to 2^-8)
-        bf16x8 pb[NH][2];
-        auto make_p = [&](auto hfc, auto masked) {
-          constexpr int hf = decltype(hfc)::value;
-          const float negm = m_ref[hf] == -INFINITY ? 0.f : -m_ref[hf];
-#pragma unroll
-          for (int jp = 0; jp < 8; ++jp) {
-            float p0 = fast_exp2(__builtin_fmaf(st[hf][2 * jp], cmul, negm));
-            float p1 = fast_exp2(__builtin_fmaf(st[hf][2 * jp + 1], cmul, negm));
-            if constexpr (decltype(masked)::value) {
-              const int key0 = kb + 8 * (jp >> 1) + 4 * h + 2 * (jp & 1);
-              p0 = visible(hf, key0) ? p0 : 0.f;
-              p1 = visible(hf, key0 + 1) ? p1 : 0.f;
-            }
-            lsum[hf] += p0 + p1;
-            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
-            pb[hf][jp >> 2][2 * (jp & 3)] = pair[0];
-            pb[hf][jp >> 2][2 * (jp & 3) + 1] = pair[1];
-          }
-        };
-        auto p_of_half = [&](auto hfc) {
-          if (need_mask)
-            make_p(hfc, std::true_type{});
-          else
-            make_p(hfc, std::false_type{});
-        };
-
-        // O^T += V^T P^T (two 16-key k-steps); one V^T operand feeds every half
-        const char* vr = cur + 32 * b * RB;
-        auto read_va = [&](int ks, bf16x8 (&va)[NDB]) {
-#pragma unroll
-          for (int d = 0; d < NDB; ++d) {
-            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks) * RB + v_at(d)));
-            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(vr + (16 * ks + 8) * RB + v_at(d)));
-            va[d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        };
-        if constexpr (NH == 1) {
-          p_of_half(std::integral_constant<int, 0>{});
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 va1[NDB];
-            read_va(ks, va1);
-#pragma unroll
-            for (int d = 0; d < NDB; ++d) o[0][d] = mfma32x32x16(va1[d], pb[0][ks], o[0][d]);
-            RPA_SCHED_DS_READS(2 * NDB);
-            RPA_SCHED_MFMAS(NDB);
-          }
-        } else {
-          bf16x8 va[2][NDB];
-          read_va(0, va[0]);
-          read_va(1, va[1]);
-          p_of_half(std::integral_constant<int, 0>{});
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int d = 0; d < NDB; ++d) o[0][d] = mfma32x32x16(va[ks][d], pb[0][ks], o[0][d]);
-          // the second half's softmax runs while the first half's PV MFMAs execute
-          p_of_half(std::integral_constant<int, NH - 1>{});
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int d = 0; d < NDB; ++d) o[NH - 1][d] = mfma32x32x16(va[ks][d], pb[NH - 1][ks], o[NH - 1][d]);
-        }
-        if (b == NB - 1 || ub == n_sub - 1) ring = (ring + 1) % NST;
       }
       if (!pending) break;
-      // move the reference max (every row of the wave at once; alpha <= 1)
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) {
-        const float m_new = fmaxf(m_ref[hf], m_blk[hf]);
-        const float alpha = m_ref[hf] == -INFINITY ? 0.f : fast_exp2(m_ref[hf] - m_new);
-        m_ref[hf] = m_new;
-        lsum[hf] *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[hf][d] *= alpha;
-      }
-      resume = true;
     }
+    ring = (ring0 + n_steps) % NST;
 
     // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
 #pragma unroll
