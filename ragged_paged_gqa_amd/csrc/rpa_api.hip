@@ -200,7 +200,7 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
 template <int D, bool FP8>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   {
-    constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfPageCache + 64));
+    constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfBlkTable + 64));
     constexpr int per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
     int grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid > p.max_pf_items) grid = p.max_pf_items;

@@ -292,6 +292,51 @@ __device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff,
       : "memory");
 }
 
+// N full-width DMA instructions in one M0 window: instruction j reads
+// sbase + voff[j] (per lane) into LDS at lds_addr + j * STRIDE + 16 * lane.
+// One asm statement, so that nothing the compiler schedules can see the
+// borrowed M0; every M0 write is followed by the wait state LDS DMA needs.
+#define RPA_DMA_LD(j) "global_load_lds_dwordx4 %" #j ", %[sb]\n\t"
+#define RPA_DMA_ADV "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+template <int STRIDE>
+__device__ __forceinline__ void dma16_rows2(const uint8_t* sbase, const uint32_t (&voff)[2], uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
+      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2)
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE)
+      : "memory");
+}
+template <int STRIDE>
+__device__ __forceinline__ void dma16_rows4(const uint8_t* sbase, const uint32_t (&voff)[4], uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
+      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV RPA_DMA_LD(4)
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), [sb] "s"(sbase), [la] "s"(lds_addr),
+        [st] "n"(STRIDE)
+      : "memory");
+}
+template <int STRIDE>
+__device__ __forceinline__ void dma16_rows8(const uint8_t* sbase, const uint32_t (&voff)[8], uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
+      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV RPA_DMA_LD(4) RPA_DMA_ADV
+      RPA_DMA_LD(5) RPA_DMA_ADV RPA_DMA_LD(6) RPA_DMA_ADV RPA_DMA_LD(7) RPA_DMA_ADV RPA_DMA_LD(8)
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
+        "v"(voff[7]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE)
+      : "memory");
+}
+#undef RPA_DMA_LD
+#undef RPA_DMA_ADV
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
 }

@@ -7,16 +7,16 @@
 // pulled from a device-wide queue; wave w owns rows [32w, 32w + 32). Split
 // units leave partials; the workgroup finishing a unit's last chunk merges
 // them (rpa_merge.h).
-// Per load step (64 keys for bf16 with head_dim <= 128, else 32):
+// Per load step of 32 keys:
 //   * loader: the step's K and V rows of kv head h (combined heads 2h and
 //     2h+1, adjacent in memory — `stridedLoadKv`) are gathered through the
-//     page table into a ring of LDS tiles whose rows are padded so that the
-//     MFMA operand reads below are bank-conflict free. bf16 rows go straight
-//     from HBM to LDS (global_load_lds_dwordx4, one padded row per
-//     instruction) kStagesBf16 - 1 steps ahead of the compute; fp8 rows are
-//     staged through registers one step ahead and widened to bf16 on the way.
-//     Page position is tracked incrementally (no integer division in the
-//     loop). One barrier per step publishes the tile.
+//     page table into a ring of LDS tiles laid out so that the MFMA operand
+//     reads below are bank-conflict free. bf16 rows go straight from HBM to
+//     LDS (global_load_lds_dwordx4) two steps ahead of the compute; fp8 rows
+//     are staged through registers one step ahead and widened to bf16 on the
+//     way. The physical address of every 16-key block of an item is worked
+//     out once, into an LDS table, when the item starts. One barrier per step
+//     publishes the tile.
 // Per 32-key block of the step:
 //   * S^T [32 keys x 32 rows] = K Q^T with v_mfma_f32_32x32x16_bf16, Q^T kept
 //     in registers; lane (row, half h) holds 16 keys of its row, so a row
@@ -59,13 +59,10 @@ constexpr int pf_step_keys(int D, bool fp8) { return (D > 0 && !fp8) ? 32 : 32; 
 #ifndef RPA_PF_STAGES
 #define RPA_PF_STAGES 4
 #endif
-#ifndef RPA_PF_HINTS
-#define RPA_PF_HINTS 0
-#endif
 constexpr int kStagesBf16 = RPA_PF_STAGES;
-// Cached page-table entries per item: the largest chunk over the smallest page
-// (16 keys), plus the partial pages at both ends.
-constexpr int kPfPageCache = kPfMaxChunk / 16 + 4;
+// Block table entries per item: every 16-key block of the largest chunk, plus
+// those of the load steps issued past its end.
+constexpr int kPfBlkTable = kPfMaxChunk / 16 + 16;
 
 // Two LDS layouts of a ring slot, both bank-conflict free for the MFMA
 // operand reads below:
@@ -110,9 +107,6 @@ __device__ __forceinline__ float other_half(float v) {
   return __builtin_bit_cast(float, (uint32_t)(lane_id() < 32 ? r[1] : r[0]));
 }
 
-// Scheduling hints: the next `n` LDS reads, then the next `n` MFMAs.
-#define RPA_SCHED_DS_READS(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
-#define RPA_SCHED_MFMAS(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
 // block loop has no branch and no cap arithmetic).
@@ -149,7 +143,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == (SWZ ? 16 : 8)), "a wave's rows stay in one 16-key block");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
-  __shared__ int sh_pages[kPfPageCache];  // physical pages of the current item
+  __shared__ uint32_t sh_blk[kPfBlkTable];  // physical key index of each 16-key block of the item
   __shared__ int sh_item[2];
   __shared__ int sh_last;
 
@@ -219,7 +213,6 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   };
 
   int parity = 0;
-  int ring = 0;  // LDS ring slot of the next step to compute
   for (;;) {
     if (tid == 0) sh_item[parity] = next_item();
     __syncthreads();
@@ -241,10 +234,18 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     const int n_steps = (n_sub + NB - 1) / NB;                     // load steps
     const uint8_t* kv_h = p.kv + (int64_t)2 * kvh * D * EB;
     const int32_t* ptab = p.page_indices + (int64_t)s * p.pps;
-    // physical pages of the item's key range, clamped, cached in LDS
-    const int lp0 = c_lo / p.page;
-    const int n_pg = min(n_steps > 0 ? (c_lo + n_steps * KS - 1) / p.page - lp0 + 1 : 0, kPfPageCache);
-    for (int i = tid; i < n_pg; i += NT) sh_pages[i] = min(max(ptab[min(lp0 + i, p.pps - 1)], 0), p.P - 1);
+    // Block table: physical key index (page * page_size + slot) of 16-key
+    // block b of load step m at entry NB16 m + b, for the steps the loader
+    // issues ([0, n_steps + NST - 1)). Blocks past the chunk repeat its last
+    // block: they are loaded but never computed on.
+    const int n_ent = n_steps > 0 ? (n_steps + NST - 1) * NB16 : 0;
+    const int last_blk = c_lo + 16 * ((c_hi - c_lo - 1) >> 4);
+    for (int i = tid; i < n_ent; i += NT) {
+      const int key = min(c_lo + 16 * i, last_blk);
+      const int lp = key / p.page;
+      const int ph = min(max(ptab[min(lp, p.pps - 1)], 0), p.P - 1);
+      sh_blk[i] = (uint32_t)ph * (uint32_t)p.page + (uint32_t)(key - lp * p.page);
+    }
     __syncthreads();
 
     // this lane's query rows, one per half
@@ -293,66 +294,43 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       for (int d = 0; d < NDB; ++d) o[hf][d] = f32x16{};
     }
 
-    // page position of the next step to load, advanced without division
-    int lp = c_lo / p.page;
-    int sl = c_lo - lp * p.page;
-    auto advance = [&]() {
-#pragma unroll
-      for (int b = 0; b < NB16; ++b) {
-        sl += 16;
-        if (sl >= p.page) {
-          sl -= p.page;
-          ++lp;
-        }
-      }
-    };
+    // ---- loader ----
+    // Ring slots are LDS byte offsets; every item starts its ring at slot 0
+    // (the previous item waited for all of its loads). The key block a wave
+    // loads comes from the item's block table (sh_blk), so the step loop does
+    // no page arithmetic.
+    auto adv = [](int off) { return off + BUF < NST * BUF ? off + BUF : 0; };
+    auto blk_base = [&](uint32_t ent) { return kv_h + (uint64_t)ent * (uint64_t)key_stride; };
 
-    // ---- loader, bf16: rows straight into the LDS ring ----
-    auto issue_dma = [&](int k0, char* dst) {
-      // page block my_blk of the step at (lp, sl), or block 0 past the chunk
-      // (a harmless re-read: its keys are masked and their V rows zeroed)
-      int lpb = lp, slb = sl;
-      if (k0 + 16 * my_blk < c_hi) {
-        for (int b = 0; b < my_blk; ++b) {
-          slb += 16;
-          if (slb >= p.page) {
-            slb = 0;
-            ++lpb;
-          }
-        }
-      }
-      const int ph = __builtin_amdgcn_readfirstlane(sh_pages[min(lpb - lp0, kPfPageCache - 1)]);
-      const uint8_t* base = uniform_ptr(kv_h + ((int64_t)ph * p.page + slb) * key_stride);
-      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
-          lds_addr_of(dst + (SWZ ? my_region * REG + 16 * my_blk * RB : wave * NIW * RB)));
-#pragma unroll
-      for (int j = 0; j < NIW; ++j) dma16_sbase(base, dma_off[j], dst0 + (SWZ ? 1024 : RB) * j);
-    };
-    // ---- loader, fp8: registers one step ahead, widened to bf16 ----
-    // base addresses of the 16-key blocks of the step at (lp, sl)
-    auto block_bases = [&](int k0, const uint8_t* (&bb)[NB16]) {
-      int lpb = lp, slb = sl;
-#pragma unroll
-      for (int b = 0; b < NB16; ++b) {
-        const int ph = sh_pages[min(lpb - lp0, kPfPageCache - 1)];
-        const uint8_t* base = kv_h + ((int64_t)ph * p.page + slb) * key_stride;
-        bb[b] = (b == 0 || k0 + 16 * b < c_hi) ? base : bb[0];
-        slb += 16;
-        if (slb >= p.page) {
-          slb = 0;
-          ++lpb;
-        }
+    // bf16: the step's rows straight into the LDS ring, NIW DMA instructions
+    // per wave in one M0 window
+    constexpr int DSTR = SWZ ? 1024 : RB;  // LDS bytes between a wave's DMA instructions
+    const int dma_lds = SWZ ? my_region * REG + 16 * my_blk * RB : wave * NIW * RB;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds));
+    auto issue_dma = [&](uint32_t ent, int slot_off) {
+      const uint8_t* base = uniform_ptr(blk_base(ent));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + slot_off + dma_lds);
+      static_assert(NIW == 2 || NIW == 4 || NIW == 8, "DMA instructions per wave per step");
+      if constexpr (NIW == 2) {
+        dma16_rows2<DSTR>(base, dma_off, dst);
+      } else if constexpr (NIW == 4) {
+        dma16_rows4<DSTR>(base, dma_off, dst);
+      } else {
+        dma16_rows8<DSTR>(base, dma_off, dst);
       }
     };
+    // fp8: registers one step ahead, widened to bf16 on the way into LDS
     u32x4 stage[CPT];
-    auto load_regs = [&](int k0) {
+    auto load_regs = [&](int m) {
+      const int k0 = c_lo + m * KS;
       const uint8_t* bb[NB16];
-      block_bases(k0, bb);
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) bb[b] = blk_base(__builtin_amdgcn_readfirstlane(sh_blk[m * NB16 + b]));
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + NT * c;
         const int key = idx / GCH;
-        if (idx < KS * GCH && (key < 16 || k0 + 16 * (key >> 4) < c_hi)) {
+        if (idx < KS * GCH && k0 + 16 * (key >> 4) < c_hi) {
           const int off = (key & 15) * (int)key_stride + 16 * (idx % GCH);
           stage[c] = *reinterpret_cast<const u32x4*>(bb[key >> 4] + off);
         } else {
@@ -383,109 +361,102 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     };
 
     static_assert(NH == 1 && NB == 1, "the pipelined block loop takes 32 rows and 32-key steps per wave");
-    // ring slot of this item's load step n
-    const int ring0 = ring;
-    auto slot_of = [&](int n) { return lds + ((ring0 + n) % NST) * BUF; };
-    int issued = 0;
-    // Makes load step n's K/V rows visible to every wave and keeps the ring
-    // full. Called one block ahead of the compute (before the QK product of
-    // block n), so a slot is refilled only when every wave is past the
-    // barrier here, i.e. done with the PV product of the step that used it
-    // (bf16: step n - 2; fp8, whose rows go through registers: step n - 3).
-    auto sync_step = [&](int n) {
+    static_assert(FP8 || NST >= 3, "bf16 ring: a slot in use, a slot landing, a slot in flight");
+    int fill_off = 0;  // bf16: slot that the next DMA step fills
+    int ent_v = 0;     // bf16: table entry of that step's block, read one step early
+    int issued = 0;    // fp8: load steps staged so far
+    // Makes load step n's K/V rows (in slot `cur`) visible to every wave and
+    // keeps the ring full. Called one block ahead of the compute (before the
+    // QK product of block n), so a slot is refilled only when every wave is
+    // past the barrier here, i.e. done with the PV product of the step that
+    // used it (bf16: step n - 2; fp8, whose rows go through registers: step
+    // n - 3).
+    auto sync_step = [&](int n, char* cur) {
       const int k0 = c_lo + n * KS;
-      char* cur = slot_of(n);
       if constexpr (FP8) {
         store_regs(k0, cur);
         __syncthreads();
         if (issued < n_steps) {
-          load_regs(c_lo + issued * KS);
-          advance();
+          load_regs(issued);
           ++issued;
         }
       } else {
-        // wait for this step's rows: later steps may stay in flight
-        const int ahead = issued - n - 1;
-        if (ahead >= 2) {
-          wait_vmcnt<2 * NIW>();
-        } else if (ahead == 1) {
-          wait_vmcnt<NIW>();
-        } else {
-          wait_vmcnt<0>();
-        }
+        // every step issues one DMA group (past the chunk: a re-read of its
+        // last block, never computed on), so the same count always means
+        // "step n has landed, steps n+1 .. n+NST-3 may still be in flight"
+        wait_vmcnt<(NST - 3) * NIW>();
         __syncthreads();
         if (k0 + KS > kvl || k0 + KS > c_hi) {
           // zero V of rows past kv_len or in blocks past the chunk
           for (int i = tid; i < KS * CPR; i += NT) {
             const int key = i / CPR;
-            const bool loaded = key < 16 || k0 + 16 * (key >> 4) < c_hi;
-            if (k0 + key >= kvl || !loaded)
+            if (k0 + key >= kvl || k0 + 16 * (key >> 4) >= c_hi)
               *reinterpret_cast<u32x4*>(cur + REG + key * RB + 16 * (i % CPR)) = u32x4{0u, 0u, 0u, 0u};
           }
           __syncthreads();
         }
-        if (issued < n_steps) {
-          issue_dma(c_lo + issued * KS, slot_of(issued));
-          advance();
-          ++issued;
-        }
+        issue_dma(__builtin_amdgcn_readfirstlane(ent_v), fill_off);
+        fill_off = adv(fill_off);
+        ent_v = sh_blk[(n + NST - 1) * NB16 + my_blk];
       }
     };
     // prologue: the first load steps in flight
-    if constexpr (FP8) {
-      if (n_steps > 0) {
-        load_regs(c_lo);
-        advance();
+    if (n_steps > 0) {
+      if constexpr (FP8) {
+        load_regs(0);
         issued = 1;
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int k = 0; k < NST - 2; ++k) {
-        if (k < n_steps) {
-          issue_dma(c_lo + k * KS, slot_of(k));
-          advance();
-          issued = k + 1;
+        for (int k = 0; k < NST - 2; ++k) {
+          issue_dma(__builtin_amdgcn_readfirstlane(sh_blk[k * NB16 + my_blk]), fill_off);
+          fill_off = adv(fill_off);
         }
+        ent_v = sh_blk[(NST - 2) * NB16 + my_blk];
       }
     }
 
     // S^T [32 keys x 32 rows] = K Q^T of the block in `slot`
-    auto qk = [&](const char* slot) {
+    auto qk = [&](const char* slot, float (&sv)[16]) {
       bf16x8 ka[NS];
 #pragma unroll
       for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(slot + k_at(i));
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int i = 0; i < NS; ++i) sc = mfma32x32x16(ka[i], qb[0][i], sc);
-      return sc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sv[j] = sc[j];
     };
-    // Scores of a block: soft-cap (then in base-2 units); returns the row
-    // maximum in base-2 units.
-    auto finish_scores = [&](f32x16& sc) {
+    // Scores of a block to base-2 units (soft-capped first when the cap is
+    // on); returns the row maximum. (Written as a product rather than a copy,
+    // so that the scores leave the MFMA accumulator registers once.)
+    auto to_base2 = [&](float x) {
+      if constexpr (CAP) {
+        return soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
+      } else {
+        return x * cmul;
+      }
+    };
+    auto finish_scores = [&](float (&sv)[16]) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = sc[j];
-        if constexpr (CAP) x = soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
-        sc[j] = x;
-        mx = fmaxf(mx, x);
+        sv[j] = to_base2(sv[j]);
+        mx = fmaxf(mx, sv[j]);
       }
-      mx = fmaxf(mx, other_half(mx));
-      return mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
+      return fmaxf(mx, other_half(mx));
     };
     // Hidden keys of the block at kb to -inf (masks of `flashAttention`, kv
     // length, chunk end; by selection, so NaN in unread slots cannot leak);
     // returns the new row maximum in base-2 units.
-    auto mask_scores = [&](f32x16& sc, int kb) {
+    auto mask_scores = [&](float (&sv)[16], int kb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float x = visible(0, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? sc[j] : -INFINITY;
-        sc[j] = x;
+        const float x = visible(0, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? sv[j] : -INFINITY;
+        sv[j] = x;
         mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, other_half(mx));
-      return mx * cmul;
+      return fmaxf(mx, other_half(mx));
     };
     // Lazily moved reference maximum: the accumulator is rescaled only when a
     // row's maximum outgrows the reference by more than kRescaleSlack. The
@@ -500,103 +471,121 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 #pragma unroll
       for (int d = 0; d < NDB; ++d) o[0][d] *= alpha;
     };
-    // does the block at kb hold a key that some row of the wave cannot see?
-    auto need_mask = [&](int kb) {
-      return kb + 32 > vis_hi || (p.is_causal && kb + 31 > pos_lo) || (p.window > 0 && kb <= pos_hi - p.window);
-    };
+    // Blocks that can hold a key some row of the wave cannot see: those at
+    // or past ub_mask_hi (kv length, chunk end, causal diagonal) and those
+    // before ub_mask_lo (sliding window).
+    int ub_mask_hi = n_sub, ub_mask_lo = 0;
+    {
+      int lim = vis_hi - 32;  // blocks with kb <= lim hold no key at or past vis_hi
+      if (p.is_causal) lim = min(lim, pos_lo - 31);
+      ub_mask_hi = lim < c_lo ? 0 : min(n_sub, (lim - c_lo) / 32 + 1);
+      if (p.window > 0) {
+        const int w = pos_hi - p.window;  // blocks with kb <= w hold a hidden key
+        ub_mask_lo = w < c_lo ? 0 : min(n_sub, (w - c_lo) / 32 + 1);
+      }
+    }
+    auto need_mask = [&](int b) { return b >= ub_mask_hi || b < ub_mask_lo; };
 
     // Software-pipelined block loop. Entering iteration ub, block ub's scores
     // are final (capped, masked) and the reference maximum covers them. The
     // iteration runs the next block's QK MFMAs beside this block's softmax
     // VALU work, then this block's PV MFMAs beside the next block's score
     // epilogue, so the matrix and vector units work at the same time.
-    f32x16 sc_cur = f32x16{};
+    float sc_cur[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sc_cur[j] = 0.f;
     float mb_pending = -INFINITY;
     bool pending = false;
     if (n_sub > 0) {
-      sync_step(0);
-      sc_cur = qk(slot_of(0));
+      sync_step(0, lds);
+      qk(lds, sc_cur);
       mb_pending = finish_scores(sc_cur);
-      if (need_mask(c_lo)) mb_pending = mask_scores(sc_cur, c_lo);
+      if (need_mask(0)) mb_pending = mask_scores(sc_cur, c_lo);
       pending = needs_rescale(mb_pending);
     }
     int ub = 0;
+    int cs = 0;  // ring slot of block ub
     for (;;) {
       if (pending) rescale(mb_pending);
       pending = false;
       for (; ub < n_sub; ++ub) {
-        const int kb = c_lo + 32 * ub;
+        const int ns = adv(cs);
         const bool has_next = ub + 1 < n_sub;
-        if (has_next) sync_step(ub + 1);
+        if (has_next) sync_step(ub + 1, lds + ns);
         // (the last block computes a throw-away QK on its own slot, so that
         // the two units' work stays in one straight-line block)
-        const char* nslot = slot_of(has_next ? ub + 1 : ub);
+        const char* nslot = lds + (has_next ? ns : cs);
+        const char* cslot = lds + cs;
         float mb_next;
         {
           // The iteration in an explicit order (sched_barrier fences keep the
-          // compiler's scheduler from regrouping it): the next block's K
-          // reads; each of its QK MFMAs followed by a share of this block's
-          // softmax; each PV MFMA of this block followed by a share of the
-          // next block's score epilogue, with V^T reads two MFMAs ahead.
-          const char* ns = nslot;
+          // compiler's scheduler from regrouping it): the next block's first K
+          // reads; the first P pairs of this block while they land; each QK
+          // MFMA followed by a K read KA MFMAs ahead and a share of the
+          // remaining pairs, the last ones by the first V^T reads; each PV
+          // MFMA followed by a share of the next block's score epilogue, with
+          // V^T reads VA MFMAs ahead.
+          constexpr int KA = NS / 2;  // K reads ahead of their MFMA
           bf16x8 ka[NS];
 #pragma unroll
-          for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(ns + k_at(i));
+          for (int i = 0; i < KA; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i));
           __builtin_amdgcn_sched_barrier(0);
           const float negm = m_ref[0] == -INFINITY ? 0.f : -m_ref[0];
-          f32x16 sc_next = f32x16{};
           bf16x8 pb[2];
+          // P = 2^(score - reference) for scores 2jp, 2jp+1, packed to bf16;
+          // the row sum is taken in f32 over the unrounded values (the LSE
+          // needs them: one dominant key rounded to bf16 moves it by up to
+          // 2^-8)
+          auto p_pair = [&](int jp) {
+            const float p0 = fast_exp2(sc_cur[2 * jp] + negm);
+            const float p1 = fast_exp2(sc_cur[2 * jp + 1] + negm);
+            lsum[0] += p0 + p1;
+            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
+            pb[jp >> 2][2 * (jp & 3)] = pair[0];
+            pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
+          };
+          constexpr int PRE = 2;  // pairs before the first QK MFMA
 #pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            sc_next = mfma32x32x16(ka[i], qb[0][i], sc_next);
-#pragma unroll
-            for (int jp = (8 * i) / NS; jp < (8 * (i + 1)) / NS; ++jp) {
-              // P = 2^(score - reference) for scores 2jp, 2jp+1, packed to
-              // bf16; the row sum is taken in f32 over the unrounded values
-              // (the LSE needs them: one dominant key rounded to bf16 moves it
-              // by up to 2^-8)
-              const float p0 = fast_exp2(__builtin_fmaf(sc_cur[2 * jp], cmul, negm));
-              const float p1 = fast_exp2(__builtin_fmaf(sc_cur[2 * jp + 1], cmul, negm));
-              lsum[0] += p0 + p1;
-              const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
-              pb[jp >> 2][2 * (jp & 3)] = pair[0];
-              pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          for (int jp = 0; jp < PRE; ++jp) p_pair(jp);
+          __builtin_amdgcn_sched_barrier(0);
           // O^T += V^T P^T: MFMA m = ks * NDB + d takes key half ks, 32 rows of d
-          const char* cs = slot_of(ub);
           constexpr int NM = 2 * NDB;
+          constexpr int VA = 3;  // V^T reads ahead of their MFMA
+          static_assert(NS >= VA && NM > VA, "read-ahead depth");
           bf16x8 va[NM];
           auto read_va = [&](int m) {
             const int ks = m / NDB, d = m % NDB;
-            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(cs + (16 * ks) * RB + v_at(d)));
-            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(cs + (16 * ks + 8) * RB + v_at(d)));
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16*>(cslot + (16 * ks) * RB + v_at(d)));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(cslot + (16 * ks + 8) * RB + v_at(d)));
             va[m] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           };
-          read_va(0);
-          read_va(1);
-          __builtin_amdgcn_sched_barrier(0);
+          f32x16 sc_next = f32x16{};
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            sc_next = mfma32x32x16(ka[i], qb[0][i], sc_next);
+            if (i + KA < NS) ka[i + KA] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i + KA));
+#pragma unroll
+            for (int jp = PRE + ((8 - PRE) * i) / NS; jp < PRE + ((8 - PRE) * (i + 1)) / NS; ++jp) p_pair(jp);
+            if (i >= NS - VA) read_va(i - (NS - VA));
+            __builtin_amdgcn_sched_barrier(0);
+          }
           float mx = -INFINITY;
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            if (m + 2 < NM) read_va(m + 2);
+            if (m + VA < NM) read_va(m + VA);
             o[0][m % NDB] = mfma32x32x16(va[m], pb[m / NDB], o[0][m % NDB]);
 #pragma unroll
             for (int j = (16 * m) / NM; j < (16 * (m + 1)) / NM; ++j) {
-              float x = sc_next[j];
-              if constexpr (CAP) x = soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
-              sc_next[j] = x;
-              mx = fmaxf(mx, x);
+              sc_cur[j] = to_base2(sc_next[j]);
+              mx = fmaxf(mx, sc_cur[j]);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          mx = fmaxf(mx, other_half(mx));
-          mb_next = mx * cmul;  // -inf stays -inf (cmul > 0 unless the scale is 0)
-          sc_cur = sc_next;
+          mb_next = fmaxf(mx, other_half(mx));
         }
+        cs = ns;
         if (has_next) {
-          if (need_mask(kb + 32)) mb_next = mask_scores(sc_cur, kb + 32);
+          if (need_mask(ub + 1)) mb_next = mask_scores(sc_cur, c_lo + 32 * (ub + 1));
           if (needs_rescale(mb_next)) {
             // leave the loop to rescale, then resume at the next block
             mb_pending = mb_next;
@@ -608,7 +597,8 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
       if (!pending) break;
     }
-    ring = (ring0 + n_steps) % NST;
+    // the re-reads past the chunk have landed: the ring is idle
+    if constexpr (!FP8) wait_vmcnt<0>();
 
     // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
 #pragma unroll
