@@ -64,23 +64,20 @@ constexpr int kStagesBf16 = RPA_PF_STAGES;
 // those of the load steps issued past its end.
 constexpr int kPfBlkTable = kPfMaxChunk / 16 + 16;
 
-// Two LDS layouts of a ring slot, both bank-conflict free for the MFMA
-// operand reads below:
-//   * swizzled (a key's K and V rows together are under 1 KB): the step's K
-//     rows (region 0) and V rows (region 1), each kStepKeys unpadded rows of
-//     2D bytes whose 16-byte chunks are XOR-swizzled by the key (swz_k /
-//     swz_v), so that one DMA instruction writes 1 KB of whole rows;
-//   * padded (head_dim 256: K row then V row of a key is exactly 1 KB, one
-//     DMA instruction): rows of K|V padded to 16 * (16n + 3) bytes, so 16
-//     consecutive keys start in distinct 16-byte bank groups.
+// LDS layout of a ring slot: the step's K rows (region 0) and V rows (region
+// 1), each kStepKeys unpadded rows of 2D bytes whose 16-byte chunks are
+// XOR-swizzled by the key (swz_k / swz_v), so that one DMA instruction writes
+// 1 KB of whole rows and the MFMA operand reads below are bank-conflict free.
+// (No row padding serves both reads: the K reads want 16 consecutive keys in
+// distinct 16-byte bank groups, the transposed V reads want 4 consecutive
+// keys in distinct 64-byte quarters of the 256-byte bank row.)
 template <int D, bool FP8>
 struct PrefillLds {
-  static constexpr bool kSwizzled = 4 * D < 1024;
-  static constexpr int kRowBytes = kSwizzled ? 2 * D : 4 * D + 48;  // row stride
+  static constexpr int kRowBytes = 2 * D;      // row stride
   static constexpr int kChunks = 2 * D / 16;   // 16-byte chunks per K or V row
   static constexpr int kStepKeys = pf_step_keys(D, FP8);
-  static constexpr int kRegionBytes = kSwizzled ? kStepKeys * kRowBytes : 2 * D;  // V offset
-  static constexpr int kBufBytes = kSwizzled ? 2 * kStepKeys * kRowBytes : kStepKeys * kRowBytes;
+  static constexpr int kRegionBytes = kStepKeys * kRowBytes;  // V region offset
+  static constexpr int kBufBytes = 2 * kRegionBytes;
   static constexpr int kStages = FP8 ? 3 : kStagesBf16;
   static constexpr size_t kBytes = (size_t)kStages * kBufBytes;
 };
@@ -125,22 +122,20 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   constexpr int RB = PrefillLds<D, FP8>::kRowBytes;
   constexpr int CPR = PrefillLds<D, FP8>::kChunks;
   constexpr int REG = PrefillLds<D, FP8>::kRegionBytes;  // byte offset of a key's V row from its K row
-  constexpr bool SWZ = PrefillLds<D, FP8>::kSwizzled;
   constexpr int BUF = PrefillLds<D, FP8>::kBufBytes;
   constexpr int NST = PrefillLds<D, FP8>::kStages;
   constexpr int GCH = 2 * D * EB / 16;        // 16-byte global chunks per key (K and V)
   constexpr int CPT = (KS * GCH + NT - 1) / NT;  // fp8 path: chunks per thread per step
-  // bf16 path: full-width DMA instructions of 1 KB. Swizzled: RPI rows of one
-  // region each, wave w moving region w / 2, keys [16 (w % 2), + 16).
-  // Padded: one key's K|V row each, wave w moving keys [8 w, 8 w + 8). Either
-  // way a wave's keys lie in one 16-key page block.
-  constexpr int RPI = SWZ ? 1024 / RB : 1;    // rows per DMA instruction
-  constexpr int NIW = SWZ ? (2 * KS / RPI) / NW : KS / NW;  // DMA instructions per wave per step
+  // bf16 path: full-width DMA instructions of 1 KB, RPI rows of one region
+  // each, wave w moving region w / 2, keys [16 (w % 2), + 16): a wave's keys
+  // lie in one 16-key page block.
+  constexpr int RPI = 1024 / RB;              // rows per DMA instruction
+  constexpr int NIW = (2 * KS / RPI) / NW;    // DMA instructions per wave per step
   static_assert(NDB >= 2, "head_dim >= 64");
-  static_assert(SWZ ? RPI * CPR == 64 : 2 * CPR == 64, "whole rows per full-width DMA instruction");
+  static_assert(RPI * CPR == 64, "whole rows per full-width DMA instruction");
   static_assert(KS % NW == 0 && (NB == 1 || NB == 2), "step shape");
   static_assert(!FP8 || NST == 3, "fp8 path stages through registers one step ahead");
-  static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == (SWZ ? 16 : 8)), "a wave's rows stay in one 16-key block");
+  static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == 16), "a wave's rows stay in one 16-key block");
 
   __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
   __shared__ uint32_t sh_blk[kPfBlkTable];  // physical key index of each 16-key block of the item
@@ -168,35 +163,36 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   //   K operand of k-step i: key r32, chunk 2i + h
   //   V^T operand of d-block d: key 4 (g16 / 2) + l16 / 4 (+ 8, + 16 ks),
   //   bytes 32 (g16 % 2) + 8 (l16 % 4) + 64 d of the row
-  // (swizzled: per-lane tables; padded: one base plus immediate offsets)
-  int k_off[SWZ ? NS : 1];
+  // The swizzles only permute chunks within 256-byte spans of a row (K: the
+  // low 4 bits of the chunk index, V: its bits 2-3), so the offsets of
+  // k-steps i and i + 8, and of d-blocks d and d + 4, differ by exactly 256
+  // bytes: per-lane tables of KT and VT entries plus immediate offsets.
+  constexpr int KT = NS < 8 ? NS : 8;
+  constexpr int VT = NDB < 4 ? NDB : 4;
+  int k_off[KT];
 #pragma unroll
-  for (int i = 0; i < (SWZ ? NS : 1); ++i) k_off[i] = r32 * RB + 16 * (SWZ ? ((2 * i + h) ^ swz_k<D>(r32)) : h);
+  for (int i = 0; i < KT; ++i) k_off[i] = r32 * RB + 16 * ((2 * i + h) ^ swz_k<D>(r32));
   const int g16 = lane >> 4, l16 = lane & 15;
   const int v_key = 4 * (g16 >> 1) + (l16 >> 2);
-  int v_off[SWZ ? NDB : 1];
+  int v_off[VT];
 #pragma unroll
-  for (int d = 0; d < (SWZ ? NDB : 1); ++d) {
+  for (int d = 0; d < VT; ++d) {
     const int byte = 32 * (g16 & 1) + 8 * (l16 & 3) + 64 * d;
-    v_off[d] = REG + v_key * RB + (SWZ ? 16 * ((byte >> 4) ^ swz_v<D>(v_key)) + (byte & 15) : byte);
+    v_off[d] = REG + v_key * RB + 16 * ((byte >> 4) ^ swz_v<D>(v_key)) + (byte & 15);
   }
-  auto k_at = [&](int i) { return SWZ ? k_off[SWZ ? i : 0] : k_off[0] + 32 * i; };
-  auto v_at = [&](int d) { return SWZ ? v_off[SWZ ? d : 0] : v_off[0] + 64 * d; };
+  auto k_at = [&](int i) { return k_off[i % KT] + 256 * (i / KT); };
+  auto v_at = [&](int d) { return v_off[d % VT] + 256 * (d / VT); };
   // bf16 loader: this wave's DMA instructions and its lanes' fixed source
   // offsets inside the page block
-  const int my_blk = SWZ ? (wave & 1) : (wave >> 1);
-  const int my_region = SWZ ? (wave >> 1) : 0;
+  const int my_blk = wave & 1;
+  const int my_region = wave >> 1;
   uint32_t dma_off[NIW];
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
-    if constexpr (SWZ) {
-      const int krow = RPI * j + lane / CPR;  // key within the 16-key block
-      const int c_lds = lane % CPR;
-      const int c_g = c_lds ^ (my_region ? swz_v<D>(krow) : swz_k<D>(krow));
-      dma_off[j] = (uint32_t)(krow * key_stride) + (uint32_t)(my_region * 2 * D) + 16u * c_g;
-    } else {
-      dma_off[j] = (uint32_t)(((wave * NIW + j) & 15) * key_stride) + 16u * lane;
-    }
+    const int krow = RPI * j + lane / CPR;  // key within the 16-key block
+    const int c_lds = lane % CPR;
+    const int c_g = c_lds ^ (my_region ? swz_v<D>(krow) : swz_k<D>(krow));
+    dma_off[j] = (uint32_t)(krow * key_stride) + (uint32_t)(my_region * 2 * D) + 16u * c_g;
   }
 
   // queues: start with this XCD's, then steal from the others in turn
@@ -304,8 +300,8 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 
     // bf16: the step's rows straight into the LDS ring, NIW DMA instructions
     // per wave in one M0 window
-    constexpr int DSTR = SWZ ? 1024 : RB;  // LDS bytes between a wave's DMA instructions
-    const int dma_lds = SWZ ? my_region * REG + 16 * my_blk * RB : wave * NIW * RB;
+    constexpr int DSTR = 1024;  // LDS bytes between a wave's DMA instructions
+    const int dma_lds = my_region * REG + 16 * my_blk * RB;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds));
     auto issue_dma = [&](uint32_t ent, int slot_off) {
       const uint8_t* base = uniform_ptr(blk_base(ent));
@@ -347,7 +343,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         const int gc = idx % GCH;              // 16 codes: K chunks first, then V
         const int region = gc / (GCH / 2);
         const int c0 = 2 * (gc % (GCH / 2));   // first of the two bf16 chunks they become
-        const int sw = !SWZ ? 0 : (region ? swz_v<D>(key) : swz_k<D>(key));
+        const int sw = region ? swz_v<D>(key) : swz_k<D>(key);
         char* row_p = dst + region * REG + key * RB;
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
         bf16x8 a = fp8x8_to_bf16(lo2), b = fp8x8_to_bf16(hi2);
