@@ -154,10 +154,16 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   constexpr bool capped = CAP;
   const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
   // scores in base-2 units are st * cmul (capped: the cap is applied to st
-  // first and cmul = 1); negative scales flip Q's sign instead
+  // first and cmul = 1); negative scales flip Q's sign instead. A zero scale
+  // becomes the smallest normal one, so that hidden keys (-inf) stay -inf
+  // through the product while every visible score still rounds to 0.
   const bool neg = p.sm_scale < 0.f;
   const float sm = neg ? -p.sm_scale : p.sm_scale;
-  const float cmul = capped ? 1.0f : sm * kLog2e;
+  const float cmul = capped ? 1.0f : fmaxf(sm * kLog2e, 1.17549435e-38f);
+  // Uncapped with head_dim <= 128 (MFMA results in plain VGPRs) the scores
+  // stay as the MFMA wrote them and the scale goes into the exponent's FMA
+  // (and into the row maximum): one VALU instruction per score less.
+  constexpr bool kLate = !CAP && D <= 128;
 
   // LDS read offsets inside a slot (loop-invariant per lane):
   //   K operand of k-step i: key r32, chunk 2i + h
@@ -428,9 +434,16 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     auto to_base2 = [&](float x) {
       if constexpr (CAP) {
         return soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
+      } else if constexpr (kLate) {
+        return x;
       } else {
         return x * cmul;
       }
+    };
+    // row maximum (base-2 units) from this lane's maximum of stored scores
+    auto row_max = [&](float mx) {
+      mx = fmaxf(mx, other_half(mx));
+      return kLate ? mx * cmul : mx;
     };
     auto finish_scores = [&](float (&sv)[16]) {
       float mx = -INFINITY;
@@ -439,7 +452,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         sv[j] = to_base2(sv[j]);
         mx = fmaxf(mx, sv[j]);
       }
-      return fmaxf(mx, other_half(mx));
+      return row_max(mx);
     };
     // Hidden keys of the block at kb to -inf (masks of `flashAttention`, kv
     // length, chunk end; by selection, so NaN in unread slots cannot leak);
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         sv[j] = x;
         mx = fmaxf(mx, x);
       }
-      return fmaxf(mx, other_half(mx));
+      return row_max(mx);
     };
     // Lazily moved reference maximum: the accumulator is rescaled only when a
     // row's maximum outgrows the reference by more than kRescaleSlack. The
@@ -533,8 +546,9 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
           // needs them: one dominant key rounded to bf16 moves it by up to
           // 2^-8)
           auto p_pair = [&](int jp) {
-            const float p0 = fast_exp2(sc_cur[2 * jp] + negm);
-            const float p1 = fast_exp2(sc_cur[2 * jp + 1] + negm);
+            const float p0 = fast_exp2(kLate ? __builtin_fmaf(sc_cur[2 * jp], cmul, negm) : sc_cur[2 * jp] + negm);
+            const float p1 =
+                fast_exp2(kLate ? __builtin_fmaf(sc_cur[2 * jp + 1], cmul, negm) : sc_cur[2 * jp + 1] + negm);
             lsum[0] += p0 + p1;
             const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
             pb[jp >> 2][2 * (jp & 3)] = pair[0];
@@ -577,7 +591,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          mb_next = fmaxf(mx, other_half(mx));
+          mb_next = row_max(mx);
         }
         cs = ns;
         if (has_next) {
