@@ -148,13 +148,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// c * tanh(x / c) as c - 2c / (1 + e^(2x/c)): one exp2 and one reciprocal, the
-// logistic form of the spatial-compiler page's `capped` soft-cap. Saturates to
-// +-c for large |x| (e^.. -> inf gives c, -> 0 gives -c).
-__device__ __forceinline__ float soft_cap_f(float x, float c, float two_log2e_over_c) {
-  float e = fast_exp2(x * two_log2e_over_c);
-  return c - 2.0f * c * fast_rcp(1.0f + e);
-}
+// Soft-cap in base-2 units: for a raw score s, log2(e) * c * tanh(scale * s /
+// c), as c' - 2c' / (1 + e^(2 scale s / c)) with c' = c log2(e): one exp2 and
+// one reciprocal (the logistic form of the spatial-compiler page's `capped`
+// soft-cap), the scale and the change to base 2 folded into the constants.
+// Saturates to +-c' for large |s| (e^.. -> inf gives c', -> 0 gives -c').
+struct SoftCapB2 {
+  float a;   // scale * 2 log2(e) / c
+  float c1;  // c log2(e)
+  float c2;  // 2 c log2(e)
+  __device__ __forceinline__ SoftCapB2(float scale, float c)
+      : a(scale * 2.0f * 1.4426950408889634f / c), c1(c * 1.4426950408889634f), c2(2.0f * c * 1.4426950408889634f) {}
+  __device__ __forceinline__ float operator()(float s) const {
+    return __builtin_fmaf(-c2, fast_rcp(1.0f + fast_exp2(s * a)), c1);
+  }
+};
 
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -224,16 +232,31 @@ __device__ __forceinline__ f32x2 load_coherent2(const float* src) {  // src 8-by
 // device-coherent reads); also a compiler barrier.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Lane l and lane l ^ 16 (l ^ 32) exchange values with v_permlane16_swap
+// (v_permlane32_swap): no LDS round trip. Each swap returns the pair (own,
+// partner) in some order, and max / sum do not care which.
+__device__ __forceinline__ float max_xor16(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
-__device__ __forceinline__ float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
+__device__ __forceinline__ float sum_xor16(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float wave_max_xor16_32(float v) { return max_xor32(max_xor16(v)); }
+__device__ __forceinline__ float wave_sum_xor16_32(float v) { return sum_xor32(sum_xor16(v)); }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -75,9 +75,16 @@ struct DecCfg {
   static constexpr int NI = D / 32;              // 8-wide k-slots of Q^T per lane (16x16x32 k-steps)
   static constexpr int ND = D / 16;              // 16-row blocks of O^T
   static constexpr int NLD = RB / 64;            // 16-byte K pieces per lane
-  static constexpr int VST = D + 16;             // fp8: row stride (elements) of the bf16 V staging tile
-  static constexpr int STG = FP8 ? 16 * VST * 2 : 0;
-  static constexpr int QSLOT = 16 * D * 2;       // the next item's 16 Q rows (bf16)
+  // fp8: the bf16 V staging tile. Rows are VST elements apart (288 bytes for
+  // head_dim 128: the transposed reads of 8 keys x 32 bytes cover the 64
+  // banks once) and rows 8..15 sit 16 bytes further on, so that the 16-byte
+  // writes of 16 keys at the same column also cover them once.
+  static constexpr int VST = D + 16;
+  static constexpr int STG = FP8 ? 16 * VST * 2 + 16 : 0;
+  // bf16: the next item's 16 Q rows (bf16), DMA'd during the current item.
+  // fp8 takes them into registers instead and spends the space on the ring:
+  // its 4 KB steps need three slots to keep as many bytes in flight.
+  static constexpr int QSLOT = FP8 ? 0 : 16 * D * 2;
   static constexpr int NST_FIT = (kDecWaveLds - STG - QSLOT) / STAGE;
   static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 8 ? 8 : NST_FIT);  // ring slots
   static constexpr int WAVE_LDS = NST * STAGE + STG + QSLOT;
@@ -154,8 +161,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
 
   const int n_items = uni(p.hdr->n_dec_items);
   const int key_stride = 2 * p.Hkv * D * EB;  // bytes between consecutive slots (< 2^26)
-  const float cap_k = CAP ? 2.0f * kLog2e / p.soft_cap : 0.f;
-  const float sc_mul = CAP ? p.sm_scale : p.sm_scale * kLog2e;  // uncapped: straight to base 2
+  const float sc_mul = p.sm_scale * kLog2e;  // uncapped: straight to base 2
+  const SoftCapB2 cap_b2(p.sm_scale, CAP ? p.soft_cap : 1.0f);
 
   // per-lane DMA source offsets inside a 16-key block (loop-invariant): LDS
   // chunk c of row `key` holds global chunk c ^ swizzle(key)
@@ -231,6 +238,19 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     for (int i = 0; i < NI; ++i) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qs + col * D + slot_d<FP8>(i, g));
       qb[i] = col < I.nrows ? v : bf16x8{};
+    }
+  };
+  // fp8: the same operand straight from global memory (row col of the item;
+  // rows past nrows re-read row 0 and are zeroed)
+  auto load_q = [&](const Info& I, bf16x8 (&qr)[NI]) {
+    const int prow = I.row0 + (col < I.nrows ? col : 0);
+    const int t = prow / p.G;
+    const int qh = I.h * p.G + (prow - t * p.G);
+    const uint16_t* qp = p.q + ((int64_t)(I.q0 + t) * p.Hq + qh) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + slot_d<FP8>(i, g));
+      qr[i] = col < I.nrows ? v : bf16x8{};
     }
   };
 
@@ -315,6 +335,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
   // V[4g + x/4][16 d + 4 (x%4) .. + 3] and receives V^T[16 d + x][4g .. 4g + 3]
   const int vkey = 4 * g + (col >> 2);
   const int q4 = col & 3;
+  auto stg_row = [](int key) { return key * VST + 8 * (key >> 3); };  // staging row start (elements)
   auto read_ops = [&](int slot, Ops& op) {
     const char* kr = ring + slot * STAGE;
     const char* vr = kr + REGION;
@@ -338,7 +359,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
   };
 
   // One 16-key step: keys [kb, kb + 16).
-  auto compute_step = [&](const Ops& op, int kb) {
+  auto compute_step = [&](const Ops& op, int kb_in) {
+    const int kb = __builtin_amdgcn_readfirstlane(kb_in);  // wave-uniform: scalar mask tests
     bf16x8 ka[NI];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
@@ -359,8 +381,12 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float x = sc[j] * sc_mul;
-      if constexpr (CAP) x = soft_cap_f(x, p.soft_cap, cap_k) * kLog2e;
+      float x;
+      if constexpr (CAP) {
+        x = cap_b2(sc[j]);
+      } else {
+        x = sc[j] * sc_mul;
+      }
       if (need_mask) {
         const int key = kb + 4 * g + j;
         bool vis = key < vis_hi;
@@ -392,22 +418,25 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
 
     if constexpr (FP8) {
       // widen V to bf16 through the staging tile; rows past kv_len become 0
-      const bool vok = kb + col < vis_hi;
+      bf16x8 vw[2 * NLD];
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        bf16x8 lo = fp8x8_to_bf16(u32x2{op.v[j][0], op.v[j][1]});
-        bf16x8 hi = fp8x8_to_bf16(u32x2{op.v[j][2], op.v[j][3]});
-        if (!vok) {
-          lo = bf16x8{};
-          hi = bf16x8{};
-        }
-        *reinterpret_cast<bf16x8*>(stg + col * VST + slot_d<FP8>(2 * j, g)) = lo;
-        *reinterpret_cast<bf16x8*>(stg + col * VST + slot_d<FP8>(2 * j + 1, g)) = hi;
+        vw[2 * j] = fp8x8_to_bf16(u32x2{op.v[j][0], op.v[j][1]});
+        vw[2 * j + 1] = fp8x8_to_bf16(u32x2{op.v[j][2], op.v[j][3]});
       }
+      if (kb + 16 > vis_hi) {  // (uniform) the step ends past vis_hi
+        if (kb + col >= vis_hi) {
+#pragma unroll
+          for (int j = 0; j < 2 * NLD; ++j) vw[j] = bf16x8{};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * NLD; ++j)
+        *reinterpret_cast<bf16x8*>(stg + stg_row(col) + slot_d<FP8>(j, g)) = vw[j];
       wave_sync();
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16x4 a = lds_read_tr16(stg + vkey * VST + 16 * d + 4 * q4);
+        const bf16x4 a = lds_read_tr16(stg + stg_row(vkey) + 16 * d + 4 * q4);
         o[d] = mfma16x16x16(a, pb, o[d]);
       }
       wave_sync();
@@ -455,11 +484,17 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
   C = load_info(first);
   if (!mine(C)) return;
   Info Cn = load_info(first + 1);  // the compute side's next item
-  dma_q(C);
-  wait_vmcnt<0>();
-  wave_sync();
-  read_q(C, qb);
-  if (mine(Cn)) dma_q(Cn);
+  bf16x8 qn[FP8 ? NI : 1];         // fp8: the next item's Q operand, loaded ahead
+  if constexpr (FP8) {
+    load_q(C, qb);
+    if (mine(Cn)) load_q(Cn, qn);
+  } else {
+    dma_q(C);
+    wait_vmcnt<0>();
+    wave_sync();
+    read_q(C, qb);
+    if (mine(Cn)) dma_q(Cn);
+  }
   int q_age = 0;  // steps computed since the Q slot's DMA was issued
   begin_item();
 
@@ -512,14 +547,20 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       if (!mine(Cn)) return;  // the wave's range is done
       C = Cn;
       Cn = load_info(C.idx + 1);
-      // the Q slot's DMA is complete once a wait above covered a step issued
-      // after it (NST + 1 steps later); for short items wait for it here
-      if (q_age <= NST) wait_vmcnt<0>();
-      wave_sync();
-      read_q(C, qb);
-      if (mine(Cn)) {
-        dma_q(Cn);
-        q_age = 0;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) qb[i] = qn[i];
+        if (mine(Cn)) load_q(Cn, qn);
+      } else {
+        // the Q slot's DMA is complete once a wait above covered a step
+        // issued after it (NST + 1 steps later); for short items wait here
+        if (q_age <= NST) wait_vmcnt<0>();
+        wave_sync();
+        read_q(C, qb);
+        if (mine(Cn)) {
+          dma_q(Cn);
+          q_age = 0;
+        }
       }
       begin_item();
     }

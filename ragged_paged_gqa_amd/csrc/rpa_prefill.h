@@ -97,14 +97,6 @@ __device__ __forceinline__ int swz_v(int key) {
   return (4 * (key & 3)) & (C - 1);
 }
 
-// Value of lane l ^ 32 (v_permlane32_swap; no LDS round trip).
-__device__ __forceinline__ float other_half(float v) {
-  const uint32_t b = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-  return __builtin_bit_cast(float, (uint32_t)(lane_id() < 32 ? r[1] : r[0]));
-}
-
-
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
 // block loop has no branch and no cap arithmetic).
 template <int D, bool FP8, bool CAP>
@@ -152,7 +144,6 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
   constexpr bool capped = CAP;
-  const float cap_k = capped ? 2.0f * kLog2e / p.soft_cap : 0.f;
   // scores in base-2 units are st * cmul (capped: the cap is applied to st
   // first and cmul = 1); negative scales flip Q's sign instead. A zero scale
   // becomes the smallest normal one, so that hidden keys (-inf) stay -inf
@@ -160,6 +151,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   const bool neg = p.sm_scale < 0.f;
   const float sm = neg ? -p.sm_scale : p.sm_scale;
   const float cmul = capped ? 1.0f : fmaxf(sm * kLog2e, 1.17549435e-38f);
+  const SoftCapB2 cap_b2(sm, capped ? p.soft_cap : 1.0f);
   // Uncapped with head_dim <= 128 (MFMA results in plain VGPRs) the scores
   // stay as the MFMA wrote them and the scale goes into the exponent's FMA
   // (and into the row maximum): one VALU instruction per score less.
@@ -433,7 +425,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     // so that the scores leave the MFMA accumulator registers once.)
     auto to_base2 = [&](float x) {
       if constexpr (CAP) {
-        return soft_cap_f(x * sm, p.soft_cap, cap_k) * kLog2e;
+        return cap_b2(x);
       } else if constexpr (kLate) {
         return x;
       } else {
@@ -442,7 +434,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     };
     // row maximum (base-2 units) from this lane's maximum of stored scores
     auto row_max = [&](float mx) {
-      mx = fmaxf(mx, other_half(mx));
+      mx = max_xor32(mx);
       return kLate ? mx * cmul : mx;
     };
     auto finish_scores = [&](float (&sv)[16]) {
@@ -613,7 +605,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     // lane (row, h) holds O^T[32*d + 8*(j/4) + 4*h + (j%4)][row]
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
-      const float l_row = lsum[hf] + other_half(lsum[hf]);
+      const float l_row = sum_xor32(lsum[hf]);
       const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
       const float lse_v = l_row > 0.f ? (m_ref[hf] + fast_log2(l_row)) * kLn2 : -INFINITY;
       if (!rvalid[hf]) continue;
