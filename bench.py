@@ -146,7 +146,7 @@ def ingest_counters(pmc_dir: str, workload: int) -> dict:
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         for k, v in _counter_per_kernel(
                 os.path.join(pmc_dir, f"w{workload}_{c}", "run_counter_collection.csv"), c).items():
-            for name in ("decode_kernel", "prefill_kernel", "plan_kernel"):
+            for name in ("decode_kernel", "prefill_kernel", "plan_kernel", "combine_kernel"):
                 if f"rpa::{name}" in k:
                     per.setdefault(name, {})[c] = v * 1024.0 / scale[c]
     try:
