@@ -25,8 +25,9 @@
 //
 // Work split inside the workgroup: sequences are taken in tiles of
 // kPlanThreads, one thread per sequence for the per-sequence counts and for
-// the one block scan that turns them into record offsets; a prefill
-// sequence's row blocks are handled by one wave, a row block per lane.
+// the one block scan that turns them into record offsets, and for writing a
+// decode sequence's units and items; a prefill sequence's row blocks are
+// handled by one wave, a row block per lane.
 // Divisions by G and by the chunk size use an exact double-precision
 // reciprocal.
 #pragma once
@@ -170,12 +171,6 @@ struct PfOffs {
   int32_t queue[kQueues];
 };
 
-// A decode sequence of a tile and its record offsets, for the wave that
-// writes its units and items.
-struct DecInfo {
-  int32_t s, unit0, item0, blk0, nb, rows, lo16, hi, kvl, q0, ql;
-};
-
 // floor(a / b) for 0 <= a < 2^48, 0 < b < 2^31, given inv = 1.0 / b: the
 // double product is within one of the quotient, which the remainder fixes
 // (a multiply instead of a double-precision division).
@@ -223,9 +218,8 @@ struct StreamK {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ int64_t red[2][kPlanWaves];
   __shared__ int32_t sh[kPlanWaves * kScanN];
-  __shared__ int32_t n_pf_tile, n_dec_tile;
+  __shared__ int32_t n_pf_tile;
   __shared__ PfInfo pf_info[kPlanThreads];
-  __shared__ DecInfo dec_info[kPlanThreads];
   __shared__ int32_t sk_start[kPlanMaxDecWaves + 1];
   __shared__ PfOffs pf_offs[kPlanThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -300,10 +294,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   for (int k = 0; k < kScanN; ++k) base[k] = 0;
   int32_t base_blk = 0;  // decode blocks of the earlier tiles
   for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
-    if (tid == 0) {
-      n_pf_tile = 0;
-      n_dec_tile = 0;
-    }
+    if (tid == 0) n_pf_tile = 0;
     __syncthreads();
     const int32_t s = s0 + tid;
     int32_t ql = 0, kvl = 0, slot;
@@ -379,54 +370,44 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
 #pragma unroll
     for (int k = 0; k < kScanN; ++k) base[k] += tot[k];
 
-    if (is_dec) {  // listed for the wave that writes its records
-      const UnitRange r = unit_range(p, G, ql, kvl, 0, ql * p.G);
-      int32_t q0, qlx;
-      seq_tokens(p, s, q0, qlx);
-      const int32_t i = atomicAdd(&n_dec_tile, 1);
-      dec_info[i] = DecInfo{s, off[0], off[2], blk0, nb, ql * p.G, r.lo16, r.hi, kvl, q0, ql};
-    } else if (slot >= 0) {
+    if (slot >= 0) {
       pf_offs[slot].unit = off[1];
       pf_offs[slot].item = off[3];
 #pragma unroll
       for (int x = 0; x < kQueues; ++x) pf_offs[slot].queue[x] = off[5 + x];
     }
-    __syncthreads();
 
-    // (c) a wave per decode sequence: a lane per kv head writes the head's
-    // unit and its items (one per wave its blocks fall on)
-    for (int32_t i = wave; i < n_dec_tile; i += kPlanWaves) {
-      const DecInfo f = dec_info[i];
-      int32_t carry = f.item0;
-      for (int32_t h0 = 0; h0 < p.Hkv; h0 += 64) {
-        const int32_t h = h0 + lane;
-        const int32_t b0 = f.blk0 + h * f.nb;
-        int32_t wa = 0, nch = 0;
-        if (h < p.Hkv) nch = sk.n_items(b0, f.nb, wa);
-        const int32_t incl = wave_incl_scan(nch);
-        const int32_t item0 = carry + incl - nch;
-        carry += __shfl(incl, 63);
-        const int32_t ui = f.unit0 + h;
-        if (h >= p.Hkv || ui >= p.max_dec_units) continue;
+    // (c) a thread per decode sequence, head by head: the head's unit and its
+    // items (one per decode wave its blocks fall on)
+    if (is_dec) {
+      const UnitRange r = unit_range(p, G, ql, kvl, 0, ql * p.G);
+      int32_t q0, qlx;
+      seq_tokens(p, s, q0, qlx);
+      int32_t ii = off[2];
+      for (int32_t h = 0; h < p.Hkv; ++h) {
+        const int32_t b0 = blk0 + h * nb;
+        int32_t wa = 0;
+        const int32_t nch = sk.n_items(b0, nb, wa);
+        const int32_t ui = off[0] + h;
+        if (ui >= p.max_dec_units) break;
         Unit u;
-        u.seq = f.s; u.kv_head = h; u.row0 = 0; u.nrows = f.rows;
-        u.kv_lo = f.lo16; u.kv_hi = f.hi; u.nch = nch; u.item0 = item0;
+        u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = ql * p.G;
+        u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = ii;
         p.dec_units[ui] = u;
         p.unit_done[ui] = 0;
         int32_t ws = nch > 0 ? sk.start(wa) : 0;
-        for (int32_t c = 0; c < nch; ++c) {
-          const int32_t ii = item0 + c;
+        for (int32_t c = 0; c < nch; ++c, ++ii) {
           const int32_t w = wa + c;
           if (ii >= p.max_dec_items) break;
           // the unit's blocks inside wave w's range
           const int32_t we = w + 1 < sk.W ? sk.start(w + 1) : (int32_t)sk.Tb;
           const int32_t x0 = max(b0, ws);
-          const int32_t x1 = min(b0 + f.nb, we);
+          const int32_t x1 = min(b0 + nb, we);
           DecItem d;
-          d.seq = f.s; d.kv_head = h;
-          d.c_lo = f.lo16 + 16 * (x0 - b0);
-          d.c_hi = min(f.hi, f.lo16 + 16 * (x1 - b0));
-          d.kvl = f.kvl; d.q0 = f.q0; d.ql = f.ql; d.row0 = 0; d.nrows = f.rows;
+          d.seq = s; d.kv_head = h;
+          d.c_lo = r.lo16 + 16 * (x0 - b0);
+          d.c_hi = min(r.hi, r.lo16 + 16 * (x1 - b0));
+          d.kvl = kvl; d.q0 = q0; d.ql = ql; d.row0 = 0; d.nrows = ql * p.G;
           d.nch = nch; d.unit = ui; d.chunk = c; d.wave = w;
           d.pad[0] = d.pad[1] = d.pad[2] = 0;
           p.dec_items[ii] = d;
@@ -436,6 +417,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
         }
       }
     }
+    __syncthreads();
+
     // (d) a wave per prefill sequence: its units, items and queue entries
     for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
       const PfInfo f = pf_info[i];
