@@ -162,6 +162,10 @@ struct SoftCapB2 {
   __device__ __forceinline__ float operator()(float s) const {
     return __builtin_fmaf(-c2, fast_rcp(1.0f + fast_exp2(s * a)), c1);
   }
+  // the same plus a uniform offset (folded into the FMA's addend)
+  __device__ __forceinline__ float offset(float s, float off) const {
+    return __builtin_fmaf(-c2, fast_rcp(1.0f + fast_exp2(s * a)), c1 + off);
+  }
 };
 
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
@@ -316,49 +320,52 @@ __device__ __forceinline__ void dma16_sbase(const uint8_t* sbase, uint32_t voff,
 }
 
 // N full-width DMA instructions in one M0 window: instruction j reads
-// sbase + voff[j] (per lane) into LDS at lds_addr + j * STRIDE + 16 * lane.
-// One asm statement, so that nothing the compiler schedules can see the
-// borrowed M0; every M0 write is followed by the wait state LDS DMA needs.
+// sbase + voff[j] (per lane) into LDS at lds_addr + j * STRIDE + 16 * lane,
+// issued only when `go` (wave-uniform) is non-zero. One asm statement, branch
+// included, so that nothing the compiler schedules can see the borrowed M0
+// and its basic block stays whole; every M0 write is followed by the wait
+// state LDS DMA needs.
 #define RPA_DMA_LD(j) "global_load_lds_dwordx4 %" #j ", %[sb]\n\t"
 #define RPA_DMA_ADV "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+#define RPA_DMA_HEAD "s_cmp_eq_u32 %[go], 0\n\ts_cbranch_scc1 .Ldma_skip_%=\n\t" \
+                     "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
+#define RPA_DMA_TAIL "s_mov_b32 m0, %[sv]\n.Ldma_skip_%=:"
 template <int STRIDE>
-__device__ __forceinline__ void dma16_rows2(const uint8_t* sbase, const uint32_t (&voff)[2], uint32_t lds_addr) {
+__device__ __forceinline__ void dma16_rows2(const uint8_t* sbase, const uint32_t (&voff)[2], uint32_t lds_addr,
+                                            uint32_t go = 1) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
-      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2)
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : "v"(voff[0]), "v"(voff[1]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE)
-      : "memory");
+  asm volatile(RPA_DMA_HEAD RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_TAIL
+               : [sv] "=&s"(saved)
+               : "v"(voff[0]), "v"(voff[1]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE), [go] "s"(go)
+               : "memory", "scc");
 }
 template <int STRIDE>
-__device__ __forceinline__ void dma16_rows4(const uint8_t* sbase, const uint32_t (&voff)[4], uint32_t lds_addr) {
+__device__ __forceinline__ void dma16_rows4(const uint8_t* sbase, const uint32_t (&voff)[4], uint32_t lds_addr,
+                                            uint32_t go = 1) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
-      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV RPA_DMA_LD(4)
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), [sb] "s"(sbase), [la] "s"(lds_addr),
-        [st] "n"(STRIDE)
-      : "memory");
+  asm volatile(RPA_DMA_HEAD RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV
+               RPA_DMA_LD(4) RPA_DMA_TAIL
+               : [sv] "=&s"(saved)
+               : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), [sb] "s"(sbase), [la] "s"(lds_addr),
+                 [st] "n"(STRIDE), [go] "s"(go)
+               : "memory", "scc");
 }
 template <int STRIDE>
-__device__ __forceinline__ void dma16_rows8(const uint8_t* sbase, const uint32_t (&voff)[8], uint32_t lds_addr) {
+__device__ __forceinline__ void dma16_rows8(const uint8_t* sbase, const uint32_t (&voff)[8], uint32_t lds_addr,
+                                            uint32_t go = 1) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[la]\n\ts_nop 0\n\t"
-      RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV RPA_DMA_LD(4) RPA_DMA_ADV
-      RPA_DMA_LD(5) RPA_DMA_ADV RPA_DMA_LD(6) RPA_DMA_ADV RPA_DMA_LD(7) RPA_DMA_ADV RPA_DMA_LD(8)
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
-        "v"(voff[7]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE)
-      : "memory");
+  asm volatile(RPA_DMA_HEAD RPA_DMA_LD(1) RPA_DMA_ADV RPA_DMA_LD(2) RPA_DMA_ADV RPA_DMA_LD(3) RPA_DMA_ADV
+               RPA_DMA_LD(4) RPA_DMA_ADV RPA_DMA_LD(5) RPA_DMA_ADV RPA_DMA_LD(6) RPA_DMA_ADV RPA_DMA_LD(7)
+               RPA_DMA_ADV RPA_DMA_LD(8) RPA_DMA_TAIL
+               : [sv] "=&s"(saved)
+               : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
+                 "v"(voff[7]), [sb] "s"(sbase), [la] "s"(lds_addr), [st] "n"(STRIDE), [go] "s"(go)
+               : "memory", "scc");
 }
 #undef RPA_DMA_LD
 #undef RPA_DMA_ADV
+#undef RPA_DMA_HEAD
+#undef RPA_DMA_TAIL
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
