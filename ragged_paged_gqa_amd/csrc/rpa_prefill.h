@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
     };
 
-    static_assert(NH == 1 && NB == 1, "the pipelined block loop takes 32 rows and 32-key steps per wave");
+    static_assert(NB == 1, "the pipelined block loop takes 32-key steps");
     static_assert(FP8 || NST >= 3, "bf16 ring: a slot in use, a slot landing, a slot in flight");
     int fill_off = 0;  // bf16: slot that the next DMA step fills
     int ent_v = 0;     // bf16: table entry of that step's block, read one step early
@@ -409,16 +409,20 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
     }
 
-    // S^T [32 keys x 32 rows] = K Q^T of the block in `slot`
-    auto qk = [&](const char* slot, float (&sv)[16]) {
+    // S^T [32 keys x 32 rows] = K Q^T of the block in `slot`, for each of
+    // the wave's 32-row halves
+    auto qk = [&](const char* slot, float (&sv)[NH][16]) {
       bf16x8 ka[NS];
 #pragma unroll
       for (int i = 0; i < NS; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(slot + k_at(i));
-      f32x16 sc = f32x16{};
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mfma32x32x16(ka[i], qb[0][i], sc);
+      for (int hf = 0; hf < NH; ++hf) {
+        f32x16 sc = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sv[j] = sc[j];
+        for (int i = 0; i < NS; ++i) sc = mfma32x32x16(ka[i], qb[hf][i], sc);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sv[hf][j] = sc[j];
+      }
     };
     // Scores of a block to base-2 units (soft-capped first when the cap is
     // on); returns the row maximum. (Written as a product rather than a copy,
@@ -449,11 +453,11 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     // Hidden keys of the block at kb to -inf (masks of `flashAttention`, kv
     // length, chunk end; by selection, so NaN in unread slots cannot leak);
     // returns the new row maximum in base-2 units.
-    auto mask_scores = [&](float (&sv)[16], int kb) {
+    auto mask_scores = [&](int hf, float (&sv)[16], int kb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float x = visible(0, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? sv[j] : -INFINITY;
+        const float x = visible(hf, kb + 8 * (j >> 2) + 4 * h + (j & 3)) ? sv[j] : -INFINITY;
         sv[j] = x;
         mx = fmaxf(mx, x);
       }
@@ -463,14 +467,22 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     // row's maximum outgrows the reference by more than kRescaleSlack. The
     // rescale runs outside the block loop (below), so inside it the
     // accumulator is only ever an MFMA operand and stays in its registers.
-    auto needs_rescale = [&](float mb) { return __any(mb > m_ref[0] + kRescaleSlack); };
-    auto rescale = [&](float mb) {
-      const float m_new = fmaxf(m_ref[0], mb);
-      const float alpha = m_ref[0] == -INFINITY ? 0.f : fast_exp2(m_ref[0] - m_new);
-      m_ref[0] = m_new;
-      lsum[0] *= alpha;
+    auto needs_rescale = [&](const float (&mb)[NH]) {
+      bool any = false;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) o[0][d] *= alpha;
+      for (int hf = 0; hf < NH; ++hf) any = any || mb[hf] > m_ref[hf] + kRescaleSlack;
+      return __any(any);
+    };
+    auto rescale = [&](const float (&mb)[NH]) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        const float m_new = fmaxf(m_ref[hf], mb[hf]);
+        const float alpha = m_ref[hf] == -INFINITY ? 0.f : fast_exp2(m_ref[hf] - m_new);
+        m_ref[hf] = m_new;
+        lsum[hf] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[hf][d] *= alpha;
+      }
     };
     // Blocks that can hold a key some row of the wave cannot see: those at
     // or past ub_mask_hi (kv length, chunk end, causal diagonal) and those
@@ -491,17 +503,26 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     // are final (capped, masked) and the reference maximum covers them. The
     // iteration runs the next block's QK MFMAs beside this block's softmax
     // VALU work, then this block's PV MFMAs beside the next block's score
-    // epilogue, so the matrix and vector units work at the same time.
-    float sc_cur[16];
+    // epilogue, so the matrix and vector units work at the same time. With
+    // two 32-row halves per wave every K and V^T operand read serves two
+    // MFMAs.
+    float sc_cur[NH][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sc_cur[j] = 0.f;
-    float mb_pending = -INFINITY;
+    for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc_cur[hf][j] = 0.f;
+    float mb_pending[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) mb_pending[hf] = -INFINITY;
     bool pending = false;
     if (n_sub > 0) {
       sync_step(0, lds);
       qk(lds, sc_cur);
-      mb_pending = finish_scores(sc_cur);
-      if (need_mask(0)) mb_pending = mask_scores(sc_cur, c_lo);
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        mb_pending[hf] = finish_scores(sc_cur[hf]);
+        if (need_mask(0)) mb_pending[hf] = mask_scores(hf, sc_cur[hf], c_lo);
+      }
       pending = needs_rescale(mb_pending);
     }
     int ub = 0;
@@ -517,40 +538,44 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         // the two units' work stays in one straight-line block)
         const char* nslot = lds + (has_next ? ns : cs);
         const char* cslot = lds + cs;
-        float mb_next;
+        float mb_next[NH];
         {
           // The iteration in an explicit order (sched_barrier fences keep the
           // compiler's scheduler from regrouping it): the next block's first K
           // reads; the first P pairs of this block while they land; each QK
-          // MFMA followed by a K read KA MFMAs ahead and a share of the
-          // remaining pairs, the last ones by the first V^T reads; each PV
-          // MFMA followed by a share of the next block's score epilogue, with
-          // V^T reads VA MFMAs ahead.
+          // k-step (NH MFMAs) followed by a K read KA k-steps ahead and a
+          // share of the remaining pairs, the last ones by the first V^T
+          // reads; each PV step (NH MFMAs) followed by a share of the next
+          // block's score epilogue, with V^T reads VA steps ahead.
           constexpr int KA = NS / 2;  // K reads ahead of their MFMA
           bf16x8 ka[NS];
 #pragma unroll
           for (int i = 0; i < KA; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i));
           __builtin_amdgcn_sched_barrier(0);
-          const float negm = m_ref[0] == -INFINITY ? 0.f : -m_ref[0];
-          bf16x8 pb[2];
-          // P = 2^(score - reference) for scores 2jp, 2jp+1, packed to bf16;
-          // the row sum is taken in f32 over the unrounded values (the LSE
-          // needs them: one dominant key rounded to bf16 moves it by up to
-          // 2^-8)
-          auto p_pair = [&](int jp) {
-            const float p0 = fast_exp2(kLate ? __builtin_fmaf(sc_cur[2 * jp], cmul, negm) : sc_cur[2 * jp] + negm);
-            const float p1 =
-                fast_exp2(kLate ? __builtin_fmaf(sc_cur[2 * jp + 1], cmul, negm) : sc_cur[2 * jp + 1] + negm);
-            lsum[0] += p0 + p1;
-            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
-            pb[jp >> 2][2 * (jp & 3)] = pair[0];
-            pb[jp >> 2][2 * (jp & 3) + 1] = pair[1];
-          };
-          constexpr int PRE = 2;  // pairs before the first QK MFMA
+          float negm[NH];
 #pragma unroll
-          for (int jp = 0; jp < PRE; ++jp) p_pair(jp);
+          for (int hf = 0; hf < NH; ++hf) negm[hf] = m_ref[hf] == -INFINITY ? 0.f : -m_ref[hf];
+          bf16x8 pb[NH][2];
+          // P = 2^(score - reference) for scores 2jp, 2jp+1 of half hf
+          // (pair index q = 8 hf + jp), packed to bf16; the row sum is taken in
+          // f32 over the unrounded values (the LSE needs them: one dominant key
+          // rounded to bf16 moves it by up to 2^-8)
+          auto p_pair = [&](int q) {
+            const int hf = q >> 3, jp = q & 7;
+            const float s0 = sc_cur[hf][2 * jp], s1 = sc_cur[hf][2 * jp + 1];
+            const float p0 = fast_exp2(kLate ? __builtin_fmaf(s0, cmul, negm[hf]) : s0 + negm[hf]);
+            const float p1 = fast_exp2(kLate ? __builtin_fmaf(s1, cmul, negm[hf]) : s1 + negm[hf]);
+            lsum[hf] += p0 + p1;
+            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
+            pb[hf][jp >> 2][2 * (jp & 3)] = pair[0];
+            pb[hf][jp >> 2][2 * (jp & 3) + 1] = pair[1];
+          };
+          constexpr int NPP = 8 * NH;  // P pairs of the block
+          constexpr int PRE = 2;       // pairs before the first QK MFMA
+#pragma unroll
+          for (int q = 0; q < PRE; ++q) p_pair(q);
           __builtin_amdgcn_sched_barrier(0);
-          // O^T += V^T P^T: MFMA m = ks * NDB + d takes key half ks, 32 rows of d
+          // O^T += V^T P^T: step m = ks * NDB + d takes key half ks, 32 rows of d
           constexpr int NM = 2 * NDB;
           constexpr int VA = 3;  // V^T reads ahead of their MFMA
           static_assert(NS >= VA && NM > VA, "read-ahead depth");
@@ -561,36 +586,49 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
             const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16*>(cslot + (16 * ks + 8) * RB + v_at(d)));
             va[m] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           };
-          f32x16 sc_next = f32x16{};
+          f32x16 sc_next[NH];
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) sc_next[hf] = f32x16{};
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
-            sc_next = mfma32x32x16(ka[i], qb[0][i], sc_next);
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) sc_next[hf] = mfma32x32x16(ka[i], qb[hf][i], sc_next[hf]);
             if (i + KA < NS) ka[i + KA] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i + KA));
 #pragma unroll
-            for (int jp = PRE + ((8 - PRE) * i) / NS; jp < PRE + ((8 - PRE) * (i + 1)) / NS; ++jp) p_pair(jp);
+            for (int q = PRE + ((NPP - PRE) * i) / NS; q < PRE + ((NPP - PRE) * (i + 1)) / NS; ++q) p_pair(q);
             if (i >= NS - VA) read_va(i - (NS - VA));
             __builtin_amdgcn_sched_barrier(0);
           }
-          float mx = -INFINITY;
+          float mx[NH];
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) mx[hf] = -INFINITY;
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
             if (m + VA < NM) read_va(m + VA);
-            o[0][m % NDB] = mfma32x32x16(va[m], pb[m / NDB], o[0][m % NDB]);
 #pragma unroll
-            for (int j = (16 * m) / NM; j < (16 * (m + 1)) / NM; ++j) {
-              sc_cur[j] = to_base2(sc_next[j]);
-              mx = fmaxf(mx, sc_cur[j]);
+            for (int hf = 0; hf < NH; ++hf)
+              o[hf][m % NDB] = mfma32x32x16(va[m], pb[hf][m / NDB], o[hf][m % NDB]);
+#pragma unroll
+            for (int e = (16 * NH * m) / NM; e < (16 * NH * (m + 1)) / NM; ++e) {
+              const int hf = e >> 4, j = e & 15;
+              sc_cur[hf][j] = to_base2(sc_next[hf][j]);
+              mx[hf] = fmaxf(mx[hf], sc_cur[hf][j]);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          mb_next = row_max(mx);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) mb_next[hf] = row_max(mx[hf]);
         }
         cs = ns;
         if (has_next) {
-          if (need_mask(ub + 1)) mb_next = mask_scores(sc_cur, c_lo + 32 * (ub + 1));
+          if (need_mask(ub + 1)) {
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) mb_next[hf] = mask_scores(hf, sc_cur[hf], c_lo + 32 * (ub + 1));
+          }
           if (needs_rescale(mb_next)) {
             // leave the loop to rescale, then resume at the next block
-            mb_pending = mb_next;
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) mb_pending[hf] = mb_next[hf];
             pending = true;
             ++ub;
             break;
