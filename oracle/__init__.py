@@ -44,6 +44,7 @@ class _Cfg(ctypes.Structure):
         ("soft_cap", ctypes.c_double),
         ("k_scale", ctypes.c_double),
         ("v_scale", ctypes.c_double),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -94,7 +95,8 @@ def default_threads() -> int:
 
 def _cfg(w) -> _Cfg:
     c = w.cfg
-    return _Cfg(
+    sinks = getattr(w, "sinks", None)
+    cfg = _Cfg(
         num_q_tokens=c.num_q_tokens, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
         head_dim=c.head_dim, total_num_pages=c.total_num_pages, page_size=c.page_size,
         max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq, kv_dtype=KV_CODES[c.kv_dtype],
@@ -102,7 +104,13 @@ def _cfg(w) -> _Cfg:
         has_soft_cap=int(c.soft_cap is not None), sm_scale=float(c.sm_scale),
         soft_cap=float(c.soft_cap or 0.0),
         k_scale=1.0 if c.k_scale is None else float(c.k_scale),
-        v_scale=1.0 if c.v_scale is None else float(c.v_scale))
+        v_scale=1.0 if c.v_scale is None else float(c.v_scale), sinks=None)
+    if sinks is not None:
+        # f64 copy of the f32 sink logits, kept alive with the struct
+        cfg._sinks = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32), dtype=np.float64)
+        assert cfg._sinks.shape == (c.num_q_heads,)
+        cfg.sinks = cfg._sinks.ctypes.data
+    return cfg
 
 
 def _ptr(a: np.ndarray):

@@ -27,9 +27,16 @@
  * oracle writes the plain definition out instead: max, exp, sum, weighted
  * sum of V, all over the full visible key set at once.
  *
+ * Attention sinks (optional): one logit per q head that joins its rows'
+ * softmax and takes no value, as the spatial-compiler page's
+ * `flat_softmax_rows_at` takes its `sinks` (gpt-oss's attention sinks): the
+ * row's maximum starts from it and exp(sink - max) joins the denominator. The
+ * sink is compared with the final scores (after scale and soft-cap).
+ *
  * Readings where the page is silent (listed with the design notes):
  *   - the log-sum-exp output, natural log of sum exp(score) over visible keys;
- *   - a row with no visible key gets out = 0 and lse = -inf;
+ *   - a row with no visible key gets out = 0 and lse = -inf (with a sink:
+ *     lse = sink, the log of its own term);
  *   - e4m3fn decode is the OCP FP8 definition (bias 7, subnormals at
  *     exponent 0, S.1111.111 is NaN, no infinities); the page only names the
  *     dtype;
@@ -61,6 +68,7 @@ typedef struct {
   double soft_cap;
   double k_scale; /* 1.0 when absent */
   double v_scale; /* 1.0 when absent */
+  const double* sinks; /* NULL, or one logit per q head [num_q_heads] */
 } oracle_cfg;
 
 /* bf16 bits are the upper half of an IEEE binary32 value. */
@@ -164,11 +172,15 @@ static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pag
     ++n_vis;
   }
   for (int d = 0; d < D; ++d) out_row[d] = 0.0;
+  const int has_sink = c->sinks != NULL;
+  const double sink = has_sink ? c->sinks[n] : -INFINITY;
   if (n_vis == 0) {
-    *lse = -INFINITY;
+    *lse = sink; /* -inf without a sink */
     return 0;
   }
-  double l = 0.0;
+  /* the row's maximum starts from the sink */
+  if (has_sink && sink > m) m = sink;
+  double l = has_sink ? exp(sink - m) : 0.0;
   for (int64_t j = 0; j < kv_len; ++j) {
     if (!key_visible(c, j, pos)) continue;
     double p = exp(sc[j] - m);

@@ -16,6 +16,9 @@ head, a wrong causal offset or GQA index) fails at least one test:
                           slots and table entries the method never reads
 * raggedness            - each sequence alone reproduces its slice
 * dequant scales        - linearity
+* attention sinks       - closed forms (Q = 0; a single visible key), the
+                          log-sum-exp identity against the same rows without
+                          sinks, and sinks at -inf changing nothing
 """
 
 import math
@@ -357,3 +360,69 @@ def test_named_tiny_workload_shape_and_finiteness():
     assert w.cfg.total_num_pages == 32 and w.page_indices.shape == (3, 4)
     o, l = oracle.forward(w)
     assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+# ----------------------------------------------------------------------------- attention sinks
+
+def test_sinks_zero_q_closed_form():
+    """Q = 0: every visible score is 0, so out = mean(V) * n / (n + e^sink) and
+    lse = log(n + e^sink)."""
+    w = _zero_q(wl.with_sinks(wl.random_small(5, max_seqs=4, causal=True, max_q=12, max_extra_kv=40), 5))
+    out, lse = oracle.forward(w)
+    G = w.cfg.num_q_heads // w.cfg.num_kv_heads
+    for s in range(w.n_seqs):
+        q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = int(w.kv_lens[s])
+        v = _seq_kv(w, s, 1)
+        for i in range(ql):
+            n_vis = kvl - ql + i + 1
+            for n in range(w.cfg.num_q_heads):
+                sk = float(w.sinks[n])
+                want = v[n // G, :n_vis].mean(axis=0) * n_vis / (n_vis + math.exp(sk))
+                np.testing.assert_allclose(out[q0 + i, n], want, rtol=1e-12, atol=1e-15)
+                assert lse[q0 + i, n] == pytest.approx(np.logaddexp(math.log(n_vis), sk), rel=1e-13, abs=1e-13)
+
+
+def test_sinks_single_visible_key():
+    """Window 1: one visible key with score x, so out = V * sigmoid(x - sink)
+    and lse = logaddexp(x, sink)."""
+    w = wl.with_sinks(wl.random_small(8, max_seqs=4, window=1, causal=True), 8)
+    out, lse = oracle.forward(w)
+    G = w.cfg.num_q_heads // w.cfg.num_kv_heads
+    q = _q_f64(w)
+    for s in range(w.n_seqs):
+        q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = int(w.kv_lens[s])
+        k = _seq_kv(w, s, 0); v = _seq_kv(w, s, 1)
+        for i in range(ql):
+            p = kvl - ql + i
+            for n in range(w.cfg.num_q_heads):
+                x = float(np.dot(q[q0 + i, n], k[n // G, p])) * w.cfg.sm_scale
+                sk = float(w.sinks[n])
+                np.testing.assert_allclose(out[q0 + i, n], v[n // G, p] / (1.0 + math.exp(sk - x)),
+                                           rtol=1e-12, atol=1e-15)
+                assert lse[q0 + i, n] == pytest.approx(np.logaddexp(x, sk), rel=1e-13, abs=1e-13)
+
+
+@pytest.mark.parametrize("kv_dtype,cap", [(wl.KV_BF16, None), (wl.KV_FP8, 30.0)])
+def test_sinks_logsumexp_identity(kv_dtype, cap):
+    """With a sink the row is the same softmax over one more logit that carries
+    no value: lse' = logaddexp(lse, sink) and out' = out * e^(lse - lse')."""
+    base = wl.random_small(14, max_seqs=4, causal=True, kv_dtype=kv_dtype, soft_cap=cap, max_q=16)
+    o0, l0 = oracle.forward(base)
+    w = wl.with_sinks(wl.random_small(14, max_seqs=4, causal=True, kv_dtype=kv_dtype, soft_cap=cap, max_q=16),
+                      14, mean=0.0, std=3.0)
+    o1, l1 = oracle.forward(w)
+    T = w.valid_tokens()
+    sk = w.sinks.astype(np.float64)[None, :]
+    l_want = np.logaddexp(l0[:T], sk)
+    np.testing.assert_allclose(l1[:T], l_want, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o1[:T], o0[:T] * np.exp(l0[:T] - l_want)[..., None], rtol=1e-12, atol=1e-15)
+
+
+def test_sinks_at_minus_infinity_change_nothing():
+    base = wl.random_small(16, max_seqs=4, causal=True)
+    o0, l0 = oracle.forward(base)
+    w = wl.random_small(16, max_seqs=4, causal=True)
+    w.sinks = np.full(w.cfg.num_q_heads, -np.inf, dtype=np.float32)
+    o1, l1 = oracle.forward(w)
+    T = w.valid_tokens()
+    assert np.array_equal(o0[:T], o1[:T]) and np.array_equal(l0[:T], l1[:T])

@@ -80,6 +80,7 @@ class Workload:
     page_indices: np.ndarray  # int32 [max_num_seqs, pages_per_seq]
     cu_q_lens: np.ndarray     # int32 [max_num_seqs + 1]
     num_seqs: np.ndarray      # int32 [1]
+    sinks: np.ndarray | None = None  # float32 [Hq] attention-sink logits, or none
 
     @property
     def n_seqs(self) -> int:
@@ -271,6 +272,13 @@ def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
     if number == 1:
         kw["total_num_pages"] = 32
     return build(f"cfg{number}", cfg_kw(number), q_lens, kv_lens, seed, rng=rng, **kw)
+
+
+def with_sinks(w: Workload, seed: int, mean: float = 1.0, std: float = 2.0) -> Workload:
+    """w with seeded attention-sink logits, one per q head (N(mean, std^2), f32)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0x51A7]))
+    w.sinks = rng.normal(mean, std, size=w.cfg.num_q_heads).astype(np.float32)
+    return w
 
 
 def random_small(seed: int, *, max_seqs: int = 4, head_dim: int = 64,
