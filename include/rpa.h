@@ -106,16 +106,34 @@ rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes);
  * clamped to pages_per_seq and token ranges to num_q_tokens. A row with no
  * visible key gets out = 0 and lse = -inf.
  *
- * The call validates cfg and pointers on the host, then enqueues three kernels
- * (plan, prefill-class tiles, decode-class tiles; a unit split into several
- * key chunks is merged by whichever tile finishes its last chunk) on
- * `stream` and returns.
+ * The call validates cfg and pointers on the host, then enqueues four kernels
+ * on `stream` and returns: plan, prefill-class tiles, decode-class tiles, and
+ * the merge of split decode units (a split prefill unit is merged by
+ * whichever workgroup finishes its last key chunk).
  * Errors: RPA_ERR_INVALID_ARGUMENT, RPA_ERR_UNSUPPORTED,
  * RPA_ERR_WORKSPACE_TOO_SMALL (nothing enqueued), RPA_ERR_HIP (launch failed).
  */
 rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
                        const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rpa_forward with attention sinks: one logit per q head that joins each of
+ * that head's rows' softmax and carries no value (gpt-oss's attention sinks;
+ * the spatial-compiler page's `flat_softmax_rows_at` with `sinks`): the row's
+ * maximum starts from it and exp(sink - max) joins the denominator, so
+ *   out = sum_j e^(s_j) v_j / (sum_j e^(s_j) + e^sink),
+ *   lse = log(sum_j e^(s_j) + e^sink),
+ * with s_j the scores after scale, soft-cap and masks (a row with no visible
+ * key: out = 0, lse = sink).
+ *   sinks   [num_q_heads] float32 in device memory, finite or -inf; NULL: none
+ *           (exactly rpa_forward).
+ * Every other argument, precondition and error is rpa_forward's.
+ */
+rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                             const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                             const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* rpa_status_string(rpa_status status);

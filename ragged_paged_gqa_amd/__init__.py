@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
         CP = ctypes.POINTER(_Config)
         L.rpa_workspace_bytes.argtypes = [CP, ctypes.POINTER(ctypes.c_size_t)]
         L.rpa_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rpa_forward_sinks.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.rpa_status_string.argtypes = [ctypes.c_int]
         L.rpa_status_string.restype = ctypes.c_char_p
         L.rpa_check_metadata.argtypes = [CP, P, P, P, ctypes.c_int32]
@@ -109,15 +110,16 @@ def lib() -> ctypes.CDLL:
         L.rpa_debug_decode_fp8.argtypes = [P, P, ctypes.c_int32, P]
         L.rpa_profile_begin.argtypes = [ctypes.c_int32]
         L.rpa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
-        for f in ("rpa_workspace_bytes", "rpa_forward", "rpa_check_metadata", "rpa_plan", "rpa_plan_layout",
+        for f in ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_check_metadata", "rpa_plan",
+                  "rpa_plan_layout",
                   "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
 
 
-EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_status_string", "rpa_check_metadata", "rpa_plan",
-           "rpa_plan_layout", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
+EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_status_string", "rpa_check_metadata",
+           "rpa_plan", "rpa_plan_layout", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
 KERNELS = ("plan", "prefill", "decode")
 
@@ -189,13 +191,14 @@ def alloc_workspace(cfg: Config, device=None) -> torch.Tensor:
 
 
 def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config, *, out=None, lse=None,
-            workspace=None, want_lse: bool = True, stream=None):
+            workspace=None, want_lse: bool = True, stream=None, sinks=None):
     """Ragged paged attention. Returns (out, lse) as torch tensors on the device.
 
     q [T, Hq, D] bf16; kv_pages [P, page, 2*Hkv, D] bf16 or fp8 e4m3fn (uint8
     storage accepted); kv_lens [S], page_indices [S, pps], cu_q_lens [S+1],
     num_seqs [1]: int32 device tensors. Rows of padding tokens keep whatever
-    `out`/`lse` held.
+    `out`/`lse` held. `sinks`: optional float32 device tensor [Hq] of
+    attention-sink logits (rpa_forward_sinks).
     """
     _check_inputs(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs)
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
@@ -211,11 +214,21 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
     if workspace is None:
         workspace = alloc_workspace(cfg, q.device)
     c = cfg.to_c()
-    st = lib().rpa_forward(ctypes.byref(c), q.data_ptr(), kv_pages.data_ptr(), kv_lens.data_ptr(),
-                           page_indices.data_ptr(), cu_q_lens.data_ptr(), num_seqs.data_ptr(), out.data_ptr(),
-                           lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), _stream_ptr(stream))
-    _check(st, "rpa_forward")
+    if sinks is None:
+        st = lib().rpa_forward(ctypes.byref(c), q.data_ptr(), kv_pages.data_ptr(), kv_lens.data_ptr(),
+                               page_indices.data_ptr(), cu_q_lens.data_ptr(), num_seqs.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+        _check(st, "rpa_forward")
+    else:
+        if not (sinks.is_cuda and sinks.is_contiguous() and sinks.dtype == torch.float32 and sinks.numel() == Hq):
+            raise ValueError("sinks: expected a contiguous float32 CUDA tensor [Hq]")
+        st = lib().rpa_forward_sinks(ctypes.byref(c), q.data_ptr(), kv_pages.data_ptr(), kv_lens.data_ptr(),
+                                     page_indices.data_ptr(), cu_q_lens.data_ptr(), num_seqs.data_ptr(),
+                                     sinks.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(stream))
+        _check(st, "rpa_forward_sinks")
     return out, lse
 
 

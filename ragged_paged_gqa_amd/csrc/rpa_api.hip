@@ -286,6 +286,14 @@ static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspa
 rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
                        const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return rpa_forward_sinks(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, nullptr, out, lse, workspace,
+                           workspace_bytes, stream);
+}
+
+rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                             const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                             const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (!q || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs || !out)
     return RPA_ERR_INVALID_ARGUMENT;
   Params p;
@@ -300,6 +308,7 @@ rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_page
   p.num_seqs = num_seqs;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
+  p.sinks = sinks;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = nullptr;
   {

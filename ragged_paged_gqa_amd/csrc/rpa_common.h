@@ -133,6 +133,7 @@ struct Params {
   int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
   int32_t target_dec_items, target_pf_items;
   int32_t dec_waves;         // waves of the decode launch (the stream-K split)
+  const float* sinks;        // [Hq] attention-sink logits, or null
   // numerics
   float sm_scale;      // sm_scale * k_scale
   float soft_cap;      // > 0: on
@@ -147,6 +148,29 @@ struct Params {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Final statistics of a row from its reference maximum m (base-2 units, -inf
+// while no key was seen) and its sum l of 2^(score - m): the factor that
+// normalises the row's accumulated O (v_scale folded in) and the row's
+// log-sum-exp (natural log). An attention sink (`sink`: a logit in
+// natural-log units, compared with the scaled and capped scores; null: none)
+// joins the maximum and the denominator and carries no value, as the
+// spatial-compiler page's `flat_softmax_rows_at` takes its `sinks`. Without a
+// sink this is v_scale / l and (m + log2 l) ln 2 exactly.
+__device__ __forceinline__ void row_final(float m, float l, float v_scale, const float* sink, float& inv,
+                                          float& lse) {
+  const float sb = sink ? *sink * 1.4426950408889634f : -INFINITY;
+  const float mf = fmaxf(m, sb);
+  if (mf == -INFINITY || !(l > 0.f || sb > -INFINITY)) {
+    inv = 0.f;
+    lse = -INFINITY;
+    return;
+  }
+  const float a = l > 0.f ? fast_exp2(m - mf) : 0.f;
+  const float lt = l * a + (sb > -INFINITY ? fast_exp2(sb - mf) : 0.f);
+  inv = v_scale * a / lt;
+  lse = (mf + fast_log2(lt)) * 0.6931471805599453f;
+}
 
 // Soft-cap in base-2 units: for a raw score s, log2(e) * c * tanh(scale * s /
 // c), as c' - 2c' / (1 + e^(2 scale s / c)) with c' = c log2(e): one exp2 and

@@ -459,8 +459,14 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
   // Result of the current item: bf16 out + lse, or an f32 partial + lse.
   auto finish_item = [&]() {
     const float l_row = wave_sum_xor16_32(lsum);
-    const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
-    const float lse_v = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
+    float inv, lse_v;
+    if (C.nch == 1) {
+      // the whole row: the sink (if any) joins it here
+      row_final(m_ref, l_row, p.v_scale, p.sinks ? p.sinks + qh : nullptr, inv, lse_v);
+    } else {
+      // a chunk's partial; the combine kernel adds the sink
+      row_final(m_ref, l_row, p.v_scale, nullptr, inv, lse_v);
+    }
     if (!rvalid) return;
     if (C.nch == 1) {
       uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
@@ -594,6 +600,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
     if (U.nch == 1) continue;  // its item wrote the rows
     if (U.nch == 0) {
       // no visible key (only outside the data preconditions): out 0, lse -inf
+      // (with a sink: lse = the sink, its own term)
       int q0, ql;
       seq_tokens(p, U.seq, q0, ql);
       for (int e = lane; e < U.nrows * (D / 4); e += 64) {
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
         const int t = prow / p.G;
         const int qh = U.kv_head * p.G + (prow - t * p.G);
         *reinterpret_cast<u32x2*>(p.out + ((int64_t)(q0 + t) * p.Hq + qh) * D + 4 * (e % (D / 4))) = u32x2{0u, 0u};
-        if (p.lse && e % (D / 4) == 0) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = -INFINITY;
+        if (p.lse && e % (D / 4) == 0) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = p.sinks ? p.sinks[qh] : -INFINITY;
       }
       continue;
     }

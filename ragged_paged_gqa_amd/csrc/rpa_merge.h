@@ -10,7 +10,9 @@
 //   O = sum_c exp(L_c - L) * O_c,
 // summed in chunk order, so the result does not depend on which workgroup
 // merges or on timing. A row whose chunks all saw no key (every L_c = -inf)
-// gets O = 0 and L = -inf.
+// gets O = 0 and L = -inf. An attention sink (one logit per q head) is one
+// more term of the sum that carries no value: it joins max_c L_c and the sum
+// here, and never the chunks' partials.
 //
 // Two phases, both fully parallel over the cooperating threads: (A) per row,
 // the max and the normalising sum of the chunk LSEs (kept in LDS, the row's
@@ -33,19 +35,20 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
   const float* lse_base = plse + (int64_t)u.item0 * slot_rows;
   // phase A: per-row max and 1 / sum of exp(L_c - max)
   for (int r = tid; r < u.nrows; r += nt) {
-    float mx = -INFINITY;
+    const int prow = u.row0 + r;
+    const int t = prow / p.G;
+    const int qh = u.kv_head * p.G + (prow - t * p.G);
+    const float sink = p.sinks ? p.sinks[qh] : -INFINITY;
+    float mx = sink;
     for (int c = 0; c < u.nch; ++c) mx = fmaxf(mx, load_coherent(lse_base + (int64_t)c * slot_rows + r));
     float wsum = 0.f;
-    if (mx != -INFINITY)
+    if (mx != -INFINITY) {
       for (int c = 0; c < u.nch; ++c) wsum += expf(load_coherent(lse_base + (int64_t)c * slot_rows + r) - mx);
+      if (sink != -INFINITY) wsum += expf(sink - mx);
+    }
     stat[2 * r] = mx;
     stat[2 * r + 1] = wsum > 0.f ? 1.0f / wsum : 0.f;
-    if (p.lse) {
-      const int prow = u.row0 + r;
-      const int t = prow / p.G;
-      const int qh = u.kv_head * p.G + (prow - t * p.G);
-      p.lse[(int64_t)(q0 + t) * p.Hq + qh] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
-    }
+    if (p.lse) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
   }
   sync();
   // phase B: out[row, 4 elements] = sum_c exp(L_c - max) / sum * O_c[row, 4 elements]

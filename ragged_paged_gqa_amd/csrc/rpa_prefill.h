@@ -644,8 +644,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
       const float l_row = sum_xor32(lsum[hf]);
-      const float inv = l_row > 0.f ? p.v_scale / l_row : 0.f;
-      const float lse_v = l_row > 0.f ? (m_ref[hf] + fast_log2(l_row)) * kLn2 : -INFINITY;
+      float inv, lse_v;
+      // a whole row takes its sink (if any) here; a chunk's partial leaves it
+      // to the merge
+      row_final(m_ref[hf], l_row, p.v_scale, (u.nch == 1 && p.sinks) ? p.sinks + qh[hf] : nullptr, inv, lse_v);
       if (!rvalid[hf]) continue;
       if (u.nch == 1) {
         uint16_t* op = p.out + ((int64_t)tok[hf] * p.Hq + qh[hf]) * D + 4 * h;

@@ -46,12 +46,13 @@ class Device:
         self.page_indices = torch.from_numpy(w.page_indices).to(device)
         self.cu_q_lens = torch.from_numpy(w.cu_q_lens).to(device)
         self.num_seqs = torch.from_numpy(w.num_seqs).to(device)
+        self.sinks = None if w.sinks is None else torch.from_numpy(np.ascontiguousarray(w.sinks)).to(device)
         self.workspace = rpa.alloc_workspace(self.cfg)
 
     def run(self, out=None, lse=None, want_lse=True):
         out, lse = rpa.forward(self.q, self.kv, self.kv_lens, self.page_indices, self.cu_q_lens,
                                self.num_seqs, self.cfg, out=out, lse=lse, workspace=self.workspace,
-                               want_lse=want_lse)
+                               want_lse=want_lse, sinks=self.sinks)
         torch.cuda.synchronize()
         return out, lse
 
