@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sinks", action="store_true",
+                    help="attach seeded attention-sink logits (one per q head) and call rpa_forward_sinks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
@@ -216,6 +218,8 @@ def main():
     log(f"[bench] generating workload {args.workload}: {wl.WORKLOADS[args.workload]}")
     t0 = time.perf_counter()
     w = wl.named(args.workload)
+    if args.sinks:
+        w = wl.with_sinks(w, args.workload)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
     dev = Device(w)
     work = algorithmic_work(w)
@@ -231,7 +235,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         rpa.forward(dev.q, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs, dev.cfg,
-                    workspace=dev.workspace, out=dev_out(dev), lse=dev_lse(dev))
+                    workspace=dev.workspace, out=dev_out(dev), lse=dev_lse(dev), sinks=dev.sinks)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kms, ncalls = rpa.profile_end()
@@ -273,7 +277,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page table)",
         "config": {"workload": wl.WORKLOADS[args.workload], "num_seqs": w.n_seqs, "query_tokens": T,
                    "num_q_heads": w.cfg.num_q_heads, "num_kv_heads": w.cfg.num_kv_heads,
-                   "head_dim": w.cfg.head_dim, "page_size": w.cfg.page_size},
+                   "head_dim": w.cfg.head_dim, "page_size": w.cfg.page_size,
+                   **({"attention_sinks": True} if args.sinks else {})},
         "kv_hbm_gbs": round(B / step_s / 1e9, 1),
         "tflops": round(F / step_s / 1e12, 2),
         "roofline_frac_step": round(max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / step_s, 4),
