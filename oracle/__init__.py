@@ -1,4 +1,5 @@
-"""CPU f64 oracle for ragged paged GQA attention — test infrastructure.
+"""CPU f64 oracle for ragged paged GQA attention and its KV-cache append —
+test infrastructure.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. It shares no code with the HIP library
@@ -6,8 +7,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``rpa_oracle.c`` (plain C, f64, OpenMP over rows); this module only builds
 it with gcc and marshals numpy arrays.
 
-Pins: the tests in ``tests/test_oracle.py`` tie every part of the oracle to
-something other than itself (closed forms, invariants, library routines).
+Pins: the tests in ``tests/test_oracle.py`` and ``tests/test_oracle_append.py``
+tie every part of the oracle to something other than itself (closed forms,
+invariants, library routines, brute force, a hand-derived placement table).
 """
 
 from __future__ import annotations
@@ -76,9 +78,15 @@ def lib():
         L.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_soft_cap.restype = ctypes.c_double
         L.oracle_soft_cap.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
+        L.oracle_f32_to_e4m3fn.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         P = ctypes.c_void_p
         L.oracle_forward.restype = ctypes.c_int
         L.oracle_forward.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, ctypes.c_int32, P, P, ctypes.c_int]
+        L.oracle_kv_append.restype = ctypes.c_int64
+        L.oracle_kv_append.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, ctypes.c_int32]
         L.oracle_rows.restype = ctypes.c_int
         L.oracle_rows.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, ctypes.c_int32, P, P, ctypes.c_int64,
                                   P, P, P, ctypes.c_int]
@@ -175,3 +183,36 @@ def e4m3fn_to_f64(codes) -> np.ndarray:
 
 def soft_cap(x: float, c: float) -> float:
     return lib().oracle_soft_cap(float(x), float(c))
+
+
+def kv_append(w, k_new, v_new):
+    """The cache after writing k_new / v_new ([T, Hkv, D] bf16 bits) of every
+    query token of w into a copy of w.kv_pages. Returns (kv_pages, skipped):
+    skipped counts tokens whose slot falls outside the page table."""
+    c = w.cfg
+    shape = (c.num_q_tokens, c.num_kv_heads, c.head_dim)
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    assert k_new.shape == shape and v_new.shape == shape
+    kv = np.array(w.kv_pages, copy=True, order="C")
+    _, _, kvl, pi, cu = _inputs(w)
+    cfg = _cfg(w)
+    n = lib().oracle_kv_append(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(kv), _ptr(kvl), _ptr(pi),
+                               _ptr(cu), int(w.num_seqs[0]))
+    if n < 0:
+        raise ValueError("oracle_kv_append rejected the inputs")
+    return kv, int(n)
+
+
+def f32_to_e4m3fn(x) -> np.ndarray:
+    """Element-wise f32 -> e4m3fn code (nearest even, saturating at +-448)."""
+    f = lib().oracle_f32_to_e4m3fn
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint8).reshape(a.shape)
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """Element-wise f32 -> bf16 bits (nearest even)."""
+    f = lib().oracle_f32_to_bf16
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint16).reshape(a.shape)

@@ -253,3 +253,110 @@ int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages,
   }
   return bad ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------
+ * KV-cache append. Not on the pages: the ragged paged attention kernel page
+ * reads caches that already hold every query token's own key. This writes
+ * them, by the same placement rule the page uses for reading (`run` and
+ * `flashAttention`'s row ids): query token i of sequence s sits at key
+ * position kv_len - q_len + i, and key j lives in slot j % page_size of page
+ * page_indices[s, j / page_size], K of kv head h in combined head 2h, V in
+ * 2h+1. A stored value is the inverse of the attention's dequant: the f32
+ * quotient x / scale (IEEE binary32 division, rounded to nearest), then
+ * rounded to the cache type to nearest with ties to even; e4m3fn saturates
+ * at +-448 (it has no infinity), bf16 overflows to +-inf as IEEE rounding
+ * does. NaN inputs give a NaN code.
+ * ------------------------------------------------------------------------ */
+
+/* v rounded to the nearest value of a binary format with `mbits` stored
+ * mantissa bits whose normal exponents start at `emin` (subnormals below),
+ * ties to the even mantissa; no upper limit. Exact in double for the formats
+ * used here. */
+static double round_to_format(double v, int mbits, int emin) {
+  if (v == 0.0 || isinf(v) || isnan(v)) return v;
+  int e;
+  (void)frexp(fabs(v), &e); /* |v| = f * 2^e with f in [0.5, 1) */
+  int ex = e - 1;           /* floor(log2 |v|) */
+  if (ex < emin) ex = emin;
+  const double quantum = ldexp(1.0, ex - mbits);
+  const double n = nearbyint(fabs(v) / quantum); /* default mode: nearest, ties to even */
+  return copysign(n * quantum, v);
+}
+
+/* f32 -> e4m3fn code, round to nearest even, saturating at +-448. */
+uint8_t oracle_f32_to_e4m3fn(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  double r = fabs(round_to_format((double)x, 3, -6));
+  if (r > 448.0) r = 448.0;
+  if (r == 0.0) return sign;
+  int e;
+  (void)frexp(r, &e);
+  const int ex = e - 1;
+  if (ex < -6) return sign | (uint8_t)(r / ldexp(1.0, -9)); /* subnormal: m * 2^-9 */
+  const int m = (int)(r / ldexp(1.0, ex - 3)) - 8;
+  return sign | (uint8_t)(((ex + 7) << 3) | m);
+}
+
+/* f32 -> bf16 bits, round to nearest even; overflow gives +-inf. */
+uint16_t oracle_f32_to_bf16(float x) {
+  uint32_t w;
+  if (isnan(x)) {
+    memcpy(&w, &x, sizeof w);
+    return (uint16_t)((w >> 16) | 0x0040);
+  }
+  double r = round_to_format((double)x, 7, -126);
+  if (fabs(r) >= ldexp(1.0, 128)) r = copysign(INFINITY, r);
+  const float f = (float)r; /* exact: r is a bf16 value or an infinity */
+  memcpy(&w, &f, sizeof w);
+  return (uint16_t)(w >> 16);
+}
+
+/* Cache value of one new element: RN_f32(x / scale) in the cache type. */
+static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_t x_bits, double scale) {
+  uint32_t w = (uint32_t)x_bits << 16;
+  float x;
+  memcpy(&x, &w, sizeof x);
+  const float y = x / (float)scale;
+  if (c->kv_dtype == ORACLE_KV_E4M3FN)
+    ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e4m3fn(y);
+  else
+    ((uint16_t*)kv_pages)[idx] = oracle_f32_to_bf16(y);
+}
+
+/* Writes k_new / v_new [num_q_tokens, Hkv, D] (bf16 bits) of every query
+ * token of the first num_seqs sequences into kv_pages. A token whose key
+ * position or page falls outside the table (a broken precondition) is not
+ * written. Returns the number of such tokens, or -1 for a bad argument. */
+int64_t oracle_kv_append(const oracle_cfg* c, const uint16_t* k_new, const uint16_t* v_new, void* kv_pages,
+                         const int32_t* kv_lens, const int32_t* page_indices, const int32_t* cu_q_lens,
+                         int32_t num_seqs) {
+  if (num_seqs < 0 || num_seqs > c->max_num_seqs || c->num_kv_heads <= 0) return -1;
+  const int Hkv = c->num_kv_heads, D = c->head_dim;
+  int64_t skipped = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t q0 = cu_q_lens[s], q_len = (int64_t)cu_q_lens[s + 1] - q0;
+    for (int64_t i = 0; i < q_len; ++i) {
+      const int64_t t = q0 + i;
+      const int64_t pos = (int64_t)kv_lens[s] - q_len + i;
+      if (t < 0 || t >= c->num_q_tokens || pos < 0 || pos >= (int64_t)c->pages_per_seq * c->page_size) {
+        ++skipped;
+        continue;
+      }
+      const int32_t page = page_indices[(int64_t)s * c->pages_per_seq + pos / c->page_size];
+      if (page < 0 || page >= c->total_num_pages) {
+        ++skipped;
+        continue;
+      }
+      const int64_t slot = (int64_t)page * c->page_size + pos % c->page_size;
+      for (int h = 0; h < Hkv; ++h)
+        for (int d = 0; d < D; ++d) {
+          const int64_t src = (t * Hkv + h) * D + d;
+          const int64_t dst_k = (slot * 2 * Hkv + 2 * h) * D + d;
+          store_elem(c, kv_pages, dst_k, k_new[src], c->k_scale);
+          store_elem(c, kv_pages, dst_k + D, v_new[src], c->v_scale);
+        }
+    }
+  }
+  return skipped;
+}

@@ -305,3 +305,40 @@ def random_small(seed: int, *, max_seqs: int = 4, head_dim: int = 64,
                  total_num_pages=pages_needed + int(rng.integers(0, 4)),
                  max_num_seqs=S + int(rng.integers(0, 2)),
                  num_q_tokens=int(q_lens.sum()) + int(rng.integers(0, 3)) or 1)
+
+
+# ----------------------------------------------------------------------------
+# inputs of the kv-cache append
+
+def from_tables(cfg_kw: dict, q_lens, kv_lens, tables, seed: int, *, total_num_pages: int,
+                max_num_seqs: int | None = None, num_q_tokens: int | None = None,
+                pages_per_seq: int | None = None) -> Workload:
+    """A workload with an explicit page table (one list of page ids per sequence);
+    Q and the cache are drawn from PCG64(seed) as in ``build``."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    S = len(q_lens)
+    max_num_seqs = S if max_num_seqs is None else max_num_seqs
+    pps = pages_per_seq or max(len(t) for t in tables)
+    kw = dict(cfg_kw, pages_per_seq=pps)
+    w = build("tables", kw, q_lens, kv_lens, seed, total_num_pages=total_num_pages,
+              max_num_seqs=max_num_seqs, num_q_tokens=num_q_tokens)
+    w.page_indices[:] = 0
+    for s, t in enumerate(tables):
+        w.page_indices[s, :len(t)] = np.asarray(t, dtype=np.int32)
+    return w
+
+
+def new_kv(w: Workload, seed: int, std: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded new K and V rows for every query token: bf16 bits [T, Hkv, D], N(0, std^2)."""
+    c = w.cfg
+    rng = np.random.Generator(np.random.PCG64([seed, 0xA11E]))
+    shape = (c.num_q_tokens, c.num_kv_heads, c.head_dim)
+    k = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    v = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    return to_bf16_bits(k), to_bf16_bits(v)
+
+
+def finite_bf16_patterns() -> np.ndarray:
+    """Every bf16 bit pattern that encodes a finite value (uint16, ascending)."""
+    b = np.arange(1 << 16, dtype=np.uint32)
+    return b[(b & 0x7F80) != 0x7F80].astype(np.uint16)
