@@ -135,6 +135,35 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
                              const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * KV-cache append: writes every query token's new K and V rows into the
+ * paged cache, in place, before attention reads them. The pages read a cache
+ * that already holds each query token's own key; this is the write that puts
+ * it there, by the placement the ragged paged attention kernel page reads
+ * with (`run` and the row ids of `flashAttention`): query token i of sequence
+ * s (cu_q_lens[s] + i) stands at key position kv_len - q_len + i, which is
+ * slot pos % page_size of page page_indices[s, pos / page_size]; K of kv head
+ * h goes to combined head 2h, V to 2h+1 (`stridedLoadKv`).
+ *   k_new, v_new [num_q_tokens, num_kv_heads, head_dim] q_dtype (bf16)
+ *   kv_pages     [total_num_pages, page_size, 2*num_kv_heads, head_dim]
+ *                kv_dtype, updated in place
+ *   kv_lens, page_indices, cu_q_lens, num_seqs: as rpa_forward (kv_lens
+ *                already counts the new tokens)
+ * Stored value: RN_f32(x / scale) with scale = k_scale for K and v_scale for
+ * V (IEEE binary32 division), rounded to nearest even in kv_dtype; e4m3fn
+ * saturates at +-448, bf16 overflows to +-inf; a NaN input stores a NaN. With
+ * bf16 and both scales 1 this is a bit copy. Device pointers, owned by the
+ * caller; k_new, v_new and kv_pages 16-byte aligned; k_new/v_new must not
+ * overlap kv_pages. Tokens past cu_q_lens[num_seqs] and tokens whose position
+ * or page id falls outside the table (a broken precondition) write nothing;
+ * two tokens that map to one slot race. Enqueues one kernel on `stream`; no
+ * workspace. Errors: RPA_ERR_INVALID_ARGUMENT (null or misaligned pointer,
+ * bad cfg, a scale that is not > 0), RPA_ERR_UNSUPPORTED, RPA_ERR_HIP.
+ */
+rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v_new, void* kv_pages,
+                         const int32_t* kv_lens, const int32_t* page_indices, const int32_t* cu_q_lens,
+                         const int32_t* num_seqs, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* rpa_status_string(rpa_status status);
 

@@ -107,11 +107,12 @@ def lib() -> ctypes.CDLL:
         L.rpa_check_metadata.argtypes = [CP, P, P, P, ctypes.c_int32]
         L.rpa_plan.argtypes = [CP, P, P, P, P, ctypes.c_size_t, P]
         L.rpa_plan_layout.argtypes = [CP, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)]
+        L.rpa_kv_append.argtypes = [CP, P, P, P, P, P, P, P, P]
         L.rpa_debug_decode_fp8.argtypes = [P, P, ctypes.c_int32, P]
         L.rpa_profile_begin.argtypes = [ctypes.c_int32]
         L.rpa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
         for f in ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_check_metadata", "rpa_plan",
-                  "rpa_plan_layout",
+                  "rpa_plan_layout", "rpa_kv_append",
                   "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -119,7 +120,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_status_string", "rpa_check_metadata",
-           "rpa_plan", "rpa_plan_layout", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
+           "rpa_plan", "rpa_plan_layout", "rpa_kv_append", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
 KERNELS = ("plan", "prefill", "decode")
 
@@ -230,6 +231,35 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
                                      _stream_ptr(stream))
         _check(st, "rpa_forward_sinks")
     return out, lse
+
+
+def kv_append(k_new, v_new, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config, *,
+              stream=None):
+    """Write every query token's new K and V rows into kv_pages, in place (rpa_kv_append).
+
+    k_new, v_new [T, Hkv, D] bf16 CUDA tensors; the rest as in `forward`.
+    Returns kv_pages.
+    """
+    T, Hkv, D = cfg.num_q_tokens, cfg.num_kv_heads, cfg.head_dim
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2 and t.numel() == T * Hkv * D):
+            raise ValueError(f"{name}: expected a contiguous 2-byte (bf16) CUDA tensor "
+                             "[num_q_tokens, num_kv_heads, head_dim]")
+    eb = 1 if cfg.kv_dtype == DTYPE_FP8_E4M3FN else 2
+    if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb
+            and kv_pages.numel() == cfg.total_num_pages * cfg.page_size * 2 * Hkv * D):
+        raise ValueError("kv_pages: expected a contiguous CUDA tensor "
+                         "[total_num_pages, page_size, 2*num_kv_heads, head_dim] of the kv dtype")
+    _dev_i32(kv_lens, "kv_lens", cfg.max_num_seqs)
+    _dev_i32(page_indices, "page_indices", cfg.max_num_seqs * cfg.pages_per_seq)
+    _dev_i32(cu_q_lens, "cu_q_lens", cfg.max_num_seqs + 1)
+    _dev_i32(num_seqs, "num_seqs", 1)
+    c = cfg.to_c()
+    st = lib().rpa_kv_append(ctypes.byref(c), k_new.data_ptr(), v_new.data_ptr(), kv_pages.data_ptr(),
+                             kv_lens.data_ptr(), page_indices.data_ptr(), cu_q_lens.data_ptr(), num_seqs.data_ptr(),
+                             _stream_ptr(stream))
+    _check(st, "rpa_kv_append")
+    return kv_pages
 
 
 def plan(kv_lens, cu_q_lens, num_seqs, cfg: Config, workspace=None, stream=None):

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "rpa.h"
+#include "rpa_append.h"
 #include "rpa_common.h"
 #include "rpa_decode.h"
 #include "rpa_plan.h"
@@ -236,6 +237,17 @@ rpa_status launch_plan(const Params& p, hipStream_t st) {
   return check_launch();
 }
 
+template <int D>
+void launch_append(int mode, int grid, hipStream_t st, const AppendParams& p) {
+  const dim3 blk(kApWaves * 64);
+  if (mode == kApFp8)
+    hipLaunchKernelGGL((kv_append_kernel<D, kApFp8>), dim3(grid), blk, 0, st, p);
+  else if (mode == kApCopy)
+    hipLaunchKernelGGL((kv_append_kernel<D, kApCopy>), dim3(grid), blk, 0, st, p);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<D, kApBf16>), dim3(grid), blk, 0, st, p);
+}
+
 __global__ void decode_fp8_kernel(const uint8_t* codes, float* out, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * i >= n) return;
@@ -446,6 +458,51 @@ rpa_status rpa_check_metadata(const rpa_config* cfg, const int32_t* kv_lens, con
   }
   if (cu_q_lens[num_seqs] > cfg->num_q_tokens) return RPA_ERR_METADATA;
   return RPA_OK;
+}
+
+rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v_new, void* kv_pages,
+                         const int32_t* kv_lens, const int32_t* page_indices, const int32_t* cu_q_lens,
+                         const int32_t* num_seqs, void* stream) {
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  if (!k_new || !v_new || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs)
+    return RPA_ERR_INVALID_ARGUMENT;
+  for (const void* a : {k_new, v_new, (const void*)kv_pages})
+    if ((reinterpret_cast<uintptr_t>(a) & 15u) != 0) return RPA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->k_scale > 0.f) || !(cfg->v_scale > 0.f)) return RPA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_q_tokens == 0) return RPA_OK;
+  int cus = 0;
+  if (!device_cus(&cus)) return RPA_ERR_HIP;
+  AppendParams p;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.kv = kv_pages;
+  p.kv_lens = kv_lens;
+  p.page_indices = page_indices;
+  p.cu_q_lens = cu_q_lens;
+  p.num_seqs = num_seqs;
+  p.T = cfg->num_q_tokens;
+  p.Hkv = cfg->num_kv_heads;
+  p.P = cfg->total_num_pages;
+  p.page_size = cfg->page_size;
+  p.max_num_seqs = cfg->max_num_seqs;
+  p.pps = cfg->pages_per_seq;
+  p.k_scale = cfg->k_scale;
+  p.v_scale = cfg->v_scale;
+  const int mode = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN             ? kApFp8
+                   : (cfg->k_scale == 1.f && cfg->v_scale == 1.f) ? kApCopy
+                                                                    : kApBf16;
+  // a wave per token, grid-stride beyond 8 workgroups per compute unit
+  int grid = (cfg->num_q_tokens + kApWaves - 1) / kApWaves;
+  if (grid > cus * 8) grid = cus * 8;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (cfg->head_dim) {
+    case 64: launch_append<64>(mode, grid, s, p); break;
+    case 128: launch_append<128>(mode, grid, s, p); break;
+    case 256: launch_append<256>(mode, grid, s, p); break;
+    default: return RPA_ERR_UNSUPPORTED;
+  }
+  return check_launch();
 }
 
 rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, void* stream) {

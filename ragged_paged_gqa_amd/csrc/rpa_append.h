@@ -1,0 +1,144 @@
+// rpa_append.h — writing a step's new K and V rows into the paged cache.
+//
+// The ragged paged attention kernel page (zml platforms/tpu/ragged_paged.zig)
+// reads a cache that already holds every query token's own key; this is the
+// write that puts it there, by the page's own placement rule (`run` and the
+// row ids of `flashAttention`): query token i of sequence s stands at key
+// position kv_len - q_len + i, and key j is slot j % page_size of page
+// page_indices[s, j / page_size], K of kv head h in combined head 2h and V in
+// 2h+1 (`stridedLoadKv`). A stored value inverts the attention's dequant
+// factor: RN_f32(x / scale), rounded to nearest even in the cache type
+// (e4m3fn saturates at +-448; NaN stays NaN).
+//
+// HBM-bound: per token 2*Hkv*D bf16 elements are read and 2*Hkv*D cache
+// elements written, contiguous on both sides. One wave per token; each lane
+// moves 16-byte chunks (8 elements), loads first, then converts and stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rpa_common.h"
+
+namespace rpa {
+
+constexpr int kApWaves = 4;   // waves per workgroup, one token each at a time
+constexpr int kApUnroll = 4;  // 16-byte chunks in flight per lane
+
+// Cache element type of an append launch.
+enum ApMode : int {
+  kApCopy = 0,  // bf16 cache with both scales 1: the quotient is x itself
+  kApBf16 = 1,  // bf16 cache, general scales
+  kApFp8 = 2,   // e4m3fn cache
+};
+
+struct AppendParams {
+  const uint16_t* k_new;  // [T, Hkv, D] bf16 bits
+  const uint16_t* v_new;  // [T, Hkv, D] bf16 bits
+  void* kv;               // [P, page_size, 2*Hkv, D] cache elements
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* cu_q_lens;
+  const int32_t* num_seqs;
+  int T, Hkv, P, page_size, max_num_seqs, pps;
+  float k_scale, v_scale;
+};
+
+// Sequence holding token t: the last s < nseq with cu[s] <= t, given
+// cu[0] <= t. The candidate range shrinks 64-fold per round, one probe per
+// lane; every probe stays inside cu[0, nseq) whatever cu holds.
+__device__ __forceinline__ int ap_seq_of_token(const int32_t* cu, int nseq, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = nseq;
+  while (n > 1) {
+    const int step = (n + 63) >> 6;
+    const int k = lane * step;
+    const bool le = k < n && cu[lo + k] <= t;
+    const int c = __popcll(__ballot(le));  // >= 1: lane 0 probes cu[lo] <= t
+    lo += (c - 1) * step;
+    n = min(step, n - (c - 1) * step);
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float ap_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float ap_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// e4m3fn code pair of two f32 quotients into the low (HI false) or high 16
+// bits of `old`: clamp to the finite range (NaN kept), then the hardware
+// conversion, round to nearest even.
+template <bool HI>
+__device__ __forceinline__ uint32_t ap_fp8_pair(float a, float b, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a == a ? ca : a, b == b ? cb : b, (int)old, HI);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per head row
+  const int lane = threadIdx.x & 63;
+  const int nseq = min(max(p.num_seqs[0], 0), p.max_num_seqs);
+  if (nseq == 0) return;
+  const int t_begin = max(p.cu_q_lens[0], 0);
+  const int t_end = min(p.cu_q_lens[nseq], p.T);
+  const int nch = 2 * p.Hkv * CPR;
+  const int stride = gridDim.x * kApWaves;
+  const int64_t pos_cap = (int64_t)p.pps * p.page_size;
+  // wave-uniform token loop
+  for (int t = t_begin + blockIdx.x * kApWaves + (int)(threadIdx.x >> 6); t < t_end; t += stride) {
+    const int s = ap_seq_of_token(p.cu_q_lens, nseq, t);
+    const int q0 = p.cu_q_lens[s];
+    const int q_len = p.cu_q_lens[s + 1] - q0;
+    const int64_t pos = (int64_t)p.kv_lens[s] - q_len + (t - q0);
+    if (pos < 0 || pos >= pos_cap) continue;
+    const int page = p.page_indices[(int64_t)s * p.pps + pos / p.page_size];
+    if (page < 0 || page >= p.P) continue;
+    const int64_t slot = (int64_t)page * p.page_size + pos % p.page_size;
+    const uint16_t* kr = p.k_new + (int64_t)t * p.Hkv * D;
+    const uint16_t* vr = p.v_new + (int64_t)t * p.Hkv * D;
+    for (int c0 = lane; c0 < nch; c0 += 64 * kApUnroll) {
+      u32x4 x[kApUnroll];
+#pragma unroll
+      for (int u = 0; u < kApUnroll; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nch) {
+          const int ch = c / CPR;  // combined head: 2h = K, 2h+1 = V
+          const uint16_t* src = ((ch & 1) ? vr : kr) + (ch >> 1) * D + (c % CPR) * 8;
+          x[u] = *reinterpret_cast<const u32x4*>(src);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kApUnroll; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= nch) continue;
+        const int64_t e0 = slot * 2 * p.Hkv * D + (int64_t)c * 8;  // first cache element
+        if (MODE == kApCopy) {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = x[u];
+          continue;
+        }
+        const float sc = ((c / CPR) & 1) ? p.v_scale : p.k_scale;
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = ap_bf16_lo(x[u][i]) / sc;
+          f[2 * i + 1] = ap_bf16_hi(x[u][i]) / sc;
+        }
+        if (MODE == kApBf16) {
+          u32x4 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = bf16x2_bits(f[2 * i], f[2 * i + 1]);
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
+        } else {
+          u32x2 y;
+          y[0] = ap_fp8_pair<true>(f[2], f[3], ap_fp8_pair<false>(f[0], f[1], 0u));
+          y[1] = ap_fp8_pair<true>(f[6], f[7], ap_fp8_pair<false>(f[4], f[5], 0u));
+          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.kv) + e0) = y;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace rpa
