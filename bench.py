@@ -2,7 +2,8 @@
 
 One step = one rpa_forward call (plan, prefill-class tiles, decode-class
 tiles, split-KV merge inside them) over one batch of seeded synthetic inputs
-already resident in HBM.
+already resident in HBM; with --append, an rpa_kv_append of the step's new
+K/V rows first.
 The default workload is the decode batch (256 sequences x 1 query token,
 kv_len U[512, 8192], 32 q / 8 kv heads, head_dim 128, page 16, bf16).
 
@@ -178,6 +179,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sinks", action="store_true",
                     help="attach seeded attention-sink logits (one per q head) and call rpa_forward_sinks")
+    ap.add_argument("--append", action="store_true",
+                    help="each step first writes the step's new K/V rows into the cache (rpa_kv_append), "
+                         "then attends; the append kernel is timed on its own as well")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
@@ -227,13 +231,33 @@ def main():
     F = work["decode"][0] + work["prefill"][0]
     B = work["decode"][1] + work["prefill"][1]
 
+    if args.append:
+        k_np, v_np = wl.new_kv(w, 1000 + args.workload)
+        k_new = torch.from_numpy(k_np.view(np.int16)).cuda().view(torch.bfloat16)
+        v_new = torch.from_numpy(v_np.view(np.int16)).cuda().view(torch.bfloat16)
+        stream = torch.cuda.current_stream()
+        ap_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+
+    def append(i=None):
+        if i is not None:
+            ap_ev[i][0].record(stream)
+        rpa.kv_append(k_new, v_new, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs,
+                      dev.cfg, stream=stream)
+        if i is not None:
+            ap_ev[i][1].record(stream)
+
     for _ in range(args.warmup):
+        if args.append:
+            append()
         dev.run()
     torch.cuda.synchronize()
     rpa.profile_begin(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if args.append:
+            append(i)
         rpa.forward(dev.q, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs, dev.cfg,
                     workspace=dev.workspace, out=dev_out(dev), lse=dev_lse(dev), sinks=dev.sinks)
     torch.cuda.synchronize()
@@ -285,6 +309,18 @@ def main():
         "kernel_ms": {k: round(v, 4) for k, v in kmean.items()},
         "roofline": roof,
     }
+    if args.append:
+        # bytes the append must move: each new K and V element read once as
+        # bf16 and written once in the cache type
+        c = w.cfg
+        b_kv = 1 if c.kv_dtype == wl.KV_FP8 else 2
+        ab = float(T * 2 * c.num_kv_heads * c.head_dim * (2 + b_kv))
+        ams = sum(a.elapsed_time(b) for a, b in ap_ev) / args.steps
+        result["config"]["kv_append"] = True
+        result["kv_append"] = {"kernel": "kv_append_kernel", "kernel_ms": round(ams, 5), "algorithmic_bytes": ab,
+                               "achieved": round(ab / (ams * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(ab / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] kv_append {ams * 1e3:.2f} us, {ab / 1e6:.2f} MB")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w)

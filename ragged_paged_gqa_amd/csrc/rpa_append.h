@@ -75,6 +75,58 @@ __device__ __forceinline__ uint32_t ap_fp8_pair(float a, float b, uint32_t old) 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a == a ? ca : a, b == b ? cb : b, (int)old, HI);
 }
 
+// Loads chunks c0, c0+64, ... (kApUnroll of them, those below nch) of one
+// token's K|V rows: chunk c is 8 elements of combined head c / (D/8).
+template <int D>
+__device__ __forceinline__ void load_chunks(u32x4 (&x)[kApUnroll], const uint16_t* kr, const uint16_t* vr, int c0,
+                                            int nch) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int u = 0; u < kApUnroll; ++u) {
+    const int c = c0 + 64 * u;
+    if (c < nch) {
+      const int ch = c / CPR;  // combined head: 2h = K, 2h+1 = V
+      x[u] = *reinterpret_cast<const u32x4*>(((ch & 1) ? vr : kr) + (ch >> 1) * D + (c % CPR) * 8);
+    }
+  }
+}
+
+// Converts and stores the chunks load_chunks fetched; e_slot is the slot's
+// first cache element.
+template <int D, int MODE>
+__device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const AppendParams& p, int64_t e_slot,
+                                             int c0, int nch) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int u = 0; u < kApUnroll; ++u) {
+    const int c = c0 + 64 * u;
+    if (c >= nch) continue;
+    const int64_t e0 = e_slot + (int64_t)c * 8;
+    if (MODE == kApCopy) {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = x[u];
+      continue;
+    }
+    const float sc = ((c / CPR) & 1) ? p.v_scale : p.k_scale;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = ap_bf16_lo(x[u][i]) / sc;
+      f[2 * i + 1] = ap_bf16_hi(x[u][i]) / sc;
+    }
+    if (MODE == kApBf16) {
+      u32x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = bf16x2_bits(f[2 * i], f[2 * i + 1]);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
+    } else {
+      u32x2 y;
+      y[0] = ap_fp8_pair<true>(f[2], f[3], ap_fp8_pair<false>(f[0], f[1], 0u));
+      y[1] = ap_fp8_pair<true>(f[6], f[7], ap_fp8_pair<false>(f[4], f[5], 0u));
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.kv) + e0) = y;
+    }
+  }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p) {
   constexpr int CPR = D / 8;  // 16-byte chunks per head row
@@ -88,6 +140,11 @@ __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p
   const int64_t pos_cap = (int64_t)p.pps * p.page_size;
   // wave-uniform token loop
   for (int t = t_begin + blockIdx.x * kApWaves + (int)(threadIdx.x >> 6); t < t_end; t += stride) {
+    const uint16_t* kr = p.k_new + (int64_t)t * p.Hkv * D;
+    const uint16_t* vr = p.v_new + (int64_t)t * p.Hkv * D;
+    // the token's first rows are in flight while its slot is looked up
+    u32x4 x[kApUnroll];
+    load_chunks<D>(x, kr, vr, lane, nch);
     const int s = ap_seq_of_token(p.cu_q_lens, nseq, t);
     const int q0 = p.cu_q_lens[s];
     const int q_len = p.cu_q_lens[s + 1] - q0;
@@ -96,47 +153,11 @@ __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p
     const int page = p.page_indices[(int64_t)s * p.pps + pos / p.page_size];
     if (page < 0 || page >= p.P) continue;
     const int64_t slot = (int64_t)page * p.page_size + pos % p.page_size;
-    const uint16_t* kr = p.k_new + (int64_t)t * p.Hkv * D;
-    const uint16_t* vr = p.v_new + (int64_t)t * p.Hkv * D;
-    for (int c0 = lane; c0 < nch; c0 += 64 * kApUnroll) {
-      u32x4 x[kApUnroll];
-#pragma unroll
-      for (int u = 0; u < kApUnroll; ++u) {
-        const int c = c0 + 64 * u;
-        if (c < nch) {
-          const int ch = c / CPR;  // combined head: 2h = K, 2h+1 = V
-          const uint16_t* src = ((ch & 1) ? vr : kr) + (ch >> 1) * D + (c % CPR) * 8;
-          x[u] = *reinterpret_cast<const u32x4*>(src);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kApUnroll; ++u) {
-        const int c = c0 + 64 * u;
-        if (c >= nch) continue;
-        const int64_t e0 = slot * 2 * p.Hkv * D + (int64_t)c * 8;  // first cache element
-        if (MODE == kApCopy) {
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = x[u];
-          continue;
-        }
-        const float sc = ((c / CPR) & 1) ? p.v_scale : p.k_scale;
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = ap_bf16_lo(x[u][i]) / sc;
-          f[2 * i + 1] = ap_bf16_hi(x[u][i]) / sc;
-        }
-        if (MODE == kApBf16) {
-          u32x4 y;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = bf16x2_bits(f[2 * i], f[2 * i + 1]);
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
-        } else {
-          u32x2 y;
-          y[0] = ap_fp8_pair<true>(f[2], f[3], ap_fp8_pair<false>(f[0], f[1], 0u));
-          y[1] = ap_fp8_pair<true>(f[6], f[7], ap_fp8_pair<false>(f[4], f[5], 0u));
-          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.kv) + e0) = y;
-        }
-      }
+    for (int c0 = lane;;) {
+      store_chunks<D, MODE>(x, p, slot * 2 * p.Hkv * D, c0, nch);
+      c0 += 64 * kApUnroll;
+      if (c0 >= nch) break;
+      load_chunks<D>(x, kr, vr, c0, nch);
     }
   }
 }
