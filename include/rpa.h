@@ -229,17 +229,18 @@ rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, 
 /*
  * Event timing for benchmarks. rpa_profile_begin(max_calls) makes the next
  * max_calls rpa_forward calls (process-wide) record HIP events on their
- * stream before and after each of their three kernels (plan, prefill-class
- * tiles, decode-class tiles). rpa_profile_end waits for the last recorded
- * event and returns, per kernel, the elapsed milliseconds summed over the
- * recorded calls, and how many calls were recorded; it then releases the
+ * stream before and after each of their four kernels (plan, prefill-class
+ * tiles, decode-class tiles, merge of split decode units). rpa_profile_end
+ * waits for the last recorded event and returns in kernel_ms[0..3], per
+ * kernel in that order, the elapsed milliseconds summed over the recorded
+ * calls, and how many calls were recorded; it then releases the
  * events. Events are created in rpa_profile_begin, never on the forward path.
  * Not meant for concurrent forward calls from several threads.
  * Errors: RPA_ERR_INVALID_ARGUMENT (bad count, nested begin, end without
  * begin), RPA_ERR_HIP.
  */
 rpa_status rpa_profile_begin(int32_t max_calls);
-rpa_status rpa_profile_end(float kernel_ms[3], int32_t* n_calls);
+rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls);
 
 #ifdef __cplusplus
 }

@@ -122,7 +122,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_status_string", "rpa_check_metadata",
            "rpa_plan", "rpa_plan_layout", "rpa_kv_append", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
-KERNELS = ("plan", "prefill", "decode")
+KERNELS = ("plan", "prefill", "decode", "combine")
 
 
 def _check(status: int, what: str) -> None:

@@ -183,7 +183,8 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
 
 rpa_status check_launch() { return hipGetLastError() == hipSuccess ? RPA_OK : RPA_ERR_HIP; }
 
-// Optional event timing of the four launches of each call (for benchmarks).
+// Optional event timing of the four launches of each call (for benchmarks):
+// events before plan, prefill, decode and combine, and after combine.
 struct Profiler {
   std::mutex mu;
   bool on = false;
@@ -191,7 +192,7 @@ struct Profiler {
   int n_calls = 0;
   std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
 };
-constexpr int kProfEvents = 4;
+constexpr int kProfEvents = 5;
 Profiler g_prof;
 
 void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
@@ -221,13 +222,14 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     else
       hipLaunchKernelGGL((decode_kernel<D, FP8, false>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    prof_record(ev, 3, st);
     // merge of the split decode units (a wave per unit, grid-stride)
     int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
     if (cgrid > cus * 4) cgrid = cus * 4;
     if (cgrid < 1) cgrid = 1;
     hipLaunchKernelGGL((combine_kernel<D>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 3, st);
+    prof_record(ev, 4, st);
   }
   return RPA_OK;
 }
@@ -359,7 +361,7 @@ rpa_status rpa_profile_begin(int32_t max_calls) {
   return RPA_OK;
 }
 
-rpa_status rpa_profile_end(float kernel_ms[3], int32_t* n_calls) {
+rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
   if (!kernel_ms || !n_calls) return RPA_ERR_INVALID_ARGUMENT;
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on) return RPA_ERR_INVALID_ARGUMENT;

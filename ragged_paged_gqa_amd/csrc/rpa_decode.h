@@ -35,7 +35,8 @@
 //      with ds_read_b64_tr_b16, P^T exactly the S^T result layout. V rows past
 //      kv_len are zeroed first (0 * NaN would otherwise poison the sum).
 // fp8 e4m3fn K/V are widened to bf16 exactly with v_cvt_scalef32_pk_bf16_fp8
-// after the LDS read (V through a small bf16 staging tile); k_scale is folded
+// after the LDS read (V written back as a bf16 tile into its own ring slot,
+// which is refilled only after the transposed reads); k_scale is folded
 // into the score scale and v_scale into the final normalisation. The
 // contraction over head_dim may visit d in any order as long as K and Q use
 // the same one: a lane's 16-byte K piece covers 16 consecutive d for fp8,
@@ -75,19 +76,21 @@ struct DecCfg {
   static constexpr int NI = D / 32;              // 8-wide k-slots of Q^T per lane (16x16x32 k-steps)
   static constexpr int ND = D / 16;              // 16-row blocks of O^T
   static constexpr int NLD = RB / 64;            // 16-byte K pieces per lane
-  // fp8: the bf16 V staging tile. Rows are VST elements apart (288 bytes for
-  // head_dim 128: the transposed reads of 8 keys x 32 bytes cover the 64
-  // banks once) and rows 8..15 sit 16 bytes further on, so that the 16-byte
-  // writes of 16 keys at the same column also cover them once.
-  static constexpr int VST = D + 16;
-  static constexpr int STG = FP8 ? 16 * VST * 2 + 16 : 0;
+  // fp8: V is widened to bf16 in the step's own ring slot once the slot's
+  // raw rows are in registers (16 keys x D bf16 is exactly one slot), and the
+  // slot is refilled after the PV reads. Rows are XOR-swizzled by the key
+  // (sswz), so that the 16-byte writes of 16 keys at one column and the
+  // transposed reads both spread over all banks.
   // bf16: the next item's 16 Q rows (bf16), DMA'd during the current item.
-  // fp8 takes them into registers instead and spends the space on the ring:
-  // its 4 KB steps need three slots to keep as many bytes in flight.
+  // fp8 takes them into registers instead and spends the space on the ring.
   static constexpr int QSLOT = FP8 ? 0 : 16 * D * 2;
-  static constexpr int NST_FIT = (kDecWaveLds - STG - QSLOT) / STAGE;
+  // fp8 head_dim 256 needs more than 256 registers: one wave per SIMD, so
+  // each wave takes twice the LDS
+  static constexpr int BUDGET = (FP8 && D >= 256) ? 2 * kDecWaveLds : kDecWaveLds;
+  static constexpr int NST_FIT = (BUDGET - QSLOT) / STAGE;
   static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 8 ? 8 : NST_FIT);  // ring slots
-  static constexpr int WAVE_LDS = NST * STAGE + STG + QSLOT;
+  static constexpr int WAVE_LDS = NST * STAGE + QSLOT;
+  static_assert(!FP8 || 16 * D * 2 == STAGE, "fp8: the bf16 V tile fills one slot");
   static_assert(REGION % 1024 == 0, "whole 1 KB DMA instructions per region");
   static_assert(WAVE_LDS * kDecWavesPerBlock <= 160 * 1024, "LDS of a workgroup");
   static_assert((NST - 1) * NDMA < 64, "vmcnt range");
@@ -118,6 +121,25 @@ __device__ __forceinline__ int dswz_v(int key) {
   return 2 * ((key / C::RP) & ((C::CPR < 16 ? C::CPR : 16) / 2 - 1));
 }
 
+// fp8: chunk swizzle of a key's K|V segment (2 * D bytes) in a ring slot:
+// the 16 keys' reads of one chunk, and the DMA's writes, cover all banks.
+template <int D>
+__device__ __forceinline__ int dswz_kv(int key) {
+  constexpr int SEG = 2 * D;
+  constexpr int RPS = SEG >= 256 ? 1 : 256 / SEG;
+  constexpr int CPS = SEG / 16 < 16 ? SEG / 16 : 16;
+  return (key / RPS) & (CPS - 1);
+}
+
+// fp8: chunk swizzle of the bf16 V tile staged in a ring slot (rows of 2D
+// bytes, key = row 0..15).
+template <int D>
+__device__ __forceinline__ int sswz(int key) {
+  constexpr int RPS = 2 * D >= 256 ? 1 : 256 / (2 * D);
+  constexpr int CPS = D / 8 < 16 ? D / 8 : 16;
+  return (key / RPS) & (CPS - 1);
+}
+
 // First d of k-slot i for lane group g (K pieces and Q use the same map).
 // bf16: the 16-byte piece i of lane g is d = 32 i + 8 g; fp8: piece j = i / 2
 // of lane g covers d = 64 j + 16 g .. + 15, split in two 8-wide slots.
@@ -144,18 +166,16 @@ template <int D, bool FP8, bool CAP>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8)) void decode_kernel(Params p) {
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
-                NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, VST = Cf::VST,
-                NST = Cf::NST;
+                NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, NST = Cf::NST;
   __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * Cf::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: the loader and item logic stay scalar
   const int col = lane & 15;
   const int g = lane >> 4;
-  char* wl = lds + wave * Cf::WAVE_LDS;       // this wave's LDS: ring slots, then staging, then Q slot
+  char* wl = lds + wave * Cf::WAVE_LDS;       // this wave's LDS: ring slots, then the Q slot
   char* ring = wl;
-  __bf16* stg = reinterpret_cast<__bf16*>(wl + NST * STAGE);
-  __bf16* qs = reinterpret_cast<__bf16*>(wl + NST * STAGE + Cf::STG);
+  __bf16* qs = reinterpret_cast<__bf16*>(wl + NST * STAGE);
   const uint32_t ring_lds = lds_addr_of(ring);
   const uint32_t qs_lds = lds_addr_of(qs);
 
@@ -166,16 +186,27 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
 
   // per-lane DMA source offsets inside a 16-key block (loop-invariant): LDS
   // chunk c of row `key` holds global chunk c ^ swizzle(key)
+  // bf16: the K region (16 rows), then the V region. fp8: every key's K row
+  // and V row are adjacent in memory (combined heads 2h, 2h+1) and move
+  // together, as one 2*RB-byte segment per key, so each DMA instruction reads
+  // whole K|V segments; chunks are swizzled over the segment (dswz_kv).
   uint32_t voff[2][NDR];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int j = 0; j < NDR; ++j) {
-      const int o = 1024 * j + 16 * lane;
-      const int key = o / RB;
-      const int cl = (o % RB) / 16;
-      const int sw = (r == 1 && !FP8) ? dswz_v<D, FP8>(key) : dswz_k<D, FP8>(key);
-      voff[r][j] = (uint32_t)(key * key_stride + r * RB + 16 * (cl ^ sw));
+      if constexpr (FP8) {
+        const int o = 1024 * (r * NDR + j) + 16 * lane;
+        const int key = o / (2 * RB);
+        const int cl = (o % (2 * RB)) / 16;
+        voff[r][j] = (uint32_t)(key * key_stride + 16 * (cl ^ dswz_kv<D>(key)));
+      } else {
+        const int o = 1024 * j + 16 * lane;
+        const int key = o / RB;
+        const int cl = (o % RB) / 16;
+        const int sw = r == 1 ? dswz_v<D, FP8>(key) : dswz_k<D, FP8>(key);
+        voff[r][j] = (uint32_t)(key * key_stride + r * RB + 16 * (cl ^ sw));
+      }
     }
 
   auto wave_sync = [] {
@@ -335,18 +366,21 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
   // V[4g + x/4][16 d + 4 (x%4) .. + 3] and receives V^T[16 d + x][4g .. 4g + 3]
   const int vkey = 4 * g + (col >> 2);
   const int q4 = col & 3;
-  auto stg_row = [](int key) { return key * VST + 8 * (key >> 3); };  // staging row start (elements)
   auto read_ops = [&](int slot, Ops& op) {
     const char* kr = ring + slot * STAGE;
     const char* vr = kr + REGION;
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)
-      op.k[j] = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
     if constexpr (FP8) {
+      // key col's segment: K chunks 0 .. RB/16 - 1, then V
+      const char* seg = kr + col * (2 * RB);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        op.k[j] = *reinterpret_cast<const u32x4*>(seg + 16 * ((4 * j + g) ^ dswz_kv<D>(col)));
+        op.v[j] = *reinterpret_cast<const u32x4*>(seg + 16 * ((RB / 16 + 4 * j + g) ^ dswz_kv<D>(col)));
+      }
+    } else {
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
-        op.v[j] = *reinterpret_cast<const u32x4*>(vr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
-    } else {
+        op.k[j] = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const int chunk = 2 * d + (q4 >> 1);
@@ -358,8 +392,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // One 16-key step: keys [kb, kb + 16).
-  auto compute_step = [&](const Ops& op, int kb_in) {
+  // One 16-key step: keys [kb, kb + 16), its rows in ring slot `slot`.
+  auto compute_step = [&](const Ops& op, int kb_in, int slot) {
     const int kb = __builtin_amdgcn_readfirstlane(kb_in);  // wave-uniform: scalar mask tests
     bf16x8 ka[NI];
 #pragma unroll
@@ -378,25 +412,27 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
     // does the step hold a key that some row of the unit cannot see?
     const bool need_mask = kb + 16 > vis_hi || (p.is_causal && kb + 15 > pos_lo) ||
                            (p.window > 0 && kb <= pos_hi - p.window);
-    float mx = -INFINITY;
+    // the four scores' chains first (independent, so their latencies
+    // overlap), then the masks in one uniform branch
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float x;
       if constexpr (CAP) {
-        x = cap_b2(sc[j]);
+        sc[j] = cap_b2(sc[j]);
       } else {
-        x = sc[j] * sc_mul;
+        sc[j] = sc[j] * sc_mul;
       }
-      if (need_mask) {
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
         const int key = kb + 4 * g + j;
         bool vis = key < vis_hi;
         if (p.is_causal) vis = vis && key <= pos;
         if (p.window > 0) vis = vis && key > pos - p.window;
-        x = vis ? x : -INFINITY;
+        sc[j] = vis ? sc[j] : -INFINITY;
       }
-      sc[j] = x;
-      mx = fmaxf(mx, x);
     }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = wave_max_xor16_32(mx);
     // lazily moved reference maximum
     if (__any(mx > m_ref + kDecSlack)) {
@@ -408,16 +444,17 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       for (int d = 0; d < ND; ++d) o[d] *= alpha;
     }
     const float negm = m_ref == -INFINITY ? 0.f : -m_ref;
-    bf16x4 pb;
+    float pj[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float pj = fast_exp2(sc[j] + negm);
-      lsum += pj;
-      pb[j] = (__bf16)pj;
+      pj[j] = fast_exp2(sc[j] + negm);
+      lsum += pj[j];
     }
+    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{bf16x2_bits(pj[0], pj[1]), bf16x2_bits(pj[2], pj[3])});
 
     if constexpr (FP8) {
-      // widen V to bf16 through the staging tile; rows past kv_len become 0
+      // widen V to bf16 (rows past kv_len become 0) and stage it for the
+      // transposed reads
       bf16x8 vw[2 * NLD];
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
@@ -430,16 +467,18 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
           for (int j = 0; j < 2 * NLD; ++j) vw[j] = bf16x8{};
         }
       }
+      // the slot's raw rows are in registers: it takes the bf16 tile
+      char* st = ring + slot * STAGE;
 #pragma unroll
       for (int j = 0; j < 2 * NLD; ++j)
-        *reinterpret_cast<bf16x8*>(stg + stg_row(col) + slot_d<FP8>(j, g)) = vw[j];
+        *reinterpret_cast<bf16x8*>(st + col * (2 * D) + 16 * ((slot_d<FP8>(j, g) / 8) ^ sswz<D>(col))) = vw[j];
       wave_sync();
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16x4 a = lds_read_tr16(stg + stg_row(vkey) + 16 * d + 4 * q4);
+        const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(
+            st + vkey * (2 * D) + 16 * ((2 * d + (q4 >> 1)) ^ sswz<D>(vkey)) + 8 * (q4 & 1)));
         o[d] = mfma16x16x16(a, pb, o[d]);
       }
-      wave_sync();
     } else {
       // V of keys at or past vis_hi reads as 0 (0 * NaN would poison the sum)
       const bool partial = kb + 16 > vis_hi;
@@ -538,13 +577,19 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       wait_vmcnt<0>();
     }
     read_ops(n % NST, op);
-    // refill the slot just read
-    if (loading) {
+    // refill the slot just read (fp8: once its bf16 V tile has been read)
+    if (!FP8 && loading) {
       issue_step(L, n % NST);
       ++ahead;
       loader_next();
     }
-    compute_step(op, C.c_lo + steps_done * kDecStepKeys);
+    compute_step(op, C.c_lo + steps_done * kDecStepKeys, n % NST);
+    if (FP8 && loading) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_step(L, n % NST);
+      ++ahead;
+      loader_next();
+    }
     ++steps_done;
     ++q_age;
     --ahead;
