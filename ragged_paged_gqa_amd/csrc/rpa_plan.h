@@ -25,9 +25,10 @@
 //
 // Work split inside the workgroup: sequences are taken in tiles of
 // kPlanThreads, one thread per sequence for the per-sequence counts and for
-// the one block scan that turns them into record offsets, and for writing a
-// decode sequence's units and items; a prefill sequence's row blocks are
-// handled by one wave, a row block per lane.
+// the one block scan that turns them into record offsets; a thread per
+// (decode sequence, kv head) for that unit and its items, staged in LDS and
+// stored in contiguous runs; a wave per prefill sequence, a row block per
+// lane.
 // Divisions by G and by the chunk size use an exact double-precision
 // reciprocal.
 #pragma once
@@ -165,6 +166,16 @@ struct PfInfo {
   int32_t max_nch;   // most chunks of one row block
 };
 
+// A decode sequence of a tile, for the writing of its units and items.
+struct DecSeq {
+  int32_t s, ql, kvl, q0;
+  int32_t blk0, nb;  // its first stream-K block, blocks per kv head
+  int32_t lo16, hi;  // key range of its units
+};
+// Decode items staged in LDS per round of (sequence, kv head) pairs; a round
+// with more items writes the rest directly.
+constexpr int kPlanItemBuf = 1024;
+
 // Offsets of a prefill sequence's records, from the block scan.
 struct PfOffs {
   int32_t unit, item;
@@ -222,6 +233,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ PfInfo pf_info[kPlanThreads];
   __shared__ int32_t sk_start[kPlanMaxDecWaves + 1];
   __shared__ PfOffs pf_offs[kPlanThreads];
+  __shared__ DecSeq dec_seq[kPlanThreads];
+  __shared__ int4 ubuf[kPlanThreads][2];
+  __shared__ int4 ibuf[kPlanItemBuf][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t n = *p.num_seqs;
   n = n < 0 ? 0 : (n > p.S_max ? p.S_max : n);
@@ -365,6 +379,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     }
     int32_t off[kScanN], tot[kScanN];
     block_scan<kScanN>(cnt, off, tot, sh);
+    const int32_t tile_u0 = base[0], tile_i0 = base[2], n_dec_units_tile = tot[0];
 #pragma unroll
     for (int k = 0; k < kScanN; ++k) off[k] += base[k];
 #pragma unroll
@@ -377,47 +392,90 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       for (int x = 0; x < kQueues; ++x) pf_offs[slot].queue[x] = off[5 + x];
     }
 
-    // (c) a thread per decode sequence, head by head: the head's unit and its
-    // items (one per decode wave its blocks fall on)
+    // (c) decode units and items. Each decode sequence of the tile leaves its
+    // metadata in LDS (at its rank among the tile's decode sequences), then a
+    // thread per (sequence, kv head) pair builds that unit and its items (one
+    // per decode wave its blocks fall on) in LDS, a block scan placing the
+    // items, and the whole block copies them out with contiguous 16-byte
+    // stores: the records of consecutive pairs are consecutive in memory, so
+    // the stores of one compute unit stay coalesced.
     if (is_dec) {
       const UnitRange r = unit_range(p, G, ql, kvl, 0, ql * p.G);
       int32_t q0, qlx;
       seq_tokens(p, s, q0, qlx);
-      int32_t ii = off[2];
-      for (int32_t h = 0; h < p.Hkv; ++h) {
-        const int32_t b0 = blk0 + h * nb;
-        int32_t wa = 0;
-        const int32_t nch = sk.n_items(b0, nb, wa);
-        const int32_t ui = off[0] + h;
-        if (ui >= p.max_dec_units) break;
-        Unit u;
-        u.seq = s; u.kv_head = h; u.row0 = 0; u.nrows = ql * p.G;
-        u.kv_lo = r.lo16; u.kv_hi = r.hi; u.nch = nch; u.item0 = ii;
-        p.dec_units[ui] = u;
-        p.unit_done[ui] = 0;
-        int32_t ws = nch > 0 ? sk.start(wa) : 0;
-        for (int32_t c = 0; c < nch; ++c, ++ii) {
-          const int32_t w = wa + c;
-          if (ii >= p.max_dec_items) break;
-          // the unit's blocks inside wave w's range
-          const int32_t we = w + 1 < sk.W ? sk.start(w + 1) : (int32_t)sk.Tb;
-          const int32_t x0 = max(b0, ws);
-          const int32_t x1 = min(b0 + nb, we);
-          DecItem d;
-          d.seq = s; d.kv_head = h;
-          d.c_lo = r.lo16 + 16 * (x0 - b0);
-          d.c_hi = min(r.hi, r.lo16 + 16 * (x1 - b0));
-          d.kvl = kvl; d.q0 = q0; d.ql = ql; d.row0 = 0; d.nrows = ql * p.G;
-          d.nch = nch; d.unit = ui; d.chunk = c; d.wave = w;
-          d.pad[0] = d.pad[1] = d.pad[2] = 0;
-          p.dec_items[ii] = d;
-          // the item holding a wave's first block starts the wave's items
-          if (b0 <= ws) p.dec_wave_first[w] = ii;
-          ws = we;
-        }
-      }
+      dec_seq[(off[0] - tile_u0) / p.Hkv] = DecSeq{s, ql, kvl, q0, blk0, nb, r.lo16, r.hi};
     }
     __syncthreads();
+    {
+      const int32_t npairs = n_dec_units_tile;  // decode sequences of the tile x Hkv
+      int32_t round_i0 = tile_i0;
+      for (int32_t P = 0; P < npairs; P += kPlanThreads) {
+        const int32_t pair = P + tid;
+        const bool valid = pair < npairs;
+        DecSeq ds{};
+        int32_t h = 0, b0 = 0, nch = 0, wa = 0;
+        if (valid) {
+          const int32_t i = pair / p.Hkv;
+          h = pair - i * p.Hkv;
+          ds = dec_seq[i];
+          b0 = ds.blk0 + h * ds.nb;
+          nch = sk.n_items(b0, ds.nb, wa);
+        }
+        int32_t excl[1], tot_i[1];
+        {
+          const int32_t v[1] = {nch};
+          block_scan<1>(v, excl, tot_i, sh);
+        }
+        const int32_t ui = tile_u0 + pair;
+        const int32_t ii0 = round_i0 + excl[0];
+        const int32_t nrows = ds.ql * p.G;
+        if (valid && ui < p.max_dec_units) {
+          // Unit {seq, kv_head, row0, nrows | kv_lo, kv_hi, nch, item0}
+          ubuf[tid][0] = int4{ds.s, h, 0, nrows};
+          ubuf[tid][1] = int4{ds.lo16, ds.hi, nch, ii0};
+          p.unit_done[ui] = 0;
+          int32_t ws = nch > 0 ? sk.start(wa) : 0;
+          for (int32_t c = 0; c < nch; ++c) {
+            const int32_t ii = ii0 + c;
+            const int32_t w = wa + c;
+            if (ii >= p.max_dec_items) break;
+            // the unit's blocks inside wave w's range
+            const int32_t we = w + 1 < sk.W ? sk.start(w + 1) : (int32_t)sk.Tb;
+            const int32_t x0 = max(b0, ws);
+            const int32_t x1 = min(b0 + ds.nb, we);
+            // DecItem {seq, kv_head, c_lo, c_hi | kvl, q0, ql, row0 |
+            //          nrows, nch, unit, chunk | wave, 0, 0, 0}
+            const int4 rec[4] = {int4{ds.s, h, ds.lo16 + 16 * (x0 - b0), min(ds.hi, ds.lo16 + 16 * (x1 - b0))},
+                                 int4{ds.kvl, ds.q0, ds.ql, 0}, int4{nrows, nch, ui, c}, int4{w, 0, 0, 0}};
+            const int32_t loc = ii - round_i0;
+            if (loc < kPlanItemBuf) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) ibuf[loc][k] = rec[k];
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) reinterpret_cast<int4*>(p.dec_items + ii)[k] = rec[k];
+            }
+            // the item holding a wave's first block starts the wave's items
+            if (b0 <= ws) p.dec_wave_first[w] = ii;
+            ws = we;
+          }
+        }
+        __syncthreads();
+        // copy-out: units [tile_u0 + P, + n_u), items [round_i0, + n_i)
+        const int32_t n_u = min(kPlanThreads, npairs - P);
+        for (int32_t k = tid; k < 2 * n_u; k += kPlanThreads) {
+          const int32_t u = tile_u0 + P + k / 2;
+          if (u < p.max_dec_units) reinterpret_cast<int4*>(p.dec_units + u)[k & 1] = ubuf[k / 2][k & 1];
+        }
+        const int32_t n_i = min(tot_i[0], kPlanItemBuf);
+        for (int32_t k = tid; k < 4 * n_i; k += kPlanThreads) {
+          const int32_t it = round_i0 + k / 4;
+          if (it < p.max_dec_items) reinterpret_cast<int4*>(p.dec_items + it)[k & 3] = ibuf[k / 4][k & 3];
+        }
+        round_i0 += tot_i[0];
+        __syncthreads();
+      }
+    }
 
     // (d) a wave per prefill sequence: its units, items and queue entries
     for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
