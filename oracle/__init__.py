@@ -25,7 +25,7 @@ _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_BUILD, "librpa_oracle.so")
 
-KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1}
+KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2}
 
 
 class _Cfg(ctypes.Structure):
@@ -76,6 +76,10 @@ def lib():
         L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_e4m3fn_to_f64.restype = ctypes.c_double
         L.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_to_f64.restype = ctypes.c_double
+        L.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_f32_to_e5m2.restype = ctypes.c_uint8
+        L.oracle_f32_to_e5m2.argtypes = [ctypes.c_float]
         L.oracle_soft_cap.restype = ctypes.c_double
         L.oracle_soft_cap.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
@@ -181,6 +185,12 @@ def e4m3fn_to_f64(codes) -> np.ndarray:
     return np.array([L.oracle_e4m3fn_to_f64(int(x)) for x in b]).reshape(np.shape(codes))
 
 
+def e5m2_to_f64(codes) -> np.ndarray:
+    L = lib()
+    b = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([L.oracle_e5m2_to_f64(int(x)) for x in b]).reshape(np.shape(codes))
+
+
 def soft_cap(x: float, c: float) -> float:
     return lib().oracle_soft_cap(float(x), float(c))
 
@@ -207,6 +217,13 @@ def kv_append(w, k_new, v_new):
 def f32_to_e4m3fn(x) -> np.ndarray:
     """Element-wise f32 -> e4m3fn code (nearest even, saturating at +-448)."""
     f = lib().oracle_f32_to_e4m3fn
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint8).reshape(a.shape)
+
+
+def f32_to_e5m2(x) -> np.ndarray:
+    """Element-wise f32 -> e5m2 code (nearest even, saturating at +-57344)."""
+    f = lib().oracle_f32_to_e5m2
     a = np.asarray(x, dtype=np.float32)
     return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint8).reshape(a.shape)
 

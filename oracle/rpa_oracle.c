@@ -38,8 +38,9 @@
  *   - a row with no visible key gets out = 0 and lse = -inf (with a sink:
  *     lse = sink, the log of its own term);
  *   - e4m3fn decode is the OCP FP8 definition (bias 7, subnormals at
- *     exponent 0, S.1111.111 is NaN, no infinities); the page only names the
- *     dtype;
+ *     exponent 0, S.1111.111 is NaN, no infinities), and e5m2 the OCP one
+ *     with bias 15 and IEEE-style infinities and NaN; the page only names
+ *     the dtypes (`Cfg` kv_dtype, f8e4m3fn and f8e5m2);
  *   - dequantised values are code*scale exactly (f64), not re-rounded to the
  *     q dtype.
  */
@@ -50,6 +51,7 @@
 
 #define ORACLE_KV_BF16 0
 #define ORACLE_KV_E4M3FN 1
+#define ORACLE_KV_E5M2 2
 
 typedef struct {
   int32_t num_q_tokens;
@@ -60,7 +62,7 @@ typedef struct {
   int32_t page_size;
   int32_t max_num_seqs;
   int32_t pages_per_seq;
-  int32_t kv_dtype;       /* ORACLE_KV_BF16 or ORACLE_KV_E4M3FN */
+  int32_t kv_dtype;       /* ORACLE_KV_BF16, ORACLE_KV_E4M3FN or ORACLE_KV_E5M2 */
   int32_t is_causal;      /* 0 or 1 */
   int32_t sliding_window; /* <= 0: no window */
   int32_t has_soft_cap;   /* 0 or 1 */
@@ -96,11 +98,32 @@ double oracle_e4m3fn_to_f64(uint8_t code) {
   return sign ? -mag : mag;
 }
 
+/* OCP FP8 E5M2: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits
+ * (the IEEE-style format: exponent 31 holds the infinities, mantissa 0, and
+ * NaN). Exponent 0 encodes subnormals m/4 * 2^-14; everything else is
+ * (1 + m/4) * 2^(e-15). */
+double oracle_e5m2_to_f64(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 2) & 31;
+  int m = code & 3;
+  double mag;
+  if (e == 31) {
+    if (m != 0) return NAN;
+    mag = INFINITY;
+  } else if (e == 0) {
+    mag = ldexp((double)m / 4.0, -14);
+  } else {
+    mag = ldexp(1.0 + (double)m / 4.0, e - 15);
+  }
+  return sign ? -mag : mag;
+}
+
 /* Soft-cap of the kernel page's `Cfg`/`flashAttention`: c * tanh(x / c). */
 double oracle_soft_cap(double x, double c) { return c * tanh(x / c); }
 
 static double kv_elem(const oracle_cfg* c, const void* kv_pages, int64_t idx) {
   if (c->kv_dtype == ORACLE_KV_E4M3FN) return oracle_e4m3fn_to_f64(((const uint8_t*)kv_pages)[idx]);
+  if (c->kv_dtype == ORACLE_KV_E5M2) return oracle_e5m2_to_f64(((const uint8_t*)kv_pages)[idx]);
   return oracle_bf16_to_f64(((const uint16_t*)kv_pages)[idx]);
 }
 
@@ -264,8 +287,9 @@ int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages,
  * 2h+1. A stored value is the inverse of the attention's dequant: the f32
  * quotient x / scale (IEEE binary32 division, rounded to nearest), then
  * rounded to the cache type to nearest with ties to even; e4m3fn saturates
- * at +-448 (it has no infinity), bf16 overflows to +-inf as IEEE rounding
- * does. NaN inputs give a NaN code.
+ * at +-448 (it has no infinity) and e5m2 the same way at +-57344 (its
+ * largest finite value), bf16 overflows to +-inf as IEEE rounding does. NaN
+ * inputs give a NaN code.
  * ------------------------------------------------------------------------ */
 
 /* v rounded to the nearest value of a binary format with `mbits` stored
@@ -298,6 +322,21 @@ uint8_t oracle_f32_to_e4m3fn(float x) {
   return sign | (uint8_t)(((ex + 7) << 3) | m);
 }
 
+/* f32 -> e5m2 code, round to nearest even, saturating at +-57344. */
+uint8_t oracle_f32_to_e5m2(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  double r = fabs(round_to_format((double)x, 2, -14));
+  if (r > 57344.0) r = 57344.0;
+  if (r == 0.0) return sign;
+  int e;
+  (void)frexp(r, &e);
+  const int ex = e - 1;
+  if (ex < -14) return sign | (uint8_t)(r / ldexp(1.0, -16)); /* subnormal: m * 2^-16 */
+  const int m = (int)(r / ldexp(1.0, ex - 2)) - 4;
+  return sign | (uint8_t)(((ex + 15) << 2) | m);
+}
+
 /* f32 -> bf16 bits, round to nearest even; overflow gives +-inf. */
 uint16_t oracle_f32_to_bf16(float x) {
   uint32_t w;
@@ -320,6 +359,8 @@ static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_
   const float y = x / (float)scale;
   if (c->kv_dtype == ORACLE_KV_E4M3FN)
     ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e4m3fn(y);
+  else if (c->kv_dtype == ORACLE_KV_E5M2)
+    ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e5m2(y);
   else
     ((uint16_t*)kv_pages)[idx] = oracle_f32_to_bf16(y);
 }

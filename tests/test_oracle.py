@@ -4,7 +4,9 @@ Every part of the oracle is tied here to a closed form, an invariant, or a
 library routine, so that a plausible slip in it (a dropped term, a swapped K/V
 head, a wrong causal offset or GQA index) fails at least one test:
 
-* dtype decode          - torch's own casts, plus printed e4m3fn values
+* dtype decode          - torch's own casts, plus printed e4m3fn and e5m2
+                          values; fp8 caches end to end against sdpa over
+                          torch's decode
 * softmax/PV/GQA/scale  - torch.scaled_dot_product_attention in f64
 * causal offsets        - Q = 0 closed form: lse = ln(#visible keys)
 * window boundary       - window 1 returns V at the query position exactly;
@@ -46,8 +48,9 @@ def _seq_kv(w, s, comb):
     phys = w.page_indices[s, idx // c.page_size]
     slot = idx % c.page_size
     bits = w.kv_pages[phys, slot]  # [kv_len, 2Hkv, D]
-    if c.kv_dtype == wl.KV_FP8:
-        vals = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if wl.is_fp8(c.kv_dtype):
+        tdt = torch.float8_e4m3fn if c.kv_dtype == wl.KV_FP8 else torch.float8_e5m2
+        vals = torch.from_numpy(bits.copy()).view(tdt).to(torch.float64).numpy()
         scale = (c.k_scale if comb == 0 else c.v_scale)
         vals = vals * scale
     else:
@@ -79,6 +82,27 @@ def test_e4m3fn_printed_values():
     for code, val in table.items():
         assert oracle.e4m3fn_to_f64(np.array([code], np.uint8))[0] == val
     assert math.copysign(1.0, oracle.e4m3fn_to_f64(np.array([0x80], np.uint8))[0]) == -1.0
+
+
+def test_e5m2_all_codes_match_torch_cast():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e5m2_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    # NaN at exponent 31 with a non-zero mantissa, infinities at S.11111.00
+    assert set(np.flatnonzero(np.isnan(mine))) == {0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF}
+    assert mine[0x7C] == np.inf and mine[0xFC] == -np.inf
+
+
+def test_e5m2_printed_values():
+    # OCP FP8 E5M2: largest finite 57344, smallest subnormal 2^-16, smallest normal 2^-14.
+    table = {0x00: 0.0, 0x3C: 1.0, 0x7B: 57344.0, 0xFB: -57344.0, 0x01: 2.0 ** -16,
+             0x04: 2.0 ** -14, 0x03: 3 * 2.0 ** -16, 0x40: 2.0, 0x3E: 1.5}
+    for code, val in table.items():
+        assert oracle.e5m2_to_f64(np.array([code], np.uint8))[0] == val
+    assert math.copysign(1.0, oracle.e5m2_to_f64(np.array([0x80], np.uint8))[0]) == -1.0
 
 
 def test_bf16_decode_matches_torch():
@@ -137,6 +161,23 @@ def test_matches_torch_sdpa_square(G, Hkv, D, kv_len, causal):
         scores = scores.masked_fill(torch.ones(kv_len, kv_len, dtype=torch.bool).triu(1), float("-inf"))
     ref_lse = torch.logsumexp(scores, dim=-1)[0].permute(1, 0).numpy()
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_dtype", [wl.KV_FP8, wl.KV_E5M2])
+def test_fp8_cache_matches_torch_sdpa_on_decoded_values(kv_dtype):
+    """fp8 K/V (each kind) are read as code * scale: the oracle equals sdpa in
+    f64 over torch's own decode of the same codes, scaled."""
+    G, Hkv, D, kv_len = 2, 2, 32, 40
+    kw = dict(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=16, pages_per_seq=None,
+              sm_scale=0.3, is_causal=True, kv_dtype=kv_dtype, k_scale=0.25, v_scale=3.0)
+    w = wl.build("fp8sdpa", kw, [kv_len], [kv_len], 17)
+    out, _ = oracle.forward(w)
+    q = torch.from_numpy(_q_f64(w)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(_seq_kv(w, 0, 0).copy())[None]
+    v = torch.from_numpy(_seq_kv(w, 0, 1).copy())[None]
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.cfg.sm_scale,
+                                         enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
 def test_bottom_right_causal_equals_suffix_of_square_problem():
@@ -271,7 +312,7 @@ def test_soft_cap_closed_form_end_to_end():
 
 # ----------------------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8])
+@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2])
 def test_page_permutation_invariance(kv_dtype):
     w = wl.random_small(21, max_seqs=4, kv_dtype=kv_dtype, window=9)
     o1, l1 = oracle.forward(w)

@@ -10,6 +10,8 @@
                    even code, saturation at +-448) over every finite bf16 value
                    and over the midpoints between adjacent e4m3fn values; and
                    torch's float8_e4m3fn cast after clamping
+* e5m2 rounding  - the same brute force over the finite e5m2 codes (saturation
+                   at +-57344) and torch's float8_e5m2 cast
 * bf16 rounding  - torch's float32 -> bfloat16 cast on random bit patterns,
                    subnormals and values next to the overflow threshold
 * the quotient   - the appended code is the brute-force nearest code of
@@ -176,6 +178,50 @@ def test_e4m3fn_rounding_matches_torch_cast_after_clamp():
     x = np.concatenate([x, _e4m3fn_midpoints()])
     ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(oracle.f32_to_e4m3fn(x), ref)
+
+
+def _e5m2_table():
+    codes = np.array([c for c in range(256) if ((c >> 2) & 31) != 31], dtype=np.uint8)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).to(torch.float64).numpy()
+    return vals, codes
+
+
+def brute_e5m2(x):
+    """Nearest finite e5m2 code (same sign, ties to the even code, saturating at
+    +-57344), by brute force over the finite codes."""
+    vals, codes = _e5m2_table()
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), 57344.0)
+    pos = (codes & 0x80) == 0
+    pv, pc = vals[pos], codes[pos]
+    d = np.abs(a[:, None] - pv[None, :])
+    tie = d == d.min(axis=1, keepdims=True)
+    idx = np.argmax(np.where(tie & ((pc[None, :] & 1) == 0), 1, 0) + tie, axis=1)
+    out = pc[idx].astype(np.uint8)
+    return np.where(neg, out | 0x80, out).astype(np.uint8)
+
+
+def test_e5m2_rounding_matches_brute_force_and_torch():
+    x = _f32(wl.finite_bf16_patterns())
+    vals, codes = _e5m2_table()
+    pv = np.sort(vals[(codes & 0x80) == 0])
+    mids = ((pv[1:] + pv[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+                        -mids, np.float32([57344, 61440, 65536, 1e9])])
+    got = oracle.f32_to_e5m2(x)
+    assert np.array_equal(got, brute_e5m2(x))
+    ref = torch.from_numpy(np.clip(x, -57344, 57344)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e5m2_append_is_the_nearest_code_of_the_f32_quotient():
+    w = placement_case(wl.KV_E5M2, k_scale=0.01, v_scale=7.0)
+    k_new, v_new = wl.new_kv(w, 9, std=5.0)
+    kv, _ = oracle.kv_append(w, k_new, v_new)
+    for t, s_, pos, page, slot in golden_rows():
+        assert np.array_equal(kv[page, slot, 0::2], brute_e5m2(_f32(k_new[t]).ravel() / np.float32(0.01)).reshape(2, 64))
+        assert np.array_equal(kv[page, slot, 1::2], brute_e5m2(_f32(v_new[t]).ravel() / np.float32(7.0)).reshape(2, 64))
 
 
 def test_bf16_rounding_matches_torch_cast():

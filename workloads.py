@@ -21,7 +21,8 @@ the workload's number as seed; draw order lengths -> page permutation -> Q
 -> K/V. Sequence s owns ``ceil(kv_len_s / page_size)`` consecutive entries of
 the permutation; unused page-table entries hold 0 (or a poison value).
 Q/K/V values are N(0,1) rounded to bf16 (round to nearest even); fp8 K/V are
-N(0,1)/scale rounded to e4m3fn (saturated at +-448). K/V pages are drawn in
+N(0,1)/scale rounded to e4m3fn (saturated at +-448) or to e5m2 (saturated at
++-57344). K/V pages are drawn in
 chunks of ``PAGE_CHUNK`` pages, each from its own spawned PCG64 stream, so
 large caches are generated in parallel yet identically on every machine.
 """
@@ -40,6 +41,13 @@ PAGE_CHUNK = 256
 
 KV_BF16 = "bf16"
 KV_FP8 = "fp8_e4m3fn"
+KV_E5M2 = "fp8_e5m2"
+FP8_KINDS = (KV_FP8, KV_E5M2)
+
+
+def is_fp8(kv_dtype: str) -> bool:
+    """One-byte K/V codes (e4m3fn or e5m2)."""
+    return kv_dtype in FP8_KINDS
 
 
 @dataclasses.dataclass
@@ -75,7 +83,7 @@ class Workload:
     name: str
     cfg: Config
     q: np.ndarray             # uint16 bf16 bits [T, Hq, D]
-    kv_pages: np.ndarray      # uint16 (bf16) or uint8 (e4m3fn) bits [P, page, 2*Hkv, D]
+    kv_pages: np.ndarray      # uint16 (bf16) or uint8 (e4m3fn, e5m2) bits [P, page, 2*Hkv, D]
     kv_lens: np.ndarray       # int32 [max_num_seqs]
     page_indices: np.ndarray  # int32 [max_num_seqs, pages_per_seq]
     cu_q_lens: np.ndarray     # int32 [max_num_seqs + 1]
@@ -110,6 +118,13 @@ def to_e4m3fn_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.uint8).numpy()
 
 
+def to_e5m2_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> fp8 e5m2 bits, saturated at +-57344 then rounded to nearest even."""
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -57344.0, 57344.0)
+    t = torch.from_numpy(x).to(torch.float8_e5m2)
+    return t.view(torch.uint8).numpy()
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
@@ -130,6 +145,8 @@ def _fill_kv(kv: np.ndarray, seed: int, kv_dtype: str, scale: float | None,
         z = rng.standard_normal((p1 - p0) * per_page, dtype=np.float32)
         if kv_dtype == KV_FP8:
             kv[p0:p1] = to_e4m3fn_bits(z / np.float32(scale)).reshape(kv[p0:p1].shape)
+        elif kv_dtype == KV_E5M2:
+            kv[p0:p1] = to_e5m2_bits(z / np.float32(scale)).reshape(kv[p0:p1].shape)
         else:
             kv[p0:p1] = to_bf16_bits(z).reshape(kv[p0:p1].shape)
 
@@ -195,9 +212,9 @@ def build(name: str, cfg_kw: dict, q_lens, kv_lens, seed: int, *, rng=None,
         qz *= np.float32(q_mult)
     q = to_bf16_bits(qz)
 
-    kv_np_dtype = np.uint8 if cfg.kv_dtype == KV_FP8 else np.uint16
+    kv_np_dtype = np.uint8 if is_fp8(cfg.kv_dtype) else np.uint16
     kv = np.empty((total_num_pages, page, 2 * Hkv, D), dtype=kv_np_dtype)
-    _fill_kv(kv, seed, cfg.kv_dtype, cfg.k_scale if cfg.kv_dtype == KV_FP8 else None)
+    _fill_kv(kv, seed, cfg.kv_dtype, cfg.k_scale if is_fp8(cfg.kv_dtype) else None)
 
     kv_lens_arr = np.zeros(max_num_seqs, dtype=np.int32)
     kv_lens_arr[:S] = kv_lens
@@ -298,7 +315,7 @@ def random_small(seed: int, *, max_seqs: int = 4, head_dim: int = 64,
               page_size=page_size, pages_per_seq=None,
               sm_scale=1.0 / math.sqrt(head_dim), kv_dtype=kv_dtype,
               is_causal=causal, sliding_window=window, soft_cap=soft_cap)
-    if kv_dtype == KV_FP8:
+    if is_fp8(kv_dtype):
         kw.update(k_scale=0.05, v_scale=0.05)
     pages_needed = int(((kv_lens + page_size - 1) // page_size).sum())
     return build(f"rand{seed}", kw, q_lens, kv_lens, seed, rng=rng,
