@@ -70,7 +70,8 @@ rpa_status validate(const rpa_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return RPA_ERR_UNSUPPORTED;
   if (c->page_size % 16 != 0 || c->page_size > 1024) return RPA_ERR_UNSUPPORTED;
   if (c->q_dtype != RPA_DTYPE_BF16) return RPA_ERR_UNSUPPORTED;
-  if (c->kv_dtype != RPA_DTYPE_BF16 && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN) return RPA_ERR_UNSUPPORTED;
+  if (c->kv_dtype != RPA_DTYPE_BF16 && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN && c->kv_dtype != RPA_DTYPE_FP8_E5M2)
+    return RPA_ERR_UNSUPPORTED;
   return RPA_OK;
 }
 
@@ -87,7 +88,7 @@ int dec_grid(int cus) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 int dec_grid_for(const rpa_config* c, int cus) {
-  const bool fp8 = c->kv_dtype == RPA_DTYPE_FP8_E4M3FN;
+  const bool fp8 = c->kv_dtype != RPA_DTYPE_BF16;
   switch (c->head_dim) {
     case 64: return fp8 ? dec_grid<64, true>(cus) : dec_grid<64, false>(cus);
     case 128: return fp8 ? dec_grid<128, true>(cus) : dec_grid<128, false>(cus);
@@ -199,8 +200,9 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev[k], st);
 }
 
-template <int D, bool FP8>
+template <int D, int KVT>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
+  constexpr bool FP8 = KVT != kKvBf16;
   {
     constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfBlkTable + 64));
     constexpr int per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
@@ -208,9 +210,9 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     if (grid > p.max_pf_items) grid = p.max_pf_items;
     if (grid < 1) grid = 1;
     if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((prefill_kernel<D, FP8, true>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<D, KVT, true>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     else
-      hipLaunchKernelGGL((prefill_kernel<D, FP8, false>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<D, KVT, false>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
   }
@@ -218,9 +220,9 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     // exactly the waves the planner split the decode work over
     const int grid = p.dec_waves / kDecWavesPerBlock;
     if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((decode_kernel<D, FP8, true>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, true>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     else
-      hipLaunchKernelGGL((decode_kernel<D, FP8, false>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, false>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
     // merge of the split decode units (a wave per unit, grid-stride)
@@ -234,6 +236,16 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
   return RPA_OK;
 }
 
+template <int D>
+rpa_status launch_for_kv(int32_t kv_dtype, const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
+  switch (kv_dtype) {
+    case RPA_DTYPE_BF16: return launch_attention<D, kKvBf16>(p, cus, st, ev);
+    case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3>(p, cus, st, ev);
+    case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2>(p, cus, st, ev);
+    default: return RPA_ERR_UNSUPPORTED;
+  }
+}
+
 rpa_status launch_plan(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
   return check_launch();
@@ -244,6 +256,8 @@ void launch_append(int mode, int grid, hipStream_t st, const AppendParams& p) {
   const dim3 blk(kApWaves * 64);
   if (mode == kApFp8)
     hipLaunchKernelGGL((kv_append_kernel<D, kApFp8>), dim3(grid), blk, 0, st, p);
+  else if (mode == kApE5M2)
+    hipLaunchKernelGGL((kv_append_kernel<D, kApE5M2>), dim3(grid), blk, 0, st, p);
   else if (mode == kApCopy)
     hipLaunchKernelGGL((kv_append_kernel<D, kApCopy>), dim3(grid), blk, 0, st, p);
   else
@@ -257,7 +271,7 @@ __global__ void decode_fp8_kernel(const uint8_t* codes, float* out, int n) {
   for (int k = 0; k < 4; ++k)
     if (4 * i + k < n) w |= (uint32_t)codes[4 * i + k] << (8 * k);
   u32x2 ww = {w, 0u};
-  bf16x8 b = fp8x8_to_bf16(ww);
+  bf16x8 b = fp8x8_to_bf16<kKvE4M3>(ww);
   for (int k = 0; k < 4; ++k)
     if (4 * i + k < n) out[4 * i + k] = (float)b[k];
 }
@@ -333,11 +347,10 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
   st = launch_plan(p, s);
   if (st != RPA_OK) return st;
   prof_record(ev, 1, s);
-  const bool fp8 = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN;
   switch (cfg->head_dim) {
-    case 64: return fp8 ? launch_attention<64, true>(p, cus, s, ev) : launch_attention<64, false>(p, cus, s, ev);
-    case 128: return fp8 ? launch_attention<128, true>(p, cus, s, ev) : launch_attention<128, false>(p, cus, s, ev);
-    case 256: return fp8 ? launch_attention<256, true>(p, cus, s, ev) : launch_attention<256, false>(p, cus, s, ev);
+    case 64: return launch_for_kv<64>(cfg->kv_dtype, p, cus, s, ev);
+    case 128: return launch_for_kv<128>(cfg->kv_dtype, p, cus, s, ev);
+    case 256: return launch_for_kv<256>(cfg->kv_dtype, p, cus, s, ev);
     default: return RPA_ERR_UNSUPPORTED;
   }
 }
@@ -492,6 +505,7 @@ rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v
   p.k_scale = cfg->k_scale;
   p.v_scale = cfg->v_scale;
   const int mode = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN             ? kApFp8
+                   : cfg->kv_dtype == RPA_DTYPE_FP8_E5M2             ? kApE5M2
                    : (cfg->k_scale == 1.f && cfg->v_scale == 1.f) ? kApCopy
                                                                     : kApBf16;
   // a wave per token, grid-stride beyond 8 workgroups per compute unit

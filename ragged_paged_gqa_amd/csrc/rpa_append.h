@@ -8,7 +8,7 @@
 // page_indices[s, j / page_size], K of kv head h in combined head 2h and V in
 // 2h+1 (`stridedLoadKv`). A stored value inverts the attention's dequant
 // factor: RN_f32(x / scale), rounded to nearest even in the cache type
-// (e4m3fn saturates at +-448; NaN stays NaN).
+// (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN).
 //
 // HBM-bound: per token 2*Hkv*D bf16 elements are read and 2*Hkv*D cache
 // elements written, contiguous on both sides. One wave per token; each lane
@@ -31,6 +31,7 @@ enum ApMode : int {
   kApCopy = 0,  // bf16 cache with both scales 1: the quotient is x itself
   kApBf16 = 1,  // bf16 cache, general scales
   kApFp8 = 2,   // e4m3fn cache
+  kApE5M2 = 3,  // e5m2 cache
 };
 
 struct AppendParams {
@@ -65,14 +66,18 @@ __device__ __forceinline__ int ap_seq_of_token(const int32_t* cu, int nseq, int 
 __device__ __forceinline__ float ap_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float ap_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// e4m3fn code pair of two f32 quotients into the low (HI false) or high 16
-// bits of `old`: clamp to the finite range (NaN kept), then the hardware
-// conversion, round to nearest even.
-template <bool HI>
+// fp8 code pair (e4m3fn, or e5m2) of two f32 quotients into the low (HI
+// false) or high 16 bits of `old`: clamp to the finite range (NaN kept),
+// then the hardware conversion, round to nearest even.
+template <bool HI, bool E5M2>
 __device__ __forceinline__ uint32_t ap_fp8_pair(float a, float b, uint32_t old) {
-  const float ca = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
-  const float cb = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a == a ? ca : a, b == b ? cb : b, (int)old, HI);
+  constexpr float kMax = E5M2 ? 57344.f : 448.f;  // largest finite value
+  const float ca = __builtin_amdgcn_fmed3f(a, -kMax, kMax);
+  const float cb = __builtin_amdgcn_fmed3f(b, -kMax, kMax);
+  if constexpr (E5M2)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a == a ? ca : a, b == b ? cb : b, (int)old, HI);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a == a ? ca : a, b == b ? cb : b, (int)old, HI);
 }
 
 // Loads chunks c0, c0+64, ... (kApUnroll of them, those below nch) of one
@@ -120,8 +125,9 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
     } else {
       u32x2 y;
-      y[0] = ap_fp8_pair<true>(f[2], f[3], ap_fp8_pair<false>(f[0], f[1], 0u));
-      y[1] = ap_fp8_pair<true>(f[6], f[7], ap_fp8_pair<false>(f[4], f[5], 0u));
+      constexpr bool E5 = MODE == kApE5M2;
+      y[0] = ap_fp8_pair<true, E5>(f[2], f[3], ap_fp8_pair<false, E5>(f[0], f[1], 0u));
+      y[1] = ap_fp8_pair<true, E5>(f[6], f[7], ap_fp8_pair<false, E5>(f[4], f[5], 0u));
       *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.kv) + e0) = y;
     }
   }

@@ -197,13 +197,28 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Eight fp8 e4m3fn codes (two dwords) -> eight bf16 (exact: every e4m3fn value
-// is a bf16 value).
+// K/V element types of the attention kernels (template parameter KVT).
+constexpr int kKvBf16 = 0;
+constexpr int kKvE4M3 = 1;  // OCP fp8 e4m3fn
+constexpr int kKvE5M2 = 2;  // OCP fp8 e5m2
+
+// Eight fp8 codes (two dwords) -> eight bf16, exactly: every e4m3fn and every
+// e5m2 value (infinities and NaN included) is a bf16 value.
+template <int KVT>
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, true);
+  static_assert(KVT == kKvE4M3 || KVT == kKvE5M2, "an fp8 kind");
+  bf16x2 a, b, c, d;
+  if constexpr (KVT == kKvE5M2) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w[0], 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w[0], 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w[1], 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w[1], 1.0f, true);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, true);
+  }
   bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   return r;
 }

@@ -162,8 +162,10 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel
 // carries no cap arithmetic at all).
-template <int D, bool FP8, bool CAP>
-__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8)) void decode_kernel(Params p) {
+template <int D, int KVT, bool CAP>
+__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
+    Params p) {
+  constexpr bool FP8 = KVT != kKvBf16;
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
                 NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, NST = Cf::NST;
@@ -399,8 +401,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       if constexpr (FP8) {
-        ka[2 * j] = fp8x8_to_bf16(u32x2{op.k[j][0], op.k[j][1]});
-        ka[2 * j + 1] = fp8x8_to_bf16(u32x2{op.k[j][2], op.k[j][3]});
+        ka[2 * j] = fp8x8_to_bf16<KVT>(u32x2{op.k[j][0], op.k[j][1]});
+        ka[2 * j + 1] = fp8x8_to_bf16<KVT>(u32x2{op.k[j][2], op.k[j][3]});
       } else {
         ka[j] = __builtin_bit_cast(bf16x8, op.k[j]);
       }
@@ -458,8 +460,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, FP8))
       bf16x8 vw[2 * NLD];
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        vw[2 * j] = fp8x8_to_bf16(u32x2{op.v[j][0], op.v[j][1]});
-        vw[2 * j + 1] = fp8x8_to_bf16(u32x2{op.v[j][2], op.v[j][3]});
+        vw[2 * j] = fp8x8_to_bf16<KVT>(u32x2{op.v[j][0], op.v[j][1]});
+        vw[2 * j + 1] = fp8x8_to_bf16<KVT>(u32x2{op.v[j][2], op.v[j][3]});
       }
       if (kb + 16 > vis_hi) {  // (uniform) the step ends past vis_hi
         if (kb + col >= vis_hi) {

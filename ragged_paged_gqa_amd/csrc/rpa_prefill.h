@@ -99,8 +99,9 @@ __device__ __forceinline__ int swz_v(int key) {
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
 // block loop has no branch and no cap arithmetic).
-template <int D, bool FP8, bool CAP>
+template <int D, int KVT, bool CAP>
 __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
+  constexpr bool FP8 = KVT != kKvBf16;
   constexpr int NW = kPfWaves;
   constexpr int NH = pf_halves_for(D);        // 32-row halves per wave
   constexpr int WR = 32 * NH;                 // rows per wave
@@ -344,7 +345,9 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         const int sw = region ? swz_v<D>(key) : swz_k<D>(key);
         char* row_p = dst + region * REG + key * RB;
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
-        bf16x8 a = fp8x8_to_bf16(lo2), b = fp8x8_to_bf16(hi2);
+        // (this lambda is also compiled, unused, into the bf16 kernels)
+        constexpr int F8 = KVT == kKvE5M2 ? kKvE5M2 : kKvE4M3;
+        bf16x8 a = fp8x8_to_bf16<F8>(lo2), b = fp8x8_to_bf16<F8>(hi2);
         if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
           a = bf16x8{};
           b = bf16x8{};

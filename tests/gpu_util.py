@@ -24,7 +24,7 @@ def lib_config(w: wl.Workload) -> rpa.Config:
         num_q_tokens=c.num_q_tokens, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
         head_dim=c.head_dim, total_num_pages=c.total_num_pages, page_size=c.page_size,
         max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq,
-        kv_dtype=rpa.DTYPE_FP8_E4M3FN if c.kv_dtype == wl.KV_FP8 else rpa.DTYPE_BF16,
+        kv_dtype={wl.KV_FP8: rpa.DTYPE_FP8_E4M3FN, wl.KV_E5M2: rpa.DTYPE_FP8_E5M2}.get(c.kv_dtype, rpa.DTYPE_BF16),
         sm_scale=c.sm_scale, soft_cap=c.soft_cap or 0.0,
         k_scale=1.0 if c.k_scale is None else c.k_scale,
         v_scale=1.0 if c.v_scale is None else c.v_scale,
@@ -38,7 +38,7 @@ class Device:
         self.w = w
         self.cfg = lib_config(w)
         self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
-        if w.cfg.kv_dtype == wl.KV_FP8:
+        if wl.is_fp8(w.cfg.kv_dtype):
             self.kv = torch.from_numpy(w.kv_pages).to(device)
         else:
             self.kv = torch.from_numpy(w.kv_pages.view(np.int16)).to(device).view(torch.bfloat16)

@@ -281,14 +281,25 @@ def cfg_kw(number: int) -> dict:
 
 
 def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
-          seed: int | None = None) -> Workload:
+          seed: int | None = None, kv_dtype: str | None = None) -> Workload:
+    """A named workload; `kv_dtype` swaps its K/V type (fp8 kinds take the fp8
+    decode workload's scales, 0.05, when the workload has none)."""
     seed = number if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     q_lens, kv_lens = lengths(number, rng)
     kw = dict(q_mult=q_mult, unused_entry=unused_entry)
     if number == 1:
         kw["total_num_pages"] = 32
-    return build(f"cfg{number}", cfg_kw(number), q_lens, kv_lens, seed, rng=rng, **kw)
+    ckw = cfg_kw(number)
+    if kv_dtype is not None:
+        ckw["kv_dtype"] = kv_dtype
+        if is_fp8(kv_dtype):
+            ckw.setdefault("k_scale", 0.05)
+            ckw.setdefault("v_scale", 0.05)
+        else:
+            ckw.pop("k_scale", None)
+            ckw.pop("v_scale", None)
+    return build(f"cfg{number}", ckw, q_lens, kv_lens, seed, rng=rng, **kw)
 
 
 def with_sinks(w: Workload, seed: int, mean: float = 1.0, std: float = 2.0) -> Workload:
