@@ -25,7 +25,8 @@ _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_BUILD, "librpa_oracle.so")
 
-KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2}
+KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2, "f16": 3}
+Q_CODES = {"bf16": 0, "f16": 3}
 
 
 class _Cfg(ctypes.Structure):
@@ -47,6 +48,7 @@ class _Cfg(ctypes.Structure):
         ("k_scale", ctypes.c_double),
         ("v_scale", ctypes.c_double),
         ("sinks", ctypes.c_void_p),
+        ("q_dtype", ctypes.c_int32),
     ]
 
 
@@ -78,6 +80,10 @@ def lib():
         L.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_e5m2_to_f64.restype = ctypes.c_double
         L.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_e5m2.restype = ctypes.c_uint8
         L.oracle_f32_to_e5m2.argtypes = [ctypes.c_float]
         L.oracle_soft_cap.restype = ctypes.c_double
@@ -116,7 +122,8 @@ def _cfg(w) -> _Cfg:
         has_soft_cap=int(c.soft_cap is not None), sm_scale=float(c.sm_scale),
         soft_cap=float(c.soft_cap or 0.0),
         k_scale=1.0 if c.k_scale is None else float(c.k_scale),
-        v_scale=1.0 if c.v_scale is None else float(c.v_scale), sinks=None)
+        v_scale=1.0 if c.v_scale is None else float(c.v_scale), sinks=None,
+        q_dtype=Q_CODES[getattr(c, "q_dtype", "bf16")])
     if sinks is not None:
         # f64 copy of the f32 sink logits, kept alive with the struct
         cfg._sinks = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32), dtype=np.float64)
@@ -191,12 +198,25 @@ def e5m2_to_f64(codes) -> np.ndarray:
     return np.array([L.oracle_e5m2_to_f64(int(x)) for x in b]).reshape(np.shape(codes))
 
 
+def f16_to_f64(bits) -> np.ndarray:
+    L = lib()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([L.oracle_f16_to_f64(int(x)) for x in b]).reshape(np.shape(bits))
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """Element-wise f32 -> f16 bits (nearest even; overflow to +-inf)."""
+    f = lib().oracle_f32_to_f16
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint16).reshape(a.shape)
+
+
 def soft_cap(x: float, c: float) -> float:
     return lib().oracle_soft_cap(float(x), float(c))
 
 
 def kv_append(w, k_new, v_new):
-    """The cache after writing k_new / v_new ([T, Hkv, D] bf16 bits) of every
+    """The cache after writing k_new / v_new ([T, Hkv, D] bits of the q dtype) of every
     query token of w into a copy of w.kv_pages. Returns (kv_pages, skipped):
     skipped counts tokens whose slot falls outside the page table."""
     c = w.cfg

@@ -42,7 +42,9 @@
  *     with bias 15 and IEEE-style infinities and NaN; the page only names
  *     the dtypes (`Cfg` kv_dtype, f8e4m3fn and f8e5m2);
  *   - dequantised values are code*scale exactly (f64), not re-rounded to the
- *     q dtype.
+ *     q dtype;
+ *   - q (and out) are bf16 or f16 (`Cfg` q_dtype); K/V bf16, f16, e4m3fn or
+ *     e5m2 (`Cfg` kv_dtype), all read exactly.
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,6 +54,7 @@
 #define ORACLE_KV_BF16 0
 #define ORACLE_KV_E4M3FN 1
 #define ORACLE_KV_E5M2 2
+#define ORACLE_F16 3 /* IEEE binary16: q/out type, or K/V type */
 
 typedef struct {
   int32_t num_q_tokens;
@@ -62,7 +65,7 @@ typedef struct {
   int32_t page_size;
   int32_t max_num_seqs;
   int32_t pages_per_seq;
-  int32_t kv_dtype;       /* ORACLE_KV_BF16, ORACLE_KV_E4M3FN or ORACLE_KV_E5M2 */
+  int32_t kv_dtype;       /* ORACLE_KV_BF16, ORACLE_KV_E4M3FN, ORACLE_KV_E5M2 or ORACLE_F16 */
   int32_t is_causal;      /* 0 or 1 */
   int32_t sliding_window; /* <= 0: no window */
   int32_t has_soft_cap;   /* 0 or 1 */
@@ -71,6 +74,7 @@ typedef struct {
   double k_scale; /* 1.0 when absent */
   double v_scale; /* 1.0 when absent */
   const double* sinks; /* NULL, or one logit per q head [num_q_heads] */
+  int32_t q_dtype;     /* 0: bf16 q (and new K/V rows of the append), ORACLE_F16: f16 */
 } oracle_cfg;
 
 /* bf16 bits are the upper half of an IEEE binary32 value. */
@@ -98,6 +102,25 @@ double oracle_e4m3fn_to_f64(uint8_t code) {
   return sign ? -mag : mag;
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits with bias 15, 10 mantissa bits;
+ * exponent 0 encodes subnormals m/1024 * 2^-14, exponent 31 the infinities
+ * (mantissa 0) and NaN. */
+double oracle_f16_to_f64(uint16_t bits) {
+  int sign = (bits >> 15) & 1;
+  int e = (bits >> 10) & 31;
+  int m = bits & 1023;
+  double mag;
+  if (e == 31) {
+    if (m != 0) return NAN;
+    mag = INFINITY;
+  } else if (e == 0) {
+    mag = ldexp((double)m / 1024.0, -14);
+  } else {
+    mag = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  }
+  return sign ? -mag : mag;
+}
+
 /* OCP FP8 E5M2: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits
  * (the IEEE-style format: exponent 31 holds the infinities, mantissa 0, and
  * NaN). Exponent 0 encodes subnormals m/4 * 2^-14; everything else is
@@ -121,9 +144,15 @@ double oracle_e5m2_to_f64(uint8_t code) {
 /* Soft-cap of the kernel page's `Cfg`/`flashAttention`: c * tanh(x / c). */
 double oracle_soft_cap(double x, double c) { return c * tanh(x / c); }
 
+/* A q element (or a new K/V element of the append) in the q dtype. */
+static double q_elem(const oracle_cfg* c, uint16_t bits) {
+  return c->q_dtype == ORACLE_F16 ? oracle_f16_to_f64(bits) : oracle_bf16_to_f64(bits);
+}
+
 static double kv_elem(const oracle_cfg* c, const void* kv_pages, int64_t idx) {
   if (c->kv_dtype == ORACLE_KV_E4M3FN) return oracle_e4m3fn_to_f64(((const uint8_t*)kv_pages)[idx]);
   if (c->kv_dtype == ORACLE_KV_E5M2) return oracle_e5m2_to_f64(((const uint8_t*)kv_pages)[idx]);
+  if (c->kv_dtype == ORACLE_F16) return oracle_f16_to_f64(((const uint16_t*)kv_pages)[idx]);
   return oracle_bf16_to_f64(((const uint16_t*)kv_pages)[idx]);
 }
 
@@ -186,7 +215,7 @@ static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pag
     int64_t base = kv_index(c, page_indices, s, j, 2 * h, 0);
     if (base < 0) goto invalid;
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += oracle_bf16_to_f64(qrow[d]) * (kv_elem(c, kv_pages, base + d) * c->k_scale);
+    for (int d = 0; d < D; ++d) dot += q_elem(c, qrow[d]) * (kv_elem(c, kv_pages, base + d) * c->k_scale);
     double x = dot * c->sm_scale;
     if (c->has_soft_cap) x = oracle_soft_cap(x, c->soft_cap);
     sc[j] = x;
@@ -288,8 +317,8 @@ int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages,
  * quotient x / scale (IEEE binary32 division, rounded to nearest), then
  * rounded to the cache type to nearest with ties to even; e4m3fn saturates
  * at +-448 (it has no infinity) and e5m2 the same way at +-57344 (its
- * largest finite value), bf16 overflows to +-inf as IEEE rounding does. NaN
- * inputs give a NaN code.
+ * largest finite value), bf16 and f16 overflow to +-inf as IEEE rounding
+ * does. NaN inputs give a NaN code. The new rows come in the q dtype.
  * ------------------------------------------------------------------------ */
 
 /* v rounded to the nearest value of a binary format with `mbits` stored
@@ -337,6 +366,21 @@ uint8_t oracle_f32_to_e5m2(float x) {
   return sign | (uint8_t)(((ex + 15) << 2) | m);
 }
 
+/* f32 -> IEEE binary16 bits, round to nearest even; overflow gives +-inf. */
+uint16_t oracle_f32_to_f16(float x) {
+  const uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  if (isnan(x)) return sign | 0x7E00;
+  double r = fabs(round_to_format((double)x, 10, -14));
+  if (r >= 65536.0) return sign | 0x7C00; /* past the largest finite value after rounding */
+  if (r == 0.0) return sign;
+  int e;
+  (void)frexp(r, &e);
+  const int ex = e - 1;
+  if (ex < -14) return sign | (uint16_t)(r / ldexp(1.0, -24)); /* subnormal: m * 2^-24 */
+  const int m = (int)(r / ldexp(1.0, ex - 10)) - 1024;
+  return sign | (uint16_t)(((ex + 15) << 10) | m);
+}
+
 /* f32 -> bf16 bits, round to nearest even; overflow gives +-inf. */
 uint16_t oracle_f32_to_bf16(float x) {
   uint32_t w;
@@ -351,16 +395,17 @@ uint16_t oracle_f32_to_bf16(float x) {
   return (uint16_t)(w >> 16);
 }
 
-/* Cache value of one new element: RN_f32(x / scale) in the cache type. */
+/* Cache value of one new element (x in the q dtype): RN_f32(x / scale) in
+ * the cache type. */
 static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_t x_bits, double scale) {
-  uint32_t w = (uint32_t)x_bits << 16;
-  float x;
-  memcpy(&x, &w, sizeof x);
+  const float x = (float)q_elem(c, x_bits); /* exact: bf16 and f16 values are f32 values */
   const float y = x / (float)scale;
   if (c->kv_dtype == ORACLE_KV_E4M3FN)
     ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e4m3fn(y);
   else if (c->kv_dtype == ORACLE_KV_E5M2)
     ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e5m2(y);
+  else if (c->kv_dtype == ORACLE_F16)
+    ((uint16_t*)kv_pages)[idx] = oracle_f32_to_f16(y);
   else
     ((uint16_t*)kv_pages)[idx] = oracle_f32_to_bf16(y);
 }

@@ -4,9 +4,9 @@ Every part of the oracle is tied here to a closed form, an invariant, or a
 library routine, so that a plausible slip in it (a dropped term, a swapped K/V
 head, a wrong causal offset or GQA index) fails at least one test:
 
-* dtype decode          - torch's own casts, plus printed e4m3fn and e5m2
-                          values; fp8 caches end to end against sdpa over
-                          torch's decode
+* dtype decode          - torch's own casts (numpy's for f16), plus printed
+                          e4m3fn, e5m2 and binary16 values; fp8 caches and f16
+                          q / K/V end to end against sdpa over those decodes
 * softmax/PV/GQA/scale  - torch.scaled_dot_product_attention in f64
 * causal offsets        - Q = 0 closed form: lse = ln(#visible keys)
 * window boundary       - window 1 returns V at the query position exactly;
@@ -53,12 +53,16 @@ def _seq_kv(w, s, comb):
         vals = torch.from_numpy(bits.copy()).view(tdt).to(torch.float64).numpy()
         scale = (c.k_scale if comb == 0 else c.v_scale)
         vals = vals * scale
+    elif c.kv_dtype == wl.KV_F16:
+        vals = bits.view(np.float16).astype(np.float64)
     else:
         vals = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
     return np.transpose(vals[:, comb::2, :], (1, 0, 2))
 
 
 def _q_f64(w):
+    if w.cfg.q_dtype == wl.Q_F16:
+        return w.q.view(np.float16).astype(np.float64)
     return torch.from_numpy(w.q.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
 
 
@@ -103,6 +107,17 @@ def test_e5m2_printed_values():
     for code, val in table.items():
         assert oracle.e5m2_to_f64(np.array([code], np.uint8))[0] == val
     assert math.copysign(1.0, oracle.e5m2_to_f64(np.array([0x80], np.uint8))[0]) == -1.0
+
+
+def test_f16_all_patterns_match_numpy_cast():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    # IEEE binary16: largest finite 65504, smallest subnormal 2^-24
+    assert mine[0x7BFF] == 65504.0 and mine[0x0001] == 2.0 ** -24 and mine[0x7C00] == np.inf
 
 
 def test_bf16_decode_matches_torch():
@@ -171,6 +186,25 @@ def test_fp8_cache_matches_torch_sdpa_on_decoded_values(kv_dtype):
     kw = dict(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=16, pages_per_seq=None,
               sm_scale=0.3, is_causal=True, kv_dtype=kv_dtype, k_scale=0.25, v_scale=3.0)
     w = wl.build("fp8sdpa", kw, [kv_len], [kv_len], 17)
+    out, _ = oracle.forward(w)
+    q = torch.from_numpy(_q_f64(w)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(_seq_kv(w, 0, 0).copy())[None]
+    v = torch.from_numpy(_seq_kv(w, 0, 1).copy())[None]
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.cfg.sm_scale,
+                                         enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_dtype", [wl.KV_F16, wl.KV_FP8, wl.KV_E5M2])
+def test_f16_q_matches_torch_sdpa_on_decoded_values(kv_dtype):
+    """f16 q (the page's `Cfg` q_dtype) with f16 or fp8 K/V: sdpa in f64 over
+    numpy's / torch's decode of the same bits."""
+    G, Hkv, D, kv_len = 2, 2, 32, 40
+    kw = dict(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=16, pages_per_seq=None,
+              sm_scale=0.3, is_causal=True, kv_dtype=kv_dtype, q_dtype=wl.Q_F16)
+    if wl.is_fp8(kv_dtype):
+        kw.update(k_scale=0.25, v_scale=3.0)
+    w = wl.build("f16sdpa", kw, [kv_len], [kv_len], 18)
     out, _ = oracle.forward(w)
     q = torch.from_numpy(_q_f64(w)).permute(1, 0, 2)[None]
     k = torch.from_numpy(_seq_kv(w, 0, 0).copy())[None]
@@ -312,9 +346,10 @@ def test_soft_cap_closed_form_end_to_end():
 
 # ----------------------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2])
+@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2, wl.KV_F16])
 def test_page_permutation_invariance(kv_dtype):
-    w = wl.random_small(21, max_seqs=4, kv_dtype=kv_dtype, window=9)
+    w = wl.random_small(21, max_seqs=4, kv_dtype=kv_dtype, window=9,
+                        q_dtype=wl.Q_F16 if kv_dtype == wl.KV_F16 else wl.Q_BF16)
     o1, l1 = oracle.forward(w)
     rng = np.random.default_rng(7)
     P = w.cfg.total_num_pages

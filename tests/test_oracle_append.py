@@ -12,6 +12,8 @@
                    torch's float8_e4m3fn cast after clamping
 * e5m2 rounding  - the same brute force over the finite e5m2 codes (saturation
                    at +-57344) and torch's float8_e5m2 cast
+* f16 rounding   - numpy's float32 -> float16 cast (random patterns, midpoints,
+                   the overflow edge); rows in f16 (f16 q) into f16 and fp8 caches
 * bf16 rounding  - torch's float32 -> bfloat16 cast on random bit patterns,
                    subnormals and values next to the overflow threshold
 * the quotient   - the appended code is the brute-force nearest code of
@@ -222,6 +224,45 @@ def test_e5m2_append_is_the_nearest_code_of_the_f32_quotient():
     for t, s_, pos, page, slot in golden_rows():
         assert np.array_equal(kv[page, slot, 0::2], brute_e5m2(_f32(k_new[t]).ravel() / np.float32(0.01)).reshape(2, 64))
         assert np.array_equal(kv[page, slot, 1::2], brute_e5m2(_f32(v_new[t]).ravel() / np.float32(7.0)).reshape(2, 64))
+
+
+def test_f16_rounding_matches_numpy_cast():
+    rng = np.random.Generator(np.random.PCG64(14))
+    bits = rng.integers(0, 1 << 32, size=60000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]
+    x = bits.view(np.float32)
+    # f16 midpoints (exact in f32) and their neighbours, subnormals, the overflow edge
+    h = np.arange(0, 0x7C00, 7, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = ((h[1:] + h[:-1]) / 2).astype(np.float32)
+    edge = np.float32([65504, 65519, 65520, 65535, 65536, 1e6, 2.0 ** -25, 3 * 2.0 ** -26])
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(np.inf)), edge, -edge])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16(x), ref)
+
+
+def test_f16_rows_append_into_f16_and_fp8_caches():
+    """New rows in f16 (f16 q): an f16 cache takes RN_f16(x / scale), an
+    e4m3fn cache the nearest code of the f32 quotient."""
+    for kvd, ks in ((wl.KV_F16, 0.5), (wl.KV_FP8, 0.05)):
+        kw = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, sm_scale=0.125,
+                  kv_dtype=kvd, q_dtype=wl.Q_F16, k_scale=ks, v_scale=2.0)
+        w = wl.from_tables(kw, [1, 5, 0, 16], [8, 35, 20, 64], [[3], [7, 1, 10], [5, 6], [2, 9, 4, 11]], 12,
+                           total_num_pages=12, max_num_seqs=5, num_q_tokens=24, pages_per_seq=4)
+        k_new, v_new = wl.new_kv(w, 15, std=3.0)
+        kv, skipped = oracle.kv_append(w, k_new, v_new)
+        assert skipped == 0
+        xk = k_new.view(np.float16).astype(np.float32)
+        xv = v_new.view(np.float16).astype(np.float32)
+        for t, s_, pos, page, slot in golden_rows():
+            qk = xk[t].ravel() / np.float32(ks)
+            qv = xv[t].ravel() / np.float32(2.0)
+            if kvd == wl.KV_F16:
+                assert np.array_equal(kv[page, slot, 0::2].ravel(), qk.astype(np.float16).view(np.uint16))
+                assert np.array_equal(kv[page, slot, 1::2].ravel(), qv.astype(np.float16).view(np.uint16))
+            else:
+                assert np.array_equal(kv[page, slot, 0::2].ravel(), brute_e4m3fn(qk))
+                assert np.array_equal(kv[page, slot, 1::2].ravel(), brute_e4m3fn(qv))
 
 
 def test_bf16_rounding_matches_torch_cast():

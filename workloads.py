@@ -42,6 +42,9 @@ PAGE_CHUNK = 256
 KV_BF16 = "bf16"
 KV_FP8 = "fp8_e4m3fn"
 KV_E5M2 = "fp8_e5m2"
+KV_F16 = "f16"
+Q_BF16 = "bf16"
+Q_F16 = "f16"
 FP8_KINDS = (KV_FP8, KV_E5M2)
 
 
@@ -61,6 +64,7 @@ class Config:
     max_num_seqs: int
     num_q_tokens: int
     kv_dtype: str = KV_BF16
+    q_dtype: str = Q_BF16     # q, out and the append's new K/V rows
     sm_scale: float = 1.0
     soft_cap: float | None = None
     k_scale: float | None = None
@@ -82,8 +86,8 @@ class Config:
 class Workload:
     name: str
     cfg: Config
-    q: np.ndarray             # uint16 bf16 bits [T, Hq, D]
-    kv_pages: np.ndarray      # uint16 (bf16) or uint8 (e4m3fn, e5m2) bits [P, page, 2*Hkv, D]
+    q: np.ndarray             # uint16 bf16 (or f16) bits [T, Hq, D]
+    kv_pages: np.ndarray      # uint16 (bf16, f16) or uint8 (e4m3fn, e5m2) bits [P, page, 2*Hkv, D]
     kv_lens: np.ndarray       # int32 [max_num_seqs]
     page_indices: np.ndarray  # int32 [max_num_seqs, pages_per_seq]
     cu_q_lens: np.ndarray     # int32 [max_num_seqs + 1]
@@ -118,6 +122,15 @@ def to_e4m3fn_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.uint8).numpy()
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bits, round to nearest even (numpy's cast)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def to_q_bits(x: np.ndarray, q_dtype: str) -> np.ndarray:
+    return to_f16_bits(x) if q_dtype == Q_F16 else to_bf16_bits(x)
+
+
 def to_e5m2_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> fp8 e5m2 bits, saturated at +-57344 then rounded to nearest even."""
     x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -57344.0, 57344.0)
@@ -147,6 +160,8 @@ def _fill_kv(kv: np.ndarray, seed: int, kv_dtype: str, scale: float | None,
             kv[p0:p1] = to_e4m3fn_bits(z / np.float32(scale)).reshape(kv[p0:p1].shape)
         elif kv_dtype == KV_E5M2:
             kv[p0:p1] = to_e5m2_bits(z / np.float32(scale)).reshape(kv[p0:p1].shape)
+        elif kv_dtype == KV_F16:
+            kv[p0:p1] = to_f16_bits(z).reshape(kv[p0:p1].shape)
         else:
             kv[p0:p1] = to_bf16_bits(z).reshape(kv[p0:p1].shape)
 
@@ -210,7 +225,7 @@ def build(name: str, cfg_kw: dict, q_lens, kv_lens, seed: int, *, rng=None,
     qz = rng.standard_normal((num_q_tokens, Hq, D), dtype=np.float32)
     if q_mult != 1.0:
         qz *= np.float32(q_mult)
-    q = to_bf16_bits(qz)
+    q = to_q_bits(qz, cfg.q_dtype)
 
     kv_np_dtype = np.uint8 if is_fp8(cfg.kv_dtype) else np.uint16
     kv = np.empty((total_num_pages, page, 2 * Hkv, D), dtype=kv_np_dtype)
@@ -310,7 +325,7 @@ def with_sinks(w: Workload, seed: int, mean: float = 1.0, std: float = 2.0) -> W
 
 
 def random_small(seed: int, *, max_seqs: int = 4, head_dim: int = 64,
-                 kv_dtype: str = KV_BF16, causal: bool = True,
+                 kv_dtype: str = KV_BF16, q_dtype: str = Q_BF16, causal: bool = True,
                  window: int | None = None, soft_cap: float | None = None,
                  G: int | None = None, page_size: int = 16,
                  max_q: int = 24, max_extra_kv: int = 80) -> Workload:
@@ -324,7 +339,7 @@ def random_small(seed: int, *, max_seqs: int = 4, head_dim: int = 64,
     G = int(rng.integers(1, 5, endpoint=True)) if G is None else G
     kw = dict(num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=head_dim,
               page_size=page_size, pages_per_seq=None,
-              sm_scale=1.0 / math.sqrt(head_dim), kv_dtype=kv_dtype,
+              sm_scale=1.0 / math.sqrt(head_dim), kv_dtype=kv_dtype, q_dtype=q_dtype,
               is_causal=causal, sliding_window=window, soft_cap=soft_cap)
     if is_fp8(kv_dtype):
         kw.update(k_scale=0.05, v_scale=0.05)
@@ -357,13 +372,14 @@ def from_tables(cfg_kw: dict, q_lens, kv_lens, tables, seed: int, *, total_num_p
 
 
 def new_kv(w: Workload, seed: int, std: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
-    """Seeded new K and V rows for every query token: bf16 bits [T, Hkv, D], N(0, std^2)."""
+    """Seeded new K and V rows for every query token: bits of the q dtype
+    [T, Hkv, D], N(0, std^2)."""
     c = w.cfg
     rng = np.random.Generator(np.random.PCG64([seed, 0xA11E]))
     shape = (c.num_q_tokens, c.num_kv_heads, c.head_dim)
     k = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
     v = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
-    return to_bf16_bits(k), to_bf16_bits(v)
+    return to_q_bits(k, c.q_dtype), to_q_bits(v, c.q_dtype)
 
 
 def finite_bf16_patterns() -> np.ndarray:
