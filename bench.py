@@ -58,7 +58,7 @@ def algorithmic_work(w):
     kernel class that handles each sequence (<= 16 packed rows: decode)."""
     c = w.cfg
     G = c.num_q_heads // c.num_kv_heads
-    b_kv = 1 if c.kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2
+    b_kv = 1 if c.kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2  # bf16 and f16: 2
     sw = c.sliding_window or 0
     res = {"decode": [0.0, 0.0, 0], "prefill": [0.0, 0.0, 0]}  # flops, bytes, tokens
     for s in range(w.n_seqs):
@@ -177,8 +177,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kv-dtype", choices=["bf16", "fp8_e4m3fn", "fp8_e5m2"], default=None,
+    ap.add_argument("--kv-dtype", choices=["bf16", "f16", "fp8_e4m3fn", "fp8_e5m2"], default=None,
                     help="store the workload's K/V cache in this type instead of its own")
+    ap.add_argument("--q-dtype", choices=["bf16", "f16"], default=None,
+                    help="q/out type (f16: a bf16 cache becomes f16 too)")
     ap.add_argument("--sinks", action="store_true",
                     help="attach seeded attention-sink logits (one per q head) and call rpa_forward_sinks")
     ap.add_argument("--append", action="store_true",
@@ -223,7 +225,7 @@ def main():
 
     log(f"[bench] generating workload {args.workload}: {wl.WORKLOADS[args.workload]}")
     t0 = time.perf_counter()
-    w = wl.named(args.workload, kv_dtype=args.kv_dtype)
+    w = wl.named(args.workload, kv_dtype=args.kv_dtype, q_dtype=args.q_dtype)
     if args.sinks:
         w = wl.with_sinks(w, args.workload)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
@@ -235,8 +237,9 @@ def main():
 
     if args.append:
         k_np, v_np = wl.new_kv(w, 1000 + args.workload)
-        k_new = torch.from_numpy(k_np.view(np.int16)).cuda().view(torch.bfloat16)
-        v_new = torch.from_numpy(v_np.view(np.int16)).cuda().view(torch.bfloat16)
+        t16 = torch.float16 if w.cfg.q_dtype == wl.Q_F16 else torch.bfloat16
+        k_new = torch.from_numpy(k_np.view(np.int16)).cuda().view(t16)
+        v_new = torch.from_numpy(v_np.view(np.int16)).cuda().view(t16)
         stream = torch.cuda.current_stream()
         ap_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(args.steps)]
@@ -299,13 +302,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.cfg.kv_dtype == wl.KV_BF16 else f"bf16 q / {w.cfg.kv_dtype.replace('_', ' ')} kv",
+        "dtype": w.cfg.q_dtype if w.cfg.kv_dtype == w.cfg.q_dtype
+        else f"{w.cfg.q_dtype} q / {w.cfg.kv_dtype.replace('_', ' ')} kv",
         "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page table)",
         "config": {"workload": wl.WORKLOADS[args.workload], "num_seqs": w.n_seqs, "query_tokens": T,
                    "num_q_heads": w.cfg.num_q_heads, "num_kv_heads": w.cfg.num_kv_heads,
                    "head_dim": w.cfg.head_dim, "page_size": w.cfg.page_size,
                    **({"attention_sinks": True} if args.sinks else {}),
-                   **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {})},
+                   **({"kv_dtype": w.cfg.kv_dtype} if args.kv_dtype or args.q_dtype else {}),
+                   **({"q_dtype": w.cfg.q_dtype} if args.q_dtype else {})},
         "kv_hbm_gbs": round(B / step_s / 1e9, 1),
         "tflops": round(F / step_s / 1e12, 2),
         "roofline_frac_step": round(max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / step_s, 4),

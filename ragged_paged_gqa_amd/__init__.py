@@ -25,6 +25,7 @@ LIB_PATH = os.environ.get("RPA_LIB_PATH") or os.path.join(_HERE, "_build", "libr
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3FN = 1
 DTYPE_FP8_E5M2 = 2
+DTYPE_F16 = 3
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "HIP runtime error", 5: "metadata violates a precondition"}
@@ -75,12 +76,13 @@ class Config:
     v_scale: float = 1.0
     is_causal: bool = True
     sliding_window: int = 0      # 0: off
+    q_dtype: int = DTYPE_BF16    # q and out: DTYPE_BF16 or DTYPE_F16
 
     def to_c(self) -> _Config:
         return _Config(
             num_q_tokens=self.num_q_tokens, num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
             head_dim=self.head_dim, total_num_pages=self.total_num_pages, page_size=self.page_size,
-            max_num_seqs=self.max_num_seqs, pages_per_seq=self.pages_per_seq, q_dtype=DTYPE_BF16,
+            max_num_seqs=self.max_num_seqs, pages_per_seq=self.pages_per_seq, q_dtype=self.q_dtype,
             kv_dtype=self.kv_dtype, sm_scale=self.sm_scale, soft_cap=self.soft_cap or 0.0,
             k_scale=1.0 if self.k_scale is None else self.k_scale,
             v_scale=1.0 if self.v_scale is None else self.v_scale,
@@ -174,7 +176,7 @@ def _dev_i32(t: torch.Tensor, name: str, numel: int) -> None:
 def _check_inputs(cfg: Config, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs):
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
     if not (q.is_cuda and q.is_contiguous() and q.element_size() == 2 and q.numel() == T * Hq * D):
-        raise ValueError("q: expected a contiguous 2-byte (bf16) CUDA tensor [num_q_tokens, num_q_heads, head_dim]")
+        raise ValueError("q: expected a contiguous 2-byte (bf16 or f16) CUDA tensor [num_q_tokens, num_q_heads, head_dim]")
     eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2) else 2
     kv_numel = cfg.total_num_pages * cfg.page_size * 2 * cfg.num_kv_heads * D
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb
@@ -196,8 +198,8 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
             workspace=None, want_lse: bool = True, stream=None, sinks=None):
     """Ragged paged attention. Returns (out, lse) as torch tensors on the device.
 
-    q [T, Hq, D] bf16; kv_pages [P, page, 2*Hkv, D] bf16 or fp8 e4m3fn (uint8
-    storage accepted); kv_lens [S], page_indices [S, pps], cu_q_lens [S+1],
+    q [T, Hq, D] bf16 or f16 (cfg.q_dtype, also out's type); kv_pages
+    [P, page, 2*Hkv, D] in the q type or fp8 e4m3fn / e5m2 (uint8 storage); kv_lens [S], page_indices [S, pps], cu_q_lens [S+1],
     num_seqs [1]: int32 device tensors. Rows of padding tokens keep whatever
     `out`/`lse` held. `sinks`: optional float32 device tensor [Hq] of
     attention-sink logits (rpa_forward_sinks).
@@ -205,7 +207,8 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
     _check_inputs(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs)
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
     if out is None:
-        out = torch.zeros((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.zeros((T, Hq, D), dtype=torch.float16 if cfg.q_dtype == DTYPE_F16 else torch.bfloat16,
+                          device=q.device)
     elif not (out.is_cuda and out.is_contiguous() and out.element_size() == 2 and out.numel() == T * Hq * D):
         raise ValueError("out: expected a contiguous 2-byte CUDA tensor [T, Hq, D]")
     if want_lse and lse is None:
@@ -238,13 +241,13 @@ def kv_append(k_new, v_new, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs
               stream=None):
     """Write every query token's new K and V rows into kv_pages, in place (rpa_kv_append).
 
-    k_new, v_new [T, Hkv, D] bf16 CUDA tensors; the rest as in `forward`.
+    k_new, v_new [T, Hkv, D] CUDA tensors of the q type; the rest as in `forward`.
     Returns kv_pages.
     """
     T, Hkv, D = cfg.num_q_tokens, cfg.num_kv_heads, cfg.head_dim
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2 and t.numel() == T * Hkv * D):
-            raise ValueError(f"{name}: expected a contiguous 2-byte (bf16) CUDA tensor "
+            raise ValueError(f"{name}: expected a contiguous 2-byte (q dtype) CUDA tensor "
                              "[num_q_tokens, num_kv_heads, head_dim]")
     eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2) else 2
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb

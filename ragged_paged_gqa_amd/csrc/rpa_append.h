@@ -8,9 +8,10 @@
 // page_indices[s, j / page_size], K of kv head h in combined head 2h and V in
 // 2h+1 (`stridedLoadKv`). A stored value inverts the attention's dequant
 // factor: RN_f32(x / scale), rounded to nearest even in the cache type
-// (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN).
+// (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN). New rows
+// come in the q type (bf16 or f16).
 //
-// HBM-bound: per token 2*Hkv*D bf16 elements are read and 2*Hkv*D cache
+// HBM-bound: per token 2*Hkv*D 16-bit elements are read and 2*Hkv*D cache
 // elements written, contiguous on both sides. One wave per token; each lane
 // moves 16-byte chunks (8 elements), loads first, then converts and stores.
 #pragma once
@@ -32,11 +33,12 @@ enum ApMode : int {
   kApBf16 = 1,  // bf16 cache, general scales
   kApFp8 = 2,   // e4m3fn cache
   kApE5M2 = 3,  // e5m2 cache
+  kApF16 = 4,   // f16 cache, general scales
 };
 
 struct AppendParams {
-  const uint16_t* k_new;  // [T, Hkv, D] bf16 bits
-  const uint16_t* v_new;  // [T, Hkv, D] bf16 bits
+  const uint16_t* k_new;  // [T, Hkv, D] bits of the q type (bf16 or f16)
+  const uint16_t* v_new;  // [T, Hkv, D] bits of the q type
   void* kv;               // [P, page_size, 2*Hkv, D] cache elements
   const int32_t* kv_lens;
   const int32_t* page_indices;
@@ -63,8 +65,21 @@ __device__ __forceinline__ int ap_seq_of_token(const int32_t* cu, int nseq, int 
   return lo;
 }
 
-__device__ __forceinline__ float ap_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float ap_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// The low / high 16-bit element of a dword as f32 (exact), bf16 or f16.
+template <bool IN_F16>
+__device__ __forceinline__ float ap_lo(uint32_t w) {
+  if constexpr (IN_F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  else
+    return __uint_as_float(w << 16);
+}
+template <bool IN_F16>
+__device__ __forceinline__ float ap_hi(uint32_t w) {
+  if constexpr (IN_F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else
+    return __uint_as_float(w & 0xFFFF0000u);
+}
 
 // fp8 code pair (e4m3fn, or e5m2) of two f32 quotients into the low (HI
 // false) or high 16 bits of `old`: clamp to the finite range (NaN kept),
@@ -98,7 +113,7 @@ __device__ __forceinline__ void load_chunks(u32x4 (&x)[kApUnroll], const uint16_
 
 // Converts and stores the chunks load_chunks fetched; e_slot is the slot's
 // first cache element.
-template <int D, int MODE>
+template <int D, int MODE, bool IN_F16>
 __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const AppendParams& p, int64_t e_slot,
                                              int c0, int nch) {
   constexpr int CPR = D / 8;
@@ -115,13 +130,13 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
     float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[2 * i] = ap_bf16_lo(x[u][i]) / sc;
-      f[2 * i + 1] = ap_bf16_hi(x[u][i]) / sc;
+      f[2 * i] = ap_lo<IN_F16>(x[u][i]) / sc;
+      f[2 * i + 1] = ap_hi<IN_F16>(x[u][i]) / sc;
     }
-    if (MODE == kApBf16) {
+    if (MODE == kApBf16 || MODE == kApF16) {
       u32x4 y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = bf16x2_bits(f[2 * i], f[2 * i + 1]);
+      for (int i = 0; i < 4; ++i) y[i] = pack2<MODE == kApF16>(f[2 * i], f[2 * i + 1]);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
     } else {
       u32x2 y;
@@ -133,7 +148,7 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
   }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool IN_F16>
 __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p) {
   constexpr int CPR = D / 8;  // 16-byte chunks per head row
   const int lane = threadIdx.x & 63;
@@ -160,7 +175,7 @@ __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p
     if (page < 0 || page >= p.P) continue;
     const int64_t slot = (int64_t)page * p.page_size + pos % p.page_size;
     for (int c0 = lane;;) {
-      store_chunks<D, MODE>(x, p, slot * 2 * p.Hkv * D, c0, nch);
+      store_chunks<D, MODE, IN_F16>(x, p, slot * 2 * p.Hkv * D, c0, nch);
       c0 += 64 * kApUnroll;
       if (c0 >= nch) break;
       load_chunks<D>(x, kr, vr, c0, nch);

@@ -197,10 +197,50 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The 16-bit operand and output type of an attention path is bf16, or f16
+// (template parameter F16, the page's `Cfg` q_dtype). 16-bit vectors travel
+// as bf16x* bits either way; F16 picks the f16 conversions and MFMAs.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two f32 -> two 16-bit values (round to nearest even), lo in the low half.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (F16) {
+    const f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return bf16x2_bits(lo, hi);
+  }
+}
+
 // K/V element types of the attention kernels (template parameter KVT).
 constexpr int kKvBf16 = 0;
 constexpr int kKvE4M3 = 1;  // OCP fp8 e4m3fn
 constexpr int kKvE5M2 = 2;  // OCP fp8 e5m2
+
+// Eight fp8 codes (two dwords) -> eight f16, exactly: every e4m3fn and every
+// e5m2 value (infinities and NaN included) is an f16 value. (Bits in a bf16x8.)
+template <int KVT>
+__device__ __forceinline__ bf16x8 fp8x8_to_f16(u32x2 w) {
+  static_assert(KVT == kKvE4M3 || KVT == kKvE5M2, "an fp8 kind");
+  f16x2 a, b, c, d;
+  if constexpr (KVT == kKvE5M2) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w[0], 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w[0], 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w[1], 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w[1], 1.0f, true);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[0], 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[0], 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[1], 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[1], 1.0f, true);
+  }
+  const u32x4 r = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                   __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 // Eight fp8 codes (two dwords) -> eight bf16, exactly: every e4m3fn and every
 // e5m2 value (infinities and NaN included) is a bf16 value.
@@ -301,8 +341,22 @@ __device__ __forceinline__ float sum_xor32(float v) {
 __device__ __forceinline__ float wave_max_xor16_32(float v) { return max_xor32(max_xor16(v)); }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) { return sum_xor32(sum_xor16(v)); }
 
+// fp8 codes -> the path's 16-bit type.
+template <int KVT, bool F16>
+__device__ __forceinline__ bf16x8 fp8x8_to_16(u32x2 w) {
+  if constexpr (F16)
+    return fp8x8_to_f16<KVT>(w);
+  else
+    return fp8x8_to_bf16<KVT>(w);
+}
+
+template <bool F16>
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // LDS transpose read: within each 16-lane group, lane 4q+r receives element r

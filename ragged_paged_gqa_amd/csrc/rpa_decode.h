@@ -155,14 +155,19 @@ typedef const __attribute__((address_space(4))) int32_t cint32;
 __device__ __forceinline__ int sload(const int32_t* ptr) { return *(cint32*)(ptr); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <bool F16>
 __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
-                                                   0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                                 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                     0, 0);
 }
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel
 // carries no cap arithmetic at all).
-template <int D, int KVT, bool CAP>
+template <int D, int KVT, bool CAP, bool F16>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
     Params p) {
   constexpr bool FP8 = KVT != kKvBf16;
@@ -401,8 +406,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       if constexpr (FP8) {
-        ka[2 * j] = fp8x8_to_bf16<KVT>(u32x2{op.k[j][0], op.k[j][1]});
-        ka[2 * j + 1] = fp8x8_to_bf16<KVT>(u32x2{op.k[j][2], op.k[j][3]});
+        ka[2 * j] = fp8x8_to_16<KVT, F16>(u32x2{op.k[j][0], op.k[j][1]});
+        ka[2 * j + 1] = fp8x8_to_16<KVT, F16>(u32x2{op.k[j][2], op.k[j][3]});
       } else {
         ka[j] = __builtin_bit_cast(bf16x8, op.k[j]);
       }
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     // S^T: lane (col, g) gets keys kb + 4g + j of row `col`
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) sc = mfma16x16x32(ka[i], qb[i], sc);
+    for (int i = 0; i < NI; ++i) sc = mfma16x16x32<F16>(ka[i], qb[i], sc);
     // does the step hold a key that some row of the unit cannot see?
     const bool need_mask = kb + 16 > vis_hi || (p.is_causal && kb + 15 > pos_lo) ||
                            (p.window > 0 && kb <= pos_hi - p.window);
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       pj[j] = fast_exp2(sc[j] + negm);
       lsum += pj[j];
     }
-    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{bf16x2_bits(pj[0], pj[1]), bf16x2_bits(pj[2], pj[3])});
+    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{pack2<F16>(pj[0], pj[1]), pack2<F16>(pj[2], pj[3])});
 
     if constexpr (FP8) {
       // widen V to bf16 (rows past kv_len become 0) and stage it for the
@@ -460,8 +465,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       bf16x8 vw[2 * NLD];
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        vw[2 * j] = fp8x8_to_bf16<KVT>(u32x2{op.v[j][0], op.v[j][1]});
-        vw[2 * j + 1] = fp8x8_to_bf16<KVT>(u32x2{op.v[j][2], op.v[j][3]});
+        vw[2 * j] = fp8x8_to_16<KVT, F16>(u32x2{op.v[j][0], op.v[j][1]});
+        vw[2 * j + 1] = fp8x8_to_16<KVT, F16>(u32x2{op.v[j][2], op.v[j][3]});
       }
       if (kb + 16 > vis_hi) {  // (uniform) the step ends past vis_hi
         if (kb + col >= vis_hi) {
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       for (int d = 0; d < ND; ++d) {
         const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(
             st + vkey * (2 * D) + 16 * ((2 * d + (q4 >> 1)) ^ sswz<D>(vkey)) + 8 * (q4 & 1)));
-        o[d] = mfma16x16x16(a, pb, o[d]);
+        o[d] = mfma16x16x16<F16>(a, pb, o[d]);
       }
     } else {
       // V of keys at or past vis_hi reads as 0 (0 * NaN would poison the sum)
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
           for (int kk = 0; kk < 4; ++kk)
             if (kb + 4 * g + kk >= vis_hi) a[kk] = (__bf16)0.f;
         }
-        o[d] = mfma16x16x16(a, pb, o[d]);
+        o[d] = mfma16x16x16<F16>(a, pb, o[d]);
       }
     }
   };
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        u32x2 v = {bf16x2_bits(o[d][0] * inv, o[d][1] * inv), bf16x2_bits(o[d][2] * inv, o[d][3] * inv)};
+        u32x2 v = {pack2<F16>(o[d][0] * inv, o[d][1] * inv), pack2<F16>(o[d][2] * inv, o[d][3] * inv)};
         *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = v;
       }
       if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
@@ -623,7 +628,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
 // Merges the split decode-class units once every decode item is done: one
 // wave per unit, the items' partials combined by merge_unit; a unit with no
 // key to see (and so no item) gets out = 0 and lse = -inf.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params p) {
   __shared__ float stat[kDecWavesPerBlock][2 * kDecRows];
   const int lane = threadIdx.x & 63;
@@ -659,7 +664,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
       }
       continue;
     }
-    merge_unit<D>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
+    merge_unit<D, F16>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
     wave_sync();
   }
 }

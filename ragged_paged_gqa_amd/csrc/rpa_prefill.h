@@ -44,12 +44,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // The reference maximum of a row moves only when the row's maximum outgrows
 // it by more than this (base-2 units): exponentiated scores stay <= 2^16,
-// far inside f32 and bf16 range, and the accumulator rescale (which leaves
-// the step loop, see below) is rare.
+// far inside f32 and bf16 range (one less for f16 P, whose largest finite
+// value is 65504), and the accumulator rescale (which leaves the step loop,
+// see below) is rare.
 constexpr float kRescaleSlack = 16.0f;
 
+template <bool F16>
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Keys per load step (one LDS ring slot, one barrier). Scores are computed
@@ -99,9 +105,11 @@ __device__ __forceinline__ int swz_v(int key) {
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
 // block loop has no branch and no cap arithmetic).
-template <int D, int KVT, bool CAP>
+template <int D, int KVT, bool CAP, bool F16>
 __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
   constexpr bool FP8 = KVT != kKvBf16;
+  // f16 P must stay below 65504: exponentiated scores <= 2^15
+  constexpr float SLACK = F16 ? kRescaleSlack - 1.0f : kRescaleSlack;
   constexpr int NW = kPfWaves;
   constexpr int NH = pf_halves_for(D);        // 32-row halves per wave
   constexpr int WR = 32 * NH;                 // rows per wave
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
         // (this lambda is also compiled, unused, into the bf16 kernels)
         constexpr int F8 = KVT == kKvE5M2 ? kKvE5M2 : kKvE4M3;
-        bf16x8 a = fp8x8_to_bf16<F8>(lo2), b = fp8x8_to_bf16<F8>(hi2);
+        bf16x8 a = fp8x8_to_16<F8, F16>(lo2), b = fp8x8_to_16<F8, F16>(hi2);
         if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
           a = bf16x8{};
           b = bf16x8{};
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       for (int hf = 0; hf < NH; ++hf) {
         f32x16 sc = f32x16{};
 #pragma unroll
-        for (int i = 0; i < NS; ++i) sc = mfma32x32x16(ka[i], qb[hf][i], sc);
+        for (int i = 0; i < NS; ++i) sc = mfma32x32x16<F16>(ka[i], qb[hf][i], sc);
 #pragma unroll
         for (int j = 0; j < 16; ++j) sv[hf][j] = sc[j];
       }
@@ -473,7 +481,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     auto needs_rescale = [&](const float (&mb)[NH]) {
       bool any = false;
 #pragma unroll
-      for (int hf = 0; hf < NH; ++hf) any = any || mb[hf] > m_ref[hf] + kRescaleSlack;
+      for (int hf = 0; hf < NH; ++hf) any = any || mb[hf] > m_ref[hf] + SLACK;
       return __any(any);
     };
     auto rescale = [&](const float (&mb)[NH]) {
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
             const float p0 = fast_exp2(kLate ? __builtin_fmaf(s0, cmul, negm[hf]) : s0 + negm[hf]);
             const float p1 = fast_exp2(kLate ? __builtin_fmaf(s1, cmul, negm[hf]) : s1 + negm[hf]);
             lsum[hf] += p0 + p1;
-            const bf16x2 pair = {(__bf16)p0, (__bf16)p1};
+            const bf16x2 pair = __builtin_bit_cast(bf16x2, pack2<F16>(p0, p1));
             pb[hf][jp >> 2][2 * (jp & 3)] = pair[0];
             pb[hf][jp >> 2][2 * (jp & 3) + 1] = pair[1];
           };
@@ -595,7 +603,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
 #pragma unroll
-            for (int hf = 0; hf < NH; ++hf) sc_next[hf] = mfma32x32x16(ka[i], qb[hf][i], sc_next[hf]);
+            for (int hf = 0; hf < NH; ++hf) sc_next[hf] = mfma32x32x16<F16>(ka[i], qb[hf][i], sc_next[hf]);
             if (i + KA < NS) ka[i + KA] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i + KA));
 #pragma unroll
             for (int q = PRE + ((NPP - PRE) * i) / NS; q < PRE + ((NPP - PRE) * (i + 1)) / NS; ++q) p_pair(q);
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
             if (m + VA < NM) read_va(m + VA);
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf)
-              o[hf][m % NDB] = mfma32x32x16(va[m], pb[hf][m / NDB], o[hf][m % NDB]);
+              o[hf][m % NDB] = mfma32x32x16<F16>(va[m], pb[hf][m / NDB], o[hf][m % NDB]);
 #pragma unroll
             for (int e = (16 * NH * m) / NM; e < (16 * NH * (m + 1)) / NM; ++e) {
               const int hf = e >> 4, j = e & 15;
@@ -658,8 +666,8 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            u32x2 w = {bf16x2_bits(o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv),
-                       bf16x2_bits(o[hf][d][4 * q4 + 2] * inv, o[hf][d][4 * q4 + 3] * inv)};
+            u32x2 w = {pack2<F16>(o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv),
+                       pack2<F16>(o[hf][d][4 * q4 + 2] * inv, o[hf][d][4 * q4 + 3] * inv)};
             *reinterpret_cast<u32x2*>(op + 32 * d + 8 * q4) = w;
           }
         if (h == 0 && p.lse) p.lse[(int64_t)tok[hf] * p.Hq + qh[hf]] = lse_v;
@@ -686,7 +694,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         // the LDS ring is idle here (every wave is past its last step); it
         // holds the per-row stats of the merge
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
+        merge_unit<D, F16>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
       }
     }
     // every wave must be done with the ring before the next item refills it

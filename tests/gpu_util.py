@@ -24,7 +24,9 @@ def lib_config(w: wl.Workload) -> rpa.Config:
         num_q_tokens=c.num_q_tokens, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
         head_dim=c.head_dim, total_num_pages=c.total_num_pages, page_size=c.page_size,
         max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq,
-        kv_dtype={wl.KV_FP8: rpa.DTYPE_FP8_E4M3FN, wl.KV_E5M2: rpa.DTYPE_FP8_E5M2}.get(c.kv_dtype, rpa.DTYPE_BF16),
+        kv_dtype={wl.KV_FP8: rpa.DTYPE_FP8_E4M3FN, wl.KV_E5M2: rpa.DTYPE_FP8_E5M2,
+                  wl.KV_F16: rpa.DTYPE_F16}.get(c.kv_dtype, rpa.DTYPE_BF16),
+        q_dtype=rpa.DTYPE_F16 if c.q_dtype == wl.Q_F16 else rpa.DTYPE_BF16,
         sm_scale=c.sm_scale, soft_cap=c.soft_cap or 0.0,
         k_scale=1.0 if c.k_scale is None else c.k_scale,
         v_scale=1.0 if c.v_scale is None else c.v_scale,
@@ -37,11 +39,12 @@ class Device:
     def __init__(self, w: wl.Workload, device="cuda"):
         self.w = w
         self.cfg = lib_config(w)
-        self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
+        t16 = torch.float16 if w.cfg.q_dtype == wl.Q_F16 else torch.bfloat16
+        self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(t16)
         if wl.is_fp8(w.cfg.kv_dtype):
             self.kv = torch.from_numpy(w.kv_pages).to(device)
         else:
-            self.kv = torch.from_numpy(w.kv_pages.view(np.int16)).to(device).view(torch.bfloat16)
+            self.kv = torch.from_numpy(w.kv_pages.view(np.int16)).to(device).view(t16)
         self.kv_lens = torch.from_numpy(w.kv_lens).to(device)
         self.page_indices = torch.from_numpy(w.page_indices).to(device)
         self.cu_q_lens = torch.from_numpy(w.cu_q_lens).to(device)

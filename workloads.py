@@ -296,9 +296,10 @@ def cfg_kw(number: int) -> dict:
 
 
 def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
-          seed: int | None = None, kv_dtype: str | None = None) -> Workload:
+          seed: int | None = None, kv_dtype: str | None = None, q_dtype: str | None = None) -> Workload:
     """A named workload; `kv_dtype` swaps its K/V type (fp8 kinds take the fp8
-    decode workload's scales, 0.05, when the workload has none)."""
+    decode workload's scales, 0.05, when the workload has none) and `q_dtype`
+    its q/out type (with f16 q a bf16 cache becomes f16)."""
     seed = number if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     q_lens, kv_lens = lengths(number, rng)
@@ -306,6 +307,10 @@ def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
     if number == 1:
         kw["total_num_pages"] = 32
     ckw = cfg_kw(number)
+    if q_dtype == Q_F16:
+        ckw["q_dtype"] = Q_F16
+        if kv_dtype is None and ckw.get("kv_dtype", KV_BF16) == KV_BF16:
+            kv_dtype = KV_F16
     if kv_dtype is not None:
         ckw["kv_dtype"] = kv_dtype
         if is_fp8(kv_dtype):
