@@ -25,7 +25,7 @@ _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_BUILD, "librpa_oracle.so")
 
-KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2, "f16": 3}
+KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2, "f16": 3, "int8": 4}
 Q_CODES = {"bf16": 0, "f16": 3}
 
 
@@ -82,6 +82,8 @@ def lib():
         L.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_f16_to_f64.restype = ctypes.c_double
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_i8.restype = ctypes.c_int8
+        L.oracle_f32_to_i8.argtypes = [ctypes.c_float]
         L.oracle_f32_to_f16.restype = ctypes.c_uint16
         L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_e5m2.restype = ctypes.c_uint8
@@ -202,6 +204,13 @@ def f16_to_f64(bits) -> np.ndarray:
     L = lib()
     b = np.asarray(bits, dtype=np.uint16).ravel()
     return np.array([L.oracle_f16_to_f64(int(x)) for x in b]).reshape(np.shape(bits))
+
+
+def f32_to_i8(x) -> np.ndarray:
+    """Element-wise f32 -> int8 code (nearest integer, ties to even, saturating; NaN -> 0)."""
+    f = lib().oracle_f32_to_i8
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.int8).reshape(a.shape)
 
 
 def f32_to_f16(x) -> np.ndarray:

@@ -43,8 +43,9 @@
  *     the dtypes (`Cfg` kv_dtype, f8e4m3fn and f8e5m2);
  *   - dequantised values are code*scale exactly (f64), not re-rounded to the
  *     q dtype;
- *   - q (and out) are bf16 or f16 (`Cfg` q_dtype); K/V bf16, f16, e4m3fn or
- *     e5m2 (`Cfg` kv_dtype), all read exactly.
+ *   - q (and out) are bf16 or f16 (`Cfg` q_dtype); K/V bf16, f16, e4m3fn,
+ *     e5m2 or int8 (`Cfg` kv_dtype; int8 codes are signed integers times the
+ *     scale), all read exactly.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +56,7 @@
 #define ORACLE_KV_E4M3FN 1
 #define ORACLE_KV_E5M2 2
 #define ORACLE_F16 3 /* IEEE binary16: q/out type, or K/V type */
+#define ORACLE_KV_I8 4 /* signed 8-bit integer codes */
 
 typedef struct {
   int32_t num_q_tokens;
@@ -65,7 +67,7 @@ typedef struct {
   int32_t page_size;
   int32_t max_num_seqs;
   int32_t pages_per_seq;
-  int32_t kv_dtype;       /* ORACLE_KV_BF16, ORACLE_KV_E4M3FN, ORACLE_KV_E5M2 or ORACLE_F16 */
+  int32_t kv_dtype;       /* ORACLE_KV_BF16, ORACLE_KV_E4M3FN, ORACLE_KV_E5M2, ORACLE_F16 or ORACLE_KV_I8 */
   int32_t is_causal;      /* 0 or 1 */
   int32_t sliding_window; /* <= 0: no window */
   int32_t has_soft_cap;   /* 0 or 1 */
@@ -153,6 +155,7 @@ static double kv_elem(const oracle_cfg* c, const void* kv_pages, int64_t idx) {
   if (c->kv_dtype == ORACLE_KV_E4M3FN) return oracle_e4m3fn_to_f64(((const uint8_t*)kv_pages)[idx]);
   if (c->kv_dtype == ORACLE_KV_E5M2) return oracle_e5m2_to_f64(((const uint8_t*)kv_pages)[idx]);
   if (c->kv_dtype == ORACLE_F16) return oracle_f16_to_f64(((const uint16_t*)kv_pages)[idx]);
+  if (c->kv_dtype == ORACLE_KV_I8) return (double)((const int8_t*)kv_pages)[idx];
   return oracle_bf16_to_f64(((const uint16_t*)kv_pages)[idx]);
 }
 
@@ -318,7 +321,9 @@ int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages,
  * rounded to the cache type to nearest with ties to even; e4m3fn saturates
  * at +-448 (it has no infinity) and e5m2 the same way at +-57344 (its
  * largest finite value), bf16 and f16 overflow to +-inf as IEEE rounding
- * does. NaN inputs give a NaN code. The new rows come in the q dtype.
+ * does; int8 rounds to an integer, ties to even, saturating at -128 and
+ * 127. NaN inputs give a NaN code (int8: 0). The new rows come in the q
+ * dtype.
  * ------------------------------------------------------------------------ */
 
 /* v rounded to the nearest value of a binary format with `mbits` stored
@@ -381,6 +386,16 @@ uint16_t oracle_f32_to_f16(float x) {
   return sign | (uint16_t)(((ex + 15) << 10) | m);
 }
 
+/* f32 -> int8 code: round to the nearest integer, ties to even, saturating
+ * at -128 and 127; NaN stores 0 (an integer code has no NaN). */
+int8_t oracle_f32_to_i8(float x) {
+  if (isnan(x)) return 0;
+  double r = nearbyint((double)x); /* default mode: nearest, ties to even */
+  if (r < -128.0) r = -128.0;
+  if (r > 127.0) r = 127.0;
+  return (int8_t)r;
+}
+
 /* f32 -> bf16 bits, round to nearest even; overflow gives +-inf. */
 uint16_t oracle_f32_to_bf16(float x) {
   uint32_t w;
@@ -406,6 +421,8 @@ static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_
     ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e5m2(y);
   else if (c->kv_dtype == ORACLE_F16)
     ((uint16_t*)kv_pages)[idx] = oracle_f32_to_f16(y);
+  else if (c->kv_dtype == ORACLE_KV_I8)
+    ((int8_t*)kv_pages)[idx] = oracle_f32_to_i8(y);
   else
     ((uint16_t*)kv_pages)[idx] = oracle_f32_to_bf16(y);
 }

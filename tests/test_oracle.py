@@ -5,8 +5,9 @@ library routine, so that a plausible slip in it (a dropped term, a swapped K/V
 head, a wrong causal offset or GQA index) fails at least one test:
 
 * dtype decode          - torch's own casts (numpy's for f16), plus printed
-                          e4m3fn, e5m2 and binary16 values; fp8 caches and f16
-                          q / K/V end to end against sdpa over those decodes
+                          e4m3fn, e5m2 and binary16 values; fp8 and int8
+                          caches and f16 q / K/V end to end against sdpa over
+                          those decodes (int8: numpy's signed byte x scale)
 * softmax/PV/GQA/scale  - torch.scaled_dot_product_attention in f64
 * causal offsets        - Q = 0 closed form: lse = ln(#visible keys)
 * window boundary       - window 1 returns V at the query position exactly;
@@ -48,7 +49,9 @@ def _seq_kv(w, s, comb):
     phys = w.page_indices[s, idx // c.page_size]
     slot = idx % c.page_size
     bits = w.kv_pages[phys, slot]  # [kv_len, 2Hkv, D]
-    if wl.is_fp8(c.kv_dtype):
+    if c.kv_dtype == wl.KV_I8:
+        vals = bits.view(np.int8).astype(np.float64) * (c.k_scale if comb == 0 else c.v_scale)
+    elif wl.is_fp8(c.kv_dtype):
         tdt = torch.float8_e4m3fn if c.kv_dtype == wl.KV_FP8 else torch.float8_e5m2
         vals = torch.from_numpy(bits.copy()).view(tdt).to(torch.float64).numpy()
         scale = (c.k_scale if comb == 0 else c.v_scale)
@@ -178,7 +181,7 @@ def test_matches_torch_sdpa_square(G, Hkv, D, kv_len, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("kv_dtype", [wl.KV_FP8, wl.KV_E5M2])
+@pytest.mark.parametrize("kv_dtype", [wl.KV_FP8, wl.KV_E5M2, wl.KV_I8])
 def test_fp8_cache_matches_torch_sdpa_on_decoded_values(kv_dtype):
     """fp8 K/V (each kind) are read as code * scale: the oracle equals sdpa in
     f64 over torch's own decode of the same codes, scaled."""
@@ -195,7 +198,7 @@ def test_fp8_cache_matches_torch_sdpa_on_decoded_values(kv_dtype):
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("kv_dtype", [wl.KV_F16, wl.KV_FP8, wl.KV_E5M2])
+@pytest.mark.parametrize("kv_dtype", [wl.KV_F16, wl.KV_FP8, wl.KV_E5M2, wl.KV_I8])
 def test_f16_q_matches_torch_sdpa_on_decoded_values(kv_dtype):
     """f16 q (the page's `Cfg` q_dtype) with f16 or fp8 K/V: sdpa in f64 over
     numpy's / torch's decode of the same bits."""
@@ -346,7 +349,7 @@ def test_soft_cap_closed_form_end_to_end():
 
 # ----------------------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2, wl.KV_F16])
+@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2, wl.KV_F16, wl.KV_I8])
 def test_page_permutation_invariance(kv_dtype):
     w = wl.random_small(21, max_seqs=4, kv_dtype=kv_dtype, window=9,
                         q_dtype=wl.Q_F16 if kv_dtype == wl.KV_F16 else wl.Q_BF16)

@@ -12,6 +12,8 @@
                    torch's float8_e4m3fn cast after clamping
 * e5m2 rounding  - the same brute force over the finite e5m2 codes (saturation
                    at +-57344) and torch's float8_e5m2 cast
+* int8 rounding  - numpy's rint (ties to even) and clip to [-128, 127] over every
+                   finite bf16 value and the half-integers around the range
 * f16 rounding   - numpy's float32 -> float16 cast (random patterns, midpoints,
                    the overflow edge); rows in f16 (f16 q) into f16 and fp8 caches
 * bf16 rounding  - torch's float32 -> bfloat16 cast on random bit patterns,
@@ -263,6 +265,15 @@ def test_f16_rows_append_into_f16_and_fp8_caches():
             else:
                 assert np.array_equal(kv[page, slot, 0::2].ravel(), brute_e4m3fn(qk))
                 assert np.array_equal(kv[page, slot, 1::2].ravel(), brute_e4m3fn(qv))
+
+
+def test_i8_rounding_matches_numpy_rint_and_clip():
+    x = _f32(wl.finite_bf16_patterns())
+    halves = np.arange(-140, 140, dtype=np.float32) + np.float32(0.5)   # ties: to even
+    x = np.concatenate([x, halves, np.nextafter(halves, np.float32(np.inf)), np.nextafter(halves, np.float32(-np.inf))])
+    ref = np.clip(np.rint(x.astype(np.float64)), -128, 127).astype(np.int8)
+    assert np.array_equal(oracle.f32_to_i8(x), ref)
+    assert oracle.f32_to_i8(np.float32([np.nan]))[0] == 0
 
 
 def test_bf16_rounding_matches_torch_cast():

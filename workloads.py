@@ -22,7 +22,8 @@ the workload's number as seed; draw order lengths -> page permutation -> Q
 the permutation; unused page-table entries hold 0 (or a poison value).
 Q/K/V values are N(0,1) rounded to bf16 (round to nearest even); fp8 K/V are
 N(0,1)/scale rounded to e4m3fn (saturated at +-448) or to e5m2 (saturated at
-+-57344). K/V pages are drawn in
++-57344); int8 K/V are N(0,1)/scale rounded to the nearest integer (saturated
+at -128 / 127). K/V pages are drawn in
 chunks of ``PAGE_CHUNK`` pages, each from its own spawned PCG64 stream, so
 large caches are generated in parallel yet identically on every machine.
 """
@@ -43,14 +44,16 @@ KV_BF16 = "bf16"
 KV_FP8 = "fp8_e4m3fn"
 KV_E5M2 = "fp8_e5m2"
 KV_F16 = "f16"
+KV_I8 = "int8"
 Q_BF16 = "bf16"
 Q_F16 = "f16"
 FP8_KINDS = (KV_FP8, KV_E5M2)
+ONE_BYTE_KINDS = (KV_FP8, KV_E5M2, KV_I8)
 
 
 def is_fp8(kv_dtype: str) -> bool:
-    """One-byte K/V codes (e4m3fn or e5m2)."""
-    return kv_dtype in FP8_KINDS
+    """One-byte K/V codes with a scale (e4m3fn, e5m2 or int8)."""
+    return kv_dtype in ONE_BYTE_KINDS
 
 
 @dataclasses.dataclass
@@ -131,6 +134,11 @@ def to_q_bits(x: np.ndarray, q_dtype: str) -> np.ndarray:
     return to_f16_bits(x) if q_dtype == Q_F16 else to_bf16_bits(x)
 
 
+def to_i8_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> int8 codes: nearest integer (ties to even), saturated at -128 / 127."""
+    return np.clip(np.rint(np.ascontiguousarray(x, dtype=np.float32)), -128, 127).astype(np.int8).view(np.uint8)
+
+
 def to_e5m2_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> fp8 e5m2 bits, saturated at +-57344 then rounded to nearest even."""
     x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -57344.0, 57344.0)
@@ -162,6 +170,8 @@ def _fill_kv(kv: np.ndarray, seed: int, kv_dtype: str, scale: float | None,
             kv[p0:p1] = to_e5m2_bits(z / np.float32(scale)).reshape(kv[p0:p1].shape)
         elif kv_dtype == KV_F16:
             kv[p0:p1] = to_f16_bits(z).reshape(kv[p0:p1].shape)
+        elif kv_dtype == KV_I8:
+            kv[p0:p1] = to_i8_codes(z / np.float32(scale)).reshape(kv[p0:p1].shape)
         else:
             kv[p0:p1] = to_bf16_bits(z).reshape(kv[p0:p1].shape)
 
