@@ -58,7 +58,7 @@ def algorithmic_work(w):
     kernel class that handles each sequence (<= 16 packed rows: decode)."""
     c = w.cfg
     G = c.num_q_heads // c.num_kv_heads
-    b_kv = 1 if c.kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2  # bf16 and f16: 2
+    b_kv = 1 if c.kv_dtype in ("fp8_e4m3fn", "fp8_e5m2", "int8") else 2  # bf16 and f16: 2
     sw = c.sliding_window or 0
     res = {"decode": [0.0, 0.0, 0], "prefill": [0.0, 0.0, 0]}  # flops, bytes, tokens
     for s in range(w.n_seqs):
@@ -177,7 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kv-dtype", choices=["bf16", "f16", "fp8_e4m3fn", "fp8_e5m2"], default=None,
+    ap.add_argument("--kv-dtype", choices=["bf16", "f16", "fp8_e4m3fn", "fp8_e5m2", "int8"], default=None,
                     help="store the workload's K/V cache in this type instead of its own")
     ap.add_argument("--q-dtype", choices=["bf16", "f16"], default=None,
                     help="q/out type (f16: a bf16 cache becomes f16 too)")

@@ -43,6 +43,7 @@ typedef enum {
   RPA_DTYPE_FP8_E4M3FN = 1, /* OCP FP8 E4M3 (finite, NaN = S.1111.111) */
   RPA_DTYPE_FP8_E5M2 = 2,   /* OCP FP8 E5M2 (bias 15, infinities and NaN at exponent 31) */
   RPA_DTYPE_F16 = 3,        /* IEEE binary16 */
+  RPA_DTYPE_INT8 = 4,       /* signed 8-bit integer codes (K/V only; value = code * scale) */
 } rpa_dtype;
 
 typedef enum {
@@ -69,7 +70,7 @@ typedef struct rpa_config {
   int32_t max_num_seqs;    /* rows of page_indices and kv_lens */
   int32_t pages_per_seq;   /* columns of page_indices */
   int32_t q_dtype;         /* rpa_dtype of q and out: RPA_DTYPE_BF16 or RPA_DTYPE_F16 */
-  int32_t kv_dtype;        /* rpa_dtype: q_dtype, RPA_DTYPE_FP8_E4M3FN or RPA_DTYPE_FP8_E5M2 */
+  int32_t kv_dtype;        /* rpa_dtype: q_dtype, RPA_DTYPE_FP8_E4M3FN, RPA_DTYPE_FP8_E5M2 or RPA_DTYPE_INT8 */
   float sm_scale;          /* score scale, finite */
   float soft_cap;          /* > 0: cap on; 0: off */
   float k_scale;           /* dequant factor of K; 1.0f for none */
@@ -154,8 +155,9 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
  * Stored value: RN_f32(x / scale) with scale = k_scale for K and v_scale for
  * V (IEEE binary32 division), rounded to nearest even in kv_dtype; e4m3fn
  * saturates at +-448 and e5m2 at +-57344, bf16 and f16 overflow to +-inf; a
- * NaN input stores a NaN. With a 16-bit cache and both scales 1 this is a
- * bit copy. Device pointers, owned by the
+ * NaN input stores a NaN; int8 stores the nearest integer (ties to even)
+ * saturated to [-128, 127], and 0 for NaN. With a 16-bit cache and both
+ * scales 1 this is a bit copy. Device pointers, owned by the
  * caller; k_new, v_new and kv_pages 16-byte aligned; k_new/v_new must not
  * overlap kv_pages. Tokens past cu_q_lens[num_seqs] and tokens whose position
  * or page id falls outside the table (a broken precondition) write nothing;

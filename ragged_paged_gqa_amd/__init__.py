@@ -26,6 +26,7 @@ DTYPE_BF16 = 0
 DTYPE_FP8_E4M3FN = 1
 DTYPE_FP8_E5M2 = 2
 DTYPE_F16 = 3
+DTYPE_INT8 = 4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "HIP runtime error", 5: "metadata violates a precondition"}
@@ -177,7 +178,7 @@ def _check_inputs(cfg: Config, q, kv_pages, kv_lens, page_indices, cu_q_lens, nu
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
     if not (q.is_cuda and q.is_contiguous() and q.element_size() == 2 and q.numel() == T * Hq * D):
         raise ValueError("q: expected a contiguous 2-byte (bf16 or f16) CUDA tensor [num_q_tokens, num_q_heads, head_dim]")
-    eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2) else 2
+    eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2, DTYPE_INT8) else 2
     kv_numel = cfg.total_num_pages * cfg.page_size * 2 * cfg.num_kv_heads * D
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb
             and kv_pages.numel() == kv_numel):
@@ -249,7 +250,7 @@ def kv_append(k_new, v_new, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs
         if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2 and t.numel() == T * Hkv * D):
             raise ValueError(f"{name}: expected a contiguous 2-byte (q dtype) CUDA tensor "
                              "[num_q_tokens, num_kv_heads, head_dim]")
-    eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2) else 2
+    eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2, DTYPE_INT8) else 2
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb
             and kv_pages.numel() == cfg.total_num_pages * cfg.page_size * 2 * Hkv * D):
         raise ValueError("kv_pages: expected a contiguous CUDA tensor "

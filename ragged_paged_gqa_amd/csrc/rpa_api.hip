@@ -71,7 +71,8 @@ rpa_status validate(const rpa_config* c) {
   if (c->page_size % 16 != 0 || c->page_size > 1024) return RPA_ERR_UNSUPPORTED;
   // q (and out) bf16 or f16; K/V in the q type, or an fp8 kind
   if (c->q_dtype != RPA_DTYPE_BF16 && c->q_dtype != RPA_DTYPE_F16) return RPA_ERR_UNSUPPORTED;
-  if (c->kv_dtype != c->q_dtype && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN && c->kv_dtype != RPA_DTYPE_FP8_E5M2)
+  if (c->kv_dtype != c->q_dtype && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN && c->kv_dtype != RPA_DTYPE_FP8_E5M2 &&
+      c->kv_dtype != RPA_DTYPE_INT8)
     return RPA_ERR_UNSUPPORTED;
   return RPA_OK;
 }
@@ -89,7 +90,8 @@ int dec_grid(int cus) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 int dec_grid_for(const rpa_config* c, int cus) {
-  const bool fp8 = c->kv_dtype == RPA_DTYPE_FP8_E4M3FN || c->kv_dtype == RPA_DTYPE_FP8_E5M2;
+  const bool fp8 = c->kv_dtype == RPA_DTYPE_FP8_E4M3FN || c->kv_dtype == RPA_DTYPE_FP8_E5M2 ||
+                   c->kv_dtype == RPA_DTYPE_INT8;
   switch (c->head_dim) {
     case 64: return fp8 ? dec_grid<64, true>(cus) : dec_grid<64, false>(cus);
     case 128: return fp8 ? dec_grid<128, true>(cus) : dec_grid<128, false>(cus);
@@ -246,6 +248,7 @@ rpa_status launch_for_kv(int32_t q_dtype, int32_t kv_dtype, const Params& p, int
       case RPA_DTYPE_F16: return launch_attention<D, kKvBf16, true>(p, cus, st, ev);
       case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, true>(p, cus, st, ev);
       case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, true>(p, cus, st, ev);
+      case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, true>(p, cus, st, ev);
       default: return RPA_ERR_UNSUPPORTED;
     }
   }
@@ -253,6 +256,7 @@ rpa_status launch_for_kv(int32_t q_dtype, int32_t kv_dtype, const Params& p, int
     case RPA_DTYPE_BF16: return launch_attention<D, kKvBf16, false>(p, cus, st, ev);
     case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, false>(p, cus, st, ev);
     case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, false>(p, cus, st, ev);
+    case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, false>(p, cus, st, ev);
     default: return RPA_ERR_UNSUPPORTED;
   }
 }
@@ -268,6 +272,7 @@ void launch_append_in(int mode, int grid, hipStream_t st, const AppendParams& p)
   switch (mode) {
     case kApFp8: hipLaunchKernelGGL((kv_append_kernel<D, kApFp8, IN_F16>), dim3(grid), blk, 0, st, p); break;
     case kApE5M2: hipLaunchKernelGGL((kv_append_kernel<D, kApE5M2, IN_F16>), dim3(grid), blk, 0, st, p); break;
+    case kApI8: hipLaunchKernelGGL((kv_append_kernel<D, kApI8, IN_F16>), dim3(grid), blk, 0, st, p); break;
     case kApCopy: hipLaunchKernelGGL((kv_append_kernel<D, kApCopy, IN_F16>), dim3(grid), blk, 0, st, p); break;
     case kApF16: hipLaunchKernelGGL((kv_append_kernel<D, kApF16, IN_F16>), dim3(grid), blk, 0, st, p); break;
     default: hipLaunchKernelGGL((kv_append_kernel<D, kApBf16, IN_F16>), dim3(grid), blk, 0, st, p); break;
@@ -524,6 +529,7 @@ rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v
   const bool in_f16 = cfg->q_dtype == RPA_DTYPE_F16;  // the new rows' type
   const int mode = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN             ? kApFp8
                    : cfg->kv_dtype == RPA_DTYPE_FP8_E5M2             ? kApE5M2
+                   : cfg->kv_dtype == RPA_DTYPE_INT8                 ? kApI8
                    : (cfg->k_scale == 1.f && cfg->v_scale == 1.f) ? kApCopy
                    : in_f16                                          ? kApF16
                                                                      : kApBf16;

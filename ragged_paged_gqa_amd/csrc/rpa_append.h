@@ -8,7 +8,8 @@
 // page_indices[s, j / page_size], K of kv head h in combined head 2h and V in
 // 2h+1 (`stridedLoadKv`). A stored value inverts the attention's dequant
 // factor: RN_f32(x / scale), rounded to nearest even in the cache type
-// (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN). New rows
+// (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN; int8 rounds
+// to an integer, ties to even, saturating at -128 / 127, NaN to 0). New rows
 // come in the q type (bf16 or f16).
 //
 // HBM-bound: per token 2*Hkv*D 16-bit elements are read and 2*Hkv*D cache
@@ -34,6 +35,7 @@ enum ApMode : int {
   kApFp8 = 2,   // e4m3fn cache
   kApE5M2 = 3,  // e5m2 cache
   kApF16 = 4,   // f16 cache, general scales
+  kApI8 = 5,    // int8 cache
 };
 
 struct AppendParams {
@@ -138,6 +140,16 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = pack2<MODE == kApF16>(f[2 * i], f[2 * i + 1]);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = y;
+    } else if (MODE == kApI8) {
+      // nearest integer, ties to even, saturated to [-128, 127]; NaN -> 0
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r = __builtin_rintf(__builtin_amdgcn_fmed3f(f[i], -128.f, 127.f));
+        b[i] = (uint32_t)(f[i] == f[i] ? (int)r : 0) & 0xFFu;
+      }
+      const u32x2 y = {b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.kv) + e0) = y;
     } else {
       u32x2 y;
       constexpr bool E5 = MODE == kApE5M2;

@@ -219,6 +219,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 constexpr int kKvBf16 = 0;
 constexpr int kKvE4M3 = 1;  // OCP fp8 e4m3fn
 constexpr int kKvE5M2 = 2;  // OCP fp8 e5m2
+constexpr int kKvI8 = 3;    // signed 8-bit integer codes
 
 // Eight fp8 codes (two dwords) -> eight f16, exactly: every e4m3fn and every
 // e5m2 value (infinities and NaN included) is an f16 value. (Bits in a bf16x8.)
@@ -341,10 +342,26 @@ __device__ __forceinline__ float sum_xor32(float v) {
 __device__ __forceinline__ float wave_max_xor16_32(float v) { return max_xor32(max_xor16(v)); }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) { return sum_xor32(sum_xor16(v)); }
 
-// fp8 codes -> the path's 16-bit type.
+// Eight int8 codes (two dwords, element k in byte k) -> eight bf16 or f16,
+// exactly (|code| <= 128 needs 8 significant bits).
+template <bool F16>
+__device__ __forceinline__ bf16x8 i8x8_to_16(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = w[i >> 1];
+    const int sh = 16 * (i & 1);
+    r[i] = pack2<F16>((float)(int8_t)(word >> sh), (float)(int8_t)(word >> (sh + 8)));
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// One-byte K/V codes (fp8 kinds, int8) -> the path's 16-bit type.
 template <int KVT, bool F16>
 __device__ __forceinline__ bf16x8 fp8x8_to_16(u32x2 w) {
-  if constexpr (F16)
+  if constexpr (KVT == kKvI8)
+    return i8x8_to_16<F16>(w);
+  else if constexpr (F16)
     return fp8x8_to_f16<KVT>(w);
   else
     return fp8x8_to_bf16<KVT>(w);

@@ -170,7 +170,7 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 template <int D, int KVT, bool CAP, bool F16>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
     Params p) {
-  constexpr bool FP8 = KVT != kKvBf16;
+  constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8)
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
                 NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, NST = Cf::NST;

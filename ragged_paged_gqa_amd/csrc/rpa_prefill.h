@@ -107,7 +107,7 @@ __device__ __forceinline__ int swz_v(int key) {
 // block loop has no branch and no cap arithmetic).
 template <int D, int KVT, bool CAP, bool F16>
 __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
-  constexpr bool FP8 = KVT != kKvBf16;
+  constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8), widened in registers
   // f16 P must stay below 65504: exponentiated scores <= 2^15
   constexpr float SLACK = F16 ? kRescaleSlack - 1.0f : kRescaleSlack;
   constexpr int NW = kPfWaves;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         char* row_p = dst + region * REG + key * RB;
         u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
         // (this lambda is also compiled, unused, into the bf16 kernels)
-        constexpr int F8 = KVT == kKvE5M2 ? kKvE5M2 : kKvE4M3;
+        constexpr int F8 = KVT == kKvBf16 ? kKvE4M3 : KVT;
         bf16x8 a = fp8x8_to_16<F8, F16>(lo2), b = fp8x8_to_16<F8, F16>(hi2);
         if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
           a = bf16x8{};

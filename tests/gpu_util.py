@@ -25,7 +25,7 @@ def lib_config(w: wl.Workload) -> rpa.Config:
         head_dim=c.head_dim, total_num_pages=c.total_num_pages, page_size=c.page_size,
         max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq,
         kv_dtype={wl.KV_FP8: rpa.DTYPE_FP8_E4M3FN, wl.KV_E5M2: rpa.DTYPE_FP8_E5M2,
-                  wl.KV_F16: rpa.DTYPE_F16}.get(c.kv_dtype, rpa.DTYPE_BF16),
+                  wl.KV_F16: rpa.DTYPE_F16, wl.KV_I8: rpa.DTYPE_INT8}.get(c.kv_dtype, rpa.DTYPE_BF16),
         q_dtype=rpa.DTYPE_F16 if c.q_dtype == wl.Q_F16 else rpa.DTYPE_BF16,
         sm_scale=c.sm_scale, soft_cap=c.soft_cap or 0.0,
         k_scale=1.0 if c.k_scale is None else c.k_scale,
