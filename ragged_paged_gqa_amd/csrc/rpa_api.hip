@@ -18,10 +18,7 @@
 #include "rpa_plan.h"
 #include "rpa_prefill.h"
 
-// Work items the planner aims for per compute unit, per kernel class.
-#ifndef RPA_DEC_ITEMS_PER_CU
-#define RPA_DEC_ITEMS_PER_CU 32
-#endif
+// Prefill-class work items the planner aims for per compute unit.
 #ifndef RPA_PF_ITEMS_PER_CU
 #define RPA_PF_ITEMS_PER_CU 4
 #endif
@@ -79,7 +76,7 @@ rpa_status validate(const rpa_config* c) {
 
 struct Layout {
   size_t hdr, du, pu, di, pi, qlist, done, wfirst, dpart, dplse, ppart, pplse, total;
-  int32_t max_du, max_pu, max_di, max_pi, tgt_d, tgt_p, pf_rows, dec_waves;
+  int32_t max_du, max_pu, max_di, max_pi, tgt_p, pf_rows, dec_waves;
 };
 
 // Workgroups of the decode launch: one resident set (the stream-K split is
@@ -110,7 +107,6 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t pf_rows = pf_rows_for(c->head_dim);
   const int64_t max_du = Hkv * c->max_num_seqs;
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
-  const int64_t tgt_d = (int64_t)cus * RPA_DEC_ITEMS_PER_CU;
   const int64_t tgt_p = (int64_t)cus * RPA_PF_ITEMS_PER_CU;
   // stream-K: every decode wave boundary inside a unit adds one item
   const int64_t dec_waves = (int64_t)dec_grid_for(c, cus) * kDecWavesPerBlock;
@@ -137,7 +133,6 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   L->max_pu = (int32_t)max_pu;
   L->max_di = (int32_t)max_di;
   L->max_pi = (int32_t)max_pi;
-  L->tgt_d = (int32_t)tgt_d;
   L->tgt_p = (int32_t)tgt_p;
   L->pf_rows = (int32_t)pf_rows;
   L->dec_waves = (int32_t)dec_waves;
@@ -175,7 +170,6 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.max_pf_units = L.max_pu;
   p.max_dec_items = L.max_di;
   p.max_pf_items = L.max_pi;
-  p.target_dec_items = L.tgt_d;
   p.target_pf_items = L.tgt_p;
   p.sm_scale = c->sm_scale * c->k_scale;
   p.soft_cap = c->soft_cap;

@@ -90,7 +90,7 @@ struct Header {
   int32_t n_pf_units;
   int32_t n_dec_items;
   int32_t n_pf_items;
-  int32_t dec_chunk;
+  int32_t zero;  // 0 (decode chunks follow the stream-K split)
   int32_t pf_chunk;
   int32_t n_split_units;
   int32_t dec_blocks;   // 16-key blocks of all decode units (the stream-K total)
@@ -131,7 +131,7 @@ struct Params {
   int32_t T, Hq, Hkv, G, D, page, P, S_max, pps;
   int32_t pf_rows;           // packed rows of a prefill-class unit
   int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
-  int32_t target_dec_items, target_pf_items;
+  int32_t target_pf_items;
   int32_t dec_waves;         // waves of the decode launch (the stream-K split)
   const float* sinks;        // [Hq] attention-sink logits, or null
   // numerics

@@ -559,7 +559,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     h.n_pf_units = min(base[1], p.max_pf_units);
     h.n_dec_items = min(base[2], p.max_dec_items);
     h.n_pf_items = min(base[3], p.max_pf_items);
-    h.dec_chunk = 0;
+    h.zero = 0;
     h.pf_chunk = pf_chunk.d;
     h.n_split_units = base[4];
     h.dec_blocks = (int32_t)min(tot_dec, (int64_t)INT32_MAX);
