@@ -34,9 +34,10 @@
 //   3. O^T [D x 16 rows] += V^T P^T with v_mfma_f32_16x16x16_bf16: V^T read
 //      with ds_read_b64_tr_b16, P^T exactly the S^T result layout. V rows past
 //      kv_len are zeroed first (0 * NaN would otherwise poison the sum).
-// fp8 e4m3fn K/V are widened to bf16 exactly with v_cvt_scalef32_pk_bf16_fp8
-// after the LDS read (V written back as a bf16 tile into its own ring slot,
-// which is refilled only after the transposed reads); k_scale is folded
+// One-byte K/V codes are widened exactly after the LDS read
+// (v_cvt_scalef32_pk_bf16_fp8 / _bf8, or sign extension for int8), V written
+// back as a 16-bit tile into its own ring slot, which is refilled only after
+// the transposed reads; k_scale is folded
 // into the score scale and v_scale into the final normalisation. The
 // contraction over head_dim may visit d in any order as long as K and Q use
 // the same one: a lane's 16-byte K piece covers 16 consecutive d for fp8,
@@ -44,6 +45,11 @@
 // An item that is its unit's only one writes bf16 out and f32 lse; otherwise
 // it writes a normalised f32 partial and its lse, which the combine kernel
 // merges once every item is done (combine_kernel below).
+//
+// Element types: the kernel is instantiated per K/V kind KVT (K/V in the q
+// type, fp8 e4m3fn, fp8 e5m2, int8) and per 16-bit type F16 (bf16, or f16
+// with an f16 q: f16 MFMAs, f16 P and output). In the comments below "bf16"
+// stands for that 16-bit type and "fp8" for any one-byte code.
 #pragma once
 
 #include "rpa_common.h"

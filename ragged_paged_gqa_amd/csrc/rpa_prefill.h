@@ -30,6 +30,12 @@
 //     FMA and one exp2 per score;
 //   * O^T [D x 32 rows] += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T
 //     taken straight from the S^T accumulator layout.
+//
+// Element types: the kernel is instantiated per K/V kind KVT (K/V in the q
+// type, fp8 e4m3fn, fp8 e5m2, int8) and per 16-bit type F16 (bf16, or f16
+// with an f16 q: f16 MFMAs, f16 P and output). In the comments here "bf16"
+// stands for that 16-bit type and "fp8" for any one-byte code (widened to it
+// exactly: v_cvt_scalef32_pk_*_fp8 / _bf8, or sign extension for int8).
 #pragma once
 
 #include <climits>
