@@ -26,7 +26,7 @@ _BUILD = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_BUILD, "librpa_oracle.so")
 
 KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2, "f16": 3, "int8": 4}
-Q_CODES = {"bf16": 0, "f16": 3}
+Q_CODES = {"bf16": 0, "f16": 3, "f32": 5}
 
 
 class _Cfg(ctypes.Structure):
@@ -143,7 +143,8 @@ def _inputs(w):
             np.ascontiguousarray(w.kv_lens, dtype=np.int32),
             np.ascontiguousarray(w.page_indices, dtype=np.int32),
             np.ascontiguousarray(w.cu_q_lens, dtype=np.int32)]
-    assert arrs[0].dtype == np.uint16
+    # q: bits of the q dtype (uint16 for bf16 / f16, uint32 for f32)
+    assert arrs[0].dtype == (np.uint32 if getattr(w.cfg, "q_dtype", "bf16") == "f32" else np.uint16)
     return arrs
 
 
@@ -230,8 +231,13 @@ def kv_append(w, k_new, v_new):
     skipped counts tokens whose slot falls outside the page table."""
     c = w.cfg
     shape = (c.num_q_tokens, c.num_kv_heads, c.head_dim)
-    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
-    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    if getattr(w.cfg, "q_dtype", "bf16") == "f32":
+        # f32 rows: float32 values or their uint32 bits
+        k_new = np.ascontiguousarray(k_new).view(np.uint32)
+        v_new = np.ascontiguousarray(v_new).view(np.uint32)
+    else:
+        k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+        v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
     assert k_new.shape == shape and v_new.shape == shape
     kv = np.array(w.kv_pages, copy=True, order="C")
     _, _, kvl, pi, cu = _inputs(w)

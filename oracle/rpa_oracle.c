@@ -43,7 +43,7 @@
  *     the dtypes (`Cfg` kv_dtype, f8e4m3fn and f8e5m2);
  *   - dequantised values are code*scale exactly (f64), not re-rounded to the
  *     q dtype;
- *   - q (and out) are bf16 or f16 (`Cfg` q_dtype); K/V bf16, f16, e4m3fn,
+ *   - q (and out) are bf16, f16 or f32 (`Cfg` q_dtype); K/V bf16, f16, e4m3fn,
  *     e5m2 or int8 (`Cfg` kv_dtype; int8 codes are signed integers times the
  *     scale), all read exactly.
  */
@@ -57,6 +57,7 @@
 #define ORACLE_KV_E5M2 2
 #define ORACLE_F16 3 /* IEEE binary16: q/out type, or K/V type */
 #define ORACLE_KV_I8 4 /* signed 8-bit integer codes */
+#define ORACLE_F32 5   /* IEEE binary32: q/out type */
 
 typedef struct {
   int32_t num_q_tokens;
@@ -76,7 +77,7 @@ typedef struct {
   double k_scale; /* 1.0 when absent */
   double v_scale; /* 1.0 when absent */
   const double* sinks; /* NULL, or one logit per q head [num_q_heads] */
-  int32_t q_dtype;     /* 0: bf16 q (and new K/V rows of the append), ORACLE_F16: f16 */
+  int32_t q_dtype;     /* 0: bf16 q (and new K/V rows of the append), ORACLE_F16: f16, ORACLE_F32: f32 */
 } oracle_cfg;
 
 /* bf16 bits are the upper half of an IEEE binary32 value. */
@@ -146,8 +147,10 @@ double oracle_e5m2_to_f64(uint8_t code) {
 /* Soft-cap of the kernel page's `Cfg`/`flashAttention`: c * tanh(x / c). */
 double oracle_soft_cap(double x, double c) { return c * tanh(x / c); }
 
-/* A q element (or a new K/V element of the append) in the q dtype. */
-static double q_elem(const oracle_cfg* c, uint16_t bits) {
+/* Element idx of a q array (or of the append's new K/V rows) in the q dtype. */
+static double q_elem(const oracle_cfg* c, const void* q, int64_t idx) {
+  if (c->q_dtype == ORACLE_F32) return (double)((const float*)q)[idx];
+  const uint16_t bits = ((const uint16_t*)q)[idx];
   return c->q_dtype == ORACLE_F16 ? oracle_f16_to_f64(bits) : oracle_bf16_to_f64(bits);
 }
 
@@ -183,7 +186,7 @@ static int key_visible(const oracle_cfg* c, int64_t j, int64_t pos) {
 /* One output row (token, q head n). Returns 1 if the token is a padding
  * token (no sequence owns it), 0 on success, -1 on invalid metadata (the row
  * is then filled with NaN). `scores` is caller scratch of >= kv_len doubles. */
-static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+static int oracle_row(const oracle_cfg* c, const void* q, const void* kv_pages, const int32_t* kv_lens,
                       const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, int64_t token, int n,
                       double* out_row, double* lse, double** scores, int64_t* scores_cap) {
   const int D = c->head_dim;
@@ -208,7 +211,7 @@ static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pag
     *scores_cap = kv_len;
   }
   double* sc = *scores;
-  const uint16_t* qrow = q + (token * c->num_q_heads + n) * (int64_t)D;
+  const int64_t qrow = (token * c->num_q_heads + n) * (int64_t)D;
 
   /* scores of the visible keys */
   int64_t n_vis = 0;
@@ -218,7 +221,7 @@ static int oracle_row(const oracle_cfg* c, const uint16_t* q, const void* kv_pag
     int64_t base = kv_index(c, page_indices, s, j, 2 * h, 0);
     if (base < 0) goto invalid;
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += q_elem(c, qrow[d]) * (kv_elem(c, kv_pages, base + d) * c->k_scale);
+    for (int d = 0; d < D; ++d) dot += q_elem(c, q, qrow + d) * (kv_elem(c, kv_pages, base + d) * c->k_scale);
     double x = dot * c->sm_scale;
     if (c->has_soft_cap) x = oracle_soft_cap(x, c->soft_cap);
     sc[j] = x;
@@ -255,7 +258,7 @@ invalid:
 
 /* Rows listed by (tokens[r], heads[r]); out is [n_rows, D], lse [n_rows].
  * status[r] receives the per-row code of oracle_row. */
-int oracle_rows(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+int oracle_rows(const oracle_cfg* c, const void* q, const void* kv_pages, const int32_t* kv_lens,
                 const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, const int64_t* tokens,
                 const int32_t* heads, int64_t n_rows, double* out, double* lse, int32_t* status, int nthreads) {
   if (c->num_kv_heads <= 0 || c->num_q_heads % c->num_kv_heads != 0) return -1;
@@ -279,7 +282,7 @@ int oracle_rows(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, co
 
 /* Every row of [num_q_tokens, Hq]; rows of padding tokens are left as they
  * were in out/lse. */
-int oracle_forward(const oracle_cfg* c, const uint16_t* q, const void* kv_pages, const int32_t* kv_lens,
+int oracle_forward(const oracle_cfg* c, const void* q, const void* kv_pages, const int32_t* kv_lens,
                    const int32_t* page_indices, const int32_t* cu_q_lens, int32_t num_seqs, double* out, double* lse,
                    int nthreads) {
   if (c->num_kv_heads <= 0 || c->num_q_heads % c->num_kv_heads != 0) return -1;
@@ -412,8 +415,9 @@ uint16_t oracle_f32_to_bf16(float x) {
 
 /* Cache value of one new element (x in the q dtype): RN_f32(x / scale) in
  * the cache type. */
-static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_t x_bits, double scale) {
-  const float x = (float)q_elem(c, x_bits); /* exact: bf16 and f16 values are f32 values */
+static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, const void* x_rows, int64_t src,
+                       double scale) {
+  const float x = (float)q_elem(c, x_rows, src); /* exact: bf16, f16 and f32 values are f32 values */
   const float y = x / (float)scale;
   if (c->kv_dtype == ORACLE_KV_E4M3FN)
     ((uint8_t*)kv_pages)[idx] = oracle_f32_to_e4m3fn(y);
@@ -427,11 +431,11 @@ static void store_elem(const oracle_cfg* c, void* kv_pages, int64_t idx, uint16_
     ((uint16_t*)kv_pages)[idx] = oracle_f32_to_bf16(y);
 }
 
-/* Writes k_new / v_new [num_q_tokens, Hkv, D] (bf16 bits) of every query
+/* Writes k_new / v_new [num_q_tokens, Hkv, D] (in the q dtype) of every query
  * token of the first num_seqs sequences into kv_pages. A token whose key
  * position or page falls outside the table (a broken precondition) is not
  * written. Returns the number of such tokens, or -1 for a bad argument. */
-int64_t oracle_kv_append(const oracle_cfg* c, const uint16_t* k_new, const uint16_t* v_new, void* kv_pages,
+int64_t oracle_kv_append(const oracle_cfg* c, const void* k_new, const void* v_new, void* kv_pages,
                          const int32_t* kv_lens, const int32_t* page_indices, const int32_t* cu_q_lens,
                          int32_t num_seqs) {
   if (num_seqs < 0 || num_seqs > c->max_num_seqs || c->num_kv_heads <= 0) return -1;
@@ -456,8 +460,8 @@ int64_t oracle_kv_append(const oracle_cfg* c, const uint16_t* k_new, const uint1
         for (int d = 0; d < D; ++d) {
           const int64_t src = (t * Hkv + h) * D + d;
           const int64_t dst_k = (slot * 2 * Hkv + 2 * h) * D + d;
-          store_elem(c, kv_pages, dst_k, k_new[src], c->k_scale);
-          store_elem(c, kv_pages, dst_k + D, v_new[src], c->v_scale);
+          store_elem(c, kv_pages, dst_k, k_new, src, c->k_scale);
+          store_elem(c, kv_pages, dst_k + D, v_new, src, c->v_scale);
         }
     }
   }

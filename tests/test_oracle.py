@@ -64,6 +64,8 @@ def _seq_kv(w, s, comb):
 
 
 def _q_f64(w):
+    if w.cfg.q_dtype == wl.Q_F32:
+        return w.q.view(np.float32).astype(np.float64)
     if w.cfg.q_dtype == wl.Q_F16:
         return w.q.view(np.float16).astype(np.float64)
     return torch.from_numpy(w.q.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
@@ -215,6 +217,45 @@ def test_f16_q_matches_torch_sdpa_on_decoded_values(kv_dtype):
     ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.cfg.sm_scale,
                                          enable_gqa=True)[0].permute(1, 0, 2).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_dtype", [wl.KV_BF16, wl.KV_FP8, wl.KV_E5M2, wl.KV_I8])
+def test_f32_q_matches_torch_sdpa_on_decoded_values(kv_dtype):
+    """f32 q (the page's `Cfg` q_dtype, packing 1): every f32 bit of q counts;
+    sdpa in f64 over numpy's reading of the same bits."""
+    G, Hkv, D, kv_len = 2, 2, 32, 40
+    kw = dict(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=16, pages_per_seq=None,
+              sm_scale=0.3, is_causal=True, kv_dtype=kv_dtype, q_dtype=wl.Q_F32)
+    if wl.is_fp8(kv_dtype):
+        kw.update(k_scale=0.25, v_scale=3.0)
+    w = wl.build("f32sdpa", kw, [kv_len], [kv_len], 19)
+    assert w.q.dtype == np.uint32
+    # the generated q is not bf16-representable: the low 16 bits are used
+    assert np.any(w.q & 0xFFFF)
+    out, lse = oracle.forward(w)
+    q = torch.from_numpy(_q_f64(w)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(_seq_kv(w, 0, 0).copy())[None]
+    v = torch.from_numpy(_seq_kv(w, 0, 1).copy())[None]
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.cfg.sm_scale,
+                                         enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_f32_q_of_bf16_values_equals_bf16_q():
+    """An f32 q that holds bf16 values gives exactly the bf16-q result; with
+    its low bits kept the result moves (the f32 bits are read, not truncated)."""
+    kw = dict(num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16, pages_per_seq=None,
+              sm_scale=0.3, is_causal=True)
+    wb = wl.build("qbf16", dict(kw, q_dtype=wl.Q_BF16), [6, 1], [30, 17], 23)
+    wf = wl.build("qf32", dict(kw, q_dtype=wl.Q_F32), [6, 1], [30, 17], 23)
+    # same draw: the f32 q rounds to the bf16 q
+    assert np.array_equal(wl.to_bf16_bits(wf.q.view(np.float32)), wb.q)
+    ob, lb = oracle.forward(wb)
+    of, lf = oracle.forward(wf)
+    assert not np.allclose(lf, lb, rtol=0, atol=1e-9)
+    wf.q = (wb.q.astype(np.uint32) << 16)  # exactly the bf16 values, as f32
+    o2, l2 = oracle.forward(wf)
+    assert np.array_equal(o2, ob) and np.array_equal(l2, lb)
 
 
 def test_bottom_right_causal_equals_suffix_of_square_problem():

@@ -267,6 +267,34 @@ def test_f16_rows_append_into_f16_and_fp8_caches():
                 assert np.array_equal(kv[page, slot, 1::2].ravel(), brute_e4m3fn(qv))
 
 
+def test_f32_rows_append_into_bf16_fp8_and_int8_caches():
+    """New rows in f32 (f32 q): each cache takes its rounding of the f32
+    quotient x / scale, with every bit of x read (a bf16 cache: torch's RNE
+    cast; e4m3fn: the brute-force nearest code; int8: numpy's rint and clip)."""
+    for kvd, ks in ((wl.KV_BF16, 0.5), (wl.KV_FP8, 0.05), (wl.KV_I8, 0.05)):
+        kw = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, sm_scale=0.125,
+                  kv_dtype=kvd, q_dtype=wl.Q_F32, k_scale=ks, v_scale=2.0)
+        w = wl.from_tables(kw, [1, 5, 0, 16], [8, 35, 20, 64], [[3], [7, 1, 10], [5, 6], [2, 9, 4, 11]], 12,
+                           total_num_pages=12, max_num_seqs=5, num_q_tokens=24, pages_per_seq=4)
+        k_new, v_new = wl.new_kv(w, 16, std=3.0)
+        assert k_new.dtype == np.uint32 and np.any(k_new & 0xFFFF)
+        kv, skipped = oracle.kv_append(w, k_new, v_new)
+        assert skipped == 0
+        xk = k_new.view(np.float32)
+        xv = v_new.view(np.float32)
+        for t, s_, pos, page, slot in golden_rows():
+            for comb, x, sc in ((0, xk, ks), (1, xv, 2.0)):
+                qx = x[t].ravel() / np.float32(sc)
+                got = kv[page, slot, comb::2].ravel()
+                if kvd == wl.KV_BF16:
+                    ref = torch.from_numpy(qx.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                elif kvd == wl.KV_FP8:
+                    ref = brute_e4m3fn(qx)
+                else:
+                    ref = np.clip(np.rint(qx), -128, 127).astype(np.int8).view(np.uint8)
+                assert np.array_equal(got, ref), (kvd, t, comb)
+
+
 def test_i8_rounding_matches_numpy_rint_and_clip():
     x = _f32(wl.finite_bf16_patterns())
     halves = np.arange(-140, 140, dtype=np.float32) + np.float32(0.5)   # ties: to even

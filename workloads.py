@@ -47,6 +47,7 @@ KV_F16 = "f16"
 KV_I8 = "int8"
 Q_BF16 = "bf16"
 Q_F16 = "f16"
+Q_F32 = "f32"
 FP8_KINDS = (KV_FP8, KV_E5M2)
 ONE_BYTE_KINDS = (KV_FP8, KV_E5M2, KV_I8)
 
@@ -89,7 +90,7 @@ class Config:
 class Workload:
     name: str
     cfg: Config
-    q: np.ndarray             # uint16 bf16 (or f16) bits [T, Hq, D]
+    q: np.ndarray             # bits of the q dtype [T, Hq, D]: uint16 (bf16, f16) or uint32 (f32)
     kv_pages: np.ndarray      # uint16 (bf16, f16) or uint8 (e4m3fn, e5m2) bits [P, page, 2*Hkv, D]
     kv_lens: np.ndarray       # int32 [max_num_seqs]
     page_indices: np.ndarray  # int32 [max_num_seqs, pages_per_seq]
@@ -131,6 +132,9 @@ def to_f16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def to_q_bits(x: np.ndarray, q_dtype: str) -> np.ndarray:
+    """Values -> bits of the q dtype: uint16 for bf16 / f16, uint32 for f32."""
+    if q_dtype == Q_F32:
+        return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     return to_f16_bits(x) if q_dtype == Q_F16 else to_bf16_bits(x)
 
 
@@ -309,7 +313,7 @@ def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
           seed: int | None = None, kv_dtype: str | None = None, q_dtype: str | None = None) -> Workload:
     """A named workload; `kv_dtype` swaps its K/V type (fp8 kinds take the fp8
     decode workload's scales, 0.05, when the workload has none) and `q_dtype`
-    its q/out type (with f16 q a bf16 cache becomes f16)."""
+    its q/out type (with f16 q a bf16 cache becomes f16; f32 q keeps the cache)."""
     seed = number if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     q_lens, kv_lens = lengths(number, rng)
@@ -317,6 +321,8 @@ def named(number: int, *, q_mult: float = 1.0, unused_entry: int = 0,
     if number == 1:
         kw["total_num_pages"] = 32
     ckw = cfg_kw(number)
+    if q_dtype == Q_F32:
+        ckw["q_dtype"] = Q_F32
     if q_dtype == Q_F16:
         ckw["q_dtype"] = Q_F16
         if kv_dtype is None and ckw.get("kv_dtype", KV_BF16) == KV_BF16:
