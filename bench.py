@@ -59,6 +59,7 @@ def algorithmic_work(w):
     c = w.cfg
     G = c.num_q_heads // c.num_kv_heads
     b_kv = 1 if c.kv_dtype in ("fp8_e4m3fn", "fp8_e5m2", "int8") else 2  # bf16 and f16: 2
+    b_q = 4 if c.q_dtype == "f32" else 2  # q and out elements
     sw = c.sliding_window or 0
     res = {"decode": [0.0, 0.0, 0], "prefill": [0.0, 0.0, 0]}  # flops, bytes, tokens
     for s in range(w.n_seqs):
@@ -73,7 +74,7 @@ def algorithmic_work(w):
         n_vis = np.maximum(hi - lo, 0)
         flops = float(c.num_q_heads * 4 * c.head_dim * n_vis.sum())
         r_s = max(0, int(hi.max()) - int(lo.min()))
-        byts = float(c.num_kv_heads * 2 * c.head_dim * b_kv * r_s + ql * c.num_q_heads * (4 * c.head_dim + 4))
+        byts = float(c.num_kv_heads * 2 * c.head_dim * b_kv * r_s + ql * c.num_q_heads * (2 * b_q * c.head_dim + 4))
         cls = "decode" if ql * G <= 16 else "prefill"
         res[cls][0] += flops
         res[cls][1] += byts
@@ -179,7 +180,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-dtype", choices=["bf16", "f16", "fp8_e4m3fn", "fp8_e5m2", "int8"], default=None,
                     help="store the workload's K/V cache in this type instead of its own")
-    ap.add_argument("--q-dtype", choices=["bf16", "f16"], default=None,
+    ap.add_argument("--q-dtype", choices=["bf16", "f16", "f32"], default=None,
                     help="q/out type (f16: a bf16 cache becomes f16 too)")
     ap.add_argument("--sinks", action="store_true",
                     help="attach seeded attention-sink logits (one per q head) and call rpa_forward_sinks")
@@ -221,7 +222,7 @@ def main():
     import workloads as wl
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import Device
+    from gpu_util import Device, upload_q_bits
 
     log(f"[bench] generating workload {args.workload}: {wl.WORKLOADS[args.workload]}")
     t0 = time.perf_counter()
@@ -237,9 +238,8 @@ def main():
 
     if args.append:
         k_np, v_np = wl.new_kv(w, 1000 + args.workload)
-        t16 = torch.float16 if w.cfg.q_dtype == wl.Q_F16 else torch.bfloat16
-        k_new = torch.from_numpy(k_np.view(np.int16)).cuda().view(t16)
-        v_new = torch.from_numpy(v_np.view(np.int16)).cuda().view(t16)
+        k_new = upload_q_bits(k_np, w.cfg.q_dtype)
+        v_new = upload_q_bits(v_np, w.cfg.q_dtype)
         stream = torch.cuda.current_stream()
         ap_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(args.steps)]
@@ -318,11 +318,12 @@ def main():
         "roofline": roof,
     }
     if args.append:
-        # bytes the append must move: each new K and V element read once as
-        # bf16 and written once in the cache type
+        # bytes the append must move: each new K and V element read once in
+        # the q type and written once in the cache type
         c = w.cfg
         b_kv = 1 if wl.is_fp8(c.kv_dtype) else 2
-        ab = float(T * 2 * c.num_kv_heads * c.head_dim * (2 + b_kv))
+        b_in = 4 if c.q_dtype == wl.Q_F32 else 2
+        ab = float(T * 2 * c.num_kv_heads * c.head_dim * (b_in + b_kv))
         ams = sum(a.elapsed_time(b) for a, b in ap_ev) / args.steps
         result["config"]["kv_append"] = True
         result["kv_append"] = {"kernel": "kv_append_kernel", "kernel_ms": round(ams, 5), "algorithmic_bytes": ab,
@@ -340,11 +341,14 @@ _outs = {}
 
 def dev_out(dev):
     import torch
+
+    import ragged_paged_gqa_amd as rpa
     key = id(dev)
     if key not in _outs:
         c = dev.cfg
-        _outs[key] = (torch.empty((c.num_q_tokens, c.num_q_heads, c.head_dim), dtype=torch.bfloat16,
-                                  device="cuda"),
+        # out in the q type's width (f16 bits fit a bf16 buffer)
+        odt = torch.float32 if c.q_dtype == rpa.DTYPE_F32 else torch.bfloat16
+        _outs[key] = (torch.empty((c.num_q_tokens, c.num_q_heads, c.head_dim), dtype=odt, device="cuda"),
                       torch.empty((c.num_q_tokens, c.num_q_heads), dtype=torch.float32, device="cuda"))
     return _outs[key][0]
 

@@ -44,6 +44,7 @@ typedef enum {
   RPA_DTYPE_FP8_E5M2 = 2,   /* OCP FP8 E5M2 (bias 15, infinities and NaN at exponent 31) */
   RPA_DTYPE_F16 = 3,        /* IEEE binary16 */
   RPA_DTYPE_INT8 = 4,       /* signed 8-bit integer codes (K/V only; value = code * scale) */
+  RPA_DTYPE_F32 = 5,        /* IEEE binary32 (q and out only; the page's packing-1 q type) */
 } rpa_dtype;
 
 typedef enum {
@@ -69,8 +70,9 @@ typedef struct rpa_config {
   int32_t page_size;       /* keys per page: a multiple of 16, at most 1024 */
   int32_t max_num_seqs;    /* rows of page_indices and kv_lens */
   int32_t pages_per_seq;   /* columns of page_indices */
-  int32_t q_dtype;         /* rpa_dtype of q and out: RPA_DTYPE_BF16 or RPA_DTYPE_F16 */
-  int32_t kv_dtype;        /* rpa_dtype: q_dtype, RPA_DTYPE_FP8_E4M3FN, RPA_DTYPE_FP8_E5M2 or RPA_DTYPE_INT8 */
+  int32_t q_dtype;         /* rpa_dtype of q and out: RPA_DTYPE_BF16, RPA_DTYPE_F16 or RPA_DTYPE_F32 */
+  int32_t kv_dtype;        /* rpa_dtype: q_dtype (RPA_DTYPE_BF16 with an f32 q), RPA_DTYPE_FP8_E4M3FN,
+                              RPA_DTYPE_FP8_E5M2 or RPA_DTYPE_INT8 */
   float sm_scale;          /* score scale, finite */
   float soft_cap;          /* > 0: cap on; 0: off */
   float k_scale;           /* dequant factor of K; 1.0f for none */
@@ -100,6 +102,10 @@ rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes);
  *   workspace    >= rpa_workspace_bytes(cfg) bytes, 256-byte aligned
  * All arrays are dense, row-major, in device memory; out and lse must not
  * alias any input. Rows of tokens >= cu_q_lens[num_seqs] are left untouched.
+ * An f32 q (16-byte aligned) is computed on the bf16 path with each element
+ * carried as a bf16 pair hi + lo (within 2^-17 of it, relative); scores take
+ * both, and out is written in f32. P (the exponentiated scores) is rounded to
+ * bf16 for the P.V product as with a bf16 q.
  *
  * Data preconditions (not checked here; rpa_check_metadata checks host copies):
  * 0 <= q_len <= kv_len <= pages_per_seq * page_size, page ids in
@@ -147,7 +153,7 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
  * s (cu_q_lens[s] + i) stands at key position kv_len - q_len + i, which is
  * slot pos % page_size of page page_indices[s, pos / page_size]; K of kv head
  * h goes to combined head 2h, V to 2h+1 (`stridedLoadKv`).
- *   k_new, v_new [num_q_tokens, num_kv_heads, head_dim] q_dtype (bf16 or f16)
+ *   k_new, v_new [num_q_tokens, num_kv_heads, head_dim] q_dtype (bf16, f16 or f32)
  *   kv_pages     [total_num_pages, page_size, 2*num_kv_heads, head_dim]
  *                kv_dtype, updated in place
  *   kv_lens, page_indices, cu_q_lens, num_seqs: as rpa_forward (kv_lens
@@ -156,8 +162,8 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
  * V (IEEE binary32 division), rounded to nearest even in kv_dtype; e4m3fn
  * saturates at +-448 and e5m2 at +-57344, bf16 and f16 overflow to +-inf; a
  * NaN input stores a NaN; int8 stores the nearest integer (ties to even)
- * saturated to [-128, 127], and 0 for NaN. With a 16-bit cache and both
- * scales 1 this is a bit copy. Device pointers, owned by the
+ * saturated to [-128, 127], and 0 for NaN. With rows and cache of one 16-bit
+ * type and both scales 1 this is a bit copy. Device pointers, owned by the
  * caller; k_new, v_new and kv_pages 16-byte aligned; k_new/v_new must not
  * overlap kv_pages. Tokens past cu_q_lens[num_seqs] and tokens whose position
  * or page id falls outside the table (a broken precondition) write nothing;

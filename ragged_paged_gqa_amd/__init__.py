@@ -27,6 +27,7 @@ DTYPE_FP8_E4M3FN = 1
 DTYPE_FP8_E5M2 = 2
 DTYPE_F16 = 3
 DTYPE_INT8 = 4
+DTYPE_F32 = 5
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "HIP runtime error", 5: "metadata violates a precondition"}
@@ -77,7 +78,7 @@ class Config:
     v_scale: float = 1.0
     is_causal: bool = True
     sliding_window: int = 0      # 0: off
-    q_dtype: int = DTYPE_BF16    # q and out: DTYPE_BF16 or DTYPE_F16
+    q_dtype: int = DTYPE_BF16    # q and out: DTYPE_BF16, DTYPE_F16 or DTYPE_F32
 
     def to_c(self) -> _Config:
         return _Config(
@@ -174,10 +175,19 @@ def _dev_i32(t: torch.Tensor, name: str, numel: int) -> None:
         raise ValueError(f"{name}: expected a contiguous int32 CUDA tensor of >= {numel} elements")
 
 
+def _q_torch_dtype(cfg: Config):
+    return {DTYPE_F16: torch.float16, DTYPE_F32: torch.float32}.get(cfg.q_dtype, torch.bfloat16)
+
+
+def _q_size(cfg: Config) -> int:
+    return 4 if cfg.q_dtype == DTYPE_F32 else 2
+
+
 def _check_inputs(cfg: Config, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs):
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
-    if not (q.is_cuda and q.is_contiguous() and q.element_size() == 2 and q.numel() == T * Hq * D):
-        raise ValueError("q: expected a contiguous 2-byte (bf16 or f16) CUDA tensor [num_q_tokens, num_q_heads, head_dim]")
+    if not (q.is_cuda and q.is_contiguous() and q.element_size() == _q_size(cfg) and q.numel() == T * Hq * D):
+        raise ValueError(f"q: expected a contiguous {_q_size(cfg)}-byte (q dtype) CUDA tensor "
+                         "[num_q_tokens, num_q_heads, head_dim]")
     eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2, DTYPE_INT8) else 2
     kv_numel = cfg.total_num_pages * cfg.page_size * 2 * cfg.num_kv_heads * D
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb
@@ -199,7 +209,7 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
             workspace=None, want_lse: bool = True, stream=None, sinks=None):
     """Ragged paged attention. Returns (out, lse) as torch tensors on the device.
 
-    q [T, Hq, D] bf16 or f16 (cfg.q_dtype, also out's type); kv_pages
+    q [T, Hq, D] bf16, f16 or f32 (cfg.q_dtype, also out's type); kv_pages
     [P, page, 2*Hkv, D] in the q type or fp8 e4m3fn / e5m2 (uint8 storage); kv_lens [S], page_indices [S, pps], cu_q_lens [S+1],
     num_seqs [1]: int32 device tensors. Rows of padding tokens keep whatever
     `out`/`lse` held. `sinks`: optional float32 device tensor [Hq] of
@@ -208,10 +218,10 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
     _check_inputs(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs)
     T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
     if out is None:
-        out = torch.zeros((T, Hq, D), dtype=torch.float16 if cfg.q_dtype == DTYPE_F16 else torch.bfloat16,
-                          device=q.device)
-    elif not (out.is_cuda and out.is_contiguous() and out.element_size() == 2 and out.numel() == T * Hq * D):
-        raise ValueError("out: expected a contiguous 2-byte CUDA tensor [T, Hq, D]")
+        out = torch.zeros((T, Hq, D), dtype=_q_torch_dtype(cfg), device=q.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.element_size() == _q_size(cfg)
+              and out.numel() == T * Hq * D):
+        raise ValueError(f"out: expected a contiguous {_q_size(cfg)}-byte (q dtype) CUDA tensor [T, Hq, D]")
     if want_lse and lse is None:
         lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device=q.device)
     if lse is not None and not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32
@@ -247,8 +257,8 @@ def kv_append(k_new, v_new, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs
     """
     T, Hkv, D = cfg.num_q_tokens, cfg.num_kv_heads, cfg.head_dim
     for name, t in (("k_new", k_new), ("v_new", v_new)):
-        if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2 and t.numel() == T * Hkv * D):
-            raise ValueError(f"{name}: expected a contiguous 2-byte (q dtype) CUDA tensor "
+        if not (t.is_cuda and t.is_contiguous() and t.element_size() == _q_size(cfg) and t.numel() == T * Hkv * D):
+            raise ValueError(f"{name}: expected a contiguous {_q_size(cfg)}-byte (q dtype) CUDA tensor "
                              "[num_q_tokens, num_kv_heads, head_dim]")
     eb = 1 if cfg.kv_dtype in (DTYPE_FP8_E4M3FN, DTYPE_FP8_E5M2, DTYPE_INT8) else 2
     if not (kv_pages.is_cuda and kv_pages.is_contiguous() and kv_pages.element_size() == eb

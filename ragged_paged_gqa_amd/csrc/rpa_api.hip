@@ -66,9 +66,12 @@ rpa_status validate(const rpa_config* c) {
   if ((int64_t)c->num_kv_heads * c->head_dim > (1 << 24)) return RPA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return RPA_ERR_UNSUPPORTED;
   if (c->page_size % 16 != 0 || c->page_size > 1024) return RPA_ERR_UNSUPPORTED;
-  // q (and out) bf16 or f16; K/V in the q type, or an fp8 kind
-  if (c->q_dtype != RPA_DTYPE_BF16 && c->q_dtype != RPA_DTYPE_F16) return RPA_ERR_UNSUPPORTED;
-  if (c->kv_dtype != c->q_dtype && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN && c->kv_dtype != RPA_DTYPE_FP8_E5M2 &&
+  // q (and out) bf16, f16 or f32; K/V in the q type (bf16 with an f32 q), or
+  // a one-byte kind
+  if (c->q_dtype != RPA_DTYPE_BF16 && c->q_dtype != RPA_DTYPE_F16 && c->q_dtype != RPA_DTYPE_F32)
+    return RPA_ERR_UNSUPPORTED;
+  const int32_t kv16 = c->q_dtype == RPA_DTYPE_F32 ? RPA_DTYPE_BF16 : c->q_dtype;
+  if (c->kv_dtype != kv16 && c->kv_dtype != RPA_DTYPE_FP8_E4M3FN && c->kv_dtype != RPA_DTYPE_FP8_E5M2 &&
       c->kv_dtype != RPA_DTYPE_INT8)
     return RPA_ERR_UNSUPPORTED;
   return RPA_OK;
@@ -197,7 +200,7 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev[k], st);
 }
 
-template <int D, int KVT, bool F16>
+template <int D, int KVT, bool F16, bool Q32>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   constexpr bool FP8 = KVT != kKvBf16;
   {
@@ -207,9 +210,9 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     if (grid > p.max_pf_items) grid = p.max_pf_items;
     if (grid < 1) grid = 1;
     if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((prefill_kernel<D, KVT, true, F16>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     else
-      hipLaunchKernelGGL((prefill_kernel<D, KVT, false, F16>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
   }
@@ -217,16 +220,16 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     // exactly the waves the planner split the decode work over
     const int grid = p.dec_waves / kDecWavesPerBlock;
     if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((decode_kernel<D, KVT, true, F16>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     else
-      hipLaunchKernelGGL((decode_kernel<D, KVT, false, F16>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
     // merge of the split decode units (a wave per unit, grid-stride)
     int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
     if (cgrid > cus * 4) cgrid = cus * 4;
     if (cgrid < 1) cgrid = 1;
-    hipLaunchKernelGGL((combine_kernel<D, F16>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    hipLaunchKernelGGL((combine_kernel<D, F16, Q32>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 4, st);
   }
@@ -239,18 +242,27 @@ rpa_status launch_for_kv(int32_t q_dtype, int32_t kv_dtype, const Params& p, int
                          hipEvent_t* ev) {
   if (q_dtype == RPA_DTYPE_F16) {
     switch (kv_dtype) {
-      case RPA_DTYPE_F16: return launch_attention<D, kKvBf16, true>(p, cus, st, ev);
-      case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, true>(p, cus, st, ev);
-      case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, true>(p, cus, st, ev);
-      case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, true>(p, cus, st, ev);
+      case RPA_DTYPE_F16: return launch_attention<D, kKvBf16, true, false>(p, cus, st, ev);
+      case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, true, false>(p, cus, st, ev);
+      case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, true, false>(p, cus, st, ev);
+      case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, true, false>(p, cus, st, ev);
+      default: return RPA_ERR_UNSUPPORTED;
+    }
+  }
+  if (q_dtype == RPA_DTYPE_F32) {
+    switch (kv_dtype) {
+      case RPA_DTYPE_BF16: return launch_attention<D, kKvBf16, false, true>(p, cus, st, ev);
+      case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, false, true>(p, cus, st, ev);
+      case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, false, true>(p, cus, st, ev);
+      case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, false, true>(p, cus, st, ev);
       default: return RPA_ERR_UNSUPPORTED;
     }
   }
   switch (kv_dtype) {
-    case RPA_DTYPE_BF16: return launch_attention<D, kKvBf16, false>(p, cus, st, ev);
-    case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, false>(p, cus, st, ev);
-    case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, false>(p, cus, st, ev);
-    case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, false>(p, cus, st, ev);
+    case RPA_DTYPE_BF16: return launch_attention<D, kKvBf16, false, false>(p, cus, st, ev);
+    case RPA_DTYPE_FP8_E4M3FN: return launch_attention<D, kKvE4M3, false, false>(p, cus, st, ev);
+    case RPA_DTYPE_FP8_E5M2: return launch_attention<D, kKvE5M2, false, false>(p, cus, st, ev);
+    case RPA_DTYPE_INT8: return launch_attention<D, kKvI8, false, false>(p, cus, st, ev);
     default: return RPA_ERR_UNSUPPORTED;
   }
 }
@@ -260,24 +272,28 @@ rpa_status launch_plan(const Params& p, hipStream_t st) {
   return check_launch();
 }
 
-template <int D, bool IN_F16>
+template <int D, int IN>
 void launch_append_in(int mode, int grid, hipStream_t st, const AppendParams& p) {
   const dim3 blk(kApWaves * 64);
+  // a bit copy needs the rows in the cache type
+  if (IN == kInF32 && mode == kApCopy) mode = kApBf16;
   switch (mode) {
-    case kApFp8: hipLaunchKernelGGL((kv_append_kernel<D, kApFp8, IN_F16>), dim3(grid), blk, 0, st, p); break;
-    case kApE5M2: hipLaunchKernelGGL((kv_append_kernel<D, kApE5M2, IN_F16>), dim3(grid), blk, 0, st, p); break;
-    case kApI8: hipLaunchKernelGGL((kv_append_kernel<D, kApI8, IN_F16>), dim3(grid), blk, 0, st, p); break;
-    case kApCopy: hipLaunchKernelGGL((kv_append_kernel<D, kApCopy, IN_F16>), dim3(grid), blk, 0, st, p); break;
-    case kApF16: hipLaunchKernelGGL((kv_append_kernel<D, kApF16, IN_F16>), dim3(grid), blk, 0, st, p); break;
-    default: hipLaunchKernelGGL((kv_append_kernel<D, kApBf16, IN_F16>), dim3(grid), blk, 0, st, p); break;
+    case kApFp8: hipLaunchKernelGGL((kv_append_kernel<D, kApFp8, IN>), dim3(grid), blk, 0, st, p); break;
+    case kApE5M2: hipLaunchKernelGGL((kv_append_kernel<D, kApE5M2, IN>), dim3(grid), blk, 0, st, p); break;
+    case kApI8: hipLaunchKernelGGL((kv_append_kernel<D, kApI8, IN>), dim3(grid), blk, 0, st, p); break;
+    case kApCopy: hipLaunchKernelGGL((kv_append_kernel<D, (IN == kInF32 ? kApBf16 : kApCopy), IN>), dim3(grid), blk, 0, st, p); break;
+    case kApF16: hipLaunchKernelGGL((kv_append_kernel<D, (IN == kInF32 ? kApBf16 : kApF16), IN>), dim3(grid), blk, 0, st, p); break;
+    default: hipLaunchKernelGGL((kv_append_kernel<D, kApBf16, IN>), dim3(grid), blk, 0, st, p); break;
   }
 }
 template <int D>
-void launch_append(int mode, bool in_f16, int grid, hipStream_t st, const AppendParams& p) {
-  if (in_f16)
-    launch_append_in<D, true>(mode, grid, st, p);
+void launch_append(int mode, int in, int grid, hipStream_t st, const AppendParams& p) {
+  if (in == kInF16)
+    launch_append_in<D, kInF16>(mode, grid, st, p);
+  else if (in == kInF32)
+    launch_append_in<D, kInF32>(mode, grid, st, p);
   else
-    launch_append_in<D, false>(mode, grid, st, p);
+    launch_append_in<D, kInBf16>(mode, grid, st, p);
 }
 
 __global__ void decode_fp8_kernel(const uint8_t* codes, float* out, int n) {
@@ -505,8 +521,8 @@ rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v
   int cus = 0;
   if (!device_cus(&cus)) return RPA_ERR_HIP;
   AppendParams p;
-  p.k_new = static_cast<const uint16_t*>(k_new);
-  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.kv = kv_pages;
   p.kv_lens = kv_lens;
   p.page_indices = page_indices;
@@ -520,21 +536,22 @@ rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v
   p.pps = cfg->pages_per_seq;
   p.k_scale = cfg->k_scale;
   p.v_scale = cfg->v_scale;
-  const bool in_f16 = cfg->q_dtype == RPA_DTYPE_F16;  // the new rows' type
-  const int mode = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN             ? kApFp8
-                   : cfg->kv_dtype == RPA_DTYPE_FP8_E5M2             ? kApE5M2
-                   : cfg->kv_dtype == RPA_DTYPE_INT8                 ? kApI8
-                   : (cfg->k_scale == 1.f && cfg->v_scale == 1.f) ? kApCopy
-                   : in_f16                                          ? kApF16
-                                                                     : kApBf16;
+  // the new rows' type is the q type
+  const int in = cfg->q_dtype == RPA_DTYPE_F16 ? kInF16 : cfg->q_dtype == RPA_DTYPE_F32 ? kInF32 : kInBf16;
+  const int mode = cfg->kv_dtype == RPA_DTYPE_FP8_E4M3FN                                   ? kApFp8
+                   : cfg->kv_dtype == RPA_DTYPE_FP8_E5M2                                   ? kApE5M2
+                   : cfg->kv_dtype == RPA_DTYPE_INT8                                       ? kApI8
+                   : (in != kInF32 && cfg->k_scale == 1.f && cfg->v_scale == 1.f) ? kApCopy
+                   : in == kInF16                                                          ? kApF16
+                                                                                           : kApBf16;
   // a wave per token, grid-stride beyond 8 workgroups per compute unit
   int grid = (cfg->num_q_tokens + kApWaves - 1) / kApWaves;
   if (grid > cus * 8) grid = cus * 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg->head_dim) {
-    case 64: launch_append<64>(mode, in_f16, grid, s, p); break;
-    case 128: launch_append<128>(mode, in_f16, grid, s, p); break;
-    case 256: launch_append<256>(mode, in_f16, grid, s, p); break;
+    case 64: launch_append<64>(mode, in, grid, s, p); break;
+    case 128: launch_append<128>(mode, in, grid, s, p); break;
+    case 256: launch_append<256>(mode, in, grid, s, p); break;
     default: return RPA_ERR_UNSUPPORTED;
   }
   return check_launch();

@@ -10,10 +10,10 @@
 // factor: RN_f32(x / scale), rounded to nearest even in the cache type
 // (e4m3fn saturates at +-448, e5m2 at +-57344; NaN stays NaN; int8 rounds
 // to an integer, ties to even, saturating at -128 / 127, NaN to 0). New rows
-// come in the q type (bf16 or f16).
+// come in the q type (bf16, f16 or f32).
 //
-// HBM-bound: per token 2*Hkv*D 16-bit elements are read and 2*Hkv*D cache
-// elements written, contiguous on both sides. One wave per token; each lane
+// HBM-bound: per token 2*Hkv*D elements of the q type are read and 2*Hkv*D
+// cache elements written, contiguous on both sides. One wave per token; each lane
 // moves 16-byte chunks (8 elements), loads first, then converts and stores.
 #pragma once
 
@@ -28,9 +28,20 @@ namespace rpa {
 constexpr int kApWaves = 4;   // waves per workgroup, one token each at a time
 constexpr int kApUnroll = 4;  // 16-byte chunks in flight per lane
 
+// Element type of the new rows (template parameter IN): the q type.
+constexpr int kInBf16 = 0;
+constexpr int kInF16 = 1;
+constexpr int kInF32 = 2;
+
+// Eight new elements (one 8-element chunk of a row) as loaded.
+template <int IN>
+struct ApChunk {
+  u32x4 w[IN == kInF32 ? 2 : 1];
+};
+
 // Cache element type of an append launch.
 enum ApMode : int {
-  kApCopy = 0,  // bf16 cache with both scales 1: the quotient is x itself
+  kApCopy = 0,  // cache in the rows' own 16-bit type, both scales 1: the quotient is x itself
   kApBf16 = 1,  // bf16 cache, general scales
   kApFp8 = 2,   // e4m3fn cache
   kApE5M2 = 3,  // e5m2 cache
@@ -39,8 +50,8 @@ enum ApMode : int {
 };
 
 struct AppendParams {
-  const uint16_t* k_new;  // [T, Hkv, D] bits of the q type (bf16 or f16)
-  const uint16_t* v_new;  // [T, Hkv, D] bits of the q type
+  const void* k_new;      // [T, Hkv, D] elements of the q type (bf16, f16 or f32)
+  const void* v_new;      // [T, Hkv, D] elements of the q type
   void* kv;               // [P, page_size, 2*Hkv, D] cache elements
   const int32_t* kv_lens;
   const int32_t* page_indices;
@@ -67,20 +78,18 @@ __device__ __forceinline__ int ap_seq_of_token(const int32_t* cu, int nseq, int 
   return lo;
 }
 
-// The low / high 16-bit element of a dword as f32 (exact), bf16 or f16.
-template <bool IN_F16>
-__device__ __forceinline__ float ap_lo(uint32_t w) {
-  if constexpr (IN_F16)
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-  else
-    return __uint_as_float(w << 16);
-}
-template <bool IN_F16>
-__device__ __forceinline__ float ap_hi(uint32_t w) {
-  if constexpr (IN_F16)
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-  else
-    return __uint_as_float(w & 0xFFFF0000u);
+// Element i (0..7) of a chunk as f32, exactly.
+template <int IN>
+__device__ __forceinline__ float ap_elem(const ApChunk<IN>& x, int i) {
+  if constexpr (IN == kInF32) {
+    return __uint_as_float(x.w[i >> 2][i & 3]);
+  } else {
+    const uint32_t w = x.w[0][i >> 1];
+    if constexpr (IN == kInF16)
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+    else
+      return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
 }
 
 // fp8 code pair (e4m3fn, or e5m2) of two f32 quotients into the low (HI
@@ -99,25 +108,29 @@ __device__ __forceinline__ uint32_t ap_fp8_pair(float a, float b, uint32_t old) 
 
 // Loads chunks c0, c0+64, ... (kApUnroll of them, those below nch) of one
 // token's K|V rows: chunk c is 8 elements of combined head c / (D/8).
-template <int D>
-__device__ __forceinline__ void load_chunks(u32x4 (&x)[kApUnroll], const uint16_t* kr, const uint16_t* vr, int c0,
+template <int D, int IN>
+__device__ __forceinline__ void load_chunks(ApChunk<IN> (&x)[kApUnroll], const char* kr, const char* vr, int c0,
                                             int nch) {
   constexpr int CPR = D / 8;
+  constexpr int ES = IN == kInF32 ? 4 : 2;  // bytes per new element
 #pragma unroll
   for (int u = 0; u < kApUnroll; ++u) {
     const int c = c0 + 64 * u;
     if (c < nch) {
       const int ch = c / CPR;  // combined head: 2h = K, 2h+1 = V
-      x[u] = *reinterpret_cast<const u32x4*>(((ch & 1) ? vr : kr) + (ch >> 1) * D + (c % CPR) * 8);
+      const char* src = ((ch & 1) ? vr : kr) + ((ch >> 1) * D + (c % CPR) * 8) * ES;
+#pragma unroll
+      for (int k = 0; k < (IN == kInF32 ? 2 : 1); ++k) x[u].w[k] = *reinterpret_cast<const u32x4*>(src + 16 * k);
     }
   }
 }
 
 // Converts and stores the chunks load_chunks fetched; e_slot is the slot's
 // first cache element.
-template <int D, int MODE, bool IN_F16>
-__device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const AppendParams& p, int64_t e_slot,
-                                             int c0, int nch) {
+template <int D, int MODE, int IN>
+__device__ __forceinline__ void store_chunks(const ApChunk<IN> (&x)[kApUnroll], const AppendParams& p,
+                                             int64_t e_slot, int c0, int nch) {
+  static_assert(MODE != kApCopy || IN != kInF32, "a bit copy needs 16-bit rows");
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int u = 0; u < kApUnroll; ++u) {
@@ -125,16 +138,13 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
     if (c >= nch) continue;
     const int64_t e0 = e_slot + (int64_t)c * 8;
     if (MODE == kApCopy) {
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = x[u];
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.kv) + e0) = x[u].w[0];
       continue;
     }
     const float sc = ((c / CPR) & 1) ? p.v_scale : p.k_scale;
     float f[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = ap_lo<IN_F16>(x[u][i]) / sc;
-      f[2 * i + 1] = ap_hi<IN_F16>(x[u][i]) / sc;
-    }
+    for (int i = 0; i < 8; ++i) f[i] = ap_elem<IN>(x[u], i) / sc;
     if (MODE == kApBf16 || MODE == kApF16) {
       u32x4 y;
 #pragma unroll
@@ -160,7 +170,7 @@ __device__ __forceinline__ void store_chunks(const u32x4 (&x)[kApUnroll], const 
   }
 }
 
-template <int D, int MODE, bool IN_F16>
+template <int D, int MODE, int IN>
 __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p) {
   constexpr int CPR = D / 8;  // 16-byte chunks per head row
   const int lane = threadIdx.x & 63;
@@ -173,11 +183,12 @@ __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p
   const int64_t pos_cap = (int64_t)p.pps * p.page_size;
   // wave-uniform token loop
   for (int t = t_begin + blockIdx.x * kApWaves + (int)(threadIdx.x >> 6); t < t_end; t += stride) {
-    const uint16_t* kr = p.k_new + (int64_t)t * p.Hkv * D;
-    const uint16_t* vr = p.v_new + (int64_t)t * p.Hkv * D;
+    constexpr int ES = IN == kInF32 ? 4 : 2;
+    const char* kr = static_cast<const char*>(p.k_new) + (int64_t)t * p.Hkv * D * ES;
+    const char* vr = static_cast<const char*>(p.v_new) + (int64_t)t * p.Hkv * D * ES;
     // the token's first rows are in flight while its slot is looked up
-    u32x4 x[kApUnroll];
-    load_chunks<D>(x, kr, vr, lane, nch);
+    ApChunk<IN> x[kApUnroll];
+    load_chunks<D, IN>(x, kr, vr, lane, nch);
     const int s = ap_seq_of_token(p.cu_q_lens, nseq, t);
     const int q0 = p.cu_q_lens[s];
     const int q_len = p.cu_q_lens[s + 1] - q0;
@@ -187,10 +198,10 @@ __global__ __launch_bounds__(kApWaves * 64) void kv_append_kernel(AppendParams p
     if (page < 0 || page >= p.P) continue;
     const int64_t slot = (int64_t)page * p.page_size + pos % p.page_size;
     for (int c0 = lane;;) {
-      store_chunks<D, MODE, IN_F16>(x, p, slot * 2 * p.Hkv * D, c0, nch);
+      store_chunks<D, MODE, IN>(x, p, slot * 2 * p.Hkv * D, c0, nch);
       c0 += 64 * kApUnroll;
       if (c0 >= nch) break;
-      load_chunks<D>(x, kr, vr, c0, nch);
+      load_chunks<D, IN>(x, kr, vr, c0, nch);
     }
   }
 }

@@ -105,14 +105,14 @@ static_assert(sizeof(Header) == 256, "header is int32[64]");
 // Everything a kernel needs, passed by value.
 struct Params {
   // inputs
-  const uint16_t* q;         // [T, Hq, D] bf16 bits
+  const uint16_t* q;         // [T, Hq, D] q elements: bf16 / f16 bits, or f32 (read as float)
   const uint8_t* kv;         // [P, page, 2Hkv, D] bf16 or fp8 bytes
   const int32_t* kv_lens;
   const int32_t* page_indices;
   const int32_t* cu_q_lens;
   const int32_t* num_seqs;
   // outputs
-  uint16_t* out;             // [T, Hq, D] bf16 bits
+  uint16_t* out;             // [T, Hq, D] out elements in the q type (f32 written as float)
   float* lse;                // [T, Hq] or null
   // workspace views
   Header* hdr;
@@ -213,6 +213,36 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   } else {
     return bf16x2_bits(lo, hi);
   }
+}
+
+// An f32 q (template parameter Q32 of the attention kernels, computed on the
+// bf16 path): each element x is carried as hi = RN_bf16(x) and
+// lo = RN_bf16(x - hi), both exact enough that hi + lo is within 2^-17 |x| of
+// x (x - hi is an f32 value exactly, and lo rounds it to 8 significant bits).
+// The score is K.hi + K.lo, two MFMA chains into one f32 accumulator; K is
+// bf16 or a one-byte code widened exactly, so only the lo rounding is lost.
+// Out is written in f32. Eight f32 elements -> the hi and lo operands:
+__device__ __forceinline__ void split_q8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack2<false>(x[2 * i], x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u);
+    l[i] = pack2<false>(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Four results -> out elements [e, e + 4): the 16-bit type, or f32 (Q32).
+template <bool F16, bool Q32>
+__device__ __forceinline__ void store_out4(uint16_t* out, int64_t e, float a, float b, float c, float d) {
+  if constexpr (Q32)
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e) = f32x4{a, b, c, d};
+  else
+    *reinterpret_cast<u32x2*>(out + e) = u32x2{pack2<F16>(a, b), pack2<F16>(c, d)};
 }
 
 // K/V element types of the attention kernels (template parameter KVT).

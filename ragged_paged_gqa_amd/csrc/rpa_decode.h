@@ -50,6 +50,8 @@
 // type, fp8 e4m3fn, fp8 e5m2, int8) and per 16-bit type F16 (bf16, or f16
 // with an f16 q: f16 MFMAs, f16 P and output). In the comments below "bf16"
 // stands for that 16-bit type and "fp8" for any one-byte code.
+// Q32: an f32 q (bf16 path, K/V bf16 or one-byte): Q is split into bf16 hi
+// and lo operands (split_q8), S^T takes both MFMA chains, out is f32.
 #pragma once
 
 #include "rpa_common.h"
@@ -173,10 +175,12 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel
 // carries no cap arithmetic at all).
-template <int D, int KVT, bool CAP, bool F16>
+template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
     Params p) {
   constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8)
+  constexpr bool QREG = FP8 || Q32;     // Q operand loaded into registers (no LDS Q slot)
+  static_assert(!(Q32 && F16), "an f32 q runs on the bf16 path");
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
                 NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, NST = Cf::NST;
@@ -284,17 +288,26 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       qb[i] = col < I.nrows ? v : bf16x8{};
     }
   };
-  // fp8: the same operand straight from global memory (row col of the item;
-  // rows past nrows re-read row 0 and are zeroed)
-  auto load_q = [&](const Info& I, bf16x8 (&qr)[NI]) {
+  // fp8 and f32 q: the same operand straight from global memory (row col of
+  // the item; rows past nrows re-read row 0 and are zeroed); an f32 q also
+  // gives its lo part (split_q8)
+  auto load_q = [&](const Info& I, bf16x8 (&qr)[NI], bf16x8 (&qlr)[Q32 ? NI : 1]) {
     const int prow = I.row0 + (col < I.nrows ? col : 0);
     const int t = prow / p.G;
     const int qh = I.h * p.G + (prow - t * p.G);
-    const uint16_t* qp = p.q + ((int64_t)(I.q0 + t) * p.Hq + qh) * D;
+    const int64_t e = ((int64_t)(I.q0 + t) * p.Hq + qh) * D;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + slot_d<FP8>(i, g));
-      qr[i] = col < I.nrows ? v : bf16x8{};
+      if constexpr (Q32) {
+        const float* qp = reinterpret_cast<const float*>(p.q) + e + slot_d<FP8>(i, g);
+        bf16x8 hi, lo;
+        split_q8(*reinterpret_cast<const f32x4*>(qp), *reinterpret_cast<const f32x4*>(qp + 4), hi, lo);
+        qr[i] = col < I.nrows ? hi : bf16x8{};
+        qlr[i] = col < I.nrows ? lo : bf16x8{};
+      } else {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(p.q + e + slot_d<FP8>(i, g));
+        qr[i] = col < I.nrows ? v : bf16x8{};
+      }
     }
   };
 
@@ -344,6 +357,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   // ---- compute state of the current item ----
   Info C;
   bf16x8 qb[NI];
+  bf16x8 ql[Q32 ? NI : 1];  // f32 q: the lo part of the Q operand
   float m_ref, lsum;
   f32x4 o[ND];
   int steps_done, n_steps;
@@ -422,6 +436,10 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) sc = mfma16x16x32<F16>(ka[i], qb[i], sc);
+    if constexpr (Q32) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sc = mfma16x16x32<F16>(ka[i], ql[i], sc);
+    }
     // does the step hold a key that some row of the unit cannot see?
     const bool need_mask = kb + 16 > vis_hi || (p.is_causal && kb + 15 > pos_lo) ||
                            (p.window > 0 && kb <= pos_hi - p.window);
@@ -521,12 +539,10 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     }
     if (!rvalid) return;
     if (C.nch == 1) {
-      uint16_t* op = p.out + ((int64_t)tok * p.Hq + qh) * D;
+      const int64_t e = ((int64_t)tok * p.Hq + qh) * D + 4 * g;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        u32x2 v = {pack2<F16>(o[d][0] * inv, o[d][1] * inv), pack2<F16>(o[d][2] * inv, o[d][3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 16 * d + 4 * g) = v;
-      }
+      for (int d = 0; d < ND; ++d)
+        store_out4<F16, Q32>(p.out, e + 16 * d, o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv);
       if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
     } else {
       float* pp = p.dec_part + ((int64_t)C.idx * kDecRows + col) * D;
@@ -542,10 +558,11 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   C = load_info(first);
   if (!mine(C)) return;
   Info Cn = load_info(first + 1);  // the compute side's next item
-  bf16x8 qn[FP8 ? NI : 1];         // fp8: the next item's Q operand, loaded ahead
-  if constexpr (FP8) {
-    load_q(C, qb);
-    if (mine(Cn)) load_q(Cn, qn);
+  bf16x8 qn[QREG ? NI : 1];        // fp8, f32 q: the next item's Q operand, loaded ahead
+  bf16x8 qnl[Q32 ? NI : 1];        // f32 q: its lo part
+  if constexpr (QREG) {
+    load_q(C, qb, ql);
+    if (mine(Cn)) load_q(Cn, qn, qnl);
   } else {
     dma_q(C);
     wait_vmcnt<0>();
@@ -611,10 +628,14 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       if (!mine(Cn)) return;  // the wave's range is done
       C = Cn;
       Cn = load_info(C.idx + 1);
-      if constexpr (FP8) {
+      if constexpr (QREG) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) qb[i] = qn[i];
-        if (mine(Cn)) load_q(Cn, qn);
+        if constexpr (Q32) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) ql[i] = qnl[i];
+        }
+        if (mine(Cn)) load_q(Cn, qn, qnl);
       } else {
         // the Q slot's DMA is complete once a wait above covered a step
         // issued after it (NST + 1 steps later); for short items wait here
@@ -634,7 +655,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
 // Merges the split decode-class units once every decode item is done: one
 // wave per unit, the items' partials combined by merge_unit; a unit with no
 // key to see (and so no item) gets out = 0 and lse = -inf.
-template <int D, bool F16>
+template <int D, bool F16, bool Q32 = false>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params p) {
   __shared__ float stat[kDecWavesPerBlock][2 * kDecRows];
   const int lane = threadIdx.x & 63;
@@ -665,12 +686,12 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
         const int prow = U.row0 + e / (D / 4);
         const int t = prow / p.G;
         const int qh = U.kv_head * p.G + (prow - t * p.G);
-        *reinterpret_cast<u32x2*>(p.out + ((int64_t)(q0 + t) * p.Hq + qh) * D + 4 * (e % (D / 4))) = u32x2{0u, 0u};
+        store_out4<F16, Q32>(p.out, ((int64_t)(q0 + t) * p.Hq + qh) * D + 4 * (e % (D / 4)), 0.f, 0.f, 0.f, 0.f);
         if (p.lse && e % (D / 4) == 0) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = p.sinks ? p.sinks[qh] : -INFINITY;
       }
       continue;
     }
-    merge_unit<D, F16>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
+    merge_unit<D, F16, Q32>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
     wave_sync();
   }
 }

@@ -27,7 +27,7 @@ namespace rpa {
 // Threads tid in [0, nt) cooperate; `sync` is called between the phases and
 // must synchronise exactly those threads. `stat` is LDS scratch of
 // 2 * u.nrows floats.
-template <int D, bool F16, typename Sync>
+template <int D, bool F16, bool Q32, typename Sync>
 __device__ void merge_unit(const Params& p, const Unit& u, const float* part, const float* plse, int slot_rows,
                            int tid, int nt, float* stat, Sync sync) {
   int q0, ql;
@@ -75,9 +75,8 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
     const int prow = u.row0 + r;
     const int t = prow / p.G;
     const int qh = u.kv_head * p.G + (prow - t * p.G);
-    uint16_t* op = p.out + ((int64_t)(q0 + t) * p.Hq + qh) * D + e0;
-    const u32x2 w2 = {pack2<F16>(acc[0] * inv, acc[1] * inv), pack2<F16>(acc[2] * inv, acc[3] * inv)};
-    *reinterpret_cast<u32x2*>(op) = w2;
+    store_out4<F16, Q32>(p.out, ((int64_t)(q0 + t) * p.Hq + qh) * D + e0, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+                         acc[3] * inv);
   }
 }
 

@@ -36,6 +36,8 @@
 // with an f16 q: f16 MFMAs, f16 P and output). In the comments here "bf16"
 // stands for that 16-bit type and "fp8" for any one-byte code (widened to it
 // exactly: v_cvt_scalef32_pk_*_fp8 / _bf8, or sign extension for int8).
+// Q32: an f32 q (bf16 path, K/V bf16 or one-byte): Q is split into bf16 hi
+// and lo operands (split_q8), S^T takes both MFMA chains, out is f32.
 #pragma once
 
 #include <climits>
@@ -111,8 +113,9 @@ __device__ __forceinline__ int swz_v(int key) {
 
 // CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
 // block loop has no branch and no cap arithmetic).
-template <int D, int KVT, bool CAP, bool F16>
+template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
 __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
+  static_assert(!(Q32 && F16), "an f32 q runs on the bf16 path");
   constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8), widened in registers
   // f16 P must stay below 65504: exponentiated scores <= 2^15
   constexpr float SLACK = F16 ? kRescaleSlack - 1.0f : kRescaleSlack;
@@ -262,6 +265,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
     int row[NH], tok[NH], qh[NH], vis_end[NH], win_lo[NH];
     bool rvalid[NH];
     bf16x8 qb[NH][NS];
+    bf16x8 qlo[Q32 ? NH : 1][Q32 ? NS : 1];  // f32 q: the lo part of the Q operand (split_q8)
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
       row[hf] = WR * wave + 32 * hf + r32;
@@ -275,16 +279,29 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       win_lo[hf] = p.window > 0 ? pos - p.window : INT_MIN;  // keys <= win_lo are hidden
       vis_end[hf] = p.is_causal ? min(vis_hi, pos + 1) : vis_hi;
       if (rvalid[hf]) {
-        const uint16_t* qp = p.q + ((int64_t)tok[hf] * p.Hq + qh[hf]) * D;
+        const int64_t e = ((int64_t)tok[hf] * p.Hq + qh[hf]) * D;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * i + 8 * h);
-          if (neg) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-          qb[hf][i] = __builtin_bit_cast(bf16x8, v);
+          if constexpr (Q32) {
+            const float* qp = reinterpret_cast<const float*>(p.q) + e + 16 * i + 8 * h;
+            f32x4 a = *reinterpret_cast<const f32x4*>(qp), b = *reinterpret_cast<const f32x4*>(qp + 4);
+            if (neg) {
+              a = -a;
+              b = -b;
+            }
+            split_q8(a, b, qb[hf][i], qlo[hf][i]);
+          } else {
+            u32x4 v = *reinterpret_cast<const u32x4*>(p.q + e + 16 * i + 8 * h);
+            if (neg) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            qb[hf][i] = __builtin_bit_cast(bf16x8, v);
+          }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) qb[hf][i] = bf16x8{};
+        for (int i = 0; i < NS; ++i) {
+          qb[hf][i] = bf16x8{};
+          if constexpr (Q32) qlo[hf][i] = bf16x8{};
+        }
       }
     }
     auto visible = [&](int hf, int key) { return rvalid[hf] && key < vis_end[hf] && key > win_lo[hf]; };
@@ -437,6 +454,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         f32x16 sc = f32x16{};
 #pragma unroll
         for (int i = 0; i < NS; ++i) sc = mfma32x32x16<F16>(ka[i], qb[hf][i], sc);
+        if constexpr (Q32) {
+#pragma unroll
+          for (int i = 0; i < NS; ++i) sc = mfma32x32x16<F16>(ka[i], qlo[hf][i], sc);
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) sv[hf][j] = sc[j];
       }
@@ -609,7 +630,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
 #pragma unroll
-            for (int hf = 0; hf < NH; ++hf) sc_next[hf] = mfma32x32x16<F16>(ka[i], qb[hf][i], sc_next[hf]);
+            for (int hf = 0; hf < NH; ++hf) {
+              sc_next[hf] = mfma32x32x16<F16>(ka[i], qb[hf][i], sc_next[hf]);
+              if constexpr (Q32) sc_next[hf] = mfma32x32x16<F16>(ka[i], qlo[hf][i], sc_next[hf]);
+            }
             if (i + KA < NS) ka[i + KA] = *reinterpret_cast<const bf16x8*>(nslot + k_at(i + KA));
 #pragma unroll
             for (int q = PRE + ((NPP - PRE) * i) / NS; q < PRE + ((NPP - PRE) * (i + 1)) / NS; ++q) p_pair(q);
@@ -667,15 +691,13 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       row_final(m_ref[hf], l_row, p.v_scale, (u.nch == 1 && p.sinks) ? p.sinks + qh[hf] : nullptr, inv, lse_v);
       if (!rvalid[hf]) continue;
       if (u.nch == 1) {
-        uint16_t* op = p.out + ((int64_t)tok[hf] * p.Hq + qh[hf]) * D + 4 * h;
+        const int64_t e = ((int64_t)tok[hf] * p.Hq + qh[hf]) * D + 4 * h;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            u32x2 w = {pack2<F16>(o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv),
-                       pack2<F16>(o[hf][d][4 * q4 + 2] * inv, o[hf][d][4 * q4 + 3] * inv)};
-            *reinterpret_cast<u32x2*>(op + 32 * d + 8 * q4) = w;
-          }
+          for (int q4 = 0; q4 < 4; ++q4)
+            store_out4<F16, Q32>(p.out, e + 32 * d + 8 * q4, o[hf][d][4 * q4] * inv, o[hf][d][4 * q4 + 1] * inv,
+                                 o[hf][d][4 * q4 + 2] * inv, o[hf][d][4 * q4 + 3] * inv);
         if (h == 0 && p.lse) p.lse[(int64_t)tok[hf] * p.Hq + qh[hf]] = lse_v;
       } else {
         float* pp = p.pf_part + ((int64_t)item * p.pf_rows + row[hf]) * D + 4 * h;
@@ -700,7 +722,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         // the LDS ring is idle here (every wave is past its last step); it
         // holds the per-row stats of the merge
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D, F16>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
+        merge_unit<D, F16, Q32>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
       }
     }
     // every wave must be done with the ring before the next item refills it

@@ -26,11 +26,19 @@ def lib_config(w: wl.Workload) -> rpa.Config:
         max_num_seqs=c.max_num_seqs, pages_per_seq=c.pages_per_seq,
         kv_dtype={wl.KV_FP8: rpa.DTYPE_FP8_E4M3FN, wl.KV_E5M2: rpa.DTYPE_FP8_E5M2,
                   wl.KV_F16: rpa.DTYPE_F16, wl.KV_I8: rpa.DTYPE_INT8}.get(c.kv_dtype, rpa.DTYPE_BF16),
-        q_dtype=rpa.DTYPE_F16 if c.q_dtype == wl.Q_F16 else rpa.DTYPE_BF16,
+        q_dtype={wl.Q_F16: rpa.DTYPE_F16, wl.Q_F32: rpa.DTYPE_F32}.get(c.q_dtype, rpa.DTYPE_BF16),
         sm_scale=c.sm_scale, soft_cap=c.soft_cap or 0.0,
         k_scale=1.0 if c.k_scale is None else c.k_scale,
         v_scale=1.0 if c.v_scale is None else c.v_scale,
         is_causal=c.is_causal, sliding_window=c.sliding_window or 0)
+
+
+def upload_q_bits(bits: np.ndarray, q_dtype: str, device="cuda") -> torch.Tensor:
+    """Bits of the q dtype (workloads.to_q_bits) -> a device tensor of that dtype."""
+    if q_dtype == wl.Q_F32:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.float32)).to(device)
+    t16 = torch.float16 if q_dtype == wl.Q_F16 else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(t16)
 
 
 class Device:
@@ -40,7 +48,7 @@ class Device:
         self.w = w
         self.cfg = lib_config(w)
         t16 = torch.float16 if w.cfg.q_dtype == wl.Q_F16 else torch.bfloat16
-        self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(t16)
+        self.q = upload_q_bits(w.q, w.cfg.q_dtype, device)
         if wl.is_fp8(w.cfg.kv_dtype):
             self.kv = torch.from_numpy(w.kv_pages).to(device)
         else:

@@ -32,7 +32,11 @@ def _kv_host(dev):
 
 
 def _bits_dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    """Row bits of the q dtype on the device: uint32 (f32) as float32, 16-bit as a 2-byte tensor."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.float32)).cuda()
+    return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
 
 
 def _append(dev, k_new, v_new):

@@ -62,6 +62,10 @@ def _ws_status(cfg):
     (dict(page_size=24), 2),
     (dict(page_size=2048, pages_per_seq=2), 2),
     (dict(kv_dtype=7), 2),
+    (dict(q_dtype=rpa.DTYPE_F32, kv_dtype=rpa.DTYPE_F16), 2),   # f32 q runs on the bf16 path
+    (dict(q_dtype=rpa.DTYPE_F32, kv_dtype=rpa.DTYPE_F32), 2),   # no f32 cache
+    (dict(q_dtype=rpa.DTYPE_INT8, kv_dtype=rpa.DTYPE_INT8), 2),  # int8 is a K/V type only
+    (dict(q_dtype=rpa.DTYPE_F16, kv_dtype=rpa.DTYPE_BF16), 2),  # 16-bit K/V in the q type
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw, code):
     cfg = _cfg(**kw)
