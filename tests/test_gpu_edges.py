@@ -1,7 +1,8 @@
 """Edge cases of the attention path on the GPU against the oracle: no
 sequence at all, the largest page size (1024 keys), pure prompts (q_len =
 kv_len, ragged tails), single-key sequences, more sequences than one planner
-tile (512), and a window wider than every sequence.
+tile (512), a window wider than every sequence, and negative and zero score
+scales.
 """
 
 import numpy as np
@@ -81,3 +82,24 @@ def test_window_wider_than_every_sequence():
               sliding_window=100000)
     w = wl.build("widewin", kw, [1, 50, 3], [700, 900, 64], 66)
     _compare_all(w, "window wider than kv_len")
+
+
+@pytest.mark.parametrize("q_dtype,kvd,scale,cap", [
+    (wl.Q_BF16, wl.KV_BF16, -0.09, None),
+    (wl.Q_BF16, wl.KV_FP8, -0.09, 30.0),
+    (wl.Q_F16, wl.KV_F16, -0.09, None),
+    (wl.Q_F32, wl.KV_BF16, -0.09, None),
+    (wl.Q_F32, wl.KV_I8, -0.09, 20.0),
+    (wl.Q_BF16, wl.KV_BF16, 0.0, None),
+    (wl.Q_F32, wl.KV_E5M2, 0.0, None),
+])
+def test_negative_and_zero_score_scale(q_dtype, kvd, scale, cap):
+    """sm_scale < 0 (the kernels flip q's sign and use |scale|) and sm_scale = 0
+    (every visible key weighs the same: out is the mean of the visible V),
+    in both kernel classes."""
+    kw = dict(num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=32, pages_per_seq=None, sm_scale=scale,
+              soft_cap=cap, kv_dtype=kvd, q_dtype=q_dtype)
+    if wl.is_fp8(kvd):
+        kw.update(k_scale=0.05, v_scale=0.05)
+    w = wl.build("scale", kw, [1, 1, 40, 130], [300, 17, 200, 130], 65)
+    _compare_all(w, f"sm_scale {scale} q {q_dtype} kv {kvd} cap {cap}")
