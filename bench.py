@@ -212,10 +212,17 @@ def main():
         b = torch.empty(n, dtype=torch.uint8, device="cuda")
         a.fill_(1)
         torch.cuda.synchronize()
-        for _ in range(3):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for e0, e1 in ev:
+            e0.record()
             b.copy_(a)
+            e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "copies": 3}))
+        # the copy reads and writes n bytes: its rate is the HBM rate a plain
+        # stream reaches, beside the 8 TB/s peak
+        ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        print(json.dumps({"copy_bytes": n, "copies": 3, "copy_ms": [round(m, 4) for m in ms],
+                          "copy_gbs_best": round(2 * n / (min(ms) * 1e-3) / 1e9, 1)}))
         return
 
     import ragged_paged_gqa_amd as rpa
