@@ -17,10 +17,19 @@
 #include "rpa_decode.h"
 #include "rpa_plan.h"
 #include "rpa_prefill.h"
+#include "rpa_prefill_pp.h"
 
 // Prefill-class work items the planner aims for per compute unit.
 #ifndef RPA_PF_ITEMS_PER_CU
 #define RPA_PF_ITEMS_PER_CU 4
+#endif
+// head_dims whose 16-bit prefill runs on the two-group (ping-pong) kernel;
+// the others, an f32 q and one-byte K/V run on the 4-wave kernel.
+#ifndef RPA_PP_MIN_D
+#define RPA_PP_MIN_D 256
+#endif
+#ifndef RPA_PP_MAX_D
+#define RPA_PP_MAX_D 256
 #endif
 
 namespace {
@@ -101,13 +110,20 @@ int dec_grid_for(const rpa_config* c, int cus) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The prefill class of `c` runs on prefill_pp_kernel: 16-bit q with K/V in
+// the q type.
+bool uses_pp(const rpa_config* c) {
+  return (c->q_dtype == RPA_DTYPE_BF16 || c->q_dtype == RPA_DTYPE_F16) && c->kv_dtype == c->q_dtype &&
+         c->head_dim >= RPA_PP_MIN_D && c->head_dim <= RPA_PP_MAX_D;
+}
+
 // Sizes follow from cfg alone (see the item bound in the planning kernel:
 // items <= units + target because every chunk size is >= total / target).
 bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t G = c->num_q_heads / c->num_kv_heads;
   const int64_t Hkv = c->num_kv_heads;
   const int64_t D = c->head_dim;
-  const int64_t pf_rows = pf_rows_for(c->head_dim);
+  const int64_t pf_rows = uses_pp(c) ? kPpRows : pf_rows_for(c->head_dim);
   const int64_t max_du = Hkv * c->max_num_seqs;
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
   const int64_t tgt_p = (int64_t)cus * RPA_PF_ITEMS_PER_CU;
@@ -203,7 +219,17 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
 template <int D, int KVT, bool F16, bool Q32>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   constexpr bool FP8 = KVT != kKvBf16;
-  {
+  if constexpr (!FP8 && !Q32 && D >= RPA_PP_MIN_D && D <= RPA_PP_MAX_D) {
+    // one workgroup of 8 waves per CU
+    int grid = cus < p.max_pf_items ? cus : p.max_pf_items;
+    if (grid < 1) grid = 1;
+    if (p.soft_cap > 0.f)
+      hipLaunchKernelGGL((prefill_pp_kernel<D, true, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_pp_kernel<D, false, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
+    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
+    prof_record(ev, 2, st);
+  } else {
     constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfBlkTable + 64));
     constexpr int per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
     int grid = cus * (per_cu > 0 ? per_cu : 1);
