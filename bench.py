@@ -1,19 +1,33 @@
 """Benchmark of ragged paged GQA attention on one MI355X.
 
 One step = one rpa_forward call (plan, prefill-class tiles, decode-class
-tiles, split-KV merge inside them) over one batch of seeded synthetic inputs
-already resident in HBM; with --append, an rpa_kv_append of the step's new
-K/V rows first.
-The default workload is the decode batch (256 sequences x 1 query token,
-kv_len U[512, 8192], 32 q / 8 kv heads, head_dim 128, page 16, bf16).
+tiles, split-KV merge) over one batch of seeded synthetic inputs already
+resident in HBM; with --append, an rpa_kv_append of the step's new K/V rows
+first.
+
+The headline workload is the largest named one that fits one GPU, the long
+context batch (16 sequences x 128 query tokens, kv_len U[65536, 131072],
+32 q / 2 kv heads, head_dim 256, page 64, bf16); --workload picks another.
+After the headline, the other named workloads are measured the same way
+(--no-sweep skips them) and reported under "configs" of the same line.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr):
-  value      query tokens/s of the whole call
-  roofline   the dominant kernel's algorithmic bytes (or flops) per launch
-             over its mean launch time, measured with HIP events recorded
-             around each kernel on the launch stream during the timed steps
-  cpu_baseline  the f64 CPU oracle timed on a bounded sample of the same
-             workload on the host cores (a reported baseline, not a target)
+  value         query tokens/s of the headline workload over the K timed steps
+  roofline      the dominant kernel's algorithmic flops (or bytes) per launch
+                over its mean launch time, measured with HIP events recorded
+                around each kernel on the launch stream during the timed steps
+  timing        per-call HIP-event samples of the headline: warm (inputs and
+                plan already in cache from the previous call) and cold (a
+                1 GiB buffer written between samples, outside the events,
+                evicting L2 and the 256 MB Infinity Cache): median, p10, p90
+  configs       the same measurements for every other named workload, with a
+                call-level and a kernel-level roofline fraction
+  cpu_baseline  the f64 CPU oracle timed on a bounded sample of the headline
+                workload on the host cores (a reported baseline, not a target)
+
+Host-only modes (no GPU): --ingest-counters turns rocprofv3 FETCH_SIZE /
+WRITE_SIZE runs into the traffic file; --summarize-trace turns a rocprofv3
+kernel-stats CSV into a Markdown table.
 """
 
 from __future__ import annotations
@@ -22,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,6 +50,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "ragged paged attn: query tokens/s, KV HBM GB/s + TFLOP/s, % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+HEADLINE = 5                   # the largest named workload
+FLUSH_BYTES = 1 << 30          # written between cold samples (> 256 MB MALL + 8 x 4 MB L2)
 
 
 def log(*a):
@@ -82,6 +99,26 @@ def algorithmic_work(w):
     return res
 
 
+def host_cpu():
+    """CPU model and whether SMT is on, from /proc and /sys (Linux)."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    smt = None
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = f.read().strip() == "1"
+    except OSError:
+        pass
+    return model, smt
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle on the first n query tokens (all q heads), n sized for ~target_s."""
     import oracle
@@ -98,12 +135,15 @@ def cpu_baseline(w, target_s: float = 15.0):
         oracle.rows(w, toks, heads, nthreads=threads)
         return time.perf_counter() - t0
 
+    # grow the sample until one run takes about target_s (10-30 s of CPU work)
     n = min(T, 2)
     dt = run(n)
-    while dt < target_s / 8 and n < T:
+    while dt < 0.6 * target_s and n < T:
         n = min(T, max(n + 1, int(n * min(8.0, target_s / max(dt, 1e-3)))))
         dt = run(n)
+    model, smt = host_cpu()
     return {"value": n / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "smt": smt,
             "sample": f"first {n} of {T} query tokens, all {Hq} q heads, f64 oracle, {dt:.1f} s"}
 
 
@@ -132,6 +172,16 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
+KERNEL_CLASSES = ("decode_kernel", "prefill_pp_kernel", "prefill_kernel", "plan_kernel", "combine_kernel")
+
+
+def kernel_class(name: str):
+    for k in KERNEL_CLASSES:
+        if f"rpa::{k}<" in name or f"rpa::{k}(" in name:
+            return k
+    return None
+
+
 def ingest_counters(pmc_dir: str, workload: int) -> dict:
     """Turns two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
     WRITE_SIZE) plus the same two runs of `--copy-calibration` into HBM bytes
@@ -148,9 +198,9 @@ def ingest_counters(pmc_dir: str, workload: int) -> dict:
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         for k, v in _counter_per_kernel(
                 os.path.join(pmc_dir, f"w{workload}_{c}", "run_counter_collection.csv"), c).items():
-            for name in ("decode_kernel", "prefill_kernel", "plan_kernel", "combine_kernel"):
-                if f"rpa::{name}" in k:
-                    per.setdefault(name, {})[c] = v * 1024.0 / scale[c]
+            name = kernel_class(k)
+            if name:
+                per.setdefault(name, {})[c] = v * 1024.0 / scale[c]
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -171,17 +221,207 @@ def ingest_counters(pmc_dir: str, workload: int) -> dict:
     return {k: v for k, v in t.items() if k.endswith(f":cfg{workload}")}
 
 
+def summarize_trace(stats_csv: str) -> str:
+    """A rocprofv3 kernel-stats CSV (--kernel-trace --stats) as a Markdown
+    table: calls, average, min and max duration (us) and share, per kernel."""
+    import csv
+
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            if name.startswith("__amd_rocclr") or "at::" in name or "elementwise" in name:
+                continue  # torch's upload and fill kernels
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in sorted(rows, key=lambda x: -x[5]):
+        out.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} % |")
+    return "\n".join(out)
+
+
+def stats(samples_ms) -> dict:
+    a = np.asarray(samples_ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4), "n": int(a.size)}
+
+
+def roofline_of(flops: float, byts: float, seconds: float, prefer_mfma: bool) -> dict:
+    """Achieved rate against the roofline that bounds this work: MFMA (bf16
+    dense peak) when its arithmetic intensity is above the ridge point (or the
+    caller says it is matrix-bound), else HBM."""
+    ai = flops / max(byts, 1.0)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if prefer_mfma or ai >= ridge:
+        achieved = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    achieved = byts / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+class Runner:
+    """One workload resident on the GPU, with its timing helpers."""
+
+    def __init__(self, number, args, headline=False):
+        import torch
+
+        import ragged_paged_gqa_amd as rpa
+        import workloads as wl
+        from gpu_util import Device, upload_q_bits
+
+        self.torch, self.rpa = torch, rpa
+        self.number = number
+        kw = dict(kv_dtype=args.kv_dtype, q_dtype=args.q_dtype) if headline else {}
+        log(f"[bench] generating workload {number}: {wl.WORKLOADS[number]}")
+        t0 = time.perf_counter()
+        w = wl.named(number, **kw)
+        if headline and args.sinks:
+            w = wl.with_sinks(w, number)
+        log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
+        self.w = w
+        self.dev = Device(w)
+        self.work = algorithmic_work(w)
+        c = self.dev.cfg
+        odt = torch.float32 if c.q_dtype == rpa.DTYPE_F32 else torch.bfloat16  # f16 bits fit a bf16 buffer
+        self.out = torch.empty((c.num_q_tokens, c.num_q_heads, c.head_dim), dtype=odt, device="cuda")
+        self.lse = torch.empty((c.num_q_tokens, c.num_q_heads), dtype=torch.float32, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        self.append_new = None
+        if headline and args.append:
+            k_np, v_np = wl.new_kv(w, 1000 + number)
+            self.append_new = (upload_q_bits(k_np, w.cfg.q_dtype), upload_q_bits(v_np, w.cfg.q_dtype))
+
+    def call(self):
+        d = self.dev
+        self.rpa.forward(d.q, d.kv, d.kv_lens, d.page_indices, d.cu_q_lens, d.num_seqs, d.cfg,
+                         workspace=d.workspace, out=self.out, lse=self.lse, sinks=d.sinks)
+
+    def append(self):
+        d = self.dev
+        self.rpa.kv_append(self.append_new[0], self.append_new[1], d.kv, d.kv_lens, d.page_indices, d.cu_q_lens,
+                           d.num_seqs, d.cfg, stream=self.stream)
+
+    def timed_steps(self, steps, warmup):
+        """W untimed steps, then exactly K steps between synchronizations;
+        per-kernel HIP events of the K calls (rpa_profile_*); with --append
+        the append of each step is timed on its own with events."""
+        torch = self.torch
+        for _ in range(warmup):
+            if self.append_new is not None:
+                self.append()
+            self.call()
+        torch.cuda.synchronize()
+        ap_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        self.rpa.profile_begin(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if self.append_new is not None:
+                ap_ev[i][0].record(self.stream)
+                self.append()
+                ap_ev[i][1].record(self.stream)
+            self.call()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kms, ncalls = self.rpa.profile_end()
+        kmean = {k: v / max(ncalls, 1) for k, v in kms.items()}
+        ams = (sum(a.elapsed_time(b) for a, b in ap_ev) / steps) if self.append_new is not None else None
+        return (t1 - t0) * 1e3 / steps, kmean, ams
+
+    def samples(self, n, flush_buf=None):
+        """n single-call samples, each bracketed by HIP events on the call's
+        stream; with flush_buf, the buffer is rewritten before each sample,
+        outside the events."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            if flush_buf is not None:
+                flush_buf.fill_(i & 0xFF)
+            ev[i][0].record(self.stream)
+            self.call()
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def summary(self, steps, warmup, n_samples, flush_buf):
+        """Everything measured for this workload (the headline's steps
+        included), as one JSON-ready dict."""
+        ms_step, kmean, ams = self.timed_steps(steps, warmup)
+        warm = stats(self.samples(n_samples))
+        cold = stats(self.samples(n_samples, flush_buf))
+        work = self.work
+        F = work["decode"][0] + work["prefill"][0]
+        B = work["decode"][1] + work["prefill"][1]
+        T = self.w.valid_tokens()
+        dom = "decode" if kmean["decode"] >= kmean["prefill"] else "prefill"
+        t_dom = kmean[dom] * 1e-3
+        kroof = roofline_of(work[dom][0], work[dom][1], t_dom, prefer_mfma=(dom == "prefill"))
+        kroof["kernel"] = f"{dom}_kernel"
+        kroof["kernel_ms"] = round(kmean[dom], 4)
+        kroof["algorithmic_flops"] = work[dom][0]
+        kroof["algorithmic_bytes"] = work[dom][1]
+        kname = "prefill_pp_kernel" if dom == "prefill" and self._uses_pp() else f"{dom}_kernel"
+        kroof["kernel_name"] = kname
+        kroof["traffic"] = load_traffic(kname, self.number)
+        t_call = warm["median"] * 1e-3
+        call_frac = max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / t_call
+        res = {
+            "workload": self._name(), "query_tokens": T, "ms_per_step": round(ms_step, 4),
+            "ms_per_call_warm": warm, "ms_per_call_cold": cold,
+            "tokens_per_s": round(T / t_call, 1),
+            "tflops": round(F / t_call / 1e12, 2), "kv_hbm_gbs": round(B / t_call / 1e9, 1),
+            "roofline_frac_call": round(call_frac, 4),
+            "mfma_frac_call": round(F / t_call / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "hbm_frac_call": round(B / t_call / (HBM_PEAK_GBS * 1e9), 4),
+            "roofline_kernel": kroof,
+            "kernel_ms": {k: round(v, 4) for k, v in kmean.items()},
+            "algorithmic": {"flops": F, "bytes": B, "prefill_flops": work["prefill"][0],
+                            "prefill_bytes": work["prefill"][1], "decode_flops": work["decode"][0],
+                            "decode_bytes": work["decode"][1]},
+        }
+        if ams is not None:
+            c = self.w.cfg
+            import workloads as wl
+            b_kv = 1 if wl.is_fp8(c.kv_dtype) else 2
+            b_in = 4 if c.q_dtype == wl.Q_F32 else 2
+            ab = float(T * 2 * c.num_kv_heads * c.head_dim * (b_in + b_kv))
+            res["kv_append"] = {"kernel": "kv_append_kernel", "kernel_ms": round(ams, 5), "algorithmic_bytes": ab,
+                                "achieved": round(ab / (ams * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(ab / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] workload {self.number}: {ms_step:.4f} ms/step; warm median {warm['median']:.4f} ms "
+            f"(p10 {warm['p10']:.4f}, p90 {warm['p90']:.4f}); cold median {cold['median']:.4f} ms; kernels (ms): "
+            + ", ".join(f"{k} {v:.4f}" for k, v in kmean.items()))
+        return res
+
+    def _uses_pp(self):
+        c = self.dev.cfg
+        return c.head_dim == 256 and c.q_dtype in (self.rpa.DTYPE_BF16, self.rpa.DTYPE_F16) \
+            and c.kv_dtype == c.q_dtype
+
+    def _name(self):
+        import workloads as wl
+        return wl.WORKLOADS[self.number]
+
+    def free(self):
+        del self.dev, self.out, self.lse
+        self.torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--samples", type=int, default=50, help="single-call samples, warm and cold each")
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-sweep", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-dtype", choices=["bf16", "f16", "fp8_e4m3fn", "fp8_e5m2", "int8"], default=None,
-                    help="store the workload's K/V cache in this type instead of its own")
+                    help="store the headline workload's K/V cache in this type instead of its own")
     ap.add_argument("--q-dtype", choices=["bf16", "f16", "f32"], default=None,
-                    help="q/out type (f16: a bf16 cache becomes f16 too)")
+                    help="q/out type of the headline workload (f16: a bf16 cache becomes f16 too)")
     ap.add_argument("--sinks", action="store_true",
                     help="attach seeded attention-sink logits (one per q head) and call rpa_forward_sinks")
     ap.add_argument("--append", action="store_true",
@@ -192,10 +432,15 @@ def main():
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
                     help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
                          "(copy_<C>/ and w<workload>_<C>/) into the traffic file")
+    ap.add_argument("--summarize-trace", metavar="CSV", default=None,
+                    help="host only: print a rocprofv3 kernel-stats CSV as a Markdown table")
     args = ap.parse_args()
 
     if args.ingest_counters:
         print(json.dumps(ingest_counters(args.ingest_counters, args.workload), sort_keys=True))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
         return
 
     if args.gpus != 1:
@@ -225,144 +470,71 @@ def main():
                           "copy_gbs_best": round(2 * n / (min(ms) * 1e-3) / 1e9, 1)}))
         return
 
-    import ragged_paged_gqa_amd as rpa
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import workloads as wl
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import Device, upload_q_bits
-
-    log(f"[bench] generating workload {args.workload}: {wl.WORKLOADS[args.workload]}")
-    t0 = time.perf_counter()
-    w = wl.named(args.workload, kv_dtype=args.kv_dtype, q_dtype=args.q_dtype)
-    if args.sinks:
-        w = wl.with_sinks(w, args.workload)
-    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
-    dev = Device(w)
-    work = algorithmic_work(w)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    head = Runner(args.workload, args, headline=True)
+    hs = head.summary(args.steps, args.warmup, args.samples, flush_buf)
+    w = head.w
     T = w.valid_tokens()
-    F = work["decode"][0] + work["prefill"][0]
-    B = work["decode"][1] + work["prefill"][1]
-
-    if args.append:
-        k_np, v_np = wl.new_kv(w, 1000 + args.workload)
-        k_new = upload_q_bits(k_np, w.cfg.q_dtype)
-        v_new = upload_q_bits(v_np, w.cfg.q_dtype)
-        stream = torch.cuda.current_stream()
-        ap_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)]
-
-    def append(i=None):
-        if i is not None:
-            ap_ev[i][0].record(stream)
-        rpa.kv_append(k_new, v_new, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs,
-                      dev.cfg, stream=stream)
-        if i is not None:
-            ap_ev[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        if args.append:
-            append()
-        dev.run()
-    torch.cuda.synchronize()
-    rpa.profile_begin(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if args.append:
-            append(i)
-        rpa.forward(dev.q, dev.kv, dev.kv_lens, dev.page_indices, dev.cu_q_lens, dev.num_seqs, dev.cfg,
-                    workspace=dev.workspace, out=dev_out(dev), lse=dev_lse(dev), sinks=dev.sinks)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kms, ncalls = rpa.profile_end()
-    ms = (t1 - t0) * 1e3 / args.steps
-    kmean = {k: v / max(ncalls, 1) for k, v in kms.items()}
-    log(f"[bench] {ms:.4f} ms/step; kernels (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in kmean.items()))
-
-    dom = "decode" if kmean["decode"] >= kmean["prefill"] else "prefill"
-    f_dom, b_dom = work[dom][0], work[dom][1]
-    t_dom = kmean[dom] * 1e-3
-    ai = f_dom / max(b_dom, 1.0)
-    if dom == "decode" or ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        achieved = b_dom / t_dom / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = f_dom / t_dom / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = f"{dom}_kernel"
-    roof["kernel_ms"] = round(kmean[dom], 4)
-    roof["algorithmic_bytes"] = b_dom
-    roof["algorithmic_flops"] = f_dom
-    roof["traffic"] = load_traffic(f"{dom}_kernel", args.workload)
-
-    step_s = ms * 1e-3
+    ms = hs["ms_per_step"]
+    roof = dict(hs["roofline_kernel"])
+    dtype = w.cfg.q_dtype if w.cfg.kv_dtype == w.cfg.q_dtype \
+        else f"{w.cfg.q_dtype} q / {w.cfg.kv_dtype.replace('_', ' ')} kv"
     result = {
         "metric": METRIC,
-        "value": round(T / step_s, 1),
+        "value": round(T / (ms * 1e-3), 1),
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.cfg.q_dtype if w.cfg.kv_dtype == w.cfg.q_dtype
-        else f"{w.cfg.q_dtype} q / {w.cfg.kv_dtype.replace('_', ' ')} kv",
+        "dtype": dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page table)",
         "config": {"workload": wl.WORKLOADS[args.workload], "num_seqs": w.n_seqs, "query_tokens": T,
                    "num_q_heads": w.cfg.num_q_heads, "num_kv_heads": w.cfg.num_kv_heads,
                    "head_dim": w.cfg.head_dim, "page_size": w.cfg.page_size,
                    **({"attention_sinks": True} if args.sinks else {}),
+                   **({"kv_append": True} if args.append else {}),
                    **({"kv_dtype": w.cfg.kv_dtype} if args.kv_dtype or args.q_dtype else {}),
                    **({"q_dtype": w.cfg.q_dtype} if args.q_dtype else {})},
-        "kv_hbm_gbs": round(B / step_s / 1e9, 1),
-        "tflops": round(F / step_s / 1e12, 2),
-        "roofline_frac_step": round(max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / step_s, 4),
-        "kernel_ms": {k: round(v, 4) for k, v in kmean.items()},
+        "tflops": round(hs["algorithmic"]["flops"] / (ms * 1e-3) / 1e12, 2),
+        "kv_hbm_gbs": round(hs["algorithmic"]["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "roofline_frac_step": round(max(hs["algorithmic"]["flops"] / (BF16_PEAK_TFLOPS * 1e12),
+                                        hs["algorithmic"]["bytes"] / (HBM_PEAK_GBS * 1e9)) / (ms * 1e-3), 4),
+        "kernel_ms": hs["kernel_ms"],
         "roofline": roof,
+        "timing": {"warm": hs["ms_per_call_warm"], "cold": hs["ms_per_call_cold"],
+                   "note": "per-call HIP events; cold = a 1 GiB buffer written before each sample, "
+                           "outside the events"},
     }
-    if args.append:
-        # bytes the append must move: each new K and V element read once in
-        # the q type and written once in the cache type
-        c = w.cfg
-        b_kv = 1 if wl.is_fp8(c.kv_dtype) else 2
-        b_in = 4 if c.q_dtype == wl.Q_F32 else 2
-        ab = float(T * 2 * c.num_kv_heads * c.head_dim * (b_in + b_kv))
-        ams = sum(a.elapsed_time(b) for a, b in ap_ev) / args.steps
-        result["config"]["kv_append"] = True
-        result["kv_append"] = {"kernel": "kv_append_kernel", "kernel_ms": round(ams, 5), "algorithmic_bytes": ab,
-                               "achieved": round(ab / (ams * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": round(ab / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"[bench] kv_append {ams * 1e3:.2f} us, {ab / 1e6:.2f} MB")
-    if not args.no_cpu_baseline:
+    if "kv_append" in hs:
+        result["kv_append"] = hs["kv_append"]
+    cpu_w = None if args.no_cpu_baseline else w
+    head.free()
+    del head
+
+    # the other named workloads, the same measurements each
+    configs = {f"w{args.workload}": hs}
+    plain = not (args.kv_dtype or args.q_dtype or args.sinks or args.append)
+    if not args.no_sweep and plain:
+        for number in (1, 2, 3, 4, 5):
+            if number == args.workload:
+                continue
+            r = Runner(number, args)
+            configs[f"w{number}"] = r.summary(args.steps, args.warmup, args.samples, flush_buf)
+            r.free()
+            del r
+    if len(configs) > 1:
+        result["configs"] = configs
+    if cpu_w is not None:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(cpu_w)
     print(json.dumps(result), flush=True)
-
-
-_outs = {}
-
-
-def dev_out(dev):
-    import torch
-
-    import ragged_paged_gqa_amd as rpa
-    key = id(dev)
-    if key not in _outs:
-        c = dev.cfg
-        # out in the q type's width (f16 bits fit a bf16 buffer)
-        odt = torch.float32 if c.q_dtype == rpa.DTYPE_F32 else torch.bfloat16
-        _outs[key] = (torch.empty((c.num_q_tokens, c.num_q_heads, c.head_dim), dtype=odt, device="cuda"),
-                      torch.empty((c.num_q_tokens, c.num_q_heads), dtype=torch.float32, device="cuda"))
-    return _outs[key][0]
-
-
-def dev_lse(dev):
-    dev_out(dev)
-    return _outs[id(dev)][1]
 
 
 if __name__ == "__main__":

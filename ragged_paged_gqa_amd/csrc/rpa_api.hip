@@ -204,7 +204,7 @@ rpa_status check_launch() { return hipGetLastError() == hipSuccess ? RPA_OK : RP
 // events before plan, prefill, decode and combine, and after combine.
 struct Profiler {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};  // read without the lock on every forward call
   int max_calls = 0;
   int n_calls = 0;
   std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
@@ -382,6 +382,11 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
                              void* stream) {
   if (!q || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs || !out)
     return RPA_ERR_INVALID_ARGUMENT;
+  // the kernels move q, K/V and out in 16-byte pieces and lse / sinks as f32
+  for (const void* a : {q, kv_pages, (const void*)out})
+    if ((reinterpret_cast<uintptr_t>(a) & 15u) != 0) return RPA_ERR_INVALID_ARGUMENT;
+  for (const void* a : {(const void*)lse, (const void*)sinks})
+    if ((reinterpret_cast<uintptr_t>(a) & 3u) != 0) return RPA_ERR_INVALID_ARGUMENT;
   Params p;
   int cus = 0;
   rpa_status st = prepare(cfg, workspace, workspace_bytes, &p, &cus);
@@ -397,9 +402,10 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
   p.sinks = sinks;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = nullptr;
-  {
+  if (g_prof.on.load(std::memory_order_acquire)) {
     std::lock_guard<std::mutex> lock(g_prof.mu);
-    if (g_prof.on && g_prof.n_calls < g_prof.max_calls) ev = &g_prof.ev[kProfEvents * g_prof.n_calls++];
+    if (g_prof.on.load(std::memory_order_relaxed) && g_prof.n_calls < g_prof.max_calls)
+      ev = &g_prof.ev[kProfEvents * g_prof.n_calls++];
   }
   prof_record(ev, 0, s);
   st = launch_plan(p, s);
@@ -428,7 +434,7 @@ rpa_status rpa_profile_begin(int32_t max_calls) {
   }
   g_prof.max_calls = max_calls;
   g_prof.n_calls = 0;
-  g_prof.on = true;
+  g_prof.on.store(true, std::memory_order_release);
   return RPA_OK;
 }
 
@@ -454,7 +460,7 @@ rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
   *n_calls = g_prof.n_calls;
   for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.clear();
-  g_prof.on = false;
+  g_prof.on.store(false, std::memory_order_release);
   g_prof.n_calls = 0;
   return st;
 }

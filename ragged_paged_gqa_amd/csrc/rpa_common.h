@@ -25,8 +25,10 @@ constexpr int kDecRows = 16;
 // barriers that couple only their own 4 waves); head_dim 256 needs a whole
 // SIMD's registers per wave.
 constexpr int kPfWaves = 4;
-constexpr int pf_halves_for(int D) { return D > 0 ? 1 : 1; }  // 32-row halves per wave
-constexpr int pf_rows_for(int D) { return 32 * pf_halves_for(D) * kPfWaves; }
+// 32-row halves per wave of the 4-wave kernel: one (two, with each operand
+// read serving two MFMAs, measured slower: one wave per SIMD hides less)
+constexpr int kPfHalves = 1;
+constexpr int pf_rows_for(int /*head_dim*/) { return 32 * kPfHalves * kPfWaves; }
 constexpr int pf_wgs_per_cu(int D) { return D >= 256 ? 1 : 2; }
 // Keys per pipeline step in both attention kernels.
 constexpr int kStepKeys = 32;

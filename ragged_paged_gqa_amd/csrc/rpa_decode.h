@@ -109,10 +109,8 @@ constexpr int dec_wgs_per_cu() {
 }
 // resident decode waves per SIMD (sizes the register budget)
 constexpr int dec_waves_per_simd(int D, bool fp8) {
-  return fp8 ? dec_wgs_per_cu<64, true>() * 0 + (D == 64 ? dec_wgs_per_cu<64, true>()
-                                                  : D == 128 ? dec_wgs_per_cu<128, true>() : dec_wgs_per_cu<256, true>())
-             : (D == 64 ? dec_wgs_per_cu<64, false>()
-                        : D == 128 ? dec_wgs_per_cu<128, false>() : dec_wgs_per_cu<256, false>());
+  if (fp8) return D == 64 ? dec_wgs_per_cu<64, true>() : D == 128 ? dec_wgs_per_cu<128, true>() : dec_wgs_per_cu<256, true>();
+  return D == 64 ? dec_wgs_per_cu<64, false>() : D == 128 ? dec_wgs_per_cu<128, false>() : dec_wgs_per_cu<256, false>();
 }
 
 // Chunk swizzles of a region's rows (key = row 0..15): K pieces are read by

@@ -66,10 +66,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Keys per load step (one LDS ring slot, one barrier). Scores are computed
-// 32 keys at a time.
-constexpr int pf_step_keys(int D, bool fp8) { return (D > 0 && !fp8) ? 32 : 32; }
-
 #ifndef RPA_PF_STAGES
 #define RPA_PF_STAGES 4
 #endif
@@ -89,7 +85,7 @@ template <int D, bool FP8>
 struct PrefillLds {
   static constexpr int kRowBytes = 2 * D;      // row stride
   static constexpr int kChunks = 2 * D / 16;   // 16-byte chunks per K or V row
-  static constexpr int kStepKeys = pf_step_keys(D, FP8);
+  static constexpr int kStepKeys = rpa::kStepKeys;  // keys per load step (one ring slot, one barrier)
   static constexpr int kRegionBytes = kStepKeys * kRowBytes;  // V region offset
   static constexpr int kBufBytes = 2 * kRegionBytes;
   static constexpr int kStages = FP8 ? 3 : kStagesBf16;
@@ -120,7 +116,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   // f16 P must stay below 65504: exponentiated scores <= 2^15
   constexpr float SLACK = F16 ? kRescaleSlack - 1.0f : kRescaleSlack;
   constexpr int NW = kPfWaves;
-  constexpr int NH = pf_halves_for(D);        // 32-row halves per wave
+  constexpr int NH = kPfHalves;               // 32-row halves per wave
   constexpr int WR = 32 * NH;                 // rows per wave
   constexpr int NS = D / 16;                  // k-steps of the QK product
   constexpr int NDB = D / 32;                 // 32-row blocks of O^T
@@ -365,26 +361,26 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       }
     };
     auto store_regs = [&](int k0, char* dst) {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int idx = tid + NT * c;
-        if (idx >= KS * GCH) continue;
-        const int key = idx / GCH;
-        const int gc = idx % GCH;              // 16 codes: K chunks first, then V
-        const int region = gc / (GCH / 2);
-        const int c0 = 2 * (gc % (GCH / 2));   // first of the two bf16 chunks they become
-        const int sw = region ? swz_v<D>(key) : swz_k<D>(key);
-        char* row_p = dst + region * REG + key * RB;
-        u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
-        // (this lambda is also compiled, unused, into the bf16 kernels)
-        constexpr int F8 = KVT == kKvBf16 ? kKvE4M3 : KVT;
-        bf16x8 a = fp8x8_to_16<F8, F16>(lo2), b = fp8x8_to_16<F8, F16>(hi2);
-        if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
-          a = bf16x8{};
-          b = bf16x8{};
+        for (int c = 0; c < CPT; ++c) {
+          const int idx = tid + NT * c;
+          if (idx >= KS * GCH) continue;
+          const int key = idx / GCH;
+          const int gc = idx % GCH;              // 16 codes: K chunks first, then V
+          const int region = gc / (GCH / 2);
+          const int c0 = 2 * (gc % (GCH / 2));   // first of the two bf16 chunks they become
+          const int sw = region ? swz_v<D>(key) : swz_k<D>(key);
+          char* row_p = dst + region * REG + key * RB;
+          u32x2 lo2 = {stage[c][0], stage[c][1]}, hi2 = {stage[c][2], stage[c][3]};
+          bf16x8 a = fp8x8_to_16<KVT, F16>(lo2), b = fp8x8_to_16<KVT, F16>(hi2);
+          if (k0 + key >= kvl) {  // V past kv_len reads as zero (0 * NaN = NaN); K there is masked
+            a = bf16x8{};
+            b = bf16x8{};
+          }
+          *reinterpret_cast<bf16x8*>(row_p + 16 * (c0 ^ sw)) = a;
+          *reinterpret_cast<bf16x8*>(row_p + 16 * ((c0 + 1) ^ sw)) = b;
         }
-        *reinterpret_cast<bf16x8*>(row_p + 16 * (c0 ^ sw)) = a;
-        *reinterpret_cast<bf16x8*>(row_p + 16 * ((c0 + 1) ^ sw)) = b;
       }
     };
 

@@ -122,3 +122,19 @@ def test_check_metadata_ignores_unused_table_entries():
     pi[0, 1:] = 10 ** 6     # sequence 0 has one page; the rest is never read
     assert rpa.check_metadata(cfg, kvl, pi, cu, 3) == 0
     assert rpa.check_metadata(cfg, kvl, pi, cu, 4) == 5   # num_seqs > max_num_seqs
+
+
+@pytest.mark.parametrize("which,offset", [("q", 2), ("kv", 8), ("out", 4), ("lse", 2), ("sinks", 1)])
+def test_forward_rejects_misaligned_pointers_without_device(which, offset):
+    # q, K/V and out travel in 16-byte pieces, lse and sinks as f32: a pointer
+    # off those boundaries is an invalid argument, found before any device call
+    # (the buffers here are host memory that the library never dereferences)
+    c = _cfg().to_c()
+    buf = np.zeros(1 << 16, np.uint8)
+    base = (buf.ctypes.data + 255) & ~255
+    ptr = {k: base + 4096 * i for i, k in enumerate(("q", "kv", "kvl", "pi", "cu", "ns", "sinks", "out", "lse", "ws"))}
+    ptr[which] += offset
+    L = rpa.lib()
+    st = L.rpa_forward_sinks(ctypes.byref(c), ptr["q"], ptr["kv"], ptr["kvl"], ptr["pi"], ptr["cu"], ptr["ns"],
+                             ptr["sinks"], ptr["out"], ptr["lse"], ptr["ws"], 1 << 20, None)
+    assert st == 1
