@@ -24,7 +24,8 @@
  * All data pointers are DEVICE pointers, owned by the caller, and must stay
  * valid until the work enqueued on `stream` has finished. Nothing in this
  * library allocates device memory on the call path, synchronises, or keeps
- * state between calls beyond cached device properties. `stream` is a
+ * state between calls beyond cached device properties (and the contents of
+ * rpa_forward_noalloc's scratch array). `stream` is a
  * hipStream_t passed as void* (NULL = the null stream).
  */
 #ifndef RPA_H
@@ -143,6 +144,25 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
                              const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
                              const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * rpa_forward_sinks without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is the library's own
+ * scratch array: a static device array of 256 MiB, one copy per GPU, created with the library's code on that GPU
+ * and held until the process ends; its address is looked up once per device
+ * (hipGetSymbolAddress) on the first call. The call allocates nothing and
+ * never synchronises. `sinks` may be NULL (then exactly rpa_forward).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads, without ordering between them)
+ * race on it and give undefined results; calls ordered on one stream are
+ * safe (each call's planning kernel rewrites everything the others read).
+ * Errors: those of rpa_forward_sinks, and RPA_ERR_WORKSPACE_TOO_SMALL when
+ * rpa_workspace_bytes(cfg) exceeds the array (nothing is enqueued).
+ */
+rpa_status rpa_forward_noalloc(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                               const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                               const float* sinks, void* out, float* lse, void* stream);
 
 /*
  * KV-cache append: writes every query token's new K and V rows into the

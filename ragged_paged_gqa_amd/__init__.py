@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
         L.rpa_workspace_bytes.argtypes = [CP, ctypes.POINTER(ctypes.c_size_t)]
         L.rpa_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.rpa_forward_sinks.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rpa_forward_noalloc.argtypes = [CP, P, P, P, P, P, P, P, P, P, P]
         L.rpa_status_string.argtypes = [ctypes.c_int]
         L.rpa_status_string.restype = ctypes.c_char_p
         L.rpa_check_metadata.argtypes = [CP, P, P, P, ctypes.c_int32]
@@ -116,7 +117,8 @@ def lib() -> ctypes.CDLL:
         L.rpa_debug_decode_fp8.argtypes = [P, P, ctypes.c_int32, P]
         L.rpa_profile_begin.argtypes = [ctypes.c_int32]
         L.rpa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
-        for f in ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_check_metadata", "rpa_plan",
+        for f in ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_forward_noalloc",
+                  "rpa_check_metadata", "rpa_plan",
                   "rpa_plan_layout", "rpa_kv_append",
                   "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end"):
             getattr(L, f).restype = ctypes.c_int
@@ -124,7 +126,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_status_string", "rpa_check_metadata",
+EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_forward_noalloc", "rpa_status_string",
+           "rpa_check_metadata",
            "rpa_plan", "rpa_plan_layout", "rpa_kv_append", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
 KERNELS = ("plan", "prefill", "decode", "combine")
@@ -246,6 +249,34 @@ def forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config
                                      _stream_ptr(stream))
         _check(st, "rpa_forward_sinks")
     return out, lse
+
+
+def forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config, *, out, lse=None,
+                    sinks=None, stream=None):
+    """rpa_forward_noalloc: as `forward`, with the library's own scratch array
+    as the workspace (nothing is allocated; `out` must be given). Calls that
+    overlap on one GPU share that array and race."""
+    _check_inputs(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs)
+    T, Hq, D = cfg.num_q_tokens, cfg.num_q_heads, cfg.head_dim
+    if not (out.is_cuda and out.is_contiguous() and out.element_size() == _q_size(cfg) and out.numel() == T * Hq * D):
+        raise ValueError(f"out: expected a contiguous {_q_size(cfg)}-byte (q dtype) CUDA tensor [T, Hq, D]")
+    if lse is not None and not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32
+                                and lse.numel() == T * Hq):
+        raise ValueError("lse: expected a contiguous float32 CUDA tensor [T, Hq]")
+    if sinks is not None and not (sinks.is_cuda and sinks.is_contiguous() and sinks.dtype == torch.float32
+                                  and sinks.numel() == Hq):
+        raise ValueError("sinks: expected a contiguous float32 CUDA tensor [Hq]")
+    c = cfg.to_c()
+    st = lib().rpa_forward_noalloc(ctypes.byref(c), q.data_ptr(), kv_pages.data_ptr(), kv_lens.data_ptr(),
+                                   page_indices.data_ptr(), cu_q_lens.data_ptr(), num_seqs.data_ptr(),
+                                   sinks.data_ptr() if sinks is not None else None, out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+    _check(st, "rpa_forward_noalloc")
+    return out, lse
+
+
+# Size of rpa_forward_noalloc's scratch array: the largest workspace it serves.
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def kv_append(k_new, v_new, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, cfg: Config, *,

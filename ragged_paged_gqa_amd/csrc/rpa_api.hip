@@ -334,6 +334,27 @@ __global__ void decode_fp8_kernel(const uint8_t* codes, float* out, int n) {
     if (4 * i + k < n) out[4 * i + k] = (float)b[k];
 }
 
+// Workspace of rpa_forward_noalloc, for callers that cannot allocate: a
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses its name as an address (that is a host-side stand-in):
+// scratch_ptr() resolves each device's copy once, with hipGetSymbolAddress,
+// and every launch takes that address.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (resolved on the first call per device, with
+// that device current), or null if it cannot be resolved.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -417,6 +438,23 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
     case 256: return launch_for_kv<256>(cfg->q_dtype, cfg->kv_dtype, p, cus, s, ev);
     default: return RPA_ERR_UNSUPPORTED;
   }
+}
+
+rpa_status rpa_forward_noalloc(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                               const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                               const float* sinks, void* out, float* lse, void* stream) {
+  if (!q || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs || !out)
+    return RPA_ERR_INVALID_ARGUMENT;
+  size_t need = 0;
+  rpa_status st = rpa_workspace_bytes(cfg, &need);
+  if (st != RPA_OK) return st;
+  if (need > kScratchBytes) return RPA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_ptr();
+  if (!ws) return RPA_ERR_HIP;
+  // the planning kernel rewrites every record, counter and queue head the
+  // attention kernels read, so nothing is cleared here
+  return rpa_forward_sinks(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, sinks, out, lse, ws,
+                           kScratchBytes, stream);
 }
 
 rpa_status rpa_profile_begin(int32_t max_calls) {
