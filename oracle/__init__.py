@@ -23,7 +23,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
-_LIB = os.path.join(_BUILD, "librpa_oracle.so")
+# RPA_ORACLE_LIB may name another build of the same source (the sanitizer test's)
+_LIB = os.environ.get("RPA_ORACLE_LIB") or os.path.join(_BUILD, "librpa_oracle.so")
 
 KV_CODES = {"bf16": 0, "fp8_e4m3fn": 1, "fp8_e5m2": 2, "f16": 3, "int8": 4}
 Q_CODES = {"bf16": 0, "f16": 3, "f32": 5}

@@ -8,7 +8,10 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+# the kernels and the C entry points that launch them; the host logic that
+# touches no device (also built without HIP by the sanitizer test)
 SRC = os.path.join(HERE, "csrc", "rpa_api.hip")
+HOST_SRC = os.path.join(HERE, "csrc", "rpa_host.cpp")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "librpa.so")
 
@@ -33,7 +36,7 @@ def build(verbose: bool = False, out: str | None = None, defines: tuple[str, ...
     lib = out or LIB
     os.makedirs(os.path.dirname(lib), exist_ok=True)
     tmp = lib + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *compile_flags(), *(f"-D{d}" for d in defines), "-o", tmp, SRC]
+    cmd = [hipcc(), *compile_flags(), *(f"-D{d}" for d in defines), "-o", tmp, SRC, HOST_SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rpa_layout.h"
+
 namespace rpa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -18,92 +20,7 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Rows of a decode-class unit: one 16-wide MFMA column block.
-constexpr int kDecRows = 16;
-// A prefill-class tile is worked by 4 waves of 32 packed rows each. For
-// head_dim <= 128 two such workgroups share a CU (two waves per SIMD, with
-// barriers that couple only their own 4 waves); head_dim 256 needs a whole
-// SIMD's registers per wave.
-constexpr int kPfWaves = 4;
-// 32-row halves per wave of the 4-wave kernel: one (two, with each operand
-// read serving two MFMAs, measured slower: one wave per SIMD hides less)
-constexpr int kPfHalves = 1;
-constexpr int pf_rows_for(int /*head_dim*/) { return 32 * kPfHalves * kPfWaves; }
-constexpr int pf_wgs_per_cu(int D) { return D >= 256 ? 1 : 2; }
-// Keys per pipeline step in both attention kernels.
-constexpr int kStepKeys = 32;
-// Largest key chunk of a prefill-class item (bounds the per-item page cache).
-constexpr int kPfMaxChunk = 32768;
-
 // ----------------------------------------------------------------------------
-// Plan records written by the planning kernel, read by the attention and
-// merge kernels. A unit is one sequence, one kv head and a run of packed query
-// rows (row = token_in_seq * G + g, the GQA row packing of the kernel page's
-// per-kv-head step). An item is one key chunk of a unit.
-struct Unit {
-  int32_t seq;
-  int32_t kv_head;
-  int32_t row0;   // first packed row of the unit, relative to the sequence
-  int32_t nrows;  // number of packed rows
-  int32_t kv_lo;  // start of the unit's chunk grid (16-aligned)
-  int32_t kv_hi;  // one past the last key any of the rows can see
-  int32_t nch;    // chunks (>= 1)
-  int32_t item0;  // index of the unit's first item
-};
-static_assert(sizeof(Unit) == 32, "unit record is int32[8]");
-
-struct Item {
-  int32_t unit;
-  int32_t chunk;
-};
-
-// A decode-class item carries everything its wave needs, so that starting it
-// costs one (scalar) load: the sequence's metadata, the chunk's key range and
-// the decode wave that runs it. Decode work is scheduled stream-K style: the
-// key blocks of all decode units, laid end to end, are cut into equal
-// contiguous ranges, one per decode wave, and an item is the part of one unit
-// that falls into one wave's range.
-struct DecItem {
-  int32_t seq;
-  int32_t kv_head;
-  int32_t c_lo;   // first key of the chunk (16-aligned)
-  int32_t c_hi;   // one past its last key
-  int32_t kvl;    // kv_len, clamped to the page table's reach
-  int32_t q0;     // first token of the sequence
-  int32_t ql;     // its query tokens
-  int32_t row0;   // first packed row of the unit
-  int32_t nrows;  // packed rows of the unit
-  int32_t nch;    // chunks of the unit (1: the item writes the output itself)
-  int32_t unit;   // unit index
-  int32_t chunk;  // chunk index within the unit
-  int32_t wave;   // the decode wave that runs it
-  int32_t pad[3];
-};
-static_assert(sizeof(DecItem) == 64, "decode item record is int32[16]");
-
-// Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
-// L2). All row blocks of one (sequence, kv head) go to the same queue, one
-// after the other, so the workgroups of one XCD that run at the same time
-// stream the same K/V pages and share them through that XCD's L2.
-constexpr int kQueues = 8;
-
-struct Header {
-  int32_t n_dec_units;
-  int32_t n_pf_units;
-  int32_t n_dec_items;
-  int32_t n_pf_items;
-  int32_t zero;  // 0 (decode chunks follow the stream-K split)
-  int32_t pf_chunk;
-  int32_t n_split_units;
-  int32_t dec_blocks;   // 16-key blocks of all decode units (the stream-K total)
-  int32_t pad0[8];      // pad0[0]: decode waves given work (min(dec_waves, dec_blocks), >= 1)
-  int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist (x * max_pf_items)
-  int32_t pf_q_count[kQueues];  // its length
-  int32_t pf_q_next[kQueues];   // its head, zeroed by the planning kernel
-  int32_t pad1[24];
-};
-static_assert(sizeof(Header) == 256, "header is int32[64]");
-
 // Everything a kernel needs, passed by value.
 struct Params {
   // inputs

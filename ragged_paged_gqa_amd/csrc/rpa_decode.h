@@ -59,59 +59,9 @@
 
 namespace rpa {
 
-constexpr int kDecWavesPerBlock = 4;
-constexpr int kDecStepKeys = 16;
 // The reference maximum of a row moves only when the row's maximum outgrows it
 // by more than this (base-2 units): exponentiated scores stay <= 2^12.
 constexpr float kDecSlack = 12.0f;
-// LDS budget of one decode wave (4 waves per workgroup; 40 KB: one
-// workgroup per CU)
-#ifndef RPA_DEC_WAVE_LDS
-#define RPA_DEC_WAVE_LDS (20 * 1024)
-#endif
-constexpr int kDecWaveLds = RPA_DEC_WAVE_LDS;
-
-template <int D, bool FP8>
-struct DecCfg {
-  static constexpr int EB = FP8 ? 1 : 2;         // bytes per K/V element
-  static constexpr int RB = D * EB;              // bytes of one K (or V) row of a head
-  static constexpr int REGION = 16 * RB;         // the step's 16 K (or V) rows
-  static constexpr int STAGE = 2 * REGION;       // K region, then V region
-  static constexpr int NDR = REGION / 1024;      // DMA instructions per region
-  static constexpr int NDMA = 2 * NDR;           // DMA instructions per step
-  static constexpr int CPR = RB / 16;            // 16-byte chunks per row
-  static constexpr int RP = RB >= 256 ? 1 : 256 / RB;  // rows per 256 bytes (one LDS bank sweep)
-  static constexpr int NI = D / 32;              // 8-wide k-slots of Q^T per lane (16x16x32 k-steps)
-  static constexpr int ND = D / 16;              // 16-row blocks of O^T
-  static constexpr int NLD = RB / 64;            // 16-byte K pieces per lane
-  // fp8: V is widened to bf16 in the step's own ring slot once the slot's
-  // raw rows are in registers (16 keys x D bf16 is exactly one slot), and the
-  // slot is refilled after the PV reads. Rows are XOR-swizzled by the key
-  // (sswz), so that the 16-byte writes of 16 keys at one column and the
-  // transposed reads both spread over all banks.
-  // bf16: the next item's 16 Q rows (bf16), DMA'd during the current item.
-  // fp8 takes them into registers instead and spends the space on the ring.
-  static constexpr int QSLOT = FP8 ? 0 : 16 * D * 2;
-  // fp8 head_dim 256 needs more than 256 registers: one wave per SIMD, so
-  // each wave takes twice the LDS
-  static constexpr int BUDGET = (FP8 && D >= 256) ? 2 * kDecWaveLds : kDecWaveLds;
-  static constexpr int NST_FIT = (BUDGET - QSLOT) / STAGE;
-  static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 8 ? 8 : NST_FIT);  // ring slots
-  static constexpr int WAVE_LDS = NST * STAGE + QSLOT;
-  static_assert(!FP8 || 16 * D * 2 == STAGE, "fp8: the bf16 V tile fills one slot");
-  static_assert(REGION % 1024 == 0, "whole 1 KB DMA instructions per region");
-  static_assert(WAVE_LDS * kDecWavesPerBlock <= 160 * 1024, "LDS of a workgroup");
-  static_assert((NST - 1) * NDMA < 64, "vmcnt range");
-};
-template <int D, bool FP8>
-constexpr int dec_wgs_per_cu() {
-  return (160 * 1024) / (DecCfg<D, FP8>::WAVE_LDS * kDecWavesPerBlock);
-}
-// resident decode waves per SIMD (sizes the register budget)
-constexpr int dec_waves_per_simd(int D, bool fp8) {
-  if (fp8) return D == 64 ? dec_wgs_per_cu<64, true>() : D == 128 ? dec_wgs_per_cu<128, true>() : dec_wgs_per_cu<256, true>();
-  return D == 64 ? dec_wgs_per_cu<64, false>() : D == 128 ? dec_wgs_per_cu<128, false>() : dec_wgs_per_cu<256, false>();
-}
 
 // Chunk swizzles of a region's rows (key = row 0..15): K pieces are read by
 // 16 lanes holding 16 keys at the same chunk; V is read transposed by 4 keys

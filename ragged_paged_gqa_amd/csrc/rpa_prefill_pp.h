@@ -36,7 +36,6 @@
 
 namespace rpa {
 
-constexpr int kPpWaves = 8;   // two waves per SIMD
 constexpr int kPpStages = 4;  // ring slots: read by M(n-1)/M(n), landed, in flight
 constexpr int kPpLead = 2;    // steps between a slot's DMA and its first reader
 #ifndef RPA_PP_KA
@@ -54,9 +53,6 @@ struct PpLds {
   static constexpr int kSlot = 2 * kRegion;
   static constexpr size_t kBytes = (size_t)kPpStages * kSlot;
 };
-
-// Rows of a unit of this kernel.
-constexpr int kPpRows = 32 * kPpWaves;
 
 template <int D, bool CAP, bool F16>
 __global__ __launch_bounds__(kPpWaves * 64, 1) void prefill_pp_kernel(Params p) {
