@@ -1,11 +1,17 @@
-"""Parity at the full sizes of the five named workloads, in the launch
+"""Parity at the full sizes of the named workloads, in the launch
 configuration the benchmark times (needs an MI355X).
 
-The tiny workload is compared in full. For the four large ones the oracle
-computes a seeded sample of rows one by one (every q head of a few tokens
-plus random (token, head) pairs), which the HIP output must match at the
-stated bar; a sharpened copy (Q x 8, exact in bf16) makes the softmax peaky
-so that |out| ~ 1 and the absolute tolerance cannot hide an error.
+The oracle computes the compared rows one by one; every case also runs on a
+sharpened copy (Q x 8, exact in bf16) that makes the softmax peaky, so that
+|out| ~ 1 and the absolute tolerance cannot hide an error:
+
+* decode batch and fp8 decode: every row (all q heads of every token);
+* mixed batch: every row of the 56 decode sequences and of two whole
+  448-token prefill chunks (sharpened: the decode rows and one chunk);
+* long context: all q heads of 64 seeded random tokens, and every row of one
+  whole 128-token sequence (sharpened: all q heads of the first and last
+  token of two sequences and 192 random (token, head) pairs);
+* attention sinks at full size: the decode batch with seeded sinks, every row.
 """
 
 import numpy as np
@@ -19,27 +25,23 @@ from gpu_util import Device, assert_parity
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(w, n_random=192, seed=0):
-    rng = np.random.default_rng(seed)
-    T = w.valid_tokens()
+def _all_heads(w, tokens):
+    tokens = np.asarray(tokens, dtype=np.int64)
     Hq = w.cfg.num_q_heads
-    toks = [int(w.cu_q_lens[0]), T - 1]
-    # the first and last token of a middle sequence
-    s = w.n_seqs // 2
-    toks += [int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1]) - 1]
-    tokens = np.repeat(np.array(toks), Hq)
-    heads = np.tile(np.arange(Hq), len(toks))
-    rt = rng.integers(0, T, size=n_random)
-    rh = rng.integers(0, Hq, size=n_random)
-    return np.concatenate([tokens, rt]), np.concatenate([heads, rh])
+    return np.repeat(tokens, Hq), np.tile(np.arange(Hq), len(tokens))
 
 
-def _check_sampled(w, d, what):
+def _seq_tokens(w, s):
+    return np.arange(int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1]))
+
+
+def _check_rows(w, d, tokens, heads, what):
     print(f"[workload] {what}: running GPU", flush=True)
     out, lse = d.run()
-    tokens, heads = _sample_rows(w)
-    got_o = out[torch.from_numpy(tokens).cuda(), torch.from_numpy(heads).cuda()].float().cpu().numpy()
-    got_l = lse[torch.from_numpy(tokens).cuda(), torch.from_numpy(heads).cuda()].cpu().numpy()
+    t = torch.from_numpy(np.asarray(tokens)).cuda()
+    h = torch.from_numpy(np.asarray(heads)).cuda()
+    got_o = out[t, h].float().cpu().numpy()
+    got_l = lse[t, h].cpu().numpy()
     print(f"[workload] {what}: oracle on {len(tokens)} rows", flush=True)
     ref_o, ref_l, st = oracle.rows(w, tokens, heads)
     assert np.all(st == 0)
@@ -47,15 +49,81 @@ def _check_sampled(w, d, what):
     print(f"[workload] {what}: ok {stats}", flush=True)
 
 
-@pytest.mark.parametrize("number", [2, 3, 4, 5])
-def test_named_workload_sampled(number):
+def _sharpen(w, d):
+    w.q = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * 8.0)
+    d.q = torch.from_numpy(w.q.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _done(d):
+    del d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("number", [2, 4])
+def test_decode_workload_every_row(number):
     print(f"[workload] cfg{number}: generating", flush=True)
     w = wl.named(number)
     d = Device(w)
-    _check_sampled(w, d, f"cfg{number}")
-    # sharpened: same KV, Q x 8
-    w.q = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * 8.0)
-    d.q = torch.from_numpy(w.q.view(np.int16)).cuda().view(torch.bfloat16)
-    _check_sampled(w, d, f"cfg{number} x8")
-    del d
-    torch.cuda.empty_cache()
+    tokens, heads = _all_heads(w, np.arange(w.valid_tokens()))
+    _check_rows(w, d, tokens, heads, f"cfg{number} every row")
+    _sharpen(w, d)
+    _check_rows(w, d, tokens, heads, f"cfg{number} x8 every row")
+    _done(d)
+
+
+def test_mixed_workload_decode_sequences_and_two_prefill_chunks():
+    print("[workload] cfg3: generating", flush=True)
+    w = wl.named(3)
+    d = Device(w)
+    q_lens = w.q_lens()
+    prefill = [s for s in range(w.n_seqs) if q_lens[s] > 1]
+    decode = [s for s in range(w.n_seqs) if q_lens[s] == 1]
+    assert len(prefill) == 8 and len(decode) == 56
+    dec_tokens = np.concatenate([_seq_tokens(w, s) for s in decode])
+    # the chunks with the shortest and the longest prior context
+    prior = [int(w.kv_lens[s]) - int(q_lens[s]) for s in prefill]
+    chunks = [prefill[int(np.argmin(prior))], prefill[int(np.argmax(prior))]]
+    tokens, heads = _all_heads(w, np.concatenate([dec_tokens] + [_seq_tokens(w, s) for s in chunks]))
+    _check_rows(w, d, tokens, heads, "cfg3 decode sequences + two prefill chunks")
+    _sharpen(w, d)
+    tokens, heads = _all_heads(w, np.concatenate([dec_tokens, _seq_tokens(w, chunks[1])]))
+    _check_rows(w, d, tokens, heads, "cfg3 x8 decode sequences + one prefill chunk")
+    _done(d)
+
+
+def test_long_context_random_tokens_all_heads():
+    print("[workload] cfg5: generating", flush=True)
+    w = wl.named(5)
+    d = Device(w)
+    rng = np.random.default_rng(5)
+    tokens, heads = _all_heads(w, np.sort(rng.choice(w.valid_tokens(), size=64, replace=False)))
+    _check_rows(w, d, tokens, heads, "cfg5 all heads of 64 random tokens")
+    _done(d)
+
+
+def test_long_context_whole_sequence_and_sharpened_sample():
+    print("[workload] cfg5: generating", flush=True)
+    w = wl.named(5)
+    d = Device(w)
+    # the sequence with the longest context: its rows span the most chunks
+    s = int(np.argmax(w.kv_lens[:w.n_seqs]))
+    tokens, heads = _all_heads(w, _seq_tokens(w, s))
+    _check_rows(w, d, tokens, heads, f"cfg5 every row of sequence {s}")
+    _sharpen(w, d)
+    rng = np.random.default_rng(0)
+    mid = w.n_seqs // 2
+    ends = [int(w.cu_q_lens[0]), w.valid_tokens() - 1, int(w.cu_q_lens[mid]), int(w.cu_q_lens[mid + 1]) - 1]
+    t0, h0 = _all_heads(w, ends)
+    rt = rng.integers(0, w.valid_tokens(), size=192)
+    rh = rng.integers(0, w.cfg.num_q_heads, size=192)
+    _check_rows(w, d, np.concatenate([t0, rt]), np.concatenate([h0, rh]), "cfg5 x8 sample")
+    _done(d)
+
+
+def test_decode_workload_with_sinks_every_row():
+    print("[workload] cfg2 + sinks: generating", flush=True)
+    w = wl.with_sinks(wl.named(2), 2)
+    d = Device(w)
+    tokens, heads = _all_heads(w, np.arange(w.valid_tokens()))
+    _check_rows(w, d, tokens, heads, "cfg2 with sinks every row")
+    _done(d)
