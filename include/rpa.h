@@ -211,43 +211,44 @@ rpa_status rpa_check_metadata(const rpa_config* cfg, const int32_t* kv_lens, con
 /*
  * Plan inspection, for tests: runs only the planning kernel on `stream` into
  * `workspace`, then describes where the plan lives in it. The plan is a list
- * of units (one sequence, one kv head, a run of packed query rows
+ * of prefill units (one sequence, one kv head, a run of packed query rows
  * row = token_in_seq * (Hq/Hkv) + g, and the key range those rows can see)
- * and a list of items (a unit and one key chunk of it); see
- * rpa_plan_layout. Same errors as rpa_forward.
+ * with their items (a unit and one key chunk of it), and a table of the
+ * decode sequences; see rpa_plan_layout. Same errors as rpa_forward.
  */
 rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t* cu_q_lens,
                     const int32_t* num_seqs, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Byte offsets inside the workspace (host-only, no device access):
- *   offsets[0] header: int32[64] = {n_dec_units, n_pf_units, n_dec_items,
+ *   offsets[0] header: int32[64] = {n_dec_units, n_pf_units, n_dec_seqs,
  *              n_pf_items, 0, pf_chunk, n_split_units, dec_blocks,
  *              dec_waves_used, pad[7], queue_base[8], queue_count[8],
  *              queue_next[8], pad[24]}
- *              (n_split_units counts units with more than one item;
- *              dec_blocks is the number of 16-key blocks of all decode
- *              units, split over the first dec_waves_used = min(dec_waves,
- *              dec_blocks) decode waves (at least 1); the prefill items are dealt into 8 queues, one per XCD,
- *              and queue x is queue_count[x] entries of the queue list from
- *              queue_base[x] = x * max_pf_items on)
- *   offsets[1] decode units   int32[max_dec_units][8]
- *   offsets[2] prefill units  int32[max_pf_units][8]
- *   offsets[3] decode items   int32[max_dec_items][16]
- *   offsets[4] prefill items  int32[max_pf_items][2]
- *   offsets[5] queue list     int32[8][max_pf_items] (prefill item indices)
- *   offsets[6] first decode item of each decode wave, int32[dec_waves]
- *              (INT32_MAX for a wave with no item)
- *   offsets[7] 0 (reserved)
- * A unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}. A prefill
- * item is {unit, chunk}, covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo +
- * (chunk+1)*C)) with C = pf_chunk. A decode item is {seq, kv_head, c_lo, c_hi,
- * kv_len, q0, q_len, row0, nrows, nch, unit, chunk, wave, 0, 0, 0}: keys
- * [c_lo, c_hi) of its unit, run by decode wave `wave`; the decode units' key
- * blocks, laid end to end, are split into dec_waves_used equal contiguous
- * ranges and each wave's items are consecutive. limits = {max_dec_units,
- * max_pf_units, max_dec_items, max_pf_items, dec_rows_max, pf_rows_max,
- * dec_waves, 0}.
+ *              (n_split_units counts prefill units with more than one item;
+ *              n_dec_units = n_dec_seqs * Hkv; dec_blocks is the number of
+ *              16-key blocks of all decode units, split over the first
+ *              dec_waves_used = min(dec_waves, dec_blocks) decode waves (at
+ *              least 1); the prefill items are dealt into 8 queues, one per
+ *              XCD, and queue x is queue_count[x] entries of the queue list
+ *              from queue_base[x] = x * max_pf_items on)
+ *   offsets[1] decode sequences int32[max_num_seqs][8]
+ *   offsets[2] prefill units    int32[max_pf_units][8]
+ *   offsets[3] 0 (reserved)
+ *   offsets[4] prefill items    int32[max_pf_items][2]
+ *   offsets[5] queue list       int32[8][max_pf_items] (prefill item indices)
+ *   offsets[6], offsets[7] 0 (reserved)
+ * A prefill unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}. A
+ * prefill item is {unit, chunk}, covering keys [kv_lo + chunk*C,
+ * min(kv_hi, kv_lo + (chunk+1)*C)) with C = pf_chunk. A decode sequence
+ * record is {seq, q0, q_len, kv_len, kv_lo, kv_hi, blk0, nb}, one per
+ * sequence with 1 <= q_len * Hq/Hkv <= 16, in sequence order: its units are
+ * (seq, h) for every kv head h, all q_len * Hq/Hkv rows, keys [kv_lo, kv_hi)
+ * in nb 16-key blocks, at blocks [blk0 + h*nb, blk0 + (h+1)*nb) of the
+ * decode blocks laid end to end. Decode wave w runs blocks
+ * [floor(dec_blocks*w/W), floor(dec_blocks*(w+1)/W)) with W = dec_waves_used.
+ * limits = {max_dec_units, max_pf_units, decode partial slots (2 * dec_waves),
+ * max_pf_items, dec_rows_max, pf_rows_max, dec_waves, 0}.
  */
 rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[8], int32_t limits[8]);
 

@@ -51,13 +51,11 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   std::memset(&p, 0, sizeof p);
   char* w = static_cast<char*>(ws);
   p.hdr = reinterpret_cast<Header*>(w + L.hdr);
-  p.dec_units = reinterpret_cast<Unit*>(w + L.du);
+  p.dec_seqs = reinterpret_cast<DecSeq*>(w + L.dseq);
   p.pf_units = reinterpret_cast<Unit*>(w + L.pu);
-  p.dec_items = reinterpret_cast<DecItem*>(w + L.di);
   p.pf_items = reinterpret_cast<Item*>(w + L.pi);
   p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
-  p.dec_wave_first = reinterpret_cast<int32_t*>(w + L.wfirst);
   p.dec_waves = L.dec_waves;
   p.dec_part = reinterpret_cast<float*>(w + L.dpart);
   p.dec_plse = reinterpret_cast<float*>(w + L.dplse);
@@ -75,7 +73,6 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.pf_rows = L.pf_rows;
   p.max_dec_units = L.max_du;
   p.max_pf_units = L.max_pu;
-  p.max_dec_items = L.max_di;
   p.max_pf_items = L.max_pi;
   p.target_pf_items = L.tgt_p;
   p.sm_scale = c->sm_scale * c->k_scale;
@@ -270,8 +267,8 @@ static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspa
   if (workspace_bytes < L.total) return RPA_ERR_WORKSPACE_TOO_SMALL;
   *p = make_params(cfg, L, workspace);
   // every workspace view the kernels dereference must be assigned
-  const void* views[] = {p->hdr,       p->dec_units,      p->pf_units, p->dec_items, p->pf_items, p->pf_qlist,
-                         p->unit_done, p->dec_wave_first, p->dec_part, p->dec_plse,  p->pf_part,  p->pf_plse};
+  const void* views[] = {p->hdr,       p->dec_seqs, p->pf_units, p->pf_items, p->pf_qlist,
+                         p->unit_done, p->dec_part, p->dec_plse, p->pf_part,  p->pf_plse};
   for (const void* v : views)
     if (!v) return RPA_ERR_INVALID_ARGUMENT;
   *cus_out = cus;
@@ -413,16 +410,16 @@ rpa_status rpa_plan_layout(const rpa_config* cfg, size_t offsets[8], int32_t lim
   Layout L;
   if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
   offsets[0] = L.hdr;
-  offsets[1] = L.du;
+  offsets[1] = L.dseq;
   offsets[2] = L.pu;
-  offsets[3] = L.di;
+  offsets[3] = 0;
   offsets[4] = L.pi;
   offsets[5] = L.qlist;
-  offsets[6] = L.wfirst;
+  offsets[6] = 0;
   offsets[7] = 0;
   limits[0] = L.max_du;
   limits[1] = L.max_pu;
-  limits[2] = L.max_di;
+  limits[2] = L.dec_slots;
   limits[3] = L.max_pi;
   limits[4] = kDecRows;
   limits[5] = L.pf_rows;

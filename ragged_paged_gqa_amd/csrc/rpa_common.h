@@ -35,21 +35,19 @@ struct Params {
   float* lse;                // [T, Hq] or null
   // workspace views
   Header* hdr;
-  Unit* dec_units;
+  DecSeq* dec_seqs;          // decode sequence table [S_max]
   Unit* pf_units;
-  DecItem* dec_items;
   Item* pf_items;
   int32_t* pf_qlist;         // prefill item indices in queue order [kQueues][max_pf_items]
-  int32_t* unit_done;        // finished chunks per unit: [max_dec_units] then [max_pf_units]
-  int32_t* dec_wave_first;   // first decode item of each decode wave [dec_waves] (INT32_MAX: none)
-  float* dec_part;           // [max_dec_items][kDecRows][D]
-  float* dec_plse;           // [max_dec_items][kDecRows]
+  int32_t* unit_done;        // finished chunks per prefill unit [max_pf_units]
+  float* dec_part;           // [2 * dec_waves][kDecRows][D]: partial slots 2w, 2w + 1 of decode wave w
+  float* dec_plse;           // [2 * dec_waves][kDecRows]
   float* pf_part;            // [max_pf_items][pf_rows][D]
   float* pf_plse;            // [max_pf_items][pf_rows]
   // shapes
   int32_t T, Hq, Hkv, G, D, page, P, S_max, pps;
   int32_t pf_rows;           // packed rows of a prefill-class unit
-  int32_t max_dec_units, max_pf_units, max_dec_items, max_pf_items;
+  int32_t max_dec_units, max_pf_units, max_pf_items;
   int32_t target_pf_items;
   int32_t dec_waves;         // waves of the decode launch (the stream-K split)
   const float* sinks;        // [Hq] attention-sink logits, or null
@@ -448,5 +446,35 @@ __device__ __forceinline__ void seq_tokens(const Params& p, int32_t s, int32_t& 
   q0 = a;
   ql = b - a;
 }
+
+// floor(a / b) for 0 <= a < 2^48, 0 < b < 2^31, given inv = 1.0 / b: the
+// double product is within one of the quotient, which the remainder fixes
+// (a multiply instead of a double-precision division).
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b, double inv) {
+  int64_t q = (int64_t)((double)a * inv);
+  const int64_t r = a - q * b;
+  if (r < 0) --q;
+  else if (r >= b) ++q;
+  return q;
+}
+
+// The stream-K split of the decode work: Tb 16-key blocks (laid end to end in
+// the decode sequence table's order) cut into W contiguous ranges, range w =
+// [start(w), start(w + 1)) with start(w) = floor(Tb * w / W). The planner
+// takes W <= Tb, so that no range is empty.
+struct StreamK {
+  int64_t Tb;
+  int32_t W;
+  double inv_Tb, inv_W;
+  __device__ static StreamK make(int64_t Tb, int32_t W) {
+    return StreamK{Tb, W, Tb > 0 ? 1.0 / (double)Tb : 0.0, W > 0 ? 1.0 / (double)W : 0.0};
+  }
+  __device__ int32_t start(int32_t w) const { return (int32_t)floor_div(Tb * w, W, inv_W); }
+  // the range holding block x (0 <= x < Tb)
+  __device__ int32_t wave_of(int32_t x) const {
+    const int64_t w = floor_div((int64_t)(x + 1) * W - 1, Tb, inv_Tb);
+    return (int32_t)(w < W - 1 ? w : W - 1);
+  }
+};
 
 }  // namespace rpa

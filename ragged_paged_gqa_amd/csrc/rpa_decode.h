@@ -2,25 +2,27 @@
 // (q_len * G <= 16, e.g. one decode token of 4..16 grouped q heads).
 //
 // The kernel streams K/V from HBM and is bound by it. Work is split
-// stream-K style by the planner: the 16-key blocks of all decode units, laid
-// end to end, are cut into one equal contiguous range per wave, so every wave
-// moves the same number of bytes and no queue is needed. A wave runs its items
-// (the parts of units inside its range) as one continuous pipeline of 16-key
-// steps:
+// stream-K style: the 16-key blocks of all decode units, laid end to end, are
+// cut into one equal contiguous range per wave, so every wave moves the same
+// number of bytes and no queue is needed. The planner writes only one record
+// per decode sequence (DecSeq); a wave finds the sequence holding its first
+// block by a 64-way search over the records' first blocks and walks the units
+// from there. It runs its parts (the pieces of units inside its range) as one
+// continuous pipeline of 16-key steps:
 //   * loads: each step's K rows and V rows of kv head h (combined heads 2h and
 //     2h+1, adjacent in memory: `stridedLoadKv` on the kernel page) go
 //     straight from HBM into a per-wave ring of LDS slots with
 //     global_load_lds_dwordx4, 1 KB of whole rows per instruction, kept
-//     NST - 1 steps ahead of the compute across item boundaries. The 16-byte
+//     NST - 1 steps ahead of the compute across part boundaries. The 16-byte
 //     chunks of a row are XOR-swizzled by the key, so that the MFMA operand
 //     reads below hit distinct LDS banks. Completion is tracked by counting
 //     vector-memory instructions (s_waitcnt vmcnt), so nothing else waits on
 //     the stream;
 //   * pages and metadata: the physical page of each 16-key block (the kernel
 //     page's `createKvAsyncCopyDescriptors`: page_indices[seq, key / page])
-//     and the item descriptors are read with scalar loads one step ahead, and
-//     the next item's Q rows are fetched into an LDS slot by the same DMA
-//     while the current item runs.
+//     and the sequence records are read with scalar loads one step ahead, and
+//     the next part's Q rows are fetched into an LDS slot by the same DMA
+//     while the current part runs.
 // Per 16-key step:
 //   1. S^T [16 keys x 16 rows] = K Q^T with v_mfma_f32_16x16x32_bf16 against
 //      the register-resident Q^T, times sm_scale (k_scale folded in), the
@@ -42,9 +44,11 @@
 // contraction over head_dim may visit d in any order as long as K and Q use
 // the same one: a lane's 16-byte K piece covers 16 consecutive d for fp8,
 // which become two 8-wide k-slots of the MFMA, and Q is read to match.
-// An item that is its unit's only one writes bf16 out and f32 lse; otherwise
-// it writes a normalised f32 partial and its lse, which the combine kernel
-// merges once every item is done (combine_kernel below).
+// A part that is its unit's only one writes bf16 out and f32 lse; otherwise
+// it writes a normalised f32 partial and its lse into a slot of its wave
+// (2w for a part that continues a unit from the previous range, 2w + 1 for
+// the first part of a unit that runs on), which the combine kernel merges
+// once every wave is done (combine_kernel below).
 //
 // Element types: the kernel is instantiated per K/V kind KVT (K/V in the q
 // type, fp8 e4m3fn, fp8 e5m2, int8) and per 16-bit type F16 (bf16, or f16
@@ -144,7 +148,6 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   const uint32_t ring_lds = lds_addr_of(ring);
   const uint32_t qs_lds = lds_addr_of(qs);
 
-  const int n_items = uni(p.hdr->n_dec_items);
   const int key_stride = 2 * p.Hkv * D * EB;  // bytes between consecutive slots (< 2^26)
   const float sc_mul = p.sm_scale * kLog2e;  // uncapped: straight to base 2
   const SoftCapB2 cap_b2(p.sm_scale, CAP ? p.soft_cap : 1.0f);
@@ -180,105 +183,173 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- items ----
+  // ---- the wave's range of the stream-K split, and its parts ----
   const int w = blockIdx.x * kDecWavesPerBlock + wave;  // stream-K rank
+  const int n_dseq = uni(p.hdr->n_dec_seqs);
+  const int W = uni(p.hdr->pad0[0]);
+  const StreamK sk = StreamK::make(uni(p.hdr->dec_blocks), W);
+  // A part: the blocks of unit (decode sequence i, kv head h) that fall into
+  // this wave's range [ws, we), keys [c_lo, c_hi).
+  // (Kept small: three of these are live at once, in scalar registers; the
+  // sequence's own metadata is loaded where a part starts, see Seq.)
   struct Info {
-    int idx, s, h, c_lo, c_hi, kvl, q0, ql, row0, nrows, nch, wave;
+    bool valid;
+    int i;          // decode sequence record
+    int h, b0, nb;  // the unit: kv head h, blocks [b0, b0 + nb)
+    int lo16, hi;   // the units' key range
+    int c_lo, c_hi;
   };
-  auto load_info = [&](int idx) {
+  int ws = 0, we = 0;
+  auto load_seq = [&](Info& I, int i) {
+    const int32_t* d = reinterpret_cast<const int32_t*>(p.dec_seqs + i);
+    I.i = i;
+    I.lo16 = sload(d + 4);
+    I.hi = sload(d + 5);
+    I.b0 = sload(d + 6);  // the unit of kv head 0
+    I.nb = sload(d + 7);
+    I.h = 0;
+  };
+  auto set_part = [&](Info& I) {
+    const int x0 = max(I.b0, ws), x1 = min(I.b0 + I.nb, we);
+    I.c_lo = I.lo16 + 16 * (x0 - I.b0);
+    I.c_hi = max(min(I.hi, I.lo16 + 16 * (x1 - I.b0)), I.c_lo);
+    I.valid = true;
+  };
+  // the unit has parts in other ranges too
+  auto is_split = [&](const Info& I) { return I.b0 < ws || I.b0 + I.nb > we; };
+  // partial slot of a split part: 2w for a part that continues a unit from
+  // the previous range, 2w + 1 for the first part of a unit that runs on
+  auto slot_of = [&](const Info& I) { return 2 * w + (I.b0 < ws ? 0 : 1); };
+  struct Seq {
+    int s, q0, ql, kvl, nrows;
+  };
+  auto seq_of = [&](const Info& I) {
+    const int32_t* d = reinterpret_cast<const int32_t*>(p.dec_seqs + I.i);
+    Seq m;
+    m.s = sload(d + 0);
+    m.q0 = sload(d + 1);
+    m.ql = sload(d + 2);
+    m.kvl = sload(d + 3);
+    m.nrows = m.ql * p.G;
+    return m;
+  };
+  // The first part: the unit holding block ws, of the last decode sequence
+  // whose first block is <= ws (it has blocks: a later sequence starts after
+  // ws). The table is searched 64 probes at a time.
+  auto first_info = [&]() {
+    const int32_t* blk0 = reinterpret_cast<const int32_t*>(p.dec_seqs) + 6;  // record stride: 8 ints
+    int lo = 0, hi = n_dseq;  // blk0[lo] <= ws (blk0[0] = 0); the sequence is in [lo, hi)
+    while (hi - lo > 64) {
+      const int step = (hi - lo + 63) / 64;
+      const int j = lo + lane * step;
+      const int k = __popcll(__ballot(j < hi && blk0[(int64_t)j * 8] <= ws));  // lane 0 probes lo
+      hi = min(hi, lo + k * step);
+      lo += (k - 1) * step;
+    }
+    const int j = lo + lane;
+    const int i = uni(lo + __popcll(__ballot(j < hi && blk0[(int64_t)j * 8] <= ws)) - 1);
     Info I;
-    I.idx = idx;
-    if (idx >= n_items) {
-      I.wave = -1;
+    load_seq(I, i);
+    if (I.nb <= 0) {  // only if the table were inconsistent
+      I.valid = false;
       return I;
     }
-    const int32_t* d = reinterpret_cast<const int32_t*>(p.dec_items + idx);
-    I.s = sload(d + 0);
-    I.h = sload(d + 1);
-    I.c_lo = sload(d + 2);
-    I.c_hi = max(sload(d + 3), I.c_lo);
-    I.kvl = sload(d + 4);
-    I.q0 = sload(d + 5);
-    I.ql = sload(d + 6);
-    I.row0 = sload(d + 7);
-    I.nrows = sload(d + 8);
-    I.nch = sload(d + 9);
-    I.wave = sload(d + 12);
+    I.h = (ws - I.b0) / I.nb;
+    I.b0 += I.h * I.nb;
+    set_part(I);
     return I;
   };
-  auto mine = [&](const Info& I) { return I.wave == w; };
-  // 16-key steps of an item; an empty key range (only outside the data
+  // The part after I in the range (invalid once I reaches its end).
+  auto next_info = [&](const Info& I) {
+    Info N = I;
+    N.valid = false;
+    if (!I.valid || I.b0 + I.nb >= we) return N;
+    if (I.h + 1 < p.Hkv) {
+      N.h = I.h + 1;
+      N.b0 = I.b0 + I.nb;
+    } else {
+      // the next decode sequence with blocks (blocks remain in the range)
+      int i = I.i + 1;
+      if (i >= n_dseq) return N;
+      load_seq(N, i);
+      while (N.nb <= 0 && i + 1 < n_dseq) load_seq(N, ++i);
+    }
+    set_part(N);
+    return N;
+  };
+  // 16-key steps of a part; an empty key range (only outside the data
   // preconditions) still takes one fully masked step, so that the load and
   // compute sides always agree on the step count
   auto item_steps = [](const Info& I) { return max(1, (I.c_hi - I.c_lo + kDecStepKeys - 1) / kDecStepKeys); };
 
-  // Q rows of an item, 16 x D bf16, straight into the wave's Q slot (row r =
-  // packed row row0 + r; rows past nrows re-read row 0 and are ignored).
+  // Q rows of a part, 16 x D bf16, straight into the wave's Q slot (row r =
+  // packed row r of the sequence; rows past nrows re-read row 0 and are
+  // ignored).
   auto dma_q = [&](const Info& I) {
     constexpr int QROW = 2 * D, QRPI = 1024 / QROW, QNI = 16 / QRPI;
+    const Seq m = seq_of(I);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
 #pragma unroll
     for (int j = 0; j < QNI; ++j) {
       const int r = QRPI * j + (lane * 16) / QROW;
-      const int prow = I.row0 + (r < I.nrows ? r : 0);
+      const int prow = r < m.nrows ? r : 0;
       const int t = prow / p.G;
       const int qh = I.h * p.G + (prow - t * p.G);
       const uint8_t* src =
-          reinterpret_cast<const uint8_t*>(p.q + ((int64_t)(I.q0 + t) * p.Hq + qh) * D) + (lane * 16) % QROW;
+          reinterpret_cast<const uint8_t*>(p.q + ((int64_t)(m.q0 + t) * p.Hq + qh) * D) + (lane * 16) % QROW;
       dma16(src, qs_lds + 1024u * j);
     }
   };
   // Q^T operand from the Q slot: lane (row col, group g) takes k-slot i
-  auto read_q = [&](const Info& I, bf16x8 (&qb)[NI]) {
+  auto read_q = [&](int nrows, bf16x8 (&qb)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qs + col * D + slot_d<FP8>(i, g));
-      qb[i] = col < I.nrows ? v : bf16x8{};
+      qb[i] = col < nrows ? v : bf16x8{};
     }
   };
   // fp8 and f32 q: the same operand straight from global memory (row col of
   // the item; rows past nrows re-read row 0 and are zeroed); an f32 q also
   // gives its lo part (split_q8)
   auto load_q = [&](const Info& I, bf16x8 (&qr)[NI], bf16x8 (&qlr)[Q32 ? NI : 1]) {
-    const int prow = I.row0 + (col < I.nrows ? col : 0);
+    const Seq m = seq_of(I);
+    const int prow = col < m.nrows ? col : 0;
     const int t = prow / p.G;
     const int qh = I.h * p.G + (prow - t * p.G);
-    const int64_t e = ((int64_t)(I.q0 + t) * p.Hq + qh) * D;
+    const int64_t e = ((int64_t)(m.q0 + t) * p.Hq + qh) * D;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if constexpr (Q32) {
         const float* qp = reinterpret_cast<const float*>(p.q) + e + slot_d<FP8>(i, g);
         bf16x8 hi, lo;
         split_q8(*reinterpret_cast<const f32x4*>(qp), *reinterpret_cast<const f32x4*>(qp + 4), hi, lo);
-        qr[i] = col < I.nrows ? hi : bf16x8{};
-        qlr[i] = col < I.nrows ? lo : bf16x8{};
+        qr[i] = col < m.nrows ? hi : bf16x8{};
+        qlr[i] = col < m.nrows ? lo : bf16x8{};
       } else {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(p.q + e + slot_d<FP8>(i, g));
-        qr[i] = col < I.nrows ? v : bf16x8{};
+        qr[i] = col < m.nrows ? v : bf16x8{};
       }
     }
   };
 
   // ---- loader: the item whose steps are being loaded ----
   struct Loader {
-    Info I;
+    int s;      // sequence (its page-table row)
     int hoff;   // byte offset of combined head 2h in a slot
     int lp, sl, key;  // next block: logical page, slot in the page, first key
     int left;   // steps not yet loaded
     int pg;     // physical page of the next block (scalar-loaded ahead)
   };
-  auto page_id = [&](const Info& I, int lp) {
-    return sload(p.page_indices + (int64_t)I.s * p.pps + min(lp, p.pps - 1));
-  };
+  auto page_id = [&](int s, int lp) { return sload(p.page_indices + (int64_t)s * p.pps + min(lp, p.pps - 1)); };
   auto loader_for = [&](const Info& I) {
     Loader L;
-    L.I = I;
+    L.s = seq_of(I).s;
     L.hoff = 2 * I.h * D * EB;
     L.lp = I.c_lo / p.page;
     L.sl = I.c_lo - L.lp * p.page;
     L.key = I.c_lo;
     L.left = item_steps(I);
-    L.pg = page_id(I, L.lp);
+    L.pg = page_id(L.s, L.lp);
     return L;
   };
   // Issues the DMA of L's next step into ring slot `slot`, then moves L on.
@@ -297,13 +368,14 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       if (L.sl >= p.page) {
         L.sl = 0;
         ++L.lp;
-        L.pg = page_id(L.I, L.lp);
+        L.pg = page_id(L.s, L.lp);
       }
     }
   };
 
-  // ---- compute state of the current item ----
+  // ---- compute state of the current part ----
   Info C;
+  Seq cs;  // its sequence
   bf16x8 qb[NI];
   bf16x8 ql[Q32 ? NI : 1];  // f32 q: the lo part of the Q operand
   float m_ref, lsum;
@@ -318,16 +390,15 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     steps_done = 0;
     n_steps = item_steps(C);
-    // column `col` of S^T / O^T is packed row C.row0 + col of the sequence
-    rvalid = col < C.nrows;
-    const int prow = C.row0 + col;
-    const int t = prow / p.G;
-    qh = C.h * p.G + (prow - t * p.G);
-    tok = C.q0 + t;
-    pos = C.kvl - C.ql + t;
-    pos_lo = C.kvl - C.ql + C.row0 / p.G;
-    pos_hi = C.kvl - C.ql + (C.row0 + max(C.nrows, 1) - 1) / p.G;
-    vis_hi = min(C.c_hi, C.kvl);
+    // column `col` of S^T / O^T is packed row col of the sequence
+    rvalid = col < cs.nrows;
+    const int t = col / p.G;
+    qh = C.h * p.G + (col - t * p.G);
+    tok = cs.q0 + t;
+    pos = cs.kvl - cs.ql + t;
+    pos_lo = cs.kvl - cs.ql;
+    pos_hi = cs.kvl - cs.ql + (max(cs.nrows, 1) - 1) / p.G;
+    vis_hi = min(C.c_hi, cs.kvl);
   };
 
   // Operands of one 16-key step, read out of its ring slot so that the slot
@@ -478,7 +549,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   auto finish_item = [&]() {
     const float l_row = wave_sum_xor16_32(lsum);
     float inv, lse_v;
-    if (C.nch == 1) {
+    if (!is_split(C)) {
       // the whole row: the sink (if any) joins it here
       row_final(m_ref, l_row, p.v_scale, p.sinks ? p.sinks + qh : nullptr, inv, lse_v);
     } else {
@@ -486,37 +557,40 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       row_final(m_ref, l_row, p.v_scale, nullptr, inv, lse_v);
     }
     if (!rvalid) return;
-    if (C.nch == 1) {
+    if (!is_split(C)) {
       const int64_t e = ((int64_t)tok * p.Hq + qh) * D + 4 * g;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
         store_out4<F16, Q32>(p.out, e + 16 * d, o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv);
       if (g == 0 && p.lse) p.lse[(int64_t)tok * p.Hq + qh] = lse_v;
     } else {
-      float* pp = p.dec_part + ((int64_t)C.idx * kDecRows + col) * D;
+      const int slot = slot_of(C);
+      float* pp = p.dec_part + ((int64_t)slot * kDecRows + col) * D;
 #pragma unroll
       for (int d = 0; d < ND; ++d) *reinterpret_cast<f32x4*>(pp + 16 * d + 4 * g) = o[d] * inv;
-      if (g == 0) p.dec_plse[(int64_t)C.idx * kDecRows + col] = lse_v;
+      if (g == 0) p.dec_plse[(int64_t)slot * kDecRows + col] = lse_v;
     }
   };
 
   // ---- the wave's items, one continuous pipeline ----
-  const int first = sload(p.dec_wave_first + min(w, p.dec_waves - 1));
-  if (w >= p.dec_waves || first >= n_items) return;
-  C = load_info(first);
-  if (!mine(C)) return;
-  Info Cn = load_info(first + 1);  // the compute side's next item
+  if (w >= W || w >= p.dec_waves || n_dseq <= 0 || sk.Tb <= 0) return;
+  ws = uni(sk.start(w));
+  we = uni(sk.start(w + 1));
+  C = first_info();
+  if (!C.valid) return;
+  cs = seq_of(C);
+  Info Cn = next_info(C);  // the compute side's next part
   bf16x8 qn[QREG ? NI : 1];        // fp8, f32 q: the next item's Q operand, loaded ahead
   bf16x8 qnl[Q32 ? NI : 1];        // f32 q: its lo part
   if constexpr (QREG) {
     load_q(C, qb, ql);
-    if (mine(Cn)) load_q(Cn, qn, qnl);
+    if (Cn.valid) load_q(Cn, qn, qnl);
   } else {
     dma_q(C);
     wait_vmcnt<0>();
     wave_sync();
-    read_q(C, qb);
-    if (mine(Cn)) dma_q(Cn);
+    read_q(cs.nrows, qb);
+    if (Cn.valid) dma_q(Cn);
   }
   int q_age = 0;  // steps computed since the Q slot's DMA was issued
   begin_item();
@@ -527,9 +601,9 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   // Moves the load side to its next step: the same item, or the next of the wave.
   auto loader_next = [&]() {
     if (L.left > 0) return;
-    if (mine(Ln)) {
+    if (Ln.valid) {
       L = loader_for(Ln);
-      Ln = load_info(Ln.idx + 1);
+      Ln = next_info(Ln);
     } else {
       loading = false;
     }
@@ -573,9 +647,10 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     --ahead;
     if (steps_done == n_steps) {
       finish_item();
-      if (!mine(Cn)) return;  // the wave's range is done
+      if (!Cn.valid) return;  // the wave's range is done
       C = Cn;
-      Cn = load_info(C.idx + 1);
+      cs = seq_of(C);
+      Cn = next_info(C);
       if constexpr (QREG) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) qb[i] = qn[i];
@@ -583,14 +658,14 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
 #pragma unroll
           for (int i = 0; i < NI; ++i) ql[i] = qnl[i];
         }
-        if (mine(Cn)) load_q(Cn, qn, qnl);
+        if (Cn.valid) load_q(Cn, qn, qnl);
       } else {
         // the Q slot's DMA is complete once a wait above covered a step
         // issued after it (NST + 1 steps later); for short items wait here
         if (q_age <= NST) wait_vmcnt<0>();
         wave_sync();
-        read_q(C, qb);
-        if (mine(Cn)) {
+        read_q(cs.nrows, qb);
+        if (Cn.valid) {
           dma_q(Cn);
           q_age = 0;
         }
@@ -600,38 +675,40 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   }
 }
 
-// Merges the split decode-class units once every decode item is done: one
-// wave per unit, the items' partials combined by merge_unit; a unit with no
-// key to see (and so no item) gets out = 0 and lse = -inf.
+// Merges the split decode-class units once every decode wave is done: one
+// wave per unit (decode sequence u / Hkv, kv head u % Hkv), the parts'
+// partials combined by merge_unit in block order; a unit with no key to see
+// (and so no block) gets out = 0 and lse = -inf.
 template <int D, bool F16, bool Q32 = false>
 __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params p) {
   __shared__ float stat[kDecWavesPerBlock][2 * kDecRows];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: the unit's record comes by scalar loads
   const int n_units = uni(p.hdr->n_dec_units);
+  const StreamK sk = StreamK::make(uni(p.hdr->dec_blocks), uni(p.hdr->pad0[0]));
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   for (int u = blockIdx.x * kDecWavesPerBlock + wave; u < n_units; u += gridDim.x * kDecWavesPerBlock) {
+    const int i = u / p.Hkv;
+    const int32_t* d = reinterpret_cast<const int32_t*>(p.dec_seqs + i);
     Unit U;
-    U.seq = uni(p.dec_units[u].seq);
-    U.kv_head = uni(p.dec_units[u].kv_head);
-    U.row0 = uni(p.dec_units[u].row0);
-    U.nrows = uni(p.dec_units[u].nrows);
-    U.kv_lo = uni(p.dec_units[u].kv_lo);
-    U.kv_hi = uni(p.dec_units[u].kv_hi);
-    U.nch = uni(p.dec_units[u].nch);
-    U.item0 = uni(p.dec_units[u].item0);
-    if (U.nch == 1) continue;  // its item wrote the rows
-    if (U.nch == 0) {
+    U.seq = uni(d[0]);
+    U.kv_head = u - i * p.Hkv;
+    U.row0 = 0;
+    U.nrows = uni(d[2]) * p.G;
+    U.kv_lo = uni(d[4]);
+    U.kv_hi = uni(d[5]);
+    const int nb = uni(d[7]);
+    if (nb <= 0) {
       // no visible key (only outside the data preconditions): out 0, lse -inf
       // (with a sink: lse = the sink, its own term)
       int q0, ql;
       seq_tokens(p, U.seq, q0, ql);
       for (int e = lane; e < U.nrows * (D / 4); e += 64) {
-        const int prow = U.row0 + e / (D / 4);
+        const int prow = e / (D / 4);
         const int t = prow / p.G;
         const int qh = U.kv_head * p.G + (prow - t * p.G);
         store_out4<F16, Q32>(p.out, ((int64_t)(q0 + t) * p.Hq + qh) * D + 4 * (e % (D / 4)), 0.f, 0.f, 0.f, 0.f);
@@ -639,7 +716,15 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
       }
       continue;
     }
-    merge_unit<D, F16, Q32>(p, U, p.dec_part, p.dec_plse, kDecRows, lane, 64, stat[wave], wave_sync);
+    const int b0 = uni(d[6]) + U.kv_head * nb;
+    const int f = sk.wave_of(b0), l = sk.wave_of(b0 + nb - 1);
+    if (f == l) continue;  // one part: its wave wrote the rows
+    U.nch = l - f + 1;
+    U.item0 = 0;
+    // part c ran on wave f + c: the first in slot 2f + 1, the others in 2(f + c)
+    merge_unit<D, F16, Q32>(p, U, p.dec_part, p.dec_plse, kDecRows,
+                            [&](int c) { return c == 0 ? 2 * f + 1 : 2 * (f + c); }, lane, 64, stat[wave],
+                            wave_sync);
     wave_sync();
   }
 }

@@ -78,30 +78,32 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   const int64_t max_du = Hkv * c->max_num_seqs;
   const int64_t max_pu = Hkv * (((int64_t)c->num_q_tokens * G + pf_rows - 1) / pf_rows + c->max_num_seqs);
   const int64_t tgt_p = (int64_t)cus * RPA_PF_ITEMS_PER_CU;
-  // stream-K: every decode wave boundary inside a unit adds one item
+  // stream-K: a decode wave writes at most two partials (slots 2w, 2w + 1),
+  // and the decode blocks of all units must be countable in int32
   const int64_t dec_waves = (int64_t)dec_grid_for(c, cus) * kDecWavesPerBlock;
-  const int64_t max_di = max_du + dec_waves + 1;
+  const int64_t dec_slots = 2 * dec_waves;
+  const int64_t max_dec_blocks = max_du * (((int64_t)c->pages_per_seq * c->page_size + 15) / 16);
   // prefill chunks are also capped at kPfMaxChunk keys
   const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
   const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);
-  if (max_du >= (1 << 30) || max_pu >= (1 << 30) || max_di >= INT32_MAX || max_pi >= INT32_MAX / kQueues) return false;
+  if (max_du >= (1 << 30) || max_pu >= (1 << 30) || dec_slots >= INT32_MAX || max_dec_blocks >= INT32_MAX ||
+      max_pi >= INT32_MAX / kQueues)
+    return false;
   size_t off = 0;
   L->hdr = off;   off = align256(off + sizeof(Header));
-  L->du = off;    off = align256(off + sizeof(Unit) * (size_t)max_du);
+  L->dseq = off;  off = align256(off + sizeof(DecSeq) * (size_t)c->max_num_seqs);
   L->pu = off;    off = align256(off + sizeof(Unit) * (size_t)max_pu);
-  L->di = off;    off = align256(off + sizeof(DecItem) * (size_t)max_di);
   L->pi = off;    off = align256(off + sizeof(Item) * (size_t)max_pi);
   L->qlist = off; off = align256(off + sizeof(int32_t) * kQueues * (size_t)max_pi);
-  L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)(max_du + max_pu));
-  L->wfirst = off; off = align256(off + sizeof(int32_t) * (size_t)dec_waves);
-  L->dpart = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows * D);
-  L->dplse = off; off = align256(off + sizeof(float) * (size_t)max_di * kDecRows);
+  L->done = off;  off = align256(off + sizeof(int32_t) * (size_t)max_pu);
+  L->dpart = off; off = align256(off + sizeof(float) * (size_t)dec_slots * kDecRows * D);
+  L->dplse = off; off = align256(off + sizeof(float) * (size_t)dec_slots * kDecRows);
   L->ppart = off; off = align256(off + sizeof(float) * (size_t)max_pi * pf_rows * D);
   L->pplse = off; off = align256(off + sizeof(float) * (size_t)max_pi * pf_rows);
   L->total = off;
   L->max_du = (int32_t)max_du;
   L->max_pu = (int32_t)max_pu;
-  L->max_di = (int32_t)max_di;
+  L->dec_slots = (int32_t)dec_slots;
   L->max_pi = (int32_t)max_pi;
   L->tgt_p = (int32_t)tgt_p;
   L->pf_rows = (int32_t)pf_rows;

@@ -31,8 +31,9 @@ rpa_status validate(const rpa_config* c);
 
 // Byte offsets of the workspace regions and the record counts they bound.
 struct Layout {
-  size_t hdr, du, pu, di, pi, qlist, done, wfirst, dpart, dplse, ppart, pplse, total;
-  int32_t max_du, max_pu, max_di, max_pi, tgt_p, pf_rows, dec_waves;
+  size_t hdr, dseq, pu, pi, qlist, done, dpart, dplse, ppart, pplse, total;
+  // decode units (S_max * Hkv), prefill units and items, decode partial slots
+  int32_t max_du, max_pu, max_pi, dec_slots, tgt_p, pf_rows, dec_waves;
 };
 
 // The prefill class of `c` runs on prefill_pp_kernel.

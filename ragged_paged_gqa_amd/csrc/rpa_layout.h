@@ -47,29 +47,25 @@ struct Item {
   int32_t chunk;
 };
 
-// A decode-class item carries everything its wave needs, so that starting it
-// costs one (scalar) load: the sequence's metadata, the chunk's key range and
-// the decode wave that runs it. Decode work is scheduled stream-K style: the
-// key blocks of all decode units, laid end to end, are cut into equal
-// contiguous ranges, one per decode wave, and an item is the part of one unit
-// that falls into one wave's range.
-struct DecItem {
+// Decode-class work is scheduled stream-K style: the 16-key blocks of all
+// decode units, laid end to end in (sequence, kv head) order, are cut into
+// equal contiguous ranges, one per decode wave; each wave runs the parts of
+// the units that fall into its range. The planner writes one record per
+// decode sequence and nothing per part: a wave finds the sequence holding its
+// first block by a search over `blk0` and derives every part from the records
+// and its range. The units of a record are (seq, kv head h) for h < Hkv, each
+// with all ql * G packed rows and blocks [blk0 + h * nb, blk0 + (h + 1) * nb).
+struct DecSeq {
   int32_t seq;
-  int32_t kv_head;
-  int32_t c_lo;   // first key of the chunk (16-aligned)
-  int32_t c_hi;   // one past its last key
-  int32_t kvl;    // kv_len, clamped to the page table's reach
-  int32_t q0;     // first token of the sequence
-  int32_t ql;     // its query tokens
-  int32_t row0;   // first packed row of the unit
-  int32_t nrows;  // packed rows of the unit
-  int32_t nch;    // chunks of the unit (1: the item writes the output itself)
-  int32_t unit;   // unit index
-  int32_t chunk;  // chunk index within the unit
-  int32_t wave;   // the decode wave that runs it
-  int32_t pad[3];
+  int32_t q0;    // first token of the sequence
+  int32_t ql;    // its query tokens
+  int32_t kvl;   // kv_len, clamped to the page table's reach
+  int32_t lo16;  // first key of its units' block grid (16-aligned)
+  int32_t hi;    // one past the last key any of its rows can see
+  int32_t blk0;  // its first block in the stream-K order
+  int32_t nb;    // 16-key blocks of each of its units (0: no visible key)
 };
-static_assert(sizeof(DecItem) == 64, "decode item record is int32[16]");
+static_assert(sizeof(DecSeq) == 32, "decode sequence record is int32[8]");
 
 // Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
 // L2). All row blocks of one (sequence, kv head) go to the same queue, one
@@ -78,13 +74,13 @@ static_assert(sizeof(DecItem) == 64, "decode item record is int32[16]");
 constexpr int kQueues = 8;
 
 struct Header {
-  int32_t n_dec_units;
+  int32_t n_dec_units;  // decode sequences x Hkv
   int32_t n_pf_units;
-  int32_t n_dec_items;
+  int32_t n_dec_seqs;   // records of the decode sequence table
   int32_t n_pf_items;
   int32_t zero;  // 0 (decode chunks follow the stream-K split)
   int32_t pf_chunk;
-  int32_t n_split_units;
+  int32_t n_split_units;  // prefill units with more than one chunk
   int32_t dec_blocks;   // 16-key blocks of all decode units (the stream-K total)
   int32_t pad0[8];      // pad0[0]: decode waves given work (min(dec_waves, dec_blocks), >= 1)
   int32_t pf_q_base[kQueues];   // start of each prefill queue in pf_qlist (x * max_pf_items)

@@ -24,26 +24,53 @@
 
 namespace rpa {
 
-// Threads tid in [0, nt) cooperate; `sync` is called between the phases and
-// must synchronise exactly those threads. `stat` is LDS scratch of
-// 2 * u.nrows floats.
-template <int D, bool F16, bool Q32, typename Sync>
+// Chunk c of the unit left its partial in slot `slot(c)` of `part` / `plse`
+// (slot_rows rows each). Threads tid in [0, nt) cooperate; `sync` is called
+// between the phases and must synchronise exactly those threads. `stat` is
+// LDS scratch of 2 * u.nrows floats.
+template <int D, bool F16, bool Q32, typename Slot, typename Sync>
 __device__ void merge_unit(const Params& p, const Unit& u, const float* part, const float* plse, int slot_rows,
-                           int tid, int nt, float* stat, Sync sync) {
+                           Slot slot, int tid, int nt, float* stat, Sync sync) {
   int q0, ql;
   seq_tokens(p, u.seq, q0, ql);
-  const float* lse_base = plse + (int64_t)u.item0 * slot_rows;
+  auto lse_of = [&](int c, int r) { return load_coherent(plse + (int64_t)slot(c) * slot_rows + r); };
+  // The partials sit in memory written by other workgroups (coherent loads,
+  // long latency): each pass issues a batch of independent loads before it
+  // reduces them, always in chunk order, so the sums do not depend on the
+  // batching.
+  constexpr int BA = 8, BB = 4;
   // phase A: per-row max and 1 / sum of exp(L_c - max)
   for (int r = tid; r < u.nrows; r += nt) {
     const int prow = u.row0 + r;
     const int t = prow / p.G;
     const int qh = u.kv_head * p.G + (prow - t * p.G);
     const float sink = p.sinks ? p.sinks[qh] : -INFINITY;
+    float held[BA];  // the first BA chunks' L_c, kept for the sum
+#pragma unroll
+    for (int k = 0; k < BA; ++k) held[k] = k < u.nch ? lse_of(k, r) : -INFINITY;
     float mx = sink;
-    for (int c = 0; c < u.nch; ++c) mx = fmaxf(mx, load_coherent(lse_base + (int64_t)c * slot_rows + r));
+#pragma unroll
+    for (int k = 0; k < BA; ++k) mx = fmaxf(mx, held[k]);
+    for (int c0 = BA; c0 < u.nch; c0 += BA) {
+      float v[BA];
+#pragma unroll
+      for (int k = 0; k < BA; ++k) v[k] = c0 + k < u.nch ? lse_of(c0 + k, r) : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < BA; ++k) mx = fmaxf(mx, v[k]);
+    }
     float wsum = 0.f;
     if (mx != -INFINITY) {
-      for (int c = 0; c < u.nch; ++c) wsum += expf(load_coherent(lse_base + (int64_t)c * slot_rows + r) - mx);
+#pragma unroll
+      for (int k = 0; k < BA; ++k)
+        if (k < u.nch) wsum += expf(held[k] - mx);
+      for (int c0 = BA; c0 < u.nch; c0 += BA) {
+        float v[BA];
+#pragma unroll
+        for (int k = 0; k < BA; ++k) v[k] = c0 + k < u.nch ? lse_of(c0 + k, r) : -INFINITY;
+#pragma unroll
+        for (int k = 0; k < BA; ++k)
+          if (c0 + k < u.nch) wsum += expf(v[k] - mx);
+      }
       if (sink != -INFINITY) wsum += expf(sink - mx);
     }
     stat[2 * r] = mx;
@@ -53,7 +80,6 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
   sync();
   // phase B: out[row, 4 elements] = sum_c exp(L_c - max) / sum * O_c[row, 4 elements]
   constexpr int PIECES = D / 4;
-  const float* part_base = part + (int64_t)u.item0 * slot_rows * D;
   for (int idx = tid; idx < u.nrows * PIECES; idx += nt) {
     const int r = idx / PIECES;
     const int e0 = 4 * (idx % PIECES);
@@ -61,15 +87,28 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
     const float inv = stat[2 * r + 1];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (mx != -INFINITY) {
-#pragma unroll 4
-      for (int c = 0; c < u.nch; ++c) {
-        const float w = expf(load_coherent(lse_base + (int64_t)c * slot_rows + r) - mx);
-        const float* src = part_base + ((int64_t)c * slot_rows + r) * D + e0;
-        const f32x2 a = load_coherent2(src), b = load_coherent2(src + 2);
-        acc[0] += w * a[0];
-        acc[1] += w * a[1];
-        acc[2] += w * b[0];
-        acc[3] += w * b[1];
+      for (int c0 = 0; c0 < u.nch; c0 += BB) {
+        float l[BB];
+        f32x2 a[BB], b[BB];
+#pragma unroll
+        for (int k = 0; k < BB; ++k) {
+          if (c0 + k < u.nch) {
+            const float* src = part + ((int64_t)slot(c0 + k) * slot_rows + r) * D + e0;
+            l[k] = lse_of(c0 + k, r);
+            a[k] = load_coherent2(src);
+            b[k] = load_coherent2(src + 2);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < BB; ++k) {
+          if (c0 + k < u.nch) {
+            const float w = expf(l[k] - mx);
+            acc[0] += w * a[k][0];
+            acc[1] += w * a[k][1];
+            acc[2] += w * b[k][0];
+            acc[3] += w * b[k][1];
+          }
+        }
       }
     }
     const int prow = u.row0 + r;

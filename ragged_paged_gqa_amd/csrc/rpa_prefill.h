@@ -712,13 +712,14 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
       // publish the partial, count the chunk; the last one merges the unit
       wait_stores();
       __syncthreads();
-      if (tid == 0) sh_last = atomicAdd(&p.unit_done[p.max_dec_units + it.unit], 1) == u.nch - 1;
+      if (tid == 0) sh_last = atomicAdd(&p.unit_done[it.unit], 1) == u.nch - 1;
       __syncthreads();
       if (sh_last) {
         // the LDS ring is idle here (every wave is past its last step); it
         // holds the per-row stats of the merge
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D, F16, Q32>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds), wg_sync);
+        merge_unit<D, F16, Q32>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
+                                reinterpret_cast<float*>(lds), wg_sync);
       }
     }
     // every wave must be done with the ring before the next item refills it

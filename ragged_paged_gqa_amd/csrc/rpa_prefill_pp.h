@@ -468,14 +468,14 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void prefill_pp_kernel(Params p) 
       // publish the partial, count the chunk; the last one merges the unit
       wait_stores();
       __syncthreads();
-      if (tid == 0) sh_last = atomicAdd(&p.unit_done[p.max_dec_units + it.unit], 1) == u.nch - 1;
+      if (tid == 0) sh_last = atomicAdd(&p.unit_done[it.unit], 1) == u.nch - 1;
       __syncthreads();
       if (sh_last) {
         // the ring is idle (every wave is past its last phase); it holds the
         // merge's per-row statistics
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D, F16, false>(p, u, p.pf_part, p.pf_plse, p.pf_rows, tid, NT, reinterpret_cast<float*>(lds),
-                                  wg_sync);
+        merge_unit<D, F16, false>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
+                                  reinterpret_cast<float*>(lds), wg_sync);
       }
     }
     // every wave must be done with the ring and the block table before the

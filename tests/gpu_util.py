@@ -92,3 +92,38 @@ def assert_parity(out, lse, ref_out, ref_lse, what=""):
         badl = ~(dl <= LSE_TOL)
         assert not badl.any(), f"{what}: {int(badl.sum())} lse values off; max |d| {np.nanmax(dl):.3e}"
     return dict(max_abs=float(np.max(diff)) if diff.size else 0.0, rel_rms=rel_rms)
+
+
+def sample_rows(w: wl.Workload, n_random: int = 192, seed: int = 0):
+    """A seeded sample of (token, q head) rows of a large workload: every q
+    head of the first and last token of the batch and of a middle sequence,
+    plus n_random random pairs."""
+    rng = np.random.default_rng(seed)
+    T = w.valid_tokens()
+    Hq = w.cfg.num_q_heads
+    s = w.n_seqs // 2
+    toks = [int(w.cu_q_lens[0]), T - 1, int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1]) - 1]
+    tokens = np.repeat(np.array(toks), Hq)
+    heads = np.tile(np.arange(Hq), len(toks))
+    rt = rng.integers(0, T, size=n_random)
+    rh = rng.integers(0, Hq, size=n_random)
+    return np.concatenate([tokens, rt]), np.concatenate([heads, rh])
+
+
+def check_sampled(w: wl.Workload, d, what: str):
+    """Runs the HIP path on device workload d and compares the sampled rows
+    with the oracle, computed one by one."""
+    import oracle
+
+    print(f"[workload] {what}: running GPU", flush=True)
+    out, lse = d.run()
+    tokens, heads = sample_rows(w)
+    t = torch.from_numpy(tokens).cuda()
+    h = torch.from_numpy(heads).cuda()
+    got_o = out[t, h].float().cpu().numpy()
+    got_l = lse[t, h].cpu().numpy()
+    print(f"[workload] {what}: oracle on {len(tokens)} rows", flush=True)
+    ref_o, ref_l, st = oracle.rows(w, tokens, heads)
+    assert np.all(st == 0)
+    stats = assert_parity(got_o, got_l, ref_o, ref_l, what)
+    print(f"[workload] {what}: ok {stats}", flush=True)

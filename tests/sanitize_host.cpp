@@ -45,7 +45,7 @@ static rpa_config base_cfg() {
 
 // every region of a layout 256-byte aligned, in order, inside the total
 static void check_layout(const Layout& L, const rpa_config& c) {
-  const size_t offs[] = {L.hdr, L.du, L.pu, L.di, L.pi, L.qlist, L.done, L.wfirst, L.dpart, L.dplse, L.ppart, L.pplse};
+  const size_t offs[] = {L.hdr, L.dseq, L.pu, L.pi, L.qlist, L.done, L.dpart, L.dplse, L.ppart, L.pplse};
   for (size_t i = 0; i < sizeof offs / sizeof offs[0]; ++i) {
     CHECK(offs[i] % 256 == 0);
     if (i) CHECK(offs[i] >= offs[i - 1]);
@@ -54,7 +54,9 @@ static void check_layout(const Layout& L, const rpa_config& c) {
   CHECK(L.max_du == c.num_kv_heads * c.max_num_seqs);
   CHECK(L.pf_rows == (uses_pp(&c) ? kPpRows : pf_rows_for(c.head_dim)));
   CHECK(L.ppart + sizeof(float) * (size_t)L.max_pi * L.pf_rows * c.head_dim <= L.pplse);
-  CHECK(L.dpart + sizeof(float) * (size_t)L.max_di * kDecRows * c.head_dim <= L.dplse);
+  CHECK(L.dseq + sizeof(DecSeq) * (size_t)c.max_num_seqs <= L.pu);
+  CHECK(L.dec_slots == 2 * L.dec_waves);
+  CHECK(L.dpart + sizeof(float) * (size_t)L.dec_slots * kDecRows * c.head_dim <= L.dplse);
 }
 
 int main() {

@@ -13,10 +13,10 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import Device, assert_parity
+from gpu_util import Device, assert_parity, check_sampled
 from test_gpu_append import _append, _check, _kv_host
 from test_gpu_parity import MEDIUM, _compare_all
-from test_gpu_workloads import _check_sampled
+
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def test_e5m2_fp8_decode_workload_shape_full_size():
     print("[e5m2] fp8 decode shape: generating", flush=True)
     w = wl.build("cfg4-e5m2", kw, q, kv, 4, rng=rng)
     d = Device(w)
-    _check_sampled(w, d, "cfg4 e5m2")
+    check_sampled(w, d, "cfg4 e5m2")
     del d
     torch.cuda.empty_cache()
 

@@ -14,10 +14,10 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import Device, assert_parity
+from gpu_util import Device, assert_parity, check_sampled
 from test_gpu_append import _append, _check
 from test_gpu_parity import MEDIUM, _compare_all
-from test_gpu_workloads import _check_sampled
+
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +73,7 @@ def test_f16_named_workload_shapes_full_size(number):
     print(f"[f16] cfg{number}: generating", flush=True)
     w = wl.named(number, q_dtype=F16)
     d = Device(w)
-    _check_sampled(w, d, f"cfg{number} f16")
+    check_sampled(w, d, f"cfg{number} f16")
     del d
     torch.cuda.empty_cache()
 

@@ -17,10 +17,10 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import Device, assert_parity, run_numpy
+from gpu_util import Device, assert_parity, check_sampled, run_numpy
 from test_gpu_append import _append, _check
 from test_gpu_parity import MEDIUM, _compare_all
-from test_gpu_workloads import _check_sampled
+
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,7 @@ def test_f32_named_workload_shapes_full_size(number):
     print(f"[f32] cfg{number}: generating", flush=True)
     w = wl.named(number, q_dtype=F32)
     d = Device(w)
-    _check_sampled(w, d, f"cfg{number} f32")
+    check_sampled(w, d, f"cfg{number} f32")
     del d
     torch.cuda.empty_cache()
 

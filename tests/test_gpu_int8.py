@@ -14,10 +14,10 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import Device, assert_parity
+from gpu_util import Device, assert_parity, check_sampled
 from test_gpu_append import _append, _check
 from test_gpu_parity import MEDIUM, _compare_all
-from test_gpu_workloads import _check_sampled
+
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_int8_fp8_decode_workload_shape_full_size():
     print("[int8] fp8 decode shape: generating", flush=True)
     w = wl.named(4, kv_dtype=I8)
     d = Device(w)
-    _check_sampled(w, d, "cfg4 int8")
+    check_sampled(w, d, "cfg4 int8")
     del d
     torch.cuda.empty_cache()
 

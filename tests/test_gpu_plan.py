@@ -4,7 +4,9 @@ The plan is copied back from the workspace and checked against the metadata,
 with no second implementation of the planner: every packed query row of every
 sequence is owned by exactly one unit of the right class, each unit's key range
 covers exactly the keys its rows can see (rounded down to 16 at the start),
-and the items of each unit tile that range in chunks with no gap or overlap.
+the items of each prefill unit tile that range in chunks with no gap or
+overlap, and the decode sequence table carries each decode sequence once, in
+order, with its block count and stream-K position.
 """
 
 import numpy as np
@@ -26,42 +28,75 @@ def _plan(w):
     offs, lim = rpa.plan_layout(cfg)
     host = ws.cpu().numpy()
     hdr = host[offs[0]:offs[0] + 256].view(np.int32)
-    n_du, n_pu, n_di, n_pi, dch, pch = (int(x) for x in hdr[:6])
-    du = host[offs[1]:offs[1] + 32 * n_du].view(np.int32).reshape(n_du, 8)
+    n_du, n_pu, n_ds, n_pi, _, pch = (int(x) for x in hdr[:6])
+    # decode sequence records: seq, q0, ql, kvl, lo16, hi, blk0, nb
+    ds = host[offs[1]:offs[1] + 32 * n_ds].view(np.int32).reshape(n_ds, 8)
     pu = host[offs[2]:offs[2] + 32 * n_pu].view(np.int32).reshape(n_pu, 8)
-    # decode items are full descriptors: seq, kv_head, c_lo, c_hi, kvl, q0, ql,
-    # row0, nrows, nch, unit, chunk, 4 x pad
-    di = host[offs[3]:offs[3] + 64 * n_di].view(np.int32).reshape(n_di, 16)
     pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
     qbase, qcount, qnext = hdr[16:24].copy(), hdr[24:32].copy(), hdr[32:40].copy()
     ql = host[offs[5]:offs[5] + 4 * 8 * int(lim[3])].view(np.int32)
-    W = int(lim[6])
-    wfirst = host[offs[6]:offs[6] + 4 * W].view(np.int32)
-    return dict(du=du, pu=pu, di=di, pi=pi, dch=dch, pch=pch, lim=lim, qbase=qbase, qcount=qcount,
-                qnext=qnext, qlist=ql, W=W, wfirst=wfirst, dec_blocks=int(hdr[7]), W_used=int(hdr[8]))
+    return dict(n_du=n_du, ds=ds, pu=pu, pi=pi, pch=pch, lim=lim, qbase=qbase, qcount=qcount, qnext=qnext,
+                qlist=ql, W=int(lim[6]), dec_blocks=int(hdr[7]), W_used=int(hdr[8]))
 
 
-def _check_stream_k(P):
-    """Decode items run in stream-K order: the units' 16-key blocks laid end
-    to end are split into W equal contiguous ranges; each wave's items are
-    consecutive, cover exactly its range and start at wfirst[wave]."""
-    di, W, Tb, Wu = P["di"], P["W"], P["dec_blocks"], P["W_used"]
+def _visible_range(c, G, kvl, ql, r0, nr):
+    """[lo rounded down to 16, hi): the keys rows r0 .. r0 + nr - 1 of a
+    sequence can see, from the causal and window rules."""
+    firsts, lasts = [], []
+    for r in range(r0, r0 + nr):
+        p = kvl - ql + r // G
+        last = p if c.is_causal else kvl - 1
+        first = max(0, p - c.sliding_window + 1) if c.sliding_window else 0
+        firsts.append(first)
+        lasts.append(min(last, kvl - 1))
+    return (min(firsts) // 16) * 16, max(lasts) + 1
+
+
+def _check_decode(P, w, owner):
+    """One record per decode sequence, in sequence order, with the metadata,
+    the visible key range of all its rows, its 16-key block count and the
+    exclusive scan of Hkv * blocks; the header's stream-K totals. Then the
+    split itself (start(w) = floor(Tb * w / W)): every wave's range holds at
+    most one part that continues a unit from the previous range and at most
+    one first part of a unit that runs on, so the two partial slots of a
+    wave are never shared."""
+    c = w.cfg
+    G = c.num_q_heads // c.num_kv_heads
+    Hkv = c.num_kv_heads
+    cap = c.pages_per_seq * c.page_size
+    dec = [s for s in range(int(w.num_seqs[0]))
+           if 0 < int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s]) and
+           (int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])) * G <= P["lim"][4]]
+    ds = P["ds"]
+    assert len(ds) == len(dec) and P["n_du"] == len(dec) * Hkv
+    blk = 0
+    for k, s in enumerate(dec):
+        q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = min(int(w.kv_lens[s]), cap)
+        lo, hi = _visible_range(c, G, kvl, ql, 0, ql * G)
+        nb = -(-max(hi - lo, 0) // 16)
+        assert tuple(int(x) for x in ds[k]) == (s, q0, ql, kvl, lo, hi, blk, nb), (k, s)
+        blk += Hkv * nb
+        for h in range(Hkv):
+            for r in range(ql * G):
+                assert (s, h, r) not in owner
+                owner[(s, h, r)] = "dec"
+    Tb, W = P["dec_blocks"], P["W"]
+    assert Tb == blk
+    Wu = P["W_used"]
     assert Wu == max(1, min(W, Tb))
-    waves = di[:, 12]
-    assert np.all(np.diff(waves) >= 0)
-    assert np.all((waves >= 0) & (waves < Wu))
-    blocks = np.zeros(Wu, np.int64)
-    for d in di:
-        blocks[d[12]] += -(-(int(d[3]) - int(d[2])) // 16)
+    if Tb == 0:
+        return
     starts = (Tb * np.arange(Wu + 1, dtype=np.int64)) // Wu
-    assert np.array_equal(blocks, np.diff(starts))
-    for w in range(W):
-        idx = np.nonzero(waves == w)[0]
-        if len(idx) == 0:
-            assert P["wfirst"][w] == np.iinfo(np.int32).max
-        else:
-            assert P["wfirst"][w] == idx[0]
-            assert np.array_equal(idx, np.arange(idx[0], idx[0] + len(idx)))
+    assert np.all(np.diff(starts) >= 1)
+    unit_b0 = np.array([int(r[6]) + h * int(r[7]) for r in ds for h in range(Hkv)], np.int64)
+    unit_nb = np.array([int(r[7]) for r in ds for h in range(Hkv)], np.int64)
+    for wv in range(Wu):
+        a, b = starts[wv], starts[wv + 1]
+        inside = (unit_b0 < b) & (unit_b0 + unit_nb > a)
+        cont = inside & (unit_b0 < a)
+        first_split = inside & (unit_b0 >= a) & (unit_b0 + unit_nb > b)
+        assert cont.sum() <= 1 and first_split.sum() <= 1
+        assert unit_nb[inside].sum() >= 1
 
 
 def _check_queues(P, n_kv_heads):
@@ -94,53 +129,28 @@ def _check(w):
     P = _plan(w)
     c = w.cfg
     G = c.num_q_heads // c.num_kv_heads
-    dec_rows, pf_rows = P["lim"][4], P["lim"][5]
+    dec_rows, pf_rows, ch = P["lim"][4], P["lim"][5], P["pch"]
     owner = {}
-    for cls, units, items, ch in (("dec", P["du"], P["di"], P["dch"]), ("pf", P["pu"], P["pi"], P["pch"])):
-        seen_items = np.zeros(len(items), dtype=int)
-        for ui, (s, h, r0, nr, lo, hi, nch, it0) in enumerate(units):
-            q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = int(w.kv_lens[s])
-            rows = ql * G
-            assert (rows <= dec_rows) == (cls == "dec")
-            assert 1 <= nr <= (dec_rows if cls == "dec" else pf_rows)
-            for r in range(r0, r0 + nr):
-                assert (s, h, r) not in owner
-                owner[(s, h, r)] = cls
-            # visible key range of the unit's rows
-            firsts, lasts = [], []
-            for r in range(r0, r0 + nr):
-                p = kvl - ql + r // G
-                last = p if c.is_causal else kvl - 1
-                first = max(0, p - c.sliding_window + 1) if c.sliding_window else 0
-                firsts.append(first); lasts.append(min(last, kvl - 1))
-            assert lo == (min(firsts) // 16) * 16
-            assert hi == max(lasts) + 1
-            # items tile [lo, hi) exactly (a decode unit with no key has none)
-            if cls == "pf":
-                assert nch == max(1, -(-(hi - lo) // ch))
-            else:
-                assert nch >= (1 if hi > lo else 0) and (nch == 0) == (hi <= lo)
-            for k in range(nch):
-                seen_items[it0 + k] += 1
-                if cls == "pf":
-                    assert tuple(items[it0 + k]) == (ui, k)
-                    a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
-                    assert a < b or (nch == 1 and hi <= lo)
-                    continue
-                d = items[it0 + k]
-                assert (d[10], d[11]) == (ui, k)
-                assert (d[0], d[1], d[7], d[8], d[9]) == (s, h, r0, nr, nch)
-                assert (d[4], d[5], d[6]) == (kvl, q0, ql)
-                # consecutive, 16-aligned boundaries, on consecutive waves
-                a, b = int(d[2]), int(d[3])
-                assert a == (lo if k == 0 else int(items[it0 + k - 1][3]))
-                assert (a - lo) % 16 == 0 and (b == max(hi, lo) if k == nch - 1 else (b - lo) % 16 == 0)
-                assert a < b
-                if k > 0:
-                    assert d[12] == items[it0 + k - 1][12] + 1
-        assert np.all(seen_items == 1), cls
+    _check_decode(P, w, owner)
+    units, items = P["pu"], P["pi"]
+    seen_items = np.zeros(len(items), dtype=int)
+    for ui, (s, h, r0, nr, lo, hi, nch, it0) in enumerate(units):
+        q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = int(w.kv_lens[s])
+        assert ql * G > dec_rows
+        assert 1 <= nr <= pf_rows
+        for r in range(r0, r0 + nr):
+            assert (s, h, r) not in owner
+            owner[(s, h, r)] = "pf"
+        assert (lo, hi) == _visible_range(c, G, kvl, ql, r0, nr)
+        # items tile [lo, hi) exactly
+        assert nch == max(1, -(-(hi - lo) // ch))
+        for k in range(nch):
+            seen_items[it0 + k] += 1
+            assert tuple(items[it0 + k]) == (ui, k)
+            a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
+            assert a < b or (nch == 1 and hi <= lo)
+    assert np.all(seen_items == 1)
     _check_queues(P, c.num_kv_heads)
-    _check_stream_k(P)
     for s in range(w.n_seqs):
         ql = int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])
         for h in range(c.num_kv_heads):
