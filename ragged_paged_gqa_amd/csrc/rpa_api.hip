@@ -57,6 +57,10 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
   p.dec_waves = L.dec_waves;
+  p.dec_blk = (c->kv_dtype == RPA_DTYPE_FP8_E4M3FN || c->kv_dtype == RPA_DTYPE_FP8_E5M2 ||
+               c->kv_dtype == RPA_DTYPE_INT8)
+                  ? kDecBlk8
+                  : kDecBlk16;
   p.dec_part = reinterpret_cast<float*>(w + L.dpart);
   p.dec_plse = reinterpret_cast<float*>(w + L.dplse);
   p.pf_part = reinterpret_cast<float*>(w + L.ppart);

@@ -50,6 +50,7 @@ struct Params {
   int32_t max_dec_units, max_pf_units, max_pf_items;
   int32_t target_pf_items;
   int32_t dec_waves;         // waves of the decode launch (the stream-K split)
+  int32_t dec_blk;           // keys per stream-K block: 16, or 32 for one-byte K/V (kDecBlk)
   const float* sinks;        // [Hq] attention-sink logits, or null
   // numerics
   float sm_scale;      // sm_scale * k_scale

@@ -2,13 +2,14 @@
 // (q_len * G <= 16, e.g. one decode token of 4..16 grouped q heads).
 //
 // The kernel streams K/V from HBM and is bound by it. Work is split
-// stream-K style: the 16-key blocks of all decode units, laid end to end, are
-// cut into one equal contiguous range per wave, so every wave moves the same
-// number of bytes and no queue is needed. The planner writes only one record
+// stream-K style: the key blocks (16 keys; 32 for one-byte K/V) of all decode
+// units, laid end to end, are cut into one equal contiguous range per wave,
+// so every wave moves the same number of bytes and no queue is needed. The planner writes only one record
 // per decode sequence (DecSeq); a wave finds the sequence holding its first
 // block by a 64-way search over the records' first blocks and walks the units
 // from there. It runs its parts (the pieces of units inside its range) as one
-// continuous pipeline of 16-key steps:
+// continuous pipeline of 16-key DMA steps (computed one at a time for 16-bit
+// K/V, two at a time for one-byte K/V):
 //   * loads: each step's K rows and V rows of kv head h (combined heads 2h and
 //     2h+1, adjacent in memory: `stridedLoadKv` on the kernel page) go
 //     straight from HBM into a per-wave ring of LDS slots with
@@ -37,10 +38,12 @@
 //      with ds_read_b64_tr_b16, P^T exactly the S^T result layout. V rows past
 //      kv_len are zeroed first (0 * NaN would otherwise poison the sum).
 // One-byte K/V codes are widened exactly after the LDS read
-// (v_cvt_scalef32_pk_bf16_fp8 / _bf8, or sign extension for int8), V written
-// back as a 16-bit tile into its own ring slot, which is refilled only after
-// the transposed reads; k_scale is folded
-// into the score scale and v_scale into the final normalisation. The
+// (v_cvt_scalef32_pk_bf16_fp8 / _bf8, or sign extension for int8). Their
+// compute step covers 32 keys (two DMA slots): S^T of each 16-key half, one
+// softmax update, then O^T += V^T P^T with v_mfma_f32_16x16x32, V^T read
+// straight out of the two slots with ds_read_b64_tr_b8 and widened in
+// registers; the slots are refilled once those reads are done. k_scale is
+// folded into the score scale and v_scale into the final normalisation. The
 // contraction over head_dim may visit d in any order as long as K and Q use
 // the same one: a lane's 16-byte K piece covers 16 consecutive d for fp8,
 // which become two 8-wide k-slots of the MFMA, and Q is read to match.
@@ -88,15 +91,6 @@ __device__ __forceinline__ int dswz_kv(int key) {
   constexpr int SEG = 2 * D;
   constexpr int RPS = SEG >= 256 ? 1 : 256 / SEG;
   constexpr int CPS = SEG / 16 < 16 ? SEG / 16 : 16;
-  return (key / RPS) & (CPS - 1);
-}
-
-// fp8: chunk swizzle of the bf16 V tile staged in a ring slot (rows of 2D
-// bytes, key = row 0..15).
-template <int D>
-__device__ __forceinline__ int sswz(int key) {
-  constexpr int RPS = 2 * D >= 256 ? 1 : 256 / (2 * D);
-  constexpr int CPS = D / 8 < 16 ? D / 8 : 16;
   return (key / RPS) & (CPS - 1);
 }
 
@@ -148,6 +142,9 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   const uint32_t ring_lds = lds_addr_of(ring);
   const uint32_t qs_lds = lds_addr_of(qs);
 
+  // keys per stream-K block, 16-key DMA steps per compute step
+  constexpr int BK = FP8 ? kDecBlk8 : kDecBlk16, CS = BK / kDecStepKeys;
+  static_assert(NST >= 2 * CS, "a compute step's slots and the next ones fit the ring");
   const int key_stride = 2 * p.Hkv * D * EB;  // bytes between consecutive slots (< 2^26)
   const float sc_mul = p.sm_scale * kLog2e;  // uncapped: straight to base 2
   const SoftCapB2 cap_b2(p.sm_scale, CAP ? p.soft_cap : 1.0f);
@@ -211,8 +208,8 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   };
   auto set_part = [&](Info& I) {
     const int x0 = max(I.b0, ws), x1 = min(I.b0 + I.nb, we);
-    I.c_lo = I.lo16 + 16 * (x0 - I.b0);
-    I.c_hi = max(min(I.hi, I.lo16 + 16 * (x1 - I.b0)), I.c_lo);
+    I.c_lo = I.lo16 + BK * (x0 - I.b0);
+    I.c_hi = max(min(I.hi, I.lo16 + BK * (x1 - I.b0)), I.c_lo);
     I.valid = true;
   };
   // the unit has parts in other ranges too
@@ -277,10 +274,11 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     set_part(N);
     return N;
   };
-  // 16-key steps of a part; an empty key range (only outside the data
-  // preconditions) still takes one fully masked step, so that the load and
-  // compute sides always agree on the step count
-  auto item_steps = [](const Info& I) { return max(1, (I.c_hi - I.c_lo + kDecStepKeys - 1) / kDecStepKeys); };
+  // 16-key DMA steps of a part: whole compute steps of BK keys (the last may
+  // run past c_hi and is masked); an empty key range (only outside the data
+  // preconditions) still takes one fully masked compute step, so that the
+  // load and compute sides always agree on the step count
+  auto item_steps = [](const Info& I) { return CS * max(1, (I.c_hi - I.c_lo + BK - 1) / BK); };
 
   // Q rows of a part, 16 x D bf16, straight into the wave's Q slot (row r =
   // packed row r of the sequence; rows past nrows re-read row 0 and are
@@ -401,88 +399,113 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     vis_hi = min(C.c_hi, cs.kvl);
   };
 
-  // Operands of one 16-key step, read out of its ring slot so that the slot
-  // can be refilled while the step is computed.
+  // Operands of one compute step, read out of its ring slots so that they
+  // can be refilled while the step is computed (bf16: V^T here too; one-byte
+  // K/V: V^T is read from the slots during the step).
   struct Ops {
-    u32x4 k[NLD];                 // K pieces (raw bf16 or fp8)
-    u32x4 v[FP8 ? NLD : 1];       // fp8: V pieces (raw)
+    u32x4 k[CS][NLD];             // K pieces (raw bf16 or one-byte codes) of each 16-key slot
     bf16x4 vt[FP8 ? 1 : ND];      // bf16: V^T operand of each 16-row block of O^T
   };
   // V^T operand layout (ds_read_b64_tr_b16): lane x of group g reads
   // V[4g + x/4][16 d + 4 (x%4) .. + 3] and receives V^T[16 d + x][4g .. 4g + 3]
   const int vkey = 4 * g + (col >> 2);
   const int q4 = col & 3;
-  auto read_ops = [&](int slot, Ops& op) {
-    const char* kr = ring + slot * STAGE;
-    const char* vr = kr + REGION;
-    if constexpr (FP8) {
-      // key col's segment: K chunks 0 .. RB/16 - 1, then V
-      const char* seg = kr + col * (2 * RB);
+  // one-byte V^T (ds_read_b64_tr_b8, measured on gfx950: within a 16-lane
+  // group, lane 8q + b receives byte b of the 8-byte pieces loaded by lanes
+  // q, q + 2, ..., q + 14): lane x of group g loads 8 bytes (d = 16 d0 + 8 (x%2)
+  // .. + 7) of key row j = x/2 of the group's eight keys, so that lane x
+  // receives V^T[16 d0 + x][those eight keys]. The eight keys of group g are
+  // the four whose scores it holds in each 16-key half: keys 4g .. 4g + 3 of
+  // the first slot, then of the second.
+  const int tr_key = 4 * g + ((col >> 1) & 3);  // key row within its slot
+  const int tr_half = col >> 3;                 // 0: first slot, 1: second
+  const int tr_byte = 8 * (col & 1);
+  auto read_ops = [&](int n, Ops& op) {
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        op.k[j] = *reinterpret_cast<const u32x4*>(seg + 16 * ((4 * j + g) ^ dswz_kv<D>(col)));
-        op.v[j] = *reinterpret_cast<const u32x4*>(seg + 16 * ((RB / 16 + 4 * j + g) ^ dswz_kv<D>(col)));
-      }
-    } else {
+    for (int c = 0; c < CS; ++c) {
+      const char* kr = ring + ((n + c) % NST) * STAGE;
+      if constexpr (FP8) {
+        // key col's segment: K chunks 0 .. RB/16 - 1, then V
+        const char* seg = kr + col * (2 * RB);
 #pragma unroll
-      for (int j = 0; j < NLD; ++j)
-        op.k[j] = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
+        for (int j = 0; j < NLD; ++j)
+          op.k[c][j] = *reinterpret_cast<const u32x4*>(seg + 16 * ((4 * j + g) ^ dswz_kv<D>(col)));
+      } else {
+        const char* vr = kr + REGION;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const int chunk = 2 * d + (q4 >> 1);
-        op.vt[d] = lds_read_tr16(
-            reinterpret_cast<const __bf16*>(vr + vkey * RB + 16 * (chunk ^ dswz_v<D, FP8>(vkey)) + 8 * (q4 & 1)));
+        for (int j = 0; j < NLD; ++j)
+          op.k[c][j] = *reinterpret_cast<const u32x4*>(kr + col * RB + 16 * ((4 * j + g) ^ dswz_k<D, FP8>(col)));
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int chunk = 2 * d + (q4 >> 1);
+          op.vt[d] = lds_read_tr16(
+              reinterpret_cast<const __bf16*>(vr + vkey * RB + 16 * (chunk ^ dswz_v<D, FP8>(vkey)) + 8 * (q4 & 1)));
+        }
       }
     }
-    // every read of the slot has completed: it may be refilled
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (!FP8) {
+      // every read of the slot has completed: it may be refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
   };
 
-  // One 16-key step: keys [kb, kb + 16), its rows in ring slot `slot`.
-  auto compute_step = [&](const Ops& op, int kb_in, int slot) {
+  // One compute step: keys [kb, kb + 16 CS), its rows in the ring slots of
+  // DMA steps n .. n + CS - 1. Lane (col, g) holds the scores of keys
+  // kb + 16 c + 4g + j (c < CS, j < 4) of packed row col.
+  auto compute_step = [&](const Ops& op, int kb_in, int n) {
     const int kb = __builtin_amdgcn_readfirstlane(kb_in);  // wave-uniform: scalar mask tests
-    bf16x8 ka[NI];
+    constexpr int NS = 4 * CS;  // scores per lane
+    float sc[NS];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      if constexpr (FP8) {
-        ka[2 * j] = fp8x8_to_16<KVT, F16>(u32x2{op.k[j][0], op.k[j][1]});
-        ka[2 * j + 1] = fp8x8_to_16<KVT, F16>(u32x2{op.k[j][2], op.k[j][3]});
-      } else {
-        ka[j] = __builtin_bit_cast(bf16x8, op.k[j]);
+    for (int c = 0; c < CS; ++c) {
+      bf16x8 ka[NI];
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        if constexpr (FP8) {
+          ka[2 * j] = fp8x8_to_16<KVT, F16>(u32x2{op.k[c][j][0], op.k[c][j][1]});
+          ka[2 * j + 1] = fp8x8_to_16<KVT, F16>(u32x2{op.k[c][j][2], op.k[c][j][3]});
+        } else {
+          ka[j] = __builtin_bit_cast(bf16x8, op.k[c][j]);
+        }
       }
-    }
-    // S^T: lane (col, g) gets keys kb + 4g + j of row `col`
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      // S^T of the slot: lane (col, g) gets keys kb + 16c + 4g + j of row `col`
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) sc = mfma16x16x32<F16>(ka[i], qb[i], sc);
-    if constexpr (Q32) {
+      for (int i = 0; i < NI; ++i) s4 = mfma16x16x32<F16>(ka[i], qb[i], s4);
+      if constexpr (Q32) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) sc = mfma16x16x32<F16>(ka[i], ql[i], sc);
+        for (int i = 0; i < NI; ++i) s4 = mfma16x16x32<F16>(ka[i], ql[i], s4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[4 * c + j] = s4[j];
     }
+    auto key_of = [&](int e) { return kb + 16 * (e >> 2) + 4 * g + (e & 3); };
     // does the step hold a key that some row of the unit cannot see?
-    const bool need_mask = kb + 16 > vis_hi || (p.is_causal && kb + 15 > pos_lo) ||
+    const bool need_mask = kb + 16 * CS > vis_hi || (p.is_causal && kb + 16 * CS - 1 > pos_lo) ||
                            (p.window > 0 && kb <= pos_hi - p.window);
-    // the four scores' chains first (independent, so their latencies
-    // overlap), then the masks in one uniform branch
+    // the scores' chains first (independent, so their latencies overlap),
+    // then the masks in one uniform branch
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int e = 0; e < NS; ++e) {
       if constexpr (CAP) {
-        sc[j] = cap_b2(sc[j]);
+        sc[e] = cap_b2(sc[e]);
       } else {
-        sc[j] = sc[j] * sc_mul;
+        sc[e] = sc[e] * sc_mul;
       }
     }
     if (need_mask) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = kb + 4 * g + j;
+      for (int e = 0; e < NS; ++e) {
+        const int key = key_of(e);
         bool vis = key < vis_hi;
         if (p.is_causal) vis = vis && key <= pos;
         if (p.window > 0) vis = vis && key > pos - p.window;
-        sc[j] = vis ? sc[j] : -INFINITY;
+        sc[e] = vis ? sc[e] : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < NS; ++e) mx = fmaxf(mx, sc[e]);
     mx = wave_max_xor16_32(mx);
     // lazily moved reference maximum
     if (__any(mx > m_ref + kDecSlack)) {
@@ -494,42 +517,40 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       for (int d = 0; d < ND; ++d) o[d] *= alpha;
     }
     const float negm = m_ref == -INFINITY ? 0.f : -m_ref;
-    float pj[4];
+    float pj[NS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pj[j] = fast_exp2(sc[j] + negm);
-      lsum += pj[j];
+    for (int e = 0; e < NS; ++e) {
+      pj[e] = fast_exp2(sc[e] + negm);
+      lsum += pj[e];
     }
-    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{pack2<F16>(pj[0], pj[1]), pack2<F16>(pj[2], pj[3])});
 
     if constexpr (FP8) {
-      // widen V to bf16 (rows past kv_len become 0) and stage it for the
-      // transposed reads
-      bf16x8 vw[2 * NLD];
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        vw[2 * j] = fp8x8_to_16<KVT, F16>(u32x2{op.v[j][0], op.v[j][1]});
-        vw[2 * j + 1] = fp8x8_to_16<KVT, F16>(u32x2{op.v[j][2], op.v[j][3]});
-      }
-      if (kb + 16 > vis_hi) {  // (uniform) the step ends past vis_hi
-        if (kb + col >= vis_hi) {
-#pragma unroll
-          for (int j = 0; j < 2 * NLD; ++j) vw[j] = bf16x8{};
-        }
-      }
-      // the slot's raw rows are in registers: it takes the bf16 tile
-      char* st = ring + slot * STAGE;
-#pragma unroll
-      for (int j = 0; j < 2 * NLD; ++j)
-        *reinterpret_cast<bf16x8*>(st + col * (2 * D) + 16 * ((slot_d<FP8>(j, g) / 8) ^ sswz<D>(col))) = vw[j];
-      wave_sync();
+      // O^T += V^T P^T over the 32 keys with v_mfma_f32_16x16x32: P^T's k-slots
+      // of lane group g are exactly its eight scores; V^T comes transposed out
+      // of the two slots and is widened in registers (keys at or past vis_hi
+      // read as 0: 0 * NaN would poison the sum)
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, u32x4{pack2<F16>(pj[0], pj[1]), pack2<F16>(pj[2], pj[3]), pack2<F16>(pj[4], pj[5]),
+                        pack2<F16>(pj[6], pj[7])});
+      const char* tr_row = ring + ((n + tr_half) % NST) * STAGE + tr_key * (2 * RB) + tr_byte;
+      const bool partial = kb + 32 > vis_hi;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(
-            st + vkey * (2 * D) + 16 * ((2 * d + (q4 >> 1)) ^ sswz<D>(vkey)) + 8 * (q4 & 1)));
-        o[d] = mfma16x16x16<F16>(a, pb, o[d]);
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+        const u32x2 raw = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                       (lds_i32x2*)(tr_row + 16 * ((RB / 16 + d) ^ dswz_kv<D>(tr_key)))));
+        bf16x8 a = fp8x8_to_16<KVT, F16>(raw);
+        if (partial) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key_of(e) >= vis_hi) a[e] = (__bf16)0.f;
+        }
+        o[d] = mfma16x16x32<F16>(a, pb, o[d]);
       }
     } else {
+      const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{pack2<F16>(pj[0], pj[1]), pack2<F16>(pj[2], pj[3])});
       // V of keys at or past vis_hi reads as 0 (0 * NaN would poison the sum)
       const bool partial = kb + 16 > vis_hi;
 #pragma unroll
@@ -621,30 +642,37 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   }
   --ahead;  // the first issued step is the one computed first
   Ops op;
-  for (int n = 0;; ++n) {
-    // this step's rows are in LDS once at most `ahead` later steps are in flight
+  for (int n = 0;; n += CS) {
+    // this compute step's DMA steps n .. n + CS - 1 have landed once at most
+    // `ahead - (CS - 1)` later steps are in flight
     if (ahead == NST - 1) {
-      wait_vmcnt<(NST - 1) * NDMA>();
+      wait_vmcnt<(NST - CS) * NDMA>();
     } else {
       wait_vmcnt<0>();
     }
-    read_ops(n % NST, op);
-    // refill the slot just read (fp8: once its bf16 V tile has been read)
+    read_ops(n, op);
+    // refill the slot just read (one-byte K/V: once the step's transposed V
+    // reads are done as well)
     if (!FP8 && loading) {
       issue_step(L, n % NST);
       ++ahead;
       loader_next();
     }
-    compute_step(op, C.c_lo + steps_done * kDecStepKeys, n % NST);
+    compute_step(op, C.c_lo + steps_done * kDecStepKeys, n);
     if (FP8 && loading) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue_step(L, n % NST);
-      ++ahead;
-      loader_next();
+#pragma unroll
+      for (int c = 0; c < CS; ++c) {
+        if (loading) {
+          issue_step(L, (n + c) % NST);
+          ++ahead;
+          loader_next();
+        }
+      }
     }
-    ++steps_done;
-    ++q_age;
-    --ahead;
+    steps_done += CS;
+    q_age += CS;
+    ahead -= CS;
     if (steps_done == n_steps) {
       finish_item();
       if (!Cn.valid) return;  // the wave's range is done

@@ -82,7 +82,7 @@ bool make_layout(const rpa_config* c, int cus, Layout* L) {
   // and the decode blocks of all units must be countable in int32
   const int64_t dec_waves = (int64_t)dec_grid_for(c, cus) * kDecWavesPerBlock;
   const int64_t dec_slots = 2 * dec_waves;
-  const int64_t max_dec_blocks = max_du * (((int64_t)c->pages_per_seq * c->page_size + 15) / 16);
+  const int64_t max_dec_blocks = max_du * (((int64_t)c->pages_per_seq * c->page_size + kDecBlk16 - 1) / kDecBlk16);
   // prefill chunks are also capped at kPfMaxChunk keys
   const int64_t per_unit_cap = ((int64_t)c->pages_per_seq * c->page_size + kPfMaxChunk - 1) / kPfMaxChunk;
   const int64_t max_pi = max_pu + (tgt_p > max_pu * per_unit_cap ? tgt_p : max_pu * per_unit_cap);

@@ -47,8 +47,8 @@ struct Item {
   int32_t chunk;
 };
 
-// Decode-class work is scheduled stream-K style: the 16-key blocks of all
-// decode units, laid end to end in (sequence, kv head) order, are cut into
+// Decode-class work is scheduled stream-K style: the key blocks (kDecBlk
+// keys) of all decode units, laid end to end in (sequence, kv head) order, are cut into
 // equal contiguous ranges, one per decode wave; each wave runs the parts of
 // the units that fall into its range. The planner writes one record per
 // decode sequence and nothing per part: a wave finds the sequence holding its
@@ -63,9 +63,14 @@ struct DecSeq {
   int32_t lo16;  // first key of its units' block grid (16-aligned)
   int32_t hi;    // one past the last key any of its rows can see
   int32_t blk0;  // its first block in the stream-K order
-  int32_t nb;    // 16-key blocks of each of its units (0: no visible key)
+  int32_t nb;    // blocks of each of its units (0: no visible key)
 };
 static_assert(sizeof(DecSeq) == 32, "decode sequence record is int32[8]");
+// Keys per stream-K block: one 16-key pipeline step for 16-bit K/V; two for
+// one-byte K/V, whose decode waves compute 32 keys per step (so that every
+// part of a unit is a whole number of such steps).
+constexpr int kDecBlk16 = 16;
+constexpr int kDecBlk8 = 32;
 
 // Prefill-class items are queued per XCD (MI355X: 8 XCDs, each with its own
 // L2). All row blocks of one (sequence, kv head) go to the same queue, one
@@ -115,12 +120,7 @@ struct DecCfg {
   static constexpr int NI = D / 32;              // 8-wide k-slots of Q^T per lane (16x16x32 k-steps)
   static constexpr int ND = D / 16;              // 16-row blocks of O^T
   static constexpr int NLD = RB / 64;            // 16-byte K pieces per lane
-  // fp8: V is widened to bf16 in the step's own ring slot once the slot's
-  // raw rows are in registers (16 keys x D bf16 is exactly one slot), and the
-  // slot is refilled after the PV reads. Rows are XOR-swizzled by the key
-  // (sswz), so that the 16-byte writes of 16 keys at one column and the
-  // transposed reads both spread over all banks.
-  // bf16: the next item's 16 Q rows (bf16), DMA'd during the current item.
+  // bf16: the next part's 16 Q rows (bf16), DMA'd during the current part.
   // fp8 takes them into registers instead and spends the space on the ring.
   static constexpr int QSLOT = FP8 ? 0 : 16 * D * 2;
   // fp8 head_dim 256 needs more than 256 registers: one wave per SIMD, so
@@ -129,7 +129,6 @@ struct DecCfg {
   static constexpr int NST_FIT = (BUDGET - QSLOT) / STAGE;
   static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 8 ? 8 : NST_FIT);  // ring slots
   static constexpr int WAVE_LDS = NST * STAGE + QSLOT;
-  static_assert(!FP8 || 16 * D * 2 == STAGE, "fp8: the bf16 V tile fills one slot");
   static_assert(REGION % 1024 == 0, "whole 1 KB DMA instructions per region");
   static_assert(WAVE_LDS * kDecWavesPerBlock <= 160 * 1024, "LDS of a workgroup");
   static_assert((NST - 1) * NDMA < 64, "vmcnt range");

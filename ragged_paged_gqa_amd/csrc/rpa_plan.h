@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     int32_t nb = 0;
     if (is_dec) {
       dr = unit_range(p, G, ql, kvl, 0, ql * p.G);
-      nb = (range_keys(dr) + 15) / 16;
+      nb = (range_keys(dr) + p.dec_blk - 1) / p.dec_blk;
       cnt[0] = p.Hkv;
       cnt[2] = p.Hkv * nb;
     } else if (slot >= 0) {

@@ -64,6 +64,8 @@ def _check_decode(P, w, owner):
     G = c.num_q_heads // c.num_kv_heads
     Hkv = c.num_kv_heads
     cap = c.pages_per_seq * c.page_size
+    # keys per stream-K block: 32 for one-byte K/V, else 16
+    bk = 32 if wl.is_fp8(c.kv_dtype) else 16
     dec = [s for s in range(int(w.num_seqs[0]))
            if 0 < int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s]) and
            (int(w.cu_q_lens[s + 1]) - int(w.cu_q_lens[s])) * G <= P["lim"][4]]
@@ -73,7 +75,7 @@ def _check_decode(P, w, owner):
     for k, s in enumerate(dec):
         q0 = int(w.cu_q_lens[s]); ql = int(w.cu_q_lens[s + 1]) - q0; kvl = min(int(w.kv_lens[s]), cap)
         lo, hi = _visible_range(c, G, kvl, ql, 0, ql * G)
-        nb = -(-max(hi - lo, 0) // 16)
+        nb = -(-max(hi - lo, 0) // bk)
         assert tuple(int(x) for x in ds[k]) == (s, q0, ql, kvl, lo, hi, blk, nb), (k, s)
         blk += Hkv * nb
         for h in range(Hkv):
@@ -167,7 +169,7 @@ def test_plan_named_tiny():
     _check(wl.named(1))
 
 
-@pytest.mark.parametrize("number", [2, 3, 5])
+@pytest.mark.parametrize("number", [2, 3, 4, 5])
 def test_plan_named_lengths(number):
     # lengths of the large workloads, with a 1-page cache: the plan reads metadata only
     rng = np.random.Generator(np.random.PCG64(number))
