@@ -88,6 +88,11 @@ MEDIUM = [
          fp8=True, cap=50.0, window=1024),
     dict(name="noncausal-long", q_lens=[50, 2], kv_lens=[1200, 2222], Hq=4, Hkv=1, D=128, page=16,
          causal=False),
+    # one-byte K/V: decode units of two kv heads, with an odd head count (the
+    # last unit has one head) and with a single head
+    dict(name="fp8-odd-heads", q_lens=[1, 2, 1, 1], kv_lens=[3100, 900, 2047, 33], Hq=12, Hkv=3, D=128, page=16,
+         fp8=True),
+    dict(name="fp8-one-head", q_lens=[1, 1, 3], kv_lens=[2900, 40, 1500], Hq=4, Hkv=1, D=128, page=16, fp8=True),
 ]
 
 
