@@ -142,6 +142,11 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 __device__ __forceinline__ int32_t wave_max(int32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -157,9 +162,10 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
   return v;
 }
 
-// Per-sequence counts (scan slots): 0 decode units, 1 prefill units,
-// 2 decode items, 3 prefill items, 4 split units, 5.. prefill items per queue
-constexpr int kScanN = 5 + kQueues;
+// Per-sequence counts of the main scan: 0 decode units, 1 prefill units,
+// 2 decode blocks, 3 prefill items, 4 split units. The prefill items per queue
+// take a second scan, over the tile's prefill sequences heaviest first.
+constexpr int kScanN = 5;
 
 // Per prefill sequence of a tile, filled by its wave.
 struct PfInfo {
@@ -167,6 +173,7 @@ struct PfInfo {
   int32_t per_head;  // items of one kv head
   int32_t nsplit;    // row blocks with more than one chunk
   int32_t max_nch;   // most chunks of one row block
+  int64_t work;      // visible keys of its row blocks (one kv head)
 };
 
 // Offsets of a prefill sequence's records, from the block scan.
@@ -177,9 +184,10 @@ struct PfOffs {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ int64_t red[kPlanWaves];
-  __shared__ int32_t sh[kPlanWaves * kScanN];
+  __shared__ int32_t sh[kPlanWaves * kQueues];
   __shared__ int32_t n_pf_tile;
   __shared__ PfInfo pf_info[kPlanThreads];
+  __shared__ int32_t by_rank[kPlanThreads];  // prefill slots of the tile, heaviest sequence first
   __shared__ PfOffs pf_offs[kPlanThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t n = *p.num_seqs;
@@ -226,9 +234,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   const FastDiv pf_chunk = make_div(pick_chunk(tot_pf, p.target_pf_items, kPfMinChunk, kPfMaxChunk));
 
   // pass 2: per-sequence counts -> one scan per tile -> records
-  int32_t base[kScanN];
+  int32_t base[kScanN], base_q[kQueues];
 #pragma unroll
   for (int k = 0; k < kScanN; ++k) base[k] = 0;
+#pragma unroll
+  for (int x = 0; x < kQueues; ++x) base_q[x] = 0;
   for (int32_t s0 = 0; s0 < n; s0 += kPlanThreads) {
     if (tid == 0) n_pf_tile = 0;
     __syncthreads();
@@ -244,19 +254,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       seq_meta(p, ps, pql, pkvl);
       const int32_t rows = pql * p.G;
       int32_t items = 0, nsplit = 0, max_nch = 0;
+      int64_t work = 0;
       for (int32_t r0 = lane * R; r0 < rows; r0 += 64 * R) {
-        const int32_t nch = n_chunks(unit_range(p, G, pql, pkvl, r0, min(R, rows - r0)), pf_chunk);
+        const UnitRange r = unit_range(p, G, pql, pkvl, r0, min(R, rows - r0));
+        const int32_t nch = n_chunks(r, pf_chunk);
         items += nch;
         nsplit += nch > 1;
         max_nch = max(max_nch, nch);
+        work += range_keys(r);
       }
       items = wave_sum(items);
       nsplit = wave_sum(nsplit);
       max_nch = wave_max(max_nch);
+      work = wave_sum64(work);
       if (lane == 0) {
         pf_info[i].per_head = items;
         pf_info[i].nsplit = nsplit;
         pf_info[i].max_nch = max_nch;
+        pf_info[i].work = work;
       }
     }
     __syncthreads();
@@ -278,11 +293,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       cnt[1] = p.Hkv * nrb;
       cnt[3] = p.Hkv * f.per_head;
       cnt[4] = p.Hkv * f.nsplit;
-      for (int32_t h = 0; h < p.Hkv; ++h) {
-        const int x = (s * p.Hkv + h) % kQueues;
-#pragma unroll
-        for (int k = 0; k < kQueues; ++k) cnt[5 + k] += x == k ? f.per_head : 0;
-      }
     }
     int32_t off[kScanN], tot[kScanN];
     block_scan<kScanN>(cnt, off, tot, sh);
@@ -294,8 +304,42 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     if (slot >= 0) {
       pf_offs[slot].unit = off[1];
       pf_offs[slot].item = off[3];
+    }
+    // queue offsets: the tile's prefill sequences take their places in the
+    // queues heaviest first (visible keys; ties by sequence index), so that
+    // the longest items start first and the queues drain evenly; a sequence's
+    // entries in a queue stay contiguous and chunk-major
+    if (n_pf_tile > 0) {  // (block-uniform)
+      if (slot >= 0) {
+        const int64_t wk = pf_info[slot].work;
+        int32_t r = 0;
+        for (int32_t j = 0; j < n_pf_tile; ++j) {
+          const int64_t wj = pf_info[j].work;
+          r += wj > wk || (wj == wk && pf_info[j].s < s);
+        }
+        by_rank[r] = slot;
+      }
+      __syncthreads();
+      int32_t qc[kQueues];
 #pragma unroll
-      for (int x = 0; x < kQueues; ++x) pf_offs[slot].queue[x] = off[5 + x];
+      for (int x = 0; x < kQueues; ++x) qc[x] = 0;
+      const int32_t rs = tid < n_pf_tile ? by_rank[tid] : -1;
+      if (rs >= 0) {
+        const PfInfo& f = pf_info[rs];
+        for (int32_t h = 0; h < p.Hkv; ++h) {
+          const int x = (f.s * p.Hkv + h) % kQueues;
+#pragma unroll
+          for (int k = 0; k < kQueues; ++k) qc[k] += x == k ? f.per_head : 0;
+        }
+      }
+      int32_t qo[kQueues], qt[kQueues];
+      block_scan<kQueues>(qc, qo, qt, sh);
+      if (rs >= 0) {
+#pragma unroll
+        for (int x = 0; x < kQueues; ++x) pf_offs[rs].queue[x] = base_q[x] + qo[x];
+      }
+#pragma unroll
+      for (int x = 0; x < kQueues; ++x) base_q[x] += qt[x];
     }
 
     // (c) a decode sequence's record, at its rank among the decode sequences
@@ -399,7 +443,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     h.pad0[0] = max(1, min(max(p.dec_waves, 1), base[2]));
     for (int x = 0; x < kQueues; ++x) {
       h.pf_q_base[x] = x * p.max_pf_items;
-      h.pf_q_count[x] = max(0, min(base[5 + x], p.max_pf_items));
+      h.pf_q_count[x] = max(0, min(base_q[x], p.max_pf_items));
       h.pf_q_next[x] = 0;
     }
     *p.hdr = h;

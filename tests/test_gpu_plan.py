@@ -125,6 +125,22 @@ def _check_queues(P, n_kv_heads):
             last[(s, h)] = key
     allq = np.concatenate(entries) if entries else np.zeros(0, np.int32)
     assert np.array_equal(np.sort(allq), np.arange(n_pi))
+    # within a queue the sequences come heaviest first (the visible keys of
+    # their units of one kv head; ties by sequence index) while the plan has
+    # one tile of sequences
+    work = {}
+    for s_, h_, r0_, nr_, lo_, hi_, nch_, it0_ in P["pu"]:
+        if h_ == 0:
+            work[int(s_)] = work.get(int(s_), 0) + max(int(hi_) - int(lo_), 0)
+    if len(P["pu"]) and max(work) < 512:
+        for q in entries:
+            order = []
+            for it in q:
+                s_ = int(P["pu"][P["pi"][it][0]][0])
+                if not order or order[-1] != s_:
+                    order.append(s_)
+            keys = [(-work[s_], s_) for s_ in order]
+            assert keys == sorted(keys)
 
 
 def _check(w):
