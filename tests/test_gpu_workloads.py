@@ -8,9 +8,10 @@ sharpened copy (Q x 8, exact in bf16) that makes the softmax peaky, so that
 * decode batch and fp8 decode: every row (all q heads of every token);
 * mixed batch: every row of the 56 decode sequences and of two whole
   448-token prefill chunks (sharpened: the decode rows and one chunk);
-* long context: all q heads of 64 seeded random tokens, and every row of one
-  whole 128-token sequence (sharpened: all q heads of the first and last
-  token of two sequences and 192 random (token, head) pairs);
+* long context: all q heads of 128 seeded random tokens, and every row of two
+  whole 128-token sequences, the longest and the shortest context (sharpened:
+  all q heads of the first and last token of two sequences and 192 random
+  (token, head) pairs);
 * attention sinks at full size: the decode batch with seeded sinks, every row.
 """
 
@@ -96,8 +97,12 @@ def test_long_context_random_tokens_all_heads():
     w = wl.named(5)
     d = Device(w)
     rng = np.random.default_rng(5)
-    tokens, heads = _all_heads(w, np.sort(rng.choice(w.valid_tokens(), size=64, replace=False)))
-    _check_rows(w, d, tokens, heads, "cfg5 all heads of 64 random tokens")
+    tokens, heads = _all_heads(w, np.sort(rng.choice(w.valid_tokens(), size=128, replace=False)))
+    _check_rows(w, d, tokens, heads, "cfg5 all heads of 128 random tokens")
+    # the sequence with the shortest context, whole
+    s = int(np.argmin(w.kv_lens[:w.n_seqs]))
+    tokens, heads = _all_heads(w, _seq_tokens(w, s))
+    _check_rows(w, d, tokens, heads, f"cfg5 every row of sequence {s}")
     _done(d)
 
 
