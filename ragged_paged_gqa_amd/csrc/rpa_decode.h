@@ -750,7 +750,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
     U.nch = l - f + 1;
     U.item0 = 0;
     // part c ran on wave f + c: the first in slot 2f + 1, the others in 2(f + c)
-    merge_unit<D, F16, Q32>(p, U, p.dec_part, p.dec_plse, kDecRows,
+    merge_unit<D, F16, Q32, true>(p, U, p.dec_part, p.dec_plse, kDecRows,
                             [&](int c) { return c == 0 ? 2 * f + 1 : 2 * (f + c); }, lane, 64, stat[wave],
                             wave_sync);
     wave_sync();

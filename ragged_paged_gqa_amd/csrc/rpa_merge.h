@@ -27,8 +27,11 @@ namespace rpa {
 // Chunk c of the unit left its partial in slot `slot(c)` of `part` / `plse`
 // (slot_rows rows each). Threads tid in [0, nt) cooperate; `sync` is called
 // between the phases and must synchronise exactly those threads. `stat` is
-// LDS scratch of 2 * u.nrows floats.
-template <int D, bool F16, bool Q32, typename Slot, typename Sync>
+// LDS scratch of 2 * u.nrows floats. BATCH: issue the loads of several chunks
+// before reducing them (the combine kernel, where each wave's merge is one
+// long chain of loads); the prefill kernels' last finishers keep the plain
+// loops, which need fewer registers beside their main loop's.
+template <int D, bool F16, bool Q32, bool BATCH, typename Slot, typename Sync>
 __device__ void merge_unit(const Params& p, const Unit& u, const float* part, const float* plse, int slot_rows,
                            Slot slot, int tid, int nt, float* stat, Sync sync) {
   int q0, ql;
@@ -38,7 +41,7 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
   // long latency): each pass issues a batch of independent loads before it
   // reduces them, always in chunk order, so the sums do not depend on the
   // batching.
-  constexpr int BA = 8, BB = 4;
+  constexpr int BA = BATCH ? 8 : 1, BB = BATCH ? 4 : 1;
   // phase A: per-row max and 1 / sum of exp(L_c - max)
   for (int r = tid; r < u.nrows; r += nt) {
     const int prow = u.row0 + r;

@@ -718,7 +718,7 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
         // the LDS ring is idle here (every wave is past its last step); it
         // holds the per-row stats of the merge
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D, F16, Q32>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
+        merge_unit<D, F16, Q32, false>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
                                 reinterpret_cast<float*>(lds), wg_sync);
       }
     }

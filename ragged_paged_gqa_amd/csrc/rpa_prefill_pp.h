@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void prefill_pp_kernel(Params p) 
         // the ring is idle (every wave is past its last phase); it holds the
         // merge's per-row statistics
         auto wg_sync = [] { __syncthreads(); };
-        merge_unit<D, F16, false>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
+        merge_unit<D, F16, false, false>(p, u, p.pf_part, p.pf_plse, p.pf_rows, [&](int c) { return u.item0 + c; }, tid, NT,
                                   reinterpret_cast<float*>(lds), wg_sync);
       }
     }
