@@ -22,6 +22,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                 evicting L2 and the 256 MB Infinity Cache): median, p10, p90
   configs       the same measurements for every other named workload, with a
                 call-level and a kernel-level roofline fraction
+  practical_ceilings
+                what the chip sustains in the same session outside this
+                library (a read-only stream, a dense bf16 matmul), and the
+                headline kernel's rate as a fraction of the matching one
   cpu_baseline  the f64 CPU oracle timed on a bounded sample of the headline
                 workload on the host cores (a reported baseline, not a target)
 
@@ -238,6 +242,42 @@ def summarize_trace(stats_csv: str) -> str:
     for name, calls, avg, mn, mx, pct in sorted(rows, key=lambda x: -x[5]):
         out.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} % |")
     return "\n".join(out)
+
+
+def practical_ceilings(torch) -> dict:
+    """What the chip sustains in this session outside this library, as context
+    for the roofline fractions (taken against the nominal peaks): a read-only
+    stream (torch's row sums of a 65536-row view of 4 GiB of f32: of the torch
+    reductions tried, the one that reads fastest) and a dense bf16 matrix
+    product (torch.matmul, 8192 x 8192 x 8192, contiguous operands). Best of 5
+    after a warm-up, HIP events."""
+    def best_ms(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+    n = 1 << 30  # f32 elements: 4 GiB
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    t_read = best_ms(lambda: x.view(65536, -1).sum(dim=1))
+    del x
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    t_mm = best_ms(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    read_gbs = 4.0 * n / (t_read * 1e-3) / 1e9
+    mm_tflops = 2.0 * m * m * m / (t_mm * 1e-3) / 1e12
+    return {"read_stream_gbs": round(read_gbs, 1), "bf16_matmul_tflops": round(mm_tflops, 1),
+            "how": "best of 5 (HIP events): torch row sums over 4 GiB f32 (read-only), "
+                   "torch.matmul 8192^3 bf16"}
 
 
 def stats(samples_ms) -> dict:
@@ -531,6 +571,13 @@ def main():
             del r
     if len(configs) > 1:
         result["configs"] = configs
+    log("[bench] practical ceilings (read stream, bf16 matmul)")
+    ceil = practical_ceilings(torch)
+    if roof.get("unit") == "TFLOP/s":
+        ceil["roofline_frac_of_practical"] = round(roof["achieved"] / ceil["bf16_matmul_tflops"], 4)
+    else:
+        ceil["roofline_frac_of_practical"] = round(roof["achieved"] / ceil["read_stream_gbs"], 4)
+    result["practical_ceilings"] = ceil
     if cpu_w is not None:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(cpu_w)
