@@ -103,7 +103,7 @@ __device__ __forceinline__ int slot_d(int i, int g) {
 }
 
 // Scalar (SMEM) loads of metadata the kernel never writes: page-table entries
-// and item descriptors go to scalar registers through the scalar cache and
+// and sequence records go to scalar registers through the scalar cache and
 // never wait on (or make anything wait on) the K/V stream.
 typedef const __attribute__((address_space(4))) int32_t cint32;
 __device__ __forceinline__ int sload(const int32_t* ptr) { return *(cint32*)(ptr); }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * Cf::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
-  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: the loader and item logic stay scalar
+  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: the loader and part logic stay scalar
   const int col = lane & 15;
   const int g = lane >> 4;
   char* wl = lds + wave * Cf::WAVE_LDS;       // this wave's LDS: ring slots, then the Q slot
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     }
   };
   // fp8 and f32 q: the same operand straight from global memory (row col of
-  // the item; rows past nrows re-read row 0 and are zeroed); an f32 q also
+  // the part; rows past nrows re-read row 0 and are zeroed); an f32 q also
   // gives its lo part (split_q8)
   auto load_q = [&](const Info& I, bf16x8 (&qr)[NI], bf16x8 (&qlr)[Q32 ? NI : 1]) {
     const Seq m = seq_of(I);
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     }
   };
 
-  // ---- loader: the item whose steps are being loaded ----
+  // ---- loader: the part whose steps are being loaded ----
   struct Loader {
     int s;      // sequence (its page-table row)
     int hoff;   // byte offset of combined head 2h in a slot
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     }
   };
 
-  // Result of the current item: bf16 out + lse, or an f32 partial + lse.
+  // Result of the current part: bf16 out + lse, or an f32 partial + lse.
   auto finish_item = [&]() {
     const float l_row = wave_sum_xor16_32(lsum);
     float inv, lse_v;
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
     }
   };
 
-  // ---- the wave's items, one continuous pipeline ----
+  // ---- the wave's parts, one continuous pipeline ----
   if (w >= W || w >= p.dec_waves || n_dseq <= 0 || sk.Tb <= 0) return;
   ws = uni(sk.start(w));
   we = uni(sk.start(w + 1));
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   if (!C.valid) return;
   cs = seq_of(C);
   Info Cn = next_info(C);  // the compute side's next part
-  bf16x8 qn[QREG ? NI : 1];        // fp8, f32 q: the next item's Q operand, loaded ahead
+  bf16x8 qn[QREG ? NI : 1];        // fp8, f32 q: the next part's Q operand, loaded ahead
   bf16x8 qnl[Q32 ? NI : 1];        // f32 q: its lo part
   if constexpr (QREG) {
     load_q(C, qb, ql);
@@ -617,9 +617,9 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   begin_item();
 
   Loader L = loader_for(C);
-  Info Ln = Cn;          // the load side's next item
+  Info Ln = Cn;          // the load side's next part
   bool loading = true;   // the load side still has steps to issue
-  // Moves the load side to its next step: the same item, or the next of the wave.
+  // Moves the load side to its next step: the same part, or the next of the wave.
   auto loader_next = [&]() {
     if (L.left > 0) return;
     if (Ln.valid) {
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
         if (Cn.valid) load_q(Cn, qn, qnl);
       } else {
         // the Q slot's DMA is complete once a wait above covered a step
-        // issued after it (NST + 1 steps later); for short items wait here
+        // issued after it (NST + 1 steps later); for short parts wait here
         if (q_age <= NST) wait_vmcnt<0>();
         wave_sync();
         read_q(cs.nrows, qb);
