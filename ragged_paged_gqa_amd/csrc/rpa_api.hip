@@ -1,7 +1,9 @@
 // C ABI of the ragged paged GQA attention library: host-side validation,
-// workspace carving and the launch sequence (plan -> prefill tiles -> decode
-// tiles; split units are merged inside the tile kernels), all on the caller's
-// stream.
+// workspace carving and the launch sequence, all on the caller's stream: the
+// plan, the tiles of both classes (one launch; two in turn, prefill then
+// decode, where the prefill runs on the two-group kernel), and the merge of
+// split decode units. (A split prefill unit is merged inside the prefill
+// tiles.)
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -19,6 +21,7 @@
 #include "rpa_plan.h"
 #include "rpa_prefill.h"
 #include "rpa_prefill_pp.h"
+#include "rpa_tiles.h"
 
 namespace {
 
@@ -57,6 +60,8 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.pf_qlist = reinterpret_cast<int32_t*>(w + L.qlist);
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
   p.dec_waves = L.dec_waves;
+  p.dec_per_cu = dec_grid_for(c, 1);
+  p.fused = uses_pp(c) ? 0 : 1;
   p.dec_blk = (c->kv_dtype == RPA_DTYPE_FP8_E4M3FN || c->kv_dtype == RPA_DTYPE_FP8_E5M2 ||
                c->kv_dtype == RPA_DTYPE_INT8)
                   ? kDecBlk8
@@ -89,8 +94,10 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
 
 rpa_status check_launch() { return hipGetLastError() == hipSuccess ? RPA_OK : RPA_ERR_HIP; }
 
-// Optional event timing of the four launches of each call (for benchmarks):
-// events before plan, prefill, decode and combine, and after combine.
+// Optional event timing of the launches of each call (for benchmarks):
+// events before the plan, after it, after the first and the second tile
+// launch (the second one only where the classes run in turn), and after the
+// merge.
 struct Profiler {
   std::mutex mu;
   std::atomic<bool> on{false};  // read without the lock on every forward call
@@ -105,49 +112,71 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev[k], st);
 }
 
+// Prefill-class workgroups of a launch: the two-group kernel runs one per
+// compute unit, the 4-wave kernel as many as its LDS and registers allow;
+// never more than there are items.
+template <int D, bool FP8, bool PP>
+int prefill_grid(const Params& p, int cus) {
+  int per_cu = 1;
+  if constexpr (!PP) {
+    constexpr int by_lds = (int)((160 * 1024) / sizeof(PfShared<D, FP8>));
+    per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
+    if (per_cu < 1) per_cu = 1;
+  }
+  int grid = cus * per_cu;
+  if (grid > p.max_pf_items) grid = p.max_pf_items;
+  return grid < 1 ? 1 : grid;
+}
+
+template <int D, bool F16, bool Q32>
+rpa_status launch_combine(const Params& p, int cus, hipStream_t st) {
+  // merge of the split decode units (a wave per unit, grid-stride)
+  int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
+  if (cgrid > cus * 4) cgrid = cus * 4;
+  if (cgrid < 1) cgrid = 1;
+  hipLaunchKernelGGL((combine_kernel<D, F16, Q32>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+  return check_launch();
+}
+
+// The launches after the plan. Where the prefill class runs on the two-group
+// kernel (eight waves, a workgroup per compute unit), its launch and the
+// decode-class launch run in turn; everywhere else one launch holds the
+// workgroups of both classes (tiles_kernel). Then the merge.
 template <int D, int KVT, bool F16, bool Q32>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   constexpr bool FP8 = KVT != kKvBf16;
+  // the decode launch's workgroups: the waves of the stream-K split (those
+  // the planner gives no work exit at once)
+  const int dec_wgs = p.dec_waves / kDecWavesPerBlock;
+  if (dec_wgs < 1) return RPA_ERR_HIP;
   if constexpr (!FP8 && !Q32 && D >= RPA_PP_MIN_D && D <= RPA_PP_MAX_D) {
-    // one workgroup of 8 waves per CU
-    int grid = cus < p.max_pf_items ? cus : p.max_pf_items;
-    if (grid < 1) grid = 1;
+    const int grid = prefill_grid<D, FP8, true>(p, cus);
     if (p.soft_cap > 0.f)
       hipLaunchKernelGGL((prefill_pp_kernel<D, true, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
     else
       hipLaunchKernelGGL((prefill_pp_kernel<D, false, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 2, st);
-  } else {
-    constexpr int by_lds = (int)((160 * 1024) / (PrefillLds<D, FP8>::kBytes + 4 * kPfBlkTable + 64));
-    constexpr int per_cu = pf_wgs_per_cu(D) < by_lds ? pf_wgs_per_cu(D) : by_lds;
-    int grid = cus * (per_cu > 0 ? per_cu : 1);
-    if (grid > p.max_pf_items) grid = p.max_pf_items;
-    if (grid < 1) grid = 1;
     if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((prefill_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, true, F16, Q32>), dim3(dec_wgs), dim3(kDecWavesPerBlock * 64), 0, st,
+                         p);
     else
-      hipLaunchKernelGGL((prefill_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kPfWaves * 64), 0, st, p);
-    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 2, st);
-  }
-  {
-    // exactly the waves the planner split the decode work over
-    const int grid = p.dec_waves / kDecWavesPerBlock;
-    if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((decode_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+      hipLaunchKernelGGL((decode_kernel<D, KVT, false, F16, Q32>), dim3(dec_wgs), dim3(kDecWavesPerBlock * 64), 0, st,
+                         p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
-    // merge of the split decode units (a wave per unit, grid-stride)
-    int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
-    if (cgrid > cus * 4) cgrid = cus * 4;
-    if (cgrid < 1) cgrid = 1;
-    hipLaunchKernelGGL((combine_kernel<D, F16, Q32>), dim3(cgrid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+  } else {
+    const int grid = dec_wgs + prefill_grid<D, FP8, false>(p, cus);
+    if (p.soft_cap > 0.f)
+      hipLaunchKernelGGL((tiles_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((tiles_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 4, st);
+    prof_record(ev, 2, st);
+    prof_record(ev, 3, st);
   }
+  if (launch_combine<D, F16, Q32>(p, cus, st) != RPA_OK) return RPA_ERR_HIP;
+  prof_record(ev, 4, st);
   return RPA_OK;
 }
 
@@ -244,23 +273,7 @@ void* scratch_ptr() {
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes) {
-  if (!bytes) return RPA_ERR_INVALID_ARGUMENT;
-  rpa_status st = validate(cfg);
-  if (st != RPA_OK) return st;
-  int cus = 0;
-  if (!device_cus(&cus)) return RPA_ERR_HIP;
-  Layout L;
-  if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
-  *bytes = L.total;
-  return RPA_OK;
-}
-
-static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspace_bytes, Params* p, int* cus_out) {
+rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspace_bytes, Params* p, int* cus_out) {
   rpa_status st = validate(cfg);
   if (st != RPA_OK) return st;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RPA_ERR_INVALID_ARGUMENT;
@@ -279,17 +292,12 @@ static rpa_status prepare(const rpa_config* cfg, void* workspace, size_t workspa
   return RPA_OK;
 }
 
-rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
-                       const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
-                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return rpa_forward_sinks(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, nullptr, out, lse, workspace,
-                           workspace_bytes, stream);
-}
-
-rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
-                             const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
-                             const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+// The forward call: checks, then the plan and the attention launches on
+// `stream`.
+rpa_status forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                   const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                   const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (!q || !kv_pages || !kv_lens || !page_indices || !cu_q_lens || !num_seqs || !out)
     return RPA_ERR_INVALID_ARGUMENT;
   // the kernels move q, K/V and out in 16-byte pieces and lse / sinks as f32
@@ -329,6 +337,37 @@ rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* k
   }
 }
 
+}  // namespace
+
+extern "C" {
+
+rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes) {
+  if (!bytes) return RPA_ERR_INVALID_ARGUMENT;
+  rpa_status st = validate(cfg);
+  if (st != RPA_OK) return st;
+  int cus = 0;
+  if (!device_cus(&cus)) return RPA_ERR_HIP;
+  Layout L;
+  if (!make_layout(cfg, cus, &L)) return RPA_ERR_INVALID_ARGUMENT;
+  *bytes = L.total;
+  return RPA_OK;
+}
+
+rpa_status rpa_forward(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                       const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return rpa_forward_sinks(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, nullptr, out, lse, workspace,
+                           workspace_bytes, stream);
+}
+
+rpa_status rpa_forward_sinks(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
+                             const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
+                             const float* sinks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return forward(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, sinks, out, lse, workspace,
+                 workspace_bytes, stream);
+}
+
 rpa_status rpa_forward_noalloc(const rpa_config* cfg, const void* q, const void* kv_pages, const int32_t* kv_lens,
                                const int32_t* page_indices, const int32_t* cu_q_lens, const int32_t* num_seqs,
                                const float* sinks, void* out, float* lse, void* stream) {
@@ -342,8 +381,8 @@ rpa_status rpa_forward_noalloc(const rpa_config* cfg, const void* q, const void*
   if (!ws) return RPA_ERR_HIP;
   // the planning kernel rewrites every record, counter and queue head the
   // attention kernels read, so nothing is cleared here
-  return rpa_forward_sinks(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, sinks, out, lse, ws,
-                           kScratchBytes, stream);
+  return forward(cfg, q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, sinks, out, lse, ws, kScratchBytes,
+                 stream);
 }
 
 rpa_status rpa_profile_begin(int32_t max_calls) {
@@ -370,11 +409,11 @@ rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on) return RPA_ERR_INVALID_ARGUMENT;
   rpa_status st = RPA_OK;
-  for (int k = 0; k < kProfEvents - 1; ++k) kernel_ms[k] = 0.f;
+  for (int k = 0; k < 4; ++k) kernel_ms[k] = 0.f;
   if (g_prof.n_calls > 0 && hipEventSynchronize(g_prof.ev[kProfEvents * g_prof.n_calls - 1]) != hipSuccess)
     st = RPA_ERR_HIP;
   for (int c = 0; c < g_prof.n_calls && st == RPA_OK; ++c) {
-    for (int k = 0; k < kProfEvents - 1; ++k) {
+    for (int k = 0; k < 4; ++k) {
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, g_prof.ev[kProfEvents * c + k], g_prof.ev[kProfEvents * c + k + 1]) !=
           hipSuccess) {

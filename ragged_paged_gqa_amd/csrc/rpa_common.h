@@ -51,6 +51,8 @@ struct Params {
   int32_t target_pf_items;
   int32_t dec_waves;         // waves of the decode launch (the stream-K split)
   int32_t dec_blk;           // keys per stream-K block: 16, or 32 for one-byte K/V (kDecBlk)
+  int32_t dec_per_cu;        // decode workgroups resident per compute unit
+  int32_t fused;             // 1: one launch holds the workgroups of both classes (tiles_kernel)
   const float* sinks;        // [Hq] attention-sink logits, or null
   // numerics
   float sm_scale;      // sm_scale * k_scale

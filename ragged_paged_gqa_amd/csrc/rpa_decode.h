@@ -119,18 +119,18 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                      0, 0);
 }
 
-// CAP: the soft-cap is on (a template parameter, so the uncapped kernel
-// carries no cap arithmetic at all).
+// The decode-class tiles of one workgroup (`block`: its index among the
+// decode workgroups), in the workgroup's LDS `lds` (kDecWavesPerBlock *
+// WAVE_LDS bytes, 1 KB aligned). CAP: the soft-cap is on (a template
+// parameter, so the uncapped code carries no cap arithmetic at all).
 template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
-__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
-    Params p) {
+__device__ __forceinline__ void decode_tiles(const Params& p, char* lds, int block) {
   constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8)
   constexpr bool QREG = FP8 || Q32;     // Q operand loaded into registers (no LDS Q slot)
   static_assert(!(Q32 && F16), "an f32 q runs on the bf16 path");
   using Cf = DecCfg<D, FP8>;
   constexpr int EB = Cf::EB, RB = Cf::RB, REGION = Cf::REGION, STAGE = Cf::STAGE, NDR = Cf::NDR,
                 NDMA = Cf::NDMA, NI = Cf::NI, ND = Cf::ND, NLD = Cf::NLD, NST = Cf::NST;
-  __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * Cf::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);  // wave-uniform: the loader and part logic stay scalar
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
   };
 
   // ---- the wave's range of the stream-K split, and its parts ----
-  const int w = blockIdx.x * kDecWavesPerBlock + wave;  // stream-K rank
+  const int w = block * kDecWavesPerBlock + wave;  // stream-K rank
   const int n_dseq = uni(p.hdr->n_dec_seqs);
   const int W = uni(p.hdr->pad0[0]);
   const StreamK sk = StreamK::make(uni(p.hdr->dec_blocks), W);
@@ -701,6 +701,15 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT !
       begin_item();
     }
   }
+}
+
+// The decode-class tiles in a launch of their own (one workgroup per
+// decode-workgroup index).
+template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
+__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
+    Params p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * DecCfg<D, KVT != kKvBf16>::WAVE_LDS];
+  decode_tiles<D, KVT, CAP, F16, Q32>(p, lds, blockIdx.x);
 }
 
 // Merges the split decode-class units once every decode wave is done: one

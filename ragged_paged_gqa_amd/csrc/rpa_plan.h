@@ -162,6 +162,41 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
   return v;
 }
 
+// Decode waves given work where one launch holds both classes' workgroups
+// (elsewhere: all the launch has, up to one per block). A decode-only batch
+// uses half the workgroups wherever two fit on a compute unit: the HBM rate
+// holds on half of them. In a batch with prefill work the decode goes to
+// 1/RPA_FUSED_DIV_PF of the workgroups when the prefill class's estimated
+// time is at least RPA_FUSED_RATIO times the decode class's, else to half of
+// them; the workgroups left without work exit at once and free their place on
+// the compute unit for a prefill workgroup.
+#ifndef RPA_FUSED_DIV_PF
+#define RPA_FUSED_DIV_PF 4
+#endif
+#ifndef RPA_FUSED_RATIO
+#define RPA_FUSED_RATIO 0.5
+#endif
+// rates of the two classes on their own (measured): prefill MFMA flop/s and
+// decode K/V bytes/s
+constexpr double kPfRate = 0.8e15;
+constexpr double kDecRate = 5.5e12;
+
+__device__ inline int32_t fused_dec_waves(const Params& p, int64_t pf_keys, int32_t dec_blocks, int32_t pf_items) {
+  const int32_t wgs = max(p.dec_waves, 1) / kDecWavesPerBlock;
+  if (!p.fused || dec_blocks <= 0 || wgs <= 1) return max(p.dec_waves, 1);
+  int32_t div = 1;
+  if (pf_items <= 0) {
+    div = p.dec_per_cu >= 2 ? 2 : 1;
+  } else {
+    // prefill: every packed row of a unit against its key range, 4 * D flops
+    // per (row, key); decode: K and V of every block
+    const double t_pf = (double)pf_keys * p.pf_rows * 4.0 * p.D / kPfRate;
+    const double t_dec = (double)dec_blocks * p.dec_blk * 2.0 * p.D * (p.dec_blk == kDecBlk8 ? 1 : 2) / kDecRate;
+    div = t_pf >= RPA_FUSED_RATIO * t_dec ? RPA_FUSED_DIV_PF : 2;
+  }
+  return max(1, wgs / div) * kDecWavesPerBlock;
+}
+
 // Per-sequence counts of the main scan: 0 decode units, 1 prefill units,
 // 2 decode blocks, 3 prefill items, 4 split units. The prefill items per queue
 // take a second scan, over the tile's prefill sequences heaviest first.
@@ -440,7 +475,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     h.n_split_units = base[4];
     h.dec_blocks = base[2];
     // decode waves given work: every one of them gets at least one block
-    h.pad0[0] = max(1, min(max(p.dec_waves, 1), base[2]));
+    h.pad0[0] = max(1, min(fused_dec_waves(p, tot_pf, base[2], base[3]), base[2]));
     for (int x = 0; x < kQueues; ++x) {
       h.pf_q_base[x] = x * p.max_pf_items;
       h.pf_q_count[x] = max(0, min(base_q[x], p.max_pf_items));

@@ -107,10 +107,20 @@ __device__ __forceinline__ int swz_v(int key) {
   return (4 * (key & 3)) & (C - 1);
 }
 
-// CAP: the soft-cap is on (a template parameter, so the uncapped kernel's
-// block loop has no branch and no cap arithmetic).
+// LDS of one workgroup of prefill_tiles.
+template <int D, bool FP8>
+struct PfShared {
+  char lds[PrefillLds<D, FP8>::kBytes];  // the K/V ring (and the merge's staging)
+  uint32_t blk[kPfBlkTable];             // physical key index of each 16-key block of the item
+  int item[2];
+  int last;
+};
+
+// The prefill-class tiles of one workgroup: it takes items from the queues
+// until they are empty. CAP: the soft-cap is on (a template parameter, so the
+// uncapped code's block loop has no branch and no cap arithmetic).
 template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
-__global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kernel(Params p) {
+__device__ __forceinline__ void prefill_tiles(const Params& p, PfShared<D, KVT != kKvBf16>& shm) {
   static_assert(!(Q32 && F16), "an f32 q runs on the bf16 path");
   constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8), widened in registers
   // f16 P must stay below 65504: exponentiated scores <= 2^15
@@ -143,10 +153,10 @@ __global__ __launch_bounds__(kPfWaves * 64, pf_wgs_per_cu(D)) void prefill_kerne
   static_assert(!FP8 || NST == 3, "fp8 path stages through registers one step ahead");
   static_assert(FP8 || (KS == 32 && NW == 4 && NIW * RPI == 16), "a wave's rows stay in one 16-key block");
 
-  __shared__ __attribute__((aligned(16))) char lds[PrefillLds<D, FP8>::kBytes];
-  __shared__ uint32_t sh_blk[kPfBlkTable];  // physical key index of each 16-key block of the item
-  __shared__ int sh_item[2];
-  __shared__ int sh_last;
+  char* const lds = shm.lds;
+  uint32_t* const sh_blk = shm.blk;
+  int* const sh_item = shm.item;
+  int& sh_last = shm.last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -85,7 +85,16 @@ def _check_decode(P, w, owner):
     Tb, W = P["dec_blocks"], P["W"]
     assert Tb == blk
     Wu = P["W_used"]
-    assert Wu == max(1, min(W, Tb))
+    c = w.cfg
+    two_group = (c.head_dim == 256 and c.kv_dtype in (wl.KV_BF16, wl.KV_F16)
+                 and c.q_dtype in (wl.Q_BF16, wl.Q_F16))
+    if two_group:
+        # the decode class has a launch of its own: all its waves get work
+        assert Wu == max(1, min(W, Tb))
+    else:
+        # one launch holds both classes: the decode work may go to fewer
+        # whole workgroups (4 waves each) than the launch has
+        assert 1 <= Wu <= max(1, min(W, Tb)) and (Wu == max(1, min(W, Tb)) or Wu % 4 == 0)
     if Tb == 0:
         return
     starts = (Tb * np.arange(Wu + 1, dtype=np.int64)) // Wu
