@@ -285,6 +285,22 @@ rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, 
 rpa_status rpa_profile_begin(int32_t max_calls);
 rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls);
 
+/*
+ * Debugging switches, read from the environment once per process (a value
+ * other than empty or "0" turns a switch on):
+ *   RPA_TRACE  every forward call and every launch in it (and each
+ *              rpa_kv_append) is a roctx range on the calling thread, for
+ *              rocprofv3 --marker-trace: the launcher's counterpart of the
+ *              kernel page's trace region around QK^T. The roctx library is
+ *              opened when the first range is needed; without it the ranges
+ *              are off. Results are unchanged.
+ *   RPA_LOG    each forward call prints its plan to stderr (decode sequences,
+ *              units, blocks and waves given work; prefill units, items,
+ *              chunk size, split units and queue lengths). To read the plan
+ *              it copies it back and waits for `stream`, so the call then
+ *              synchronises; under stream capture it prints nothing.
+ */
+
 #ifdef __cplusplus
 }
 #endif

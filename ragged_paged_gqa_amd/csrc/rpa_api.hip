@@ -6,9 +6,13 @@
 // tiles.)
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -112,6 +116,74 @@ void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev[k], st);
 }
 
+// A non-empty environment variable other than "0".
+bool env_on(const char* name) {
+  const char* e = std::getenv(name);
+  return e && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+// Optional host-side trace ranges, the launcher's counterpart of the kernel
+// page's trace region around QK^T: with RPA_TRACE set when the library first
+// needs them, every forward call and every launch in it is a roctx range
+// (shown by rocprofv3 --marker-trace beside the kernels it enqueued). The
+// roctx library is opened then (dlopen), so it is no load-time dependency;
+// without it the ranges are off.
+struct Tracer {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+const Tracer& tracer() {
+  static const Tracer t = [] {
+    Tracer r;
+    if (!env_on("RPA_TRACE")) return r;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("librocprofiler-sdk-roctx.so", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return r;
+    r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!r.push || !r.pop) r = Tracer{};
+    return r;
+  }();
+  return t;
+}
+struct TraceRange {
+  bool on;
+  explicit TraceRange(const char* name) : on(tracer().push != nullptr) {
+    if (on) tracer().push(name);
+  }
+  ~TraceRange() {
+    if (on) tracer().pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
+
+// With RPA_LOG set, each forward call prints its plan to stderr: it copies
+// the plan header back and waits for `st` (a debugging aid; the call then
+// synchronises, and it prints nothing while `st` is being captured).
+void log_plan(const Params& p, hipStream_t st) {
+  static const bool on = env_on("RPA_LOG");
+  if (!on) return;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return;
+  }
+  Header h;
+  if (hipMemcpyAsync(&h, p.hdr, sizeof h, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  std::fprintf(stderr,
+               "rpa plan: decode %d seqs, %d units, %d blocks of %d keys over %d of %d waves; prefill %d units, "
+               "%d items of <= %d keys, %d split units; queues",
+               h.n_dec_seqs, h.n_dec_units, h.dec_blocks, p.dec_blk, h.pad0[0], p.dec_waves, h.n_pf_units,
+               h.n_pf_items, h.pf_chunk, h.n_split_units);
+  for (int x = 0; x < kQueues; ++x) std::fprintf(stderr, " %d", h.pf_q_count[x]);
+  std::fprintf(stderr, "\n");
+}
+
 // Prefill-class workgroups of a launch: the two-group kernel runs one per
 // compute unit, the 4-wave kernel as many as its LDS and registers allow;
 // never more than there are items.
@@ -130,6 +202,7 @@ int prefill_grid(const Params& p, int cus) {
 
 template <int D, bool F16, bool Q32>
 rpa_status launch_combine(const Params& p, int cus, hipStream_t st) {
+  TraceRange r("rpa combine");
   // merge of the split decode units (a wave per unit, grid-stride)
   int cgrid = (p.max_dec_units + kDecWavesPerBlock - 1) / kDecWavesPerBlock;
   if (cgrid > cus * 4) cgrid = cus * 4;
@@ -150,6 +223,7 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
   const int dec_wgs = p.dec_waves / kDecWavesPerBlock;
   if (dec_wgs < 1) return RPA_ERR_HIP;
   if constexpr (!FP8 && !Q32 && D >= RPA_PP_MIN_D && D <= RPA_PP_MAX_D) {
+    TraceRange r("rpa prefill, then decode");
     const int grid = prefill_grid<D, FP8, true>(p, cus);
     if (p.soft_cap > 0.f)
       hipLaunchKernelGGL((prefill_pp_kernel<D, true, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
@@ -166,6 +240,7 @@ rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
     prof_record(ev, 3, st);
   } else {
+    TraceRange r("rpa tiles");
     const int grid = dec_wgs + prefill_grid<D, FP8, false>(p, cus);
     if (p.soft_cap > 0.f)
       hipLaunchKernelGGL((tiles_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
@@ -212,6 +287,7 @@ rpa_status launch_for_kv(int32_t q_dtype, int32_t kv_dtype, const Params& p, int
 }
 
 rpa_status launch_plan(const Params& p, hipStream_t st) {
+  TraceRange r("rpa plan");
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
   return check_launch();
 }
@@ -325,10 +401,12 @@ rpa_status forward(const rpa_config* cfg, const void* q, const void* kv_pages, c
     if (g_prof.on.load(std::memory_order_relaxed) && g_prof.n_calls < g_prof.max_calls)
       ev = &g_prof.ev[kProfEvents * g_prof.n_calls++];
   }
+  TraceRange r("rpa_forward");
   prof_record(ev, 0, s);
   st = launch_plan(p, s);
   if (st != RPA_OK) return st;
   prof_record(ev, 1, s);
+  log_plan(p, s);
   switch (cfg->head_dim) {
     case 64: return launch_for_kv<64>(cfg->q_dtype, cfg->kv_dtype, p, cus, s, ev);
     case 128: return launch_for_kv<128>(cfg->q_dtype, cfg->kv_dtype, p, cus, s, ev);
@@ -512,6 +590,7 @@ rpa_status rpa_kv_append(const rpa_config* cfg, const void* k_new, const void* v
   int grid = (cfg->num_q_tokens + kApWaves - 1) / kApWaves;
   if (grid > cus * 8) grid = cus * 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  TraceRange r("rpa_kv_append");
   switch (cfg->head_dim) {
     case 64: launch_append<64>(mode, in, grid, s, p); break;
     case 128: launch_append<128>(mode, in, grid, s, p); break;
