@@ -12,7 +12,7 @@
 
 // Prefill-class work items the planner aims for per compute unit.
 #ifndef RPA_PF_ITEMS_PER_CU
-#define RPA_PF_ITEMS_PER_CU 4
+#define RPA_PF_ITEMS_PER_CU 3
 #endif
 // head_dims whose 16-bit prefill runs on the two-group (ping-pong) kernel;
 // the others, an f32 q and one-byte K/V run on the 4-wave kernel.

@@ -42,7 +42,13 @@ namespace rpa {
 
 constexpr int kPlanThreads = 512;  // 1024 would cap a wave at 128 VGPRs and spill
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPfMinChunk = 512;
+// Smallest prefill chunk (keys): an item has a fixed cost (its Q tile, block
+// table, pipeline fill, partial and share of the merge), so items are kept
+// from getting small even when that leaves fewer items than workgroups.
+#ifndef RPA_PF_MIN_CHUNK
+#define RPA_PF_MIN_CHUNK 8192
+#endif
+constexpr int kPfMinChunk = RPA_PF_MIN_CHUNK;
 
 // a / d for 0 <= a < 2^31, d > 0: the double product is within 1e-6 of the
 // quotient, so truncation is off by at most one, which the remainder fixes.
@@ -208,14 +214,37 @@ struct PfInfo {
   int32_t per_head;  // items of one kv head
   int32_t nsplit;    // row blocks with more than one chunk
   int32_t max_nch;   // most chunks of one row block
+  int32_t nrb;       // row blocks (units of one kv head)
+  int32_t lcls;      // size class of its units' last chunks (largest over its row blocks)
   int64_t work;      // visible keys of its row blocks (one kv head)
 };
 
 // Offsets of a prefill sequence's records, from the block scan.
 struct PfOffs {
   int32_t unit, item;
-  int32_t queue[kQueues];
+  int32_t qa[kQueues];  // where its heads' chunks before a unit's last one start in each queue
+  int32_t qb[kQueues];  // where its heads' last chunks start in each queue
 };
+
+// Size classes of a unit's last chunk (keys * kLastClasses / chunk): the
+// queues hold every unit's other chunks first, then the last chunks, larger
+// classes first, so that the smallest pieces of work are the last taken.
+constexpr int kLastClasses = 16;
+
+// Queue of the g-th (sequence, kv head) in work order: dealt to the queues
+// back and forth (0..7, 7..0, ...), so that every queue gets a share of
+// the heaviest and of the lightest.
+__device__ __forceinline__ int snake_queue(int32_t g) {
+  const int32_t round = g / kQueues, k = g % kQueues;
+  return (round & 1) ? kQueues - 1 - k : k;
+}
+// How many of the groups g0 .. g - 1 go to queue x (in every 2 * kQueues
+// consecutive groups, queue x takes positions x and 2 * kQueues - 1 - x).
+__device__ __forceinline__ int32_t snake_count(int32_t g0, int32_t g, int x) {
+  constexpr int32_t P = 2 * kQueues;
+  auto upto = [x](int32_t n) { return 2 * (n / P) + (x < n % P) + (P - 1 - x < n % P); };
+  return upto(g) - upto(g0);
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ int64_t red[kPlanWaves];
@@ -223,6 +252,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   __shared__ int32_t n_pf_tile;
   __shared__ PfInfo pf_info[kPlanThreads];
   __shared__ int32_t by_rank[kPlanThreads];  // prefill slots of the tile, heaviest sequence first
+  __shared__ int32_t by_rank_b[kPlanThreads];  // the same by last-chunk class, larger first
+  __shared__ int32_t rank_of[kPlanThreads];  // work rank of each prefill slot
   __shared__ PfOffs pf_offs[kPlanThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t n = *p.num_seqs;
@@ -288,7 +319,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       int32_t pql, pkvl;
       seq_meta(p, ps, pql, pkvl);
       const int32_t rows = pql * p.G;
-      int32_t items = 0, nsplit = 0, max_nch = 0;
+      int32_t items = 0, nsplit = 0, max_nch = 0, lcls = 0;
       int64_t work = 0;
       for (int32_t r0 = lane * R; r0 < rows; r0 += 64 * R) {
         const UnitRange r = unit_range(p, G, pql, pkvl, r0, min(R, rows - r0));
@@ -297,15 +328,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
         nsplit += nch > 1;
         max_nch = max(max_nch, nch);
         work += range_keys(r);
+        const int32_t last = range_keys(r) - (nch - 1) * pf_chunk.d;
+        lcls = max(lcls, min(kLastClasses - 1, fdiv(max(last, 0) * kLastClasses, pf_chunk)));
       }
       items = wave_sum(items);
       nsplit = wave_sum(nsplit);
       max_nch = wave_max(max_nch);
+      lcls = wave_max(lcls);
       work = wave_sum64(work);
       if (lane == 0) {
         pf_info[i].per_head = items;
         pf_info[i].nsplit = nsplit;
         pf_info[i].max_nch = max_nch;
+        pf_info[i].nrb = (rows + R - 1) / R;
+        pf_info[i].lcls = lcls;
         pf_info[i].work = work;
       }
     }
@@ -340,10 +376,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       pf_offs[slot].unit = off[1];
       pf_offs[slot].item = off[3];
     }
-    // queue offsets: the tile's prefill sequences take their places in the
-    // queues heaviest first (visible keys; ties by sequence index), so that
-    // the longest items start first and the queues drain evenly; a sequence's
-    // entries in a queue stay contiguous and chunk-major
+    // queue offsets. The tile's prefill sequences are ranked heaviest first
+    // (visible keys; ties by sequence index) and their (sequence, kv head)
+    // groups dealt to the queues back and forth in that order. In a queue the
+    // tile's groups first place every chunk but their units' last ones, in
+    // rank order, then the last chunks, by size class (larger first; ties by
+    // rank). A group's entries in each part stay contiguous and chunk-major.
     if (n_pf_tile > 0) {  // (block-uniform)
       if (slot >= 0) {
         const int64_t wk = pf_info[slot].work;
@@ -353,28 +391,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
           r += wj > wk || (wj == wk && pf_info[j].s < s);
         }
         by_rank[r] = slot;
+        rank_of[slot] = r;
       }
       __syncthreads();
-      int32_t qc[kQueues];
+      if (slot >= 0) {
+        const int32_t ck = pf_info[slot].lcls, rk = rank_of[slot];
+        int32_t rb = 0;
+        for (int32_t j = 0; j < n_pf_tile; ++j) {
+          const int32_t cj = pf_info[j].lcls;
+          rb += cj > ck || (cj == ck && rank_of[j] < rk);
+        }
+        by_rank_b[rb] = slot;
+      }
+      __syncthreads();
+      // the first part's offsets (thread t: the t-th sequence by work)...
+      int32_t ta[kQueues];
+      {
+        int32_t qa[kQueues], oa[kQueues];
 #pragma unroll
-      for (int x = 0; x < kQueues; ++x) qc[x] = 0;
-      const int32_t rs = tid < n_pf_tile ? by_rank[tid] : -1;
-      if (rs >= 0) {
-        const PfInfo& f = pf_info[rs];
-        for (int32_t h = 0; h < p.Hkv; ++h) {
-          const int x = (f.s * p.Hkv + h) % kQueues;
+        for (int x = 0; x < kQueues; ++x) qa[x] = 0;
+        const int32_t ra = tid < n_pf_tile ? by_rank[tid] : -1;
+        if (ra >= 0) {
+          const int32_t nq = pf_info[ra].per_head - pf_info[ra].nrb;
+          for (int32_t h = 0; h < p.Hkv; ++h) {
+            const int x = snake_queue(tid * p.Hkv + h);
 #pragma unroll
-          for (int k = 0; k < kQueues; ++k) qc[k] += x == k ? f.per_head : 0;
+            for (int k = 0; k < kQueues; ++k) qa[k] += x == k ? nq : 0;
+          }
+        }
+        block_scan<kQueues>(qa, oa, ta, sh);
+        if (ra >= 0) {
+#pragma unroll
+          for (int x = 0; x < kQueues; ++x) pf_offs[ra].qa[x] = base_q[x] + oa[x];
         }
       }
-      int32_t qo[kQueues], qt[kQueues];
-      block_scan<kQueues>(qc, qo, qt, sh);
-      if (rs >= 0) {
+      // ...then the second's (thread t: the t-th sequence by last-chunk class)
+      {
+        int32_t qb[kQueues], ob[kQueues], tb[kQueues];
 #pragma unroll
-        for (int x = 0; x < kQueues; ++x) pf_offs[rs].queue[x] = base_q[x] + qo[x];
+        for (int x = 0; x < kQueues; ++x) qb[x] = 0;
+        const int32_t rb = tid < n_pf_tile ? by_rank_b[tid] : -1;
+        if (rb >= 0) {
+          const int32_t nq = pf_info[rb].nrb, g0 = rank_of[rb] * p.Hkv;
+          for (int32_t h = 0; h < p.Hkv; ++h) {
+            const int x = snake_queue(g0 + h);
+#pragma unroll
+            for (int k = 0; k < kQueues; ++k) qb[k] += x == k ? nq : 0;
+          }
+        }
+        block_scan<kQueues>(qb, ob, tb, sh);
+        if (rb >= 0) {
+#pragma unroll
+          for (int x = 0; x < kQueues; ++x) pf_offs[rb].qb[x] = base_q[x] + ta[x] + ob[x];
+        }
+#pragma unroll
+        for (int x = 0; x < kQueues; ++x) base_q[x] += ta[x] + tb[x];
       }
-#pragma unroll
-      for (int x = 0; x < kQueues; ++x) base_q[x] += qt[x];
     }
 
     // (c) a decode sequence's record, at its rank among the decode sequences
@@ -430,9 +502,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
         }
       }
       // queue entries, chunk-major: chunk 0 of every row block, then chunk 1
-      // of those that have one, ...; a head's entries are contiguous, after
-      // those of this sequence's earlier heads in the same queue
-      int32_t pos = 0;  // entries of this sequence's head so far
+      // of those that have one, ...; a unit's last chunk goes to the second
+      // part. A head's entries in a part are contiguous, after those of this
+      // sequence's earlier heads in the same queue.
+      const int32_t rank = rank_of[i];
+      int32_t pos_a = 0, pos_b = 0;  // entries of this sequence's head so far, per part
       for (int32_t c = 0; c < f.max_nch; ++c) {
         int32_t carry_items = 0;
         for (int32_t rb0 = 0; rb0 < nrb; rb0 += 64) {
@@ -445,20 +519,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
           const int32_t incl = wave_incl_scan(nch);
           const int32_t item_off = carry_items + incl - nch;
           carry_items += __shfl(incl, 63);
-          const bool has = c < nch;
-          const uint64_t m = __ballot(has);
-          const int32_t before = __popcll(m & ((1ull << lane) - 1ull));
-          if (has) {
+          const bool in_a = c < nch - 1, in_b = c == nch - 1;
+          const uint64_t ma = __ballot(in_a), mb = __ballot(in_b);
+          const uint64_t below = (1ull << lane) - 1ull;
+          if (in_a || in_b) {
+            const int32_t before = in_a ? __popcll(ma & below) : __popcll(mb & below);
             for (int32_t h = 0; h < p.Hkv; ++h) {
-              const int x = (ps * p.Hkv + h) % kQueues;
-              const int32_t j = h / kQueues;  // earlier heads of this sequence in queue x
-              const int32_t k = pf_offs[i].queue[x] + j * f.per_head + pos + before;
+              const int x = snake_queue(rank * p.Hkv + h);
+              const int32_t j = snake_count(rank * p.Hkv, rank * p.Hkv + h, x);  // earlier heads in queue x
+              const int32_t k = in_a ? pf_offs[i].qa[x] + j * (f.per_head - f.nrb) + pos_a + before
+                                     : pf_offs[i].qb[x] + j * f.nrb + pos_b + before;
               const int32_t item = item0 + h * f.per_head + item_off + c;
               if (k < p.max_pf_items && item < p.max_pf_items)
                 p.pf_qlist[(int64_t)x * p.max_pf_items + k] = item;
             }
           }
-          pos += __popcll(m);
+          pos_a += __popcll(ma);
+          pos_b += __popcll(mb);
         }
       }
     }

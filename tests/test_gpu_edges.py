@@ -30,12 +30,14 @@ def test_no_sequences_leaves_every_row_untouched():
 
 @pytest.mark.parametrize("D,kvd", [(128, wl.KV_BF16), (256, wl.KV_BF16), (128, wl.KV_FP8), (64, wl.KV_I8)])
 def test_largest_page_size(D, kvd):
-    """page_size 1024, both kernel classes, split chunks inside one page."""
+    """page_size 1024, both kernel classes, split chunks inside one page: the
+    window starts the 20000-key sequence's key range at key 9952, so its two
+    chunks meet at key 18144, inside page 17."""
     kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=D, page_size=1024, pages_per_seq=None,
-              sm_scale=1.0 / np.sqrt(D), kv_dtype=kvd)
+              sm_scale=1.0 / np.sqrt(D), kv_dtype=kvd, sliding_window=10000)
     if wl.is_fp8(kvd):
         kw.update(k_scale=0.05, v_scale=0.05)
-    q_lens, kv_lens = [1, 40, 2, 300], [3000, 2100, 1024, 4000]
+    q_lens, kv_lens = [1, 40, 2, 300], [3000, 20000, 1024, 4000]
     pages = sum((k + 1023) // 1024 for k in kv_lens)
     w = wl.build("page1024", kw, q_lens, kv_lens, 62, total_num_pages=pages + 1, num_q_tokens=sum(q_lens) + 1)
     _compare_all(w, f"page 1024 D {D} {kvd}")

@@ -80,8 +80,9 @@ def test_small_random_sharpened(seed, D, kvd, causal, window, cap, G, page):
 MEDIUM = [
     # decode-class rows with long KV (split chunks), prefill-class rows with long KV
     dict(name="dec-split", q_lens=[1, 1, 2, 1], kv_lens=[3000, 257, 1900, 40], Hq=8, Hkv=2, D=128, page=16),
-    dict(name="pf-split", q_lens=[40, 3, 70], kv_lens=[2600, 1500, 900], Hq=8, Hkv=2, D=128, page=32),
-    dict(name="pf-split-d256", q_lens=[24, 9], kv_lens=[1800, 700], Hq=16, Hkv=2, D=256, page=64),
+    # (prefill chunks are at least 8192 keys: these units take 2 and 3)
+    dict(name="pf-split", q_lens=[40, 3, 70], kv_lens=[20000, 1500, 9000], Hq=8, Hkv=2, D=128, page=32),
+    dict(name="pf-split-d256", q_lens=[24, 9], kv_lens=[18000, 9000], Hq=16, Hkv=2, D=256, page=64),
     dict(name="mixed-window", q_lens=[33, 1, 1, 5], kv_lens=[2100, 2000, 700, 1300], Hq=8, Hkv=4, D=64,
          page=16, window=300),
     dict(name="fp8-cap-window", q_lens=[1, 1, 1], kv_lens=[4000, 2500, 1000], Hq=32, Hkv=8, D=128, page=16,
@@ -116,6 +117,29 @@ def test_medium_with_split_kv(case):
 @pytest.mark.parametrize("case", MEDIUM, ids=[c["name"] for c in MEDIUM])
 def test_medium_with_split_kv_sharpened(case):
     _compare_all(_medium(case, q_mult=8.0), case["name"] + " x8")
+
+
+@pytest.mark.parametrize("case", MEDIUM[:3], ids=[c["name"] for c in MEDIUM[:3]])
+def test_medium_cases_split(case):
+    """The split cases do split: prefill units of more than one chunk (merged
+    by the last finisher) or decode units over more than one wave (merged by
+    the combine kernel), whatever the planner's chunk and wave rules."""
+    w = _medium(case)
+    d = Device(w)
+    ws = rpa.plan(d.kv_lens, d.cu_q_lens, d.num_seqs, d.cfg)
+    torch.cuda.synchronize()
+    offs, lim = rpa.plan_layout(d.cfg)
+    host = ws.cpu().numpy()
+    hdr = host[offs[0]:offs[0] + 256].view(np.int32)
+    n_split_pf, Tb, W = int(hdr[6]), int(hdr[7]), int(hdr[8])
+    if case["name"].startswith("pf"):
+        assert n_split_pf > 0
+    else:
+        # some unit's blocks fall into the ranges of two waves
+        ds = host[offs[1]:offs[1] + 32 * int(hdr[2])].view(np.int32).reshape(-1, 8)
+        wave = lambda b: np.searchsorted((Tb * np.arange(W + 1, dtype=np.int64)) // W, b, side="right") - 1
+        assert any(wave(int(r[6]) + h * int(r[7])) != wave(int(r[6]) + (h + 1) * int(r[7]) - 1)
+                   for r in ds if int(r[7]) > 0 for h in range(case["Hkv"]))
 
 
 def test_padding_rows_untouched_and_empty_sequences():

@@ -110,46 +110,62 @@ def _check_decode(P, w, owner):
         assert unit_nb[inside].sum() >= 1
 
 
+def _snake(g):
+    r, k = divmod(g, 8)
+    return 7 - k if r & 1 else k
+
+
 def _check_queues(P, n_kv_heads):
-    """Each prefill item sits in exactly one of the 8 queues, the one of its
-    (sequence, kv head); queue x starts at x * max_pf_items and starts empty;
-    within a queue, one (sequence, kv head)'s items come chunk-major."""
+    """The queue lists, entry for entry. Each tile of 512 sequences ranks its
+    prefill sequences heaviest first (visible keys of one kv head's units;
+    ties by sequence index) and deals its (sequence, kv head) groups to the
+    8 queues back and forth: group g = rank * Hkv + h goes to queue 0..7,
+    7..0, ... In each queue the tile's entries are every chunk but the units'
+    last ones, groups in rank order, then the last chunks, groups by the size
+    class of their last chunks (16 * keys // chunk, at most 15; the largest
+    over the group's units) larger first, ties by rank; inside a part a
+    group's entries are chunk-major (chunk, then row block). Queue x starts
+    at x * max_pf_items and starts empty."""
     n_pi = len(P["pi"])
     max_pi = P["lim"][3]
+    C = P["pch"]
     assert np.all(P["qnext"] == 0)
     assert int(P["qcount"].sum()) == n_pi
     assert np.all(P["qbase"] == np.arange(8) * max_pi)
+    groups = {}
+    for ui, (s_, h_, r0_, nr_, lo_, hi_, nch_, it0_) in enumerate(P["pu"]):
+        groups.setdefault((int(s_), int(h_)), []).append(
+            (int(r0_), int(lo_), int(hi_), int(nch_), int(it0_)))
+    seqs = sorted({s_ for s_, _ in groups})
+    expect = [[] for _ in range(8)]
+    for tile in sorted({s_ // 512 for s_ in seqs}):
+        ts = [s_ for s_ in seqs if s_ // 512 == tile]
+        work = {s_: sum(max(hi - lo, 0) for _, lo, hi, _, _ in groups[(s_, 0)]) for s_ in ts}
+        cls = {s_: max(min(15, 16 * max((hi - lo) - (nch - 1) * C, 0) // C) for _, lo, hi, nch, _ in groups[(s_, 0)])
+               for s_ in ts}
+        by_work = sorted(ts, key=lambda s_: (-work[s_], s_))
+        rank = {s_: r for r, s_ in enumerate(by_work)}
+        by_cls = sorted(ts, key=lambda s_: (-cls[s_], rank[s_]))
+        part_a = [[] for _ in range(8)]
+        part_b = [[] for _ in range(8)]
+        for order, part, last in ((by_work, part_a, False), (by_cls, part_b, True)):
+            for s_ in order:
+                for h in range(n_kv_heads):
+                    ents = []
+                    for r0, lo, hi, nch, it0 in groups[(s_, h)]:
+                        for c in range(nch):
+                            if (c == nch - 1) == last:
+                                ents.append((c, r0, it0 + c))
+                    part[_snake(rank[s_] * n_kv_heads + h)] += [e[2] for e in sorted(ents)]
+        for x in range(8):
+            expect[x] += part_a[x] + part_b[x]
     entries = []
     for x in range(8):
         q = P["qlist"][x * max_pi:x * max_pi + int(P["qcount"][x])]
+        assert list(q) == expect[x], f"queue {x}"
         entries.append(q)
-        last = {}
-        for it in q:
-            ui, c = P["pi"][it]
-            s, h, r0 = P["pu"][ui][:3]
-            assert (s * n_kv_heads + h) % 8 == x
-            key = (c, r0)
-            if (s, h) in last:
-                assert key > last[(s, h)]
-            last[(s, h)] = key
     allq = np.concatenate(entries) if entries else np.zeros(0, np.int32)
     assert np.array_equal(np.sort(allq), np.arange(n_pi))
-    # within a queue the sequences come heaviest first (the visible keys of
-    # their units of one kv head; ties by sequence index) while the plan has
-    # one tile of sequences
-    work = {}
-    for s_, h_, r0_, nr_, lo_, hi_, nch_, it0_ in P["pu"]:
-        if h_ == 0:
-            work[int(s_)] = work.get(int(s_), 0) + max(int(hi_) - int(lo_), 0)
-    if len(P["pu"]) and max(work) < 512:
-        for q in entries:
-            order = []
-            for it in q:
-                s_ = int(P["pu"][P["pi"][it][0]][0])
-                if not order or order[-1] != s_:
-                    order.append(s_)
-            keys = [(-work[s_], s_) for s_ in order]
-            assert keys == sorted(keys)
 
 
 def _check(w):
@@ -211,3 +227,12 @@ def test_plan_named_lengths(number):
                     np.asarray(kv_lens, np.int32), np.zeros((S, pps), np.int32), cu, np.array([S], np.int32))
     _check(w)
     _ = page
+    # the decode waves given work, by the rule for each workload: the decode
+    # batches (2, 4) use half the launch's 4-wave workgroups (two fit on a
+    # CU at head_dim 128); the mixed batch (3), whose estimated prefill time
+    # is well above half its decode time, a quarter; the long context (5)
+    # has no decode work
+    P = _plan(w)
+    W, Tb, Wu = P["W"], P["dec_blocks"], P["W_used"]
+    expect = {2: (W // 8) * 4, 3: (W // 16) * 4, 4: (W // 8) * 4, 5: 1}[number]
+    assert Wu == min(expect, max(Tb, 1)), (Wu, expect, Tb)

@@ -24,7 +24,7 @@ def _split_batch():
     # finisher) beside decode-class rows with long KV (split, merged by the
     # combine kernel), with attention sinks
     kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=32, pages_per_seq=None, sm_scale=0.088)
-    q_lens, kv_lens = [40, 1, 70, 1, 2], [2600, 3000, 900, 257, 1900]
+    q_lens, kv_lens = [40, 1, 70, 1, 2], [20000, 3000, 900, 257, 1900]
     pages = sum((k + 31) // 32 for k in kv_lens)
     w = wl.build("noalloc-split", kw, q_lens, kv_lens, 77, total_num_pages=pages + 3, max_num_seqs=6,
                  num_q_tokens=sum(q_lens) + 2)
