@@ -184,7 +184,7 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
-KERNEL_CLASSES = ("tiles_kernel", "decode_kernel", "prefill_pp_kernel", "plan_kernel", "combine_kernel")
+KERNEL_CLASSES = ("tiles_pp_kernel", "tiles_kernel", "plan_kernel", "combine_kernel")
 
 
 def kernel_class(name: str):
@@ -410,19 +410,11 @@ class Runner:
         F = work["decode"][0] + work["prefill"][0]
         B = work["decode"][1] + work["prefill"][1]
         T = self.w.valid_tokens()
-        if self._uses_pp():
-            # the classes run in turn: the longer of the two launches
-            dom = "decode" if kmean["decode"] >= kmean["tiles"] else "prefill"
-            t_ms = kmean["decode" if dom == "decode" else "tiles"]
-            kf, kb = work[dom][0], work[dom][1]
-            kroof = roofline_of(kf, kb, t_ms * 1e-3, prefer_mfma=(dom == "prefill"))
-            kname = "prefill_pp_kernel" if dom == "prefill" else "decode_kernel"
-        else:
-            # one launch holds both classes: its work is theirs together,
-            # bound by whichever peak it needs longer on
-            t_ms, kf, kb = kmean["tiles"], F, B
-            kroof = roofline_of(kf, kb, t_ms * 1e-3, prefer_mfma=False)
-            kname = "tiles_kernel"
+        # one launch holds both classes: its work is theirs together, bound
+        # by whichever peak it needs longer on
+        t_ms, kf, kb = kmean["tiles"], F, B
+        kroof = roofline_of(kf, kb, t_ms * 1e-3, prefer_mfma=False)
+        kname = "tiles_pp_kernel" if self._uses_pp() else "tiles_kernel"
         kroof["kernel"] = kname
         kroof["kernel_ms"] = round(t_ms, 4)
         kroof["algorithmic_flops"] = kf

@@ -118,11 +118,9 @@ rpa_status rpa_workspace_bytes(const rpa_config* cfg, size_t* bytes);
  *
  * The call validates cfg and pointers on the host, then enqueues on `stream`
  * and returns: the plan; the tiles of both classes in one launch, whose
- * workgroups run decode-class or prefill-class tiles side by side (at
- * head_dim 256 with K/V in the 16-bit q type, where the prefill class runs on
- * an eight-wave kernel: a prefill-class launch, then a decode-class launch);
- * and the merge of split decode units (a split prefill unit is merged by
- * whichever workgroup finishes its last key chunk).
+ * workgroups run decode-class or prefill-class tiles side by side; and the
+ * merge of split decode units (a split prefill unit is merged by whichever
+ * workgroup finishes its last key chunk).
  * Errors: RPA_ERR_INVALID_ARGUMENT, RPA_ERR_UNSUPPORTED,
  * RPA_ERR_WORKSPACE_TOO_SMALL (nothing enqueued), RPA_ERR_HIP (launch failed).
  */
@@ -232,16 +230,17 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
  *              n_dec_units = n_dec_seqs * Hkv; dec_blocks is the number of
  *              16-key blocks (32 for one-byte K/V) of all decode units, split
  *              over the first dec_waves_used decode waves, at least 1 and at
- *              most min(dec_waves, dec_blocks): exactly that where the
- *              decode class has a launch of its own; where one launch holds
- *              both classes, min(V, dec_blocks) with V whole 4-wave
- *              workgroups: half of dec_waves for a batch with no prefill
- *              work (where two decode workgroups fit on a compute unit,
- *              else all), and for a batch with prefill work a quarter when
- *              its estimated prefill time is at least half its decode time,
- *              else half; the prefill items are dealt into 8 queues, one per
- *              XCD, and queue x is queue_count[x] entries of the queue list
- *              from queue_base[x] = x * max_pf_items on)
+ *              most min(dec_waves, dec_blocks): min(V, dec_blocks) with V
+ *              whole 4-wave workgroups, half of dec_waves for a batch with no
+ *              prefill work where two decode workgroups fit on a compute
+ *              unit (else all of them), and for a batch with prefill work a
+ *              quarter when its estimated prefill time is at least half its
+ *              decode time, else half; the prefill items are dealt into 8
+ *              queues, one per XCD, by (sequence, kv head), the heaviest
+ *              first and back and forth over the queues; a queue lists the
+ *              units' other chunks before their last ones, those by size;
+ *              queue x is queue_count[x] entries of the queue list from
+ *              queue_base[x] = x * max_pf_items on)
  *   offsets[1] decode sequences int32[max_num_seqs][8]
  *   offsets[2] prefill units    int32[max_pf_units][8]
  *   offsets[3] 0 (reserved)
@@ -271,13 +270,12 @@ rpa_status rpa_debug_decode_fp8(const uint8_t* codes, float* values, int32_t n, 
 /*
  * Event timing for benchmarks. rpa_profile_begin(max_calls) makes the next
  * max_calls forward calls (process-wide) record HIP events on their stream
- * around each of their launches. rpa_profile_end waits for the last recorded
- * event and returns in kernel_ms[0..3] the elapsed milliseconds, summed over
- * the recorded calls, of: the plan; the tile launch (both classes in one
- * launch, or the prefill class where the classes run in turn); the
- * decode-class launch where the classes run in turn (else about 0); the
- * merge of split decode units. It also returns how many calls were recorded,
- * then releases the events. Events are created in rpa_profile_begin, never on the forward path.
+ * around their launches. rpa_profile_end waits for the last recorded event
+ * and returns in kernel_ms[0..3] the elapsed milliseconds, summed over the
+ * recorded calls, of: the plan; the tile launch (both classes); the merge of
+ * split decode units; the whole call. It also returns how many calls were
+ * recorded, then releases the events. Events are created in
+ * rpa_profile_begin, never on the forward path.
  * Not meant for concurrent forward calls from several threads.
  * Errors: RPA_ERR_INVALID_ARGUMENT (bad count, nested begin, end without
  * begin), RPA_ERR_HIP.

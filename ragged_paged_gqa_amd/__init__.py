@@ -130,10 +130,9 @@ EXPORTS = ("rpa_workspace_bytes", "rpa_forward", "rpa_forward_sinks", "rpa_forwa
            "rpa_check_metadata",
            "rpa_plan", "rpa_plan_layout", "rpa_kv_append", "rpa_debug_decode_fp8", "rpa_profile_begin", "rpa_profile_end")
 
-# rpa_profile_end's slots: the plan; the tile launch (both classes in one
-# launch, or the prefill class where the classes run in turn); the
-# decode-class launch where the classes run in turn (else 0); the merge.
-KERNELS = ("plan", "tiles", "decode", "combine")
+# rpa_profile_end's slots: the plan, the tile launch (both classes), the
+# merge of split decode units, the whole call.
+KERNELS = ("plan", "tiles", "combine", "call")
 
 
 def _check(status: int, what: str) -> None:

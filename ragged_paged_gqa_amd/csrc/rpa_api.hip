@@ -65,7 +65,7 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
   p.unit_done = reinterpret_cast<int32_t*>(w + L.done);
   p.dec_waves = L.dec_waves;
   p.dec_per_cu = dec_grid_for(c, 1);
-  p.fused = uses_pp(c) ? 0 : 1;
+  p.fused = 1;
   p.dec_blk = (c->kv_dtype == RPA_DTYPE_FP8_E4M3FN || c->kv_dtype == RPA_DTYPE_FP8_E5M2 ||
                c->kv_dtype == RPA_DTYPE_INT8)
                   ? kDecBlk8
@@ -99,8 +99,7 @@ Params make_params(const rpa_config* c, const Layout& L, void* ws) {
 rpa_status check_launch() { return hipGetLastError() == hipSuccess ? RPA_OK : RPA_ERR_HIP; }
 
 // Optional event timing of the launches of each call (for benchmarks):
-// events before the plan, after it, after the first and the second tile
-// launch (the second one only where the classes run in turn), and after the
+// events before the plan, after it, after the tile launch and after the
 // merge.
 struct Profiler {
   std::mutex mu;
@@ -109,7 +108,7 @@ struct Profiler {
   int n_calls = 0;
   std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
 };
-constexpr int kProfEvents = 5;
+constexpr int kProfEvents = 4;
 Profiler g_prof;
 
 void prof_record(hipEvent_t* ev, int k, hipStream_t st) {
@@ -211,47 +210,38 @@ rpa_status launch_combine(const Params& p, int cus, hipStream_t st) {
   return check_launch();
 }
 
-// The launches after the plan. Where the prefill class runs on the two-group
-// kernel (eight waves, a workgroup per compute unit), its launch and the
-// decode-class launch run in turn; everywhere else one launch holds the
-// workgroups of both classes (tiles_kernel). Then the merge.
+// The launches after the plan: one launch holds the workgroups of both
+// classes (tiles_pp_kernel where the prefill class runs on the two-group
+// kernel, tiles_kernel elsewhere), then the merge.
 template <int D, int KVT, bool F16, bool Q32>
 rpa_status launch_attention(const Params& p, int cus, hipStream_t st, hipEvent_t* ev) {
   constexpr bool FP8 = KVT != kKvBf16;
-  // the decode launch's workgroups: the waves of the stream-K split (those
-  // the planner gives no work exit at once)
+  // the decode workgroups: the waves of the stream-K split (those the planner
+  // gives no work exit at once)
   const int dec_wgs = p.dec_waves / kDecWavesPerBlock;
   if (dec_wgs < 1) return RPA_ERR_HIP;
-  if constexpr (!FP8 && !Q32 && D >= RPA_PP_MIN_D && D <= RPA_PP_MAX_D) {
-    TraceRange r("rpa prefill, then decode");
-    const int grid = prefill_grid<D, FP8, true>(p, cus);
-    if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((prefill_pp_kernel<D, true, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
-    else
-      hipLaunchKernelGGL((prefill_pp_kernel<D, false, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
-    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 2, st);
-    if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((decode_kernel<D, KVT, true, F16, Q32>), dim3(dec_wgs), dim3(kDecWavesPerBlock * 64), 0, st,
-                         p);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, KVT, false, F16, Q32>), dim3(dec_wgs), dim3(kDecWavesPerBlock * 64), 0, st,
-                         p);
-    if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 3, st);
-  } else {
+  {
     TraceRange r("rpa tiles");
-    const int grid = dec_wgs + prefill_grid<D, FP8, false>(p, cus);
-    if (p.soft_cap > 0.f)
-      hipLaunchKernelGGL((tiles_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
-    else
-      hipLaunchKernelGGL((tiles_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st, p);
+    if constexpr (!FP8 && !Q32 && D >= RPA_PP_MIN_D && D <= RPA_PP_MAX_D) {
+      const int grid = dec_wgs + prefill_grid<D, FP8, true>(p, cus);
+      if (p.soft_cap > 0.f)
+        hipLaunchKernelGGL((tiles_pp_kernel<D, true, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
+      else
+        hipLaunchKernelGGL((tiles_pp_kernel<D, false, F16>), dim3(grid), dim3(kPpWaves * 64), 0, st, p);
+    } else {
+      const int grid = dec_wgs + prefill_grid<D, FP8, false>(p, cus);
+      if (p.soft_cap > 0.f)
+        hipLaunchKernelGGL((tiles_kernel<D, KVT, true, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st,
+                           p);
+      else
+        hipLaunchKernelGGL((tiles_kernel<D, KVT, false, F16, Q32>), dim3(grid), dim3(kDecWavesPerBlock * 64), 0, st,
+                           p);
+    }
     if (check_launch() != RPA_OK) return RPA_ERR_HIP;
-    prof_record(ev, 2, st);
-    prof_record(ev, 3, st);
   }
+  prof_record(ev, 2, st);
   if (launch_combine<D, F16, Q32>(p, cus, st) != RPA_OK) return RPA_ERR_HIP;
-  prof_record(ev, 4, st);
+  prof_record(ev, 3, st);
   return RPA_OK;
 }
 
@@ -490,11 +480,13 @@ rpa_status rpa_profile_end(float kernel_ms[4], int32_t* n_calls) {
   for (int k = 0; k < 4; ++k) kernel_ms[k] = 0.f;
   if (g_prof.n_calls > 0 && hipEventSynchronize(g_prof.ev[kProfEvents * g_prof.n_calls - 1]) != hipSuccess)
     st = RPA_ERR_HIP;
+  // plan 0 -> 1, tiles 1 -> 2, merge 2 -> 3, the whole call 0 -> 3
   for (int c = 0; c < g_prof.n_calls && st == RPA_OK; ++c) {
+    const hipEvent_t* e = &g_prof.ev[kProfEvents * c];
+    const int from[4] = {0, 1, 2, 0}, to[4] = {1, 2, 3, 3};
     for (int k = 0; k < 4; ++k) {
       float ms = 0.f;
-      if (hipEventElapsedTime(&ms, g_prof.ev[kProfEvents * c + k], g_prof.ev[kProfEvents * c + k + 1]) !=
-          hipSuccess) {
+      if (hipEventElapsedTime(&ms, e[from[k]], e[to[k]]) != hipSuccess) {
         st = RPA_ERR_HIP;
         break;
       }

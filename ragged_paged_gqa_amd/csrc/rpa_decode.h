@@ -703,15 +703,6 @@ __device__ __forceinline__ void decode_tiles(const Params& p, char* lds, int blo
   }
 }
 
-// The decode-class tiles in a launch of their own (one workgroup per
-// decode-workgroup index).
-template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
-__global__ __launch_bounds__(kDecWavesPerBlock * 64, dec_waves_per_simd(D, KVT != kKvBf16)) void decode_kernel(
-    Params p) {
-  __shared__ __attribute__((aligned(1024))) char lds[kDecWavesPerBlock * DecCfg<D, KVT != kKvBf16>::WAVE_LDS];
-  decode_tiles<D, KVT, CAP, F16, Q32>(p, lds, blockIdx.x);
-}
-
 // Merges the split decode-class units once every decode wave is done: one
 // wave per unit (decode sequence u / Hkv, kv head u % Hkv), the parts'
 // partials combined by merge_unit in block order; a unit with no key to see

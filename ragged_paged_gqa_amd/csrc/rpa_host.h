@@ -36,7 +36,7 @@ struct Layout {
   int32_t max_du, max_pu, max_pi, dec_slots, tgt_p, pf_rows, dec_waves;
 };
 
-// The prefill class of `c` runs on prefill_pp_kernel.
+// The prefill class of `c` runs on the two-group tiles (tiles_pp_kernel).
 bool uses_pp(const rpa_config* c);
 
 // Workgroups of the decode launch on a device with `cus` compute units.

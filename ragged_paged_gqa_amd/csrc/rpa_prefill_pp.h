@@ -54,8 +54,19 @@ struct PpLds {
   static constexpr size_t kBytes = (size_t)kPpStages * kSlot;
 };
 
+// LDS of one workgroup of prefill_pp_tiles.
+template <int D>
+struct PpShared {
+  char lds[PpLds<D>::kBytes];  // the K/V ring (and the merge's staging)
+  uint32_t blk[kPfBlkTable];   // physical key index of each 16-key block of the item
+  int item[2];
+  int last;
+};
+
+// The prefill-class tiles of one eight-wave workgroup: it takes items from
+// the queues until they are empty.
 template <int D, bool CAP, bool F16>
-__global__ __launch_bounds__(kPpWaves * 64, 1) void prefill_pp_kernel(Params p) {
+__device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& shm) {
   constexpr int NW = kPpWaves;
   constexpr int NT = NW * 64;
   constexpr int NS = D / 16;    // k-steps of the QK product
@@ -73,10 +84,10 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void prefill_pp_kernel(Params p) 
   static_assert(RPI * CPR == 64 && NIW * RPI == 8, "whole rows per DMA instruction");
   static_assert(kPpStages >= kPpLead + 2, "a slot is refilled once both groups are past its PV");
 
-  __shared__ __attribute__((aligned(16))) char lds[PpLds<D>::kBytes];
-  __shared__ uint32_t sh_blk[kPfBlkTable];  // physical key index of each 16-key block of the item
-  __shared__ int sh_item[2];
-  __shared__ int sh_last;
+  char* const lds = shm.lds;
+  uint32_t* const sh_blk = shm.blk;
+  int* const sh_item = shm.item;
+  int& sh_last = shm.last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
