@@ -258,6 +258,35 @@ __device__ __forceinline__ void store_coherent4(float* dst, f32x4 v) {  // dst 1
 __device__ __forceinline__ float load_coherent(const float* src) {
   return __hip_atomic_load(const_cast<float*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The next prefill-class item for a workgroup (called by one thread): this
+// XCD's queue first (`home`), then the others in turn; -1 once all are
+// drained. `qsel` counts the queues this workgroup has found drained. While
+// the home queue lasts an item costs one atomic. After that the heads are
+// read together (relaxed, device scope: one round trip), and only queues
+// that still look non-empty take an atomic: a head only grows, and all eight
+// share one cache line, where an atomic from every workgroup on every
+// drained queue would queue up behind each other while items remain.
+__device__ inline int take_item(const Params& p, int home, int& qsel) {
+  if (qsel == 0) {
+    const int k = atomicAdd(&p.hdr->pf_q_next[home], 1);
+    if (k < p.hdr->pf_q_count[home]) return p.pf_qlist[p.hdr->pf_q_base[home] + k];
+    qsel = 1;
+  }
+  uint32_t live = 0;  // queues whose head was below their length when read
+#pragma unroll
+  for (int x = 0; x < kQueues; ++x) {
+    const int head = __hip_atomic_load(&p.hdr->pf_q_next[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    live |= (uint32_t)(head < p.hdr->pf_q_count[x]) << x;
+  }
+  for (; qsel < kQueues; ++qsel) {
+    const int x = (home + qsel) % kQueues;
+    if (!((live >> x) & 1u)) continue;
+    const int k = atomicAdd(&p.hdr->pf_q_next[x], 1);
+    if (k < p.hdr->pf_q_count[x]) return p.pf_qlist[p.hdr->pf_q_base[x] + k];
+  }
+  return -1;
+}
 __device__ __forceinline__ f32x2 load_coherent2(const float* src) {  // src 8-byte aligned
   unsigned long long* s = reinterpret_cast<unsigned long long*>(const_cast<float*>(src));
   return __builtin_bit_cast(f32x2, __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));

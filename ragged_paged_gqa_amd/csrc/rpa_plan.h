@@ -36,6 +36,8 @@
 // reciprocal.
 #pragma once
 
+#include <climits>
+
 #include "rpa_common.h"
 
 namespace rpa {
@@ -107,6 +109,50 @@ __device__ __forceinline__ void seq_meta(const Params& p, int32_t s, int32_t& ql
   kvl = kvl < 0 ? 0 : (kvl > cap ? cap : kvl);
 }
 
+// Wave-wide scans and reductions with DPP lane moves (VALU operations): a
+// shift by 1, 2, 4 and 8 lanes inside each row of 16, then row 0's last lane
+// added into row 1 and row 2's into row 3, then lane 31 into rows 2 and 3.
+// Lanes whose source falls outside take the identity.
+template <typename Op>
+__device__ __forceinline__ int32_t dpp_incl_scan(int32_t v, int32_t ident, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  return dpp_incl_scan(v, 0, [](int32_t a, int32_t b) { return a + b; });
+}
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+  return __builtin_amdgcn_readlane(dpp_incl_scan(v, INT_MIN, [](int32_t a, int32_t b) { return max(a, b); }), 63);
+}
+// one DPP lane move of a 64-bit value (both halves)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int64_t dpp_move64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const int32_t lo = __builtin_amdgcn_update_dpp(0, (int32_t)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+  const int32_t hi = __builtin_amdgcn_update_dpp(0, (int32_t)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+  v += dpp_move64<0x111, 0xf>(v);
+  v += dpp_move64<0x112, 0xf>(v);
+  v += dpp_move64<0x114, 0xf>(v);
+  v += dpp_move64<0x118, 0xf>(v);
+  v += dpp_move64<0x142, 0xa>(v);
+  v += dpp_move64<0x143, 0xc>(v);
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readlane((int32_t)(uint32_t)u, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int32_t)(uint32_t)(u >> 32), 63);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Block-wide exclusive scan of NV ints per thread at once: excl[k] gets the
 // sum of v[k] over lower threads, tot[k] the block total. `sh` holds
 // kPlanWaves * NV ints.
@@ -115,15 +161,7 @@ __device__ void block_scan(const int32_t (&v)[NV], int32_t (&excl)[NV], int32_t 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t x[NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) x[k] = v[k];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int32_t y = __shfl_up(x[k], o);
-      if (lane >= o) x[k] += y;
-    }
-  }
+  for (int k = 0; k < NV; ++k) x[k] = wave_incl_scan(v[k]);
   if (lane == 63) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) sh[wave * NV + k] = x[k];
@@ -132,6 +170,7 @@ __device__ void block_scan(const int32_t (&v)[NV], int32_t (&excl)[NV], int32_t 
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     int32_t before = 0, all = 0;
+#pragma unroll
     for (int w = 0; w < kPlanWaves; ++w) {
       const int32_t t = sh[w * NV + k];
       before += w < wave ? t : 0;
@@ -141,31 +180,6 @@ __device__ void block_scan(const int32_t (&v)[NV], int32_t (&excl)[NV], int32_t 
     tot[k] = all;
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int32_t wave_max(int32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  return v;
 }
 
 // Decode waves given work where one launch holds both classes' workgroups
@@ -291,8 +305,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) pf_keys += __shfl_xor(pf_keys, o);
+  pf_keys = wave_sum64(pf_keys);
   if (lane == 0) red[wave] = pf_keys;
   __syncthreads();
   int64_t tot_pf = 0;
@@ -386,6 +399,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       if (slot >= 0) {
         const int64_t wk = pf_info[slot].work;
         int32_t r = 0;
+#pragma unroll 4
         for (int32_t j = 0; j < n_pf_tile; ++j) {
           const int64_t wj = pf_info[j].work;
           r += wj > wk || (wj == wk && pf_info[j].s < s);
@@ -397,6 +411,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
       if (slot >= 0) {
         const int32_t ck = pf_info[slot].lcls, rk = rank_of[slot];
         int32_t rb = 0;
+#pragma unroll 4
         for (int32_t j = 0; j < n_pf_tile; ++j) {
           const int32_t cj = pf_info[j].lcls;
           rb += cj > ck || (cj == ck && rank_of[j] < rk);
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
         }
         const int32_t incl = wave_incl_scan(nch);
         const int32_t item_off = carry + incl - nch;
-        carry += __shfl(incl, 63);
+        carry += __builtin_amdgcn_readlane(incl, 63);
         if (rb < nrb) {
           for (int32_t h = 0; h < p.Hkv; ++h) {
             const int32_t ui = unit0 + h * nrb + rb;
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
           }
           const int32_t incl = wave_incl_scan(nch);
           const int32_t item_off = carry_items + incl - nch;
-          carry_items += __shfl(incl, 63);
+          carry_items += __builtin_amdgcn_readlane(incl, 63);
           const bool in_a = c < nch - 1, in_b = c == nch - 1;
           const uint64_t ma = __ballot(in_a), mb = __ballot(in_b);
           const uint64_t below = (1ull << lane) - 1ull;

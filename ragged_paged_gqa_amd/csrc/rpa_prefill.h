@@ -120,7 +120,7 @@ struct PfShared {
 // until they are empty. CAP: the soft-cap is on (a template parameter, so the
 // uncapped code's block loop has no branch and no cap arithmetic).
 template <int D, int KVT, bool CAP, bool F16, bool Q32 = false>
-__device__ __forceinline__ void prefill_tiles(const Params& p, PfShared<D, KVT != kKvBf16>& shm) {
+__device__ __forceinline__ void prefill_tiles(const Params& p, PfShared<D, KVT != kKvBf16>& shm, int pf_block) {
   static_assert(!(Q32 && F16), "an f32 q runs on the bf16 path");
   constexpr bool FP8 = KVT != kKvBf16;  // one-byte codes (fp8 kinds, int8), widened in registers
   // f16 P must stay below 65504: exponentiated scores <= 2^15
@@ -164,7 +164,9 @@ __device__ __forceinline__ void prefill_tiles(const Params& p, PfShared<D, KVT !
   const int r32 = lane & 31;  // S^T column = row within a 32-row half
   const int h = lane >> 5;    // which half of the row's keys this lane holds
 
-  if (p.hdr->n_pf_items == 0) return;  // nothing of this class in the batch
+  // Every item goes to one workgroup, so workgroups past the item count
+  // would only ever find the queues drained: they leave at once.
+  if (pf_block >= p.hdr->n_pf_items) return;
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * EB;
   constexpr bool capped = CAP;
@@ -220,15 +222,7 @@ __device__ __forceinline__ void prefill_tiles(const Params& p, PfShared<D, KVT !
   // queues: start with this XCD's, then steal from the others in turn
   const int home = xcc_id() % kQueues;
   int qsel = 0;  // used by thread 0 only
-  auto next_item = [&]() -> int {
-    while (qsel < kQueues) {
-      const int x = (home + qsel) % kQueues;
-      const int k = atomicAdd(&p.hdr->pf_q_next[x], 1);
-      if (k < p.hdr->pf_q_count[x]) return p.pf_qlist[p.hdr->pf_q_base[x] + k];
-      ++qsel;
-    }
-    return -1;
-  };
+  auto next_item = [&]() { return take_item(p, home, qsel); };
 
   int parity = 0;
   for (;;) {

@@ -66,7 +66,7 @@ struct PpShared {
 // The prefill-class tiles of one eight-wave workgroup: it takes items from
 // the queues until they are empty.
 template <int D, bool CAP, bool F16>
-__device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& shm) {
+__device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& shm, int pf_block) {
   constexpr int NW = kPpWaves;
   constexpr int NT = NW * 64;
   constexpr int NS = D / 16;    // k-steps of the QK product
@@ -96,7 +96,9 @@ __device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& s
   const int r32 = lane & 31;  // S^T column = this lane's row within the wave's 32
   const int h = lane >> 5;    // which 16 of the row's 32 keys this lane holds
 
-  if (p.hdr->n_pf_items == 0) return;  // nothing of this class in the batch
+  // Every item goes to one workgroup, so workgroups past the item count
+  // would only ever find the queues drained: they leave at once.
+  if (pf_block >= p.hdr->n_pf_items) return;
   const int chunk = p.hdr->pf_chunk;
   const int64_t key_stride = (int64_t)2 * p.Hkv * D * 2;
   // Scores in base-2 units are s * cmul (capped: the cap is applied first and
@@ -152,15 +154,7 @@ __device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& s
   // queues: this XCD's first, then the others in turn
   const int home = xcc_id() % kQueues;
   int qsel = 0;  // thread 0 only
-  auto next_item = [&]() -> int {
-    while (qsel < kQueues) {
-      const int x = (home + qsel) % kQueues;
-      const int k = atomicAdd(&p.hdr->pf_q_next[x], 1);
-      if (k < p.hdr->pf_q_count[x]) return p.pf_qlist[p.hdr->pf_q_base[x] + k];
-      ++qsel;
-    }
-    return -1;
-  };
+  auto next_item = [&]() { return take_item(p, home, qsel); };
 
   int parity = 0;
   for (;;) {

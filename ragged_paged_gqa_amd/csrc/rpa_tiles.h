@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64, tiles_waves_per_simd(D, KVT
   if ((int)blockIdx.x < dec_wgs)
     decode_tiles<D, KVT, CAP, F16, Q32>(p, lds, blockIdx.x);
   else
-    prefill_tiles<D, KVT, CAP, F16, Q32>(p, *reinterpret_cast<PfShared<D, FP8>*>(lds));
+    prefill_tiles<D, KVT, CAP, F16, Q32>(p, *reinterpret_cast<PfShared<D, FP8>*>(lds), blockIdx.x - dec_wgs);
 }
 
 // The same for the two-group prefill kernel's configurations (16-bit K/V in
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void tiles_pp_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char lds[kDec > kPf ? kDec : kPf];
   const int dec_wgs = p.dec_waves / kDecWavesPerBlock;
   if ((int)blockIdx.x >= dec_wgs) {
-    prefill_pp_tiles<D, CAP, F16>(p, *reinterpret_cast<PpShared<D>*>(lds));
+    prefill_pp_tiles<D, CAP, F16>(p, *reinterpret_cast<PpShared<D>*>(lds), blockIdx.x - dec_wgs);
   } else if (threadIdx.x < kDecWavesPerBlock * 64) {
     decode_tiles<D, kKvBf16, CAP, F16, false>(p, lds, blockIdx.x);
   }
