@@ -61,8 +61,8 @@ int dec_grid_for(const rpa_config* c, int cus) {
   }
 }
 
-// The prefill class of `c` runs on prefill_pp_kernel: 16-bit q with K/V in
-// the q type.
+// The prefill class of `c` runs on the two-group tiles (prefill_pp_tiles in
+// tiles_pp_kernel): 16-bit q with K/V in the q type.
 bool uses_pp(const rpa_config* c) {
   return (c->q_dtype == RPA_DTYPE_BF16 || c->q_dtype == RPA_DTYPE_F16) && c->kv_dtype == c->q_dtype &&
          c->head_dim >= RPA_PP_MIN_D && c->head_dim <= RPA_PP_MAX_D;
