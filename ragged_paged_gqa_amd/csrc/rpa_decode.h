@@ -750,10 +750,13 @@ __global__ __launch_bounds__(kDecWavesPerBlock * 64) void combine_kernel(Params 
     U.nch = l - f + 1;
     U.item0 = 0;
     // part c ran on wave f + c: the first in slot 2f + 1, the others in 2(f + c)
-    merge_unit<D, F16, Q32, true>(p, U, p.dec_part, p.dec_plse, kDecRows,
-                            [&](int c) { return c == 0 ? 2 * f + 1 : 2 * (f + c); }, lane, 64, stat[wave],
-                            wave_sync);
-    wave_sync();
+    auto slot = [&](int c) { return c == 0 ? 2 * f + 1 : 2 * (f + c); };
+    if (U.nch <= 4) {
+      merge_unit_small<D, F16, Q32, 4>(p, U, p.dec_part, p.dec_plse, kDecRows, slot, lane, 64);
+    } else {
+      merge_unit<D, F16, Q32, true>(p, U, p.dec_part, p.dec_plse, kDecRows, slot, lane, 64, stat[wave], wave_sync);
+      wave_sync();
+    }
   }
 }
 

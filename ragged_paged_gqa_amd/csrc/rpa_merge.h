@@ -122,4 +122,62 @@ __device__ void merge_unit(const Params& p, const Unit& u, const float* part, co
   }
 }
 
+// The same merge for a unit of at most NMAX chunks, in one pass: every
+// thread takes (row, 4-element piece) items and loads all the chunks' LSEs
+// and partial pieces at once, so the merge costs one round of coherent loads
+// instead of two with a synchronisation between them. The sums run in chunk
+// order as above, so both versions give the same bits.
+template <int D, bool F16, bool Q32, int NMAX, typename Slot>
+__device__ void merge_unit_small(const Params& p, const Unit& u, const float* part, const float* plse, int slot_rows,
+                                 Slot slot, int tid, int nt) {
+  int q0, ql;
+  seq_tokens(p, u.seq, q0, ql);
+  constexpr int PIECES = D / 4;
+  for (int idx = tid; idx < u.nrows * PIECES; idx += nt) {
+    const int r = idx / PIECES;
+    const int e0 = 4 * (idx % PIECES);
+    const int prow = u.row0 + r;
+    const int t = prow / p.G;
+    const int qh = u.kv_head * p.G + (prow - t * p.G);
+    float l[NMAX];
+    f32x2 a[NMAX], b[NMAX];
+#pragma unroll
+    for (int k = 0; k < NMAX; ++k) {
+      if (k < u.nch) {
+        const float* src = part + ((int64_t)slot(k) * slot_rows + r) * D + e0;
+        l[k] = load_coherent(plse + (int64_t)slot(k) * slot_rows + r);
+        a[k] = load_coherent2(src);
+        b[k] = load_coherent2(src + 2);
+      }
+    }
+    const float sink = p.sinks ? p.sinks[qh] : -INFINITY;
+    float mx = sink;
+#pragma unroll
+    for (int k = 0; k < NMAX; ++k)
+      if (k < u.nch) mx = fmaxf(mx, l[k]);
+    float wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < NMAX; ++k)
+        if (k < u.nch) wsum += expf(l[k] - mx);
+      if (sink != -INFINITY) wsum += expf(sink - mx);
+#pragma unroll
+      for (int k = 0; k < NMAX; ++k) {
+        if (k < u.nch) {
+          const float w = expf(l[k] - mx);
+          acc[0] += w * a[k][0];
+          acc[1] += w * a[k][1];
+          acc[2] += w * b[k][0];
+          acc[3] += w * b[k][1];
+        }
+      }
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    store_out4<F16, Q32>(p.out, ((int64_t)(q0 + t) * p.Hq + qh) * D + e0, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+                         acc[3] * inv);
+    if (e0 == 0 && p.lse) p.lse[(int64_t)(q0 + t) * p.Hq + qh] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
+  }
+}
+
 }  // namespace rpa
