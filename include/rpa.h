@@ -244,12 +244,14 @@ rpa_status rpa_plan(const rpa_config* cfg, const int32_t* kv_lens, const int32_t
  *   offsets[1] decode sequences int32[max_num_seqs][8]
  *   offsets[2] prefill units    int32[max_pf_units][8]
  *   offsets[3] 0 (reserved)
- *   offsets[4] prefill items    int32[max_pf_items][2]
+ *   offsets[4] prefill items    int32[max_pf_items][16]
  *   offsets[5] queue list       int32[8][max_pf_items] (prefill item indices)
  *   offsets[6], offsets[7] 0 (reserved)
  * A prefill unit is {seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0}. A
- * prefill item is {unit, chunk}, covering keys [kv_lo + chunk*C,
- * min(kv_hi, kv_lo + (chunk+1)*C)) with C = pf_chunk. A decode sequence
+ * prefill item is {unit, chunk, the unit's 8 ints, q0, ql, kv_len, 3 pad}
+ * (the sequence's first query token, query tokens and kv length, clamped),
+ * covering keys [kv_lo + chunk*C, min(kv_hi, kv_lo + (chunk+1)*C)) with
+ * C = pf_chunk. A decode sequence
  * record is {seq, q0, q_len, kv_len, kv_lo, kv_hi, blk0, nb}, one per
  * sequence with 1 <= q_len * Hq/Hkv <= 16, in sequence order: its units are
  * (seq, h) for every kv head h, all q_len * Hq/Hkv rows, keys [kv_lo, kv_hi)

@@ -233,6 +233,16 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
   return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
+// Scalar (SMEM) loads of metadata the kernel never writes: page-table entries
+// and sequence records go to scalar registers through the scalar cache and
+// never wait on (or make anything wait on) the K/V stream.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ int sload(const int32_t* ptr) { return *(cint32*)(ptr); }
+
+// A prefill item's record: one 64-byte load (the same address on every
+// lane). The planning kernel wrote it before this launch.
+__device__ __forceinline__ Item load_item(const Params& p, int item) { return p.pf_items[item]; }
+
 // Index of the XCD (accelerator complex die) this wave runs on.
 __device__ __forceinline__ int xcc_id() {
   int v;

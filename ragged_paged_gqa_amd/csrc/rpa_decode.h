@@ -102,11 +102,6 @@ __device__ __forceinline__ int slot_d(int i, int g) {
   return FP8 ? 64 * (i >> 1) + 16 * g + 8 * (i & 1) : 32 * i + 8 * g;
 }
 
-// Scalar (SMEM) loads of metadata the kernel never writes: page-table entries
-// and sequence records go to scalar registers through the scalar cache and
-// never wait on (or make anything wait on) the K/V stream.
-typedef const __attribute__((address_space(4))) int32_t cint32;
-__device__ __forceinline__ int sload(const int32_t* ptr) { return *(cint32*)(ptr); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <bool F16>

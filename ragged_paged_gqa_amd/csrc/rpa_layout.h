@@ -42,10 +42,18 @@ struct Unit {
 };
 static_assert(sizeof(Unit) == 32, "unit record is int32[8]");
 
+// A prefill item: chunk `chunk` of unit `unit`, with a copy of the unit's
+// record and of its sequence's metadata, so that a workgroup starting the item
+// reads one 64-byte record (instead of the item, then the unit, then the
+// sequence: three round trips to memory).
 struct Item {
   int32_t unit;
   int32_t chunk;
+  int32_t seq, kv_head, row0, nrows, kv_lo, kv_hi, nch, item0;  // the unit's record (Unit)
+  int32_t q0, ql, kvl;  // the sequence's first query token, query tokens, kv length (clamped to the table)
+  int32_t pad[3];
 };
+static_assert(sizeof(Item) == 64, "item record is int32[16]");
 
 // Decode-class work is scheduled stream-K style: the key blocks (kDecBlk
 // keys) of all decode units, laid end to end in (sequence, kv head) order, are cut into

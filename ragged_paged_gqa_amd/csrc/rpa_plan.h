@@ -479,8 +479,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     for (int32_t i = wave; i < n_pf_tile; i += kPlanWaves) {
       const PfInfo f = pf_info[i];
       const int32_t ps = f.s;
-      int32_t pql, pkvl;
+      int32_t pql, pkvl, pq0, pql_t;
       seq_meta(p, ps, pql, pkvl);
+      seq_tokens(p, ps, pq0, pql_t);
       const int32_t rows = pql * p.G;
       const int32_t nrb = (rows + R - 1) / R;
       const int32_t unit0 = pf_offs[i].unit, item0 = pf_offs[i].item;
@@ -512,7 +513,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
             p.pf_units[ui] = u;
             p.unit_done[ui] = 0;
             for (int32_t c = 0; c < nch; ++c)
-              if (ii + c < p.max_pf_items) p.pf_items[ii + c] = Item{ui, c};
+              if (ii + c < p.max_pf_items)
+                p.pf_items[ii + c] = Item{ui, c, ps, h, r0, nr, r.lo16, r.hi, nch, ii, pq0, pql, pkvl, {0, 0, 0}};
           }
         }
       }

@@ -164,14 +164,21 @@ __device__ __forceinline__ void prefill_pp_tiles(const Params& p, PpShared<D>& s
     parity ^= 1;
     if (item < 0) break;
 
-    const Item it = p.pf_items[item];
-    const Unit u = p.pf_units[it.unit];
+    // the item's record, which carries
+    // its unit's record and its sequence's metadata
+    const Item it = load_item(p, item);
+    Unit u;
+    u.seq = it.seq;
+    u.kv_head = it.kv_head;
+    u.row0 = it.row0;
+    u.nrows = it.nrows;
+    u.kv_lo = it.kv_lo;
+    u.kv_hi = it.kv_hi;
+    u.nch = it.nch;
+    u.item0 = it.item0;
     const int s = u.seq;
     const int kvh = u.kv_head;
-    int q0, ql;
-    seq_tokens(p, s, q0, ql);
-    int kvl = p.kv_lens[s];
-    kvl = max(0, min(kvl, p.pps * p.page));
+    const int q0 = it.q0, ql = it.ql, kvl = it.kvl;
     const int c_lo = u.kv_lo + it.chunk * chunk;
     const int c_hi = min(u.kv_hi, c_lo + chunk);
     const int N = c_hi > c_lo ? (c_hi - c_lo + kStepKeys - 1) / kStepKeys : 0;  // 32-key steps

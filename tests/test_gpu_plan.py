@@ -32,7 +32,8 @@ def _plan(w):
     # decode sequence records: seq, q0, ql, kvl, lo16, hi, blk0, nb
     ds = host[offs[1]:offs[1] + 32 * n_ds].view(np.int32).reshape(n_ds, 8)
     pu = host[offs[2]:offs[2] + 32 * n_pu].view(np.int32).reshape(n_pu, 8)
-    pi = host[offs[4]:offs[4] + 8 * n_pi].view(np.int32).reshape(n_pi, 2)
+    # item records: unit, chunk, the unit's record (8 ints), q0, ql, kvl, 3 pad
+    pi = host[offs[4]:offs[4] + 64 * n_pi].view(np.int32).reshape(n_pi, 16)
     qbase, qcount, qnext = hdr[16:24].copy(), hdr[24:32].copy(), hdr[32:40].copy()
     ql = host[offs[5]:offs[5] + 4 * 8 * int(lim[3])].view(np.int32)
     return dict(n_du=n_du, ds=ds, pu=pu, pi=pi, pch=pch, lim=lim, qbase=qbase, qcount=qcount, qnext=qnext,
@@ -189,7 +190,11 @@ def _check(w):
         assert nch == max(1, -(-(hi - lo) // ch))
         for k in range(nch):
             seen_items[it0 + k] += 1
-            assert tuple(items[it0 + k]) == (ui, k)
+            rec = items[it0 + k]
+            assert tuple(rec[:2]) == (ui, k)
+            # the copy of the unit's record and of the sequence's metadata
+            assert tuple(rec[2:10]) == (s, h, r0, nr, lo, hi, nch, it0)
+            assert tuple(rec[10:13]) == (q0, ql, kvl)
             a, b = lo + k * ch, min(hi, lo + (k + 1) * ch)
             assert a < b or (nch == 1 and hi <= lo)
     assert np.all(seen_items == 1)
