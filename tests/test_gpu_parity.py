@@ -135,11 +135,14 @@ def test_medium_cases_split(case):
     if case["name"].startswith("pf"):
         assert n_split_pf > 0
     else:
-        # some unit's blocks fall into the ranges of two waves
+        # some unit's blocks fall into the ranges of two to four waves (the
+        # combine kernel's one-pass merge) and some into more (its batched one)
         ds = host[offs[1]:offs[1] + 32 * int(hdr[2])].view(np.int32).reshape(-1, 8)
         wave = lambda b: np.searchsorted((Tb * np.arange(W + 1, dtype=np.int64)) // W, b, side="right") - 1
-        assert any(wave(int(r[6]) + h * int(r[7])) != wave(int(r[6]) + (h + 1) * int(r[7]) - 1)
-                   for r in ds if int(r[7]) > 0 for h in range(case["Hkv"]))
+        parts = [wave(int(r[6]) + (h + 1) * int(r[7]) - 1) - wave(int(r[6]) + h * int(r[7])) + 1
+                 for r in ds if int(r[7]) > 0 for h in range(case["Hkv"])]
+        assert any(2 <= n <= 4 for n in parts), parts
+        assert any(n > 4 for n in parts), parts
 
 
 def test_padding_rows_untouched_and_empty_sequences():
