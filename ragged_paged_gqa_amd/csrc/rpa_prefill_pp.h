@@ -42,7 +42,7 @@ constexpr int kPpLead = 2;    // steps between a slot's DMA and its first reader
 #define RPA_PP_KA 3
 #endif
 #ifndef RPA_PP_VA
-#define RPA_PP_VA 3
+#define RPA_PP_VA 4  // (3: 0.6 % slower on the long-context workload; 5 and 6 slower still)
 #endif
 
 template <int D>
